@@ -1,0 +1,747 @@
+// C-ABI layer of libgpt.so: argument validation, workspace layout, the
+// paged KV-cache handle and the prefill / decode drivers that enqueue the
+// gfx950 kernels.  No device memory is allocated here; every device buffer
+// belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "../../include/gpt_profile.h"
+#include "../../include/gpt_debug.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+gpt_status fail(gpt_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+gpt_status hip_check(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return GPT_OK;
+}
+
+constexpr int kMaxPrefillSeqs = 512;
+constexpr int kPage = 64;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ------------------------------------------------------------------ profiler
+
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Profiler {
+  uint32_t mask = 0;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    hipEventCreate(&e);
+    return e;
+  }
+  void reset() {
+    for (auto &r : recs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    recs.clear();
+  }
+} g_prof;
+
+// Brackets one launch with events when its class is enabled.
+struct Timed {
+  int cls;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  double flops, bytes;
+  Timed(int c, hipStream_t st, double f, double by) : cls(c), s(st), flops(f), bytes(by) {
+    if (g_prof.mask & (1u << cls)) {
+      a = g_prof.get();
+      hipEventRecord(a, s);
+    }
+  }
+  ~Timed() {
+    if (!a) return;
+    hipEvent_t b = g_prof.get();
+    hipEventRecord(b, s);
+    g_prof.recs.push_back({cls, a, b, flops, bytes});
+  }
+};
+
+// ------------------------------------------------------------------ config
+
+gpt_status check_config(const gpt_config *c) {
+  if (!c) return fail(GPT_ERR_ARG, "config is NULL");
+  if (c->vocab <= 0 || c->n_layer <= 0 || c->d_model <= 0 || c->n_head <= 0 ||
+      c->n_kv_head <= 0 || c->head_dim <= 0 || c->d_ff <= 0 || c->max_seq <= 0)
+    return fail(GPT_ERR_ARG, "config sizes must be positive");
+  if (c->n_head % c->n_kv_head) return fail(GPT_ERR_ARG, "n_head must be a multiple of n_kv_head");
+  if (c->pos_kind != GPT_POS_LEARNED && c->pos_kind != GPT_POS_ROPE)
+    return fail(GPT_ERR_ARG, "pos_kind must be 0 or 1");
+  if (c->act != GPT_ACT_RELU && c->act != GPT_ACT_RELU2) return fail(GPT_ERR_ARG, "act must be 0 or 1");
+  if (c->qk_norm != 0 && c->qk_norm != 1) return fail(GPT_ERR_ARG, "qk_norm must be 0 or 1");
+  if (c->dtype != GPT_DTYPE_F32 && c->dtype != GPT_DTYPE_BF16) return fail(GPT_ERR_ARG, "dtype must be 0 or 1");
+  if (!(c->norm_eps >= 0.f)) return fail(GPT_ERR_ARG, "norm_eps must be >= 0");
+  if (c->pos_kind == GPT_POS_ROPE && !(c->rope_base > 0.f)) return fail(GPT_ERR_ARG, "rope_base must be > 0");
+  if (c->pos_kind == GPT_POS_ROPE && (c->head_dim & 1)) return fail(GPT_ERR_ARG, "RoPE needs an even head_dim");
+  if (c->dtype == GPT_DTYPE_BF16) {
+    if (c->head_dim != 128) return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs head_dim 128");
+    if (c->n_kv_head != 1) return fail(GPT_ERR_UNSUPPORTED, "bf16 path implements one K/V head (MQA)");
+    if (c->n_head > 16) return fail(GPT_ERR_UNSUPPORTED, "bf16 path supports at most 16 query heads");
+    if (c->pos_kind != GPT_POS_ROPE) return fail(GPT_ERR_UNSUPPORTED, "bf16 path uses rotary positions");
+    if (c->act != GPT_ACT_RELU2) return fail(GPT_ERR_UNSUPPORTED, "bf16 path uses the ReLU^2 MLP");
+    if (c->d_model % 128 || c->d_ff % 128 || c->vocab % 128)
+      return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs d_model, d_ff, vocab multiples of 128");
+  } else {
+    if (c->head_dim > 64) return fail(GPT_ERR_UNSUPPORTED, "fp32 path needs head_dim <= 64");
+    if (c->d_model % 4 || c->d_model > 4096) return fail(GPT_ERR_UNSUPPORTED, "fp32 path needs d_model % 4 == 0, <= 4096");
+  }
+  if (c->d_model != c->n_head * c->head_dim && c->dtype == GPT_DTYPE_BF16)
+    return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs d_model == n_head * head_dim");
+  return GPT_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+
+struct Bufs {
+  int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
+  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits;
+  void *h, *q, *k, *vt, *o, *u;
+  long long ldvt;
+  int max_splits;
+};
+
+size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs *b) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char * {
+    off = align256(off);
+    char *p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  const long long d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim;
+  const size_t es = c->dtype == GPT_DTYPE_BF16 ? 2 : 4;
+  Bufs t{};
+  t.cu = (int *)take((nseq + 1) * 4);
+  t.cu_pad = (int *)take((nseq + 1) * 4);
+  t.lastrows = (int *)take(nseq * 4);
+  t.seq = (int *)take(M * 4);
+  t.pos = (int *)take(M * 4);
+  t.vcol = (int *)take(M * 4);
+  t.x = (float *)take(M * d * 4);
+  t.h = take(M * d * es);
+  t.qkv = (float *)take(M * (H + 2 * Hkv) * dh * 4);
+  t.q = take(M * H * dh * es);
+  t.k = take(M * Hkv * dh * es);
+  t.ldvt = ((M + kPage * nseq) + 63) / 64 * 64;
+  if (c->dtype == GPT_DTYPE_BF16) t.vt = take(Hkv * dh * t.ldvt * es);
+  else t.vt = take(M * Hkv * dh * es);
+  t.o = take(M * H * dh * es);
+  t.u = take(M * (long long)c->d_ff * es);
+  t.lse_tmp = (float *)take(M * 4);
+  t.max_splits = (c->max_seq + kDecodeChunk - 1) / kDecodeChunk;
+  t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
+  t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
+  t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
+  if (b) *b = t;
+  return align256(off);
+}
+
+// ------------------------------------------------------------------ weights
+
+gpt_status check_weights(const gpt_config *c, const gpt_weights *w) {
+  if (!w) return fail(GPT_ERR_ARG, "weights is NULL");
+  if (!w->wte || !w->lm_head) return fail(GPT_ERR_ARG, "wte and lm_head are required");
+  if (c->pos_kind == GPT_POS_LEARNED && !w->wpe) return fail(GPT_ERR_ARG, "wpe is required for learned positions");
+  if (!w->wq || !w->wk || !w->wv || !w->wo || !w->w1 || !w->w2)
+    return fail(GPT_ERR_ARG, "per-layer weight arrays are required");
+  const void *all[3] = {w->wte, w->lm_head, w->wpe};
+  for (const void *p : all)
+    if (p && !aligned16(p)) return fail(GPT_ERR_ARG, "weights must be 16-byte aligned");
+  for (int l = 0; l < c->n_layer; ++l) {
+    const void *lp[6] = {w->wq[l], w->wk[l], w->wv[l], w->wo[l], w->w1[l], w->w2[l]};
+    for (const void *p : lp) {
+      if (!p) return fail(GPT_ERR_ARG, "layer %d has a NULL weight", l);
+      if (!aligned16(p)) return fail(GPT_ERR_ARG, "layer %d weight not 16-byte aligned", l);
+    }
+  }
+  return GPT_OK;
+}
+
+// ------------------------------------------------------------------ prefill metadata
+
+struct PrefillMeta {
+  int n;
+  int cu[kMaxPrefillSeqs + 1];
+};
+
+__global__ void prefill_meta_kernel(PrefillMeta m, int *cu, int *cu_pad, int *lastrows) {
+  for (int i = threadIdx.x; i <= m.n; i += blockDim.x) cu[i] = m.cu[i];
+  if (lastrows)
+    for (int i = threadIdx.x; i < m.n; i += blockDim.x) lastrows[i] = m.cu[i + 1] - 1;
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int i = 0; i < m.n; ++i) {
+      cu_pad[i] = acc;
+      acc += (m.cu[i + 1] - m.cu[i] + 63) / 64 * 64;
+    }
+    cu_pad[m.n] = acc;
+  }
+}
+
+GemmArgs gemm(const void *A, long long lda, const void *W, int M, int N, int K, void *C, long long ldc,
+              int epi) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W0 = g.W1 = g.W2 = W;
+  g.n1 = g.n2 = N;
+  g.ldw = K;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.C = C;
+  g.ldc = ldc;
+  g.epi = epi;
+  return g;
+}
+
+void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
+  const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
+  double out_b = g.epi == EPI_RESID ? 8.0 : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16) ? es : 4.0;
+  bool skinny = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
+  Timed t(skinny && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
+          es * ((double)g.M * g.K + (double)g.N * g.K) + out_b * g.M * g.N);
+  if (c->dtype == GPT_DTYPE_F32) launch_gemm_f32(g, s);
+  else if (skinny) launch_gemm_bf16_skinny(g, s);
+  else launch_gemm_bf16(g, s);
+}
+
+PagedKV paged_view(const gpt_kv_cache *kv);
+
+}  // namespace
+
+// ------------------------------------------------------------------ KV cache handle
+
+struct gpt_kv_cache {
+  gpt_config cfg;
+  int n_seqs, capacity, page_size, pps;
+  char *buf;
+  size_t bytes, table_off, lens_off;
+  long long layer_stride, page_stride, half_bytes;
+  std::vector<int> lens;
+};
+
+namespace {
+PagedKV paged_view(const gpt_kv_cache *kv) {
+  PagedKV p{};
+  p.base = kv->buf;
+  p.table = (const int *)(kv->buf + kv->table_off);
+  p.lens = (int *)(kv->buf + kv->lens_off);
+  p.layer_stride = kv->layer_stride;
+  p.page_stride = kv->page_stride;
+  p.half_bytes = kv->half_bytes;
+  p.pages_per_seq = kv->pps;
+  p.page_size = kv->page_size;
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+const char *gpt_last_error(void) { return g_err.c_str(); }
+
+gpt_status rope_tables(int32_t max_seq, int32_t head_dim, float base, float *cos_out, float *sin_out,
+                       gpt_stream_t stream) {
+  if (max_seq <= 0) return fail(GPT_ERR_ARG, "max_seq must be positive");
+  if (head_dim <= 0 || (head_dim & 1)) return fail(GPT_ERR_ARG, "head_dim must be positive and even");
+  if (!(base > 0.f)) return fail(GPT_ERR_ARG, "base must be positive");
+  if (!cos_out || !sin_out) return fail(GPT_ERR_ARG, "outputs are NULL");
+  const int half = head_dim / 2;
+  std::vector<float> cs((size_t)max_seq * half), sn((size_t)max_seq * half);
+  for (int i = 0; i < half; ++i) {
+    const double inv_freq = std::pow((double)base, -2.0 * i / head_dim);
+    for (int t = 0; t < max_seq; ++t) {
+      const double ang = (double)t * inv_freq;
+      cs[(size_t)t * half + i] = (float)std::cos(ang);
+      sn[(size_t)t * half + i] = (float)std::sin(ang);
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const size_t bytes = cs.size() * sizeof(float);
+  if (hipMemcpyAsync(cos_out, cs.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(sin_out, sn.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return hip_check("rope_tables copy");
+  return GPT_OK;
+}
+
+gpt_status kv_cache_alloc(const gpt_config *c, int32_t n_seqs, int32_t capacity_per_seq, int32_t page_size,
+                          void *device_buf, size_t *bytes_inout, gpt_kv_cache **out) {
+  gpt_status st = check_config(c);
+  if (st) return st;
+  if (!bytes_inout) return fail(GPT_ERR_ARG, "bytes_inout is NULL");
+  if (n_seqs <= 0 || capacity_per_seq <= 0) return fail(GPT_ERR_ARG, "n_seqs and capacity must be positive");
+  if (capacity_per_seq > c->max_seq) return fail(GPT_ERR_ARG, "capacity exceeds max_seq");
+  if (page_size != kPage) return fail(GPT_ERR_UNSUPPORTED, "page_size must be 64");
+  const long long pps = (capacity_per_seq + page_size - 1) / page_size;
+  const long long n_pages = pps * n_seqs;
+  const long long es = c->dtype == GPT_DTYPE_BF16 ? 2 : 4;
+  const long long half = (long long)page_size * c->n_kv_head * c->head_dim * es;
+  const long long layer_stride = n_pages * 2 * half;
+  const size_t table_off = align256((size_t)(layer_stride * c->n_layer));
+  const size_t lens_off = align256(table_off + (size_t)n_pages * 4);
+  const size_t need = align256(lens_off + (size_t)n_seqs * 4);
+  if (!device_buf) {
+    *bytes_inout = need;
+    return GPT_OK;
+  }
+  if (!out) return fail(GPT_ERR_ARG, "out is NULL");
+  if (*bytes_inout < need) return fail(GPT_ERR_ARG, "buffer too small: %zu < %zu bytes", *bytes_inout, need);
+  if (reinterpret_cast<uintptr_t>(device_buf) & 255) return fail(GPT_ERR_ARG, "buffer must be 256-byte aligned");
+  std::vector<int> table(n_pages);
+  for (long long i = 0; i < n_pages; ++i) table[i] = (int)i;
+  char *buf = (char *)device_buf;
+  if (hipMemcpy(buf + table_off, table.data(), table.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(buf + lens_off, 0, (size_t)n_seqs * 4) != hipSuccess)
+    return hip_check("kv_cache_alloc init");
+  gpt_kv_cache *kv = new gpt_kv_cache();
+  kv->cfg = *c;
+  kv->n_seqs = n_seqs;
+  kv->capacity = capacity_per_seq;
+  kv->page_size = page_size;
+  kv->pps = (int)pps;
+  kv->buf = buf;
+  kv->bytes = *bytes_inout;
+  kv->table_off = table_off;
+  kv->lens_off = lens_off;
+  kv->layer_stride = layer_stride;
+  kv->page_stride = 2 * half;
+  kv->half_bytes = half;
+  kv->lens.assign(n_seqs, 0);
+  *out = kv;
+  return GPT_OK;
+}
+
+gpt_status kv_cache_free(gpt_kv_cache *kv) {
+  if (!kv) return fail(GPT_ERR_ARG, "kv is NULL");
+  delete kv;
+  return GPT_OK;
+}
+
+gpt_status kv_cache_lengths(const gpt_kv_cache *kv, int32_t *lens_out) {
+  if (!kv || !lens_out) return fail(GPT_ERR_ARG, "NULL argument");
+  std::copy(kv->lens.begin(), kv->lens.end(), lens_out);
+  return GPT_OK;
+}
+
+size_t gpt_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_seqs) {
+  if (check_config(c) != GPT_OK || max_tokens <= 0 || max_seqs <= 0) return 0;
+  return carve(c, max_tokens, max_seqs, nullptr, nullptr);
+}
+
+gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                       const float *rope_sin, const int32_t *tokens, const int32_t *cu_seqlens,
+                       int32_t n_seqs, gpt_kv_cache *kv, int32_t logits_rows, float *logits, float *lse,
+                       float *probs, void *workspace, size_t workspace_bytes, gpt_stream_t stream) {
+  gpt_status st = check_config(c);
+  if (st) return st;
+  if ((st = check_weights(c, w))) return st;
+  if (!tokens || !cu_seqlens || !logits || !workspace) return fail(GPT_ERR_ARG, "NULL required pointer");
+  if (n_seqs <= 0) return fail(GPT_ERR_ARG, "n_seqs must be positive");
+  if (n_seqs > kMaxPrefillSeqs) return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences per prefill", kMaxPrefillSeqs);
+  if (logits_rows != GPT_ROWS_ALL && logits_rows != GPT_ROWS_LAST) return fail(GPT_ERR_ARG, "bad logits_rows");
+  if (c->pos_kind == GPT_POS_ROPE && (!rope_cos || !rope_sin)) return fail(GPT_ERR_ARG, "RoPE tables required");
+  if (cu_seqlens[0] != 0) return fail(GPT_ERR_ARG, "cu_seqlens[0] must be 0");
+  for (int b = 0; b < n_seqs; ++b) {
+    const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (len <= 0) return fail(GPT_ERR_ARG, "sequence %d is empty or cu_seqlens decreases", b);
+    if (len > c->max_seq) return fail(GPT_ERR_ARG, "sequence %d longer than max_seq", b);
+  }
+  const int M = cu_seqlens[n_seqs];
+  if (kv) {
+    if (kv->n_seqs != n_seqs) return fail(GPT_ERR_ARG, "n_seqs %d != kv cache's %d", n_seqs, kv->n_seqs);
+    if (kv->cfg.n_layer != c->n_layer || kv->cfg.dtype != c->dtype || kv->cfg.n_kv_head != c->n_kv_head ||
+        kv->cfg.head_dim != c->head_dim)
+      return fail(GPT_ERR_ARG, "kv cache was made for another config");
+    for (int b = 0; b < n_seqs; ++b)
+      if (cu_seqlens[b + 1] - cu_seqlens[b] > kv->capacity)
+        return fail(GPT_ERR_CAPACITY, "sequence %d exceeds the cache capacity %d", b, kv->capacity);
+  }
+  const size_t need = carve(c, M, n_seqs, nullptr, nullptr);
+  if (workspace_bytes < need) return fail(GPT_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GPT_ERR_ARG, "workspace must be 256-byte aligned");
+  if (!aligned16(logits) || (probs && !aligned16(probs))) return fail(GPT_ERR_ARG, "logits/probs must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();  // clear any stale error from unrelated work
+  Bufs bf;
+  carve(c, M, n_seqs, (char *)workspace, &bf);
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
+  const int qkv_n = (H + 2 * Hkv) * dh;
+  const int rows = logits_rows == GPT_ROWS_ALL ? M : n_seqs;
+
+  PrefillMeta meta;
+  meta.n = n_seqs;
+  for (int b = 0; b <= n_seqs; ++b) meta.cu[b] = cu_seqlens[b];
+  {
+    Timed t(GPT_PROF_NORM, s, 0, 0);
+    prefill_meta_kernel<<<1, 256, 0, s>>>(meta, bf.cu, bf.cu_pad, bf.lastrows);
+    launch_rowinfo(bf.cu, bf.cu_pad, n_seqs, M, bf.seq, bf.pos, bf.vcol, s);
+  }
+  PagedKV pv{};
+  if (kv) pv = paged_view(kv);
+  {
+    Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
+    if (bf16p) launch_embed_bf16(tokens, (const bf16 *)w->wte, bf.x, M, d, s);
+    else launch_embed_f32(tokens, (const float *)w->wte, (const float *)w->wpe, bf.pos, bf.x, M, d, s);
+  }
+  double attn_flops = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    const double L = cu_seqlens[b + 1] - cu_seqlens[b];
+    attn_flops += 4.0 * H * dh * L * (L + 1) / 2;
+  }
+  for (int l = 0; l < c->n_layer; ++l) {
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
+      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
+      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, M, d, c->norm_eps, s);
+    }
+    GemmArgs g = gemm(bf.h, d, w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+    g.W1 = w->wk[l];
+    g.W2 = w->wv[l];
+    g.n1 = H * dh;
+    g.n2 = (H + Hkv) * dh;
+    run_gemm(c, g, GPT_PROF_GEMM, s);
+    ScatterArgs sa{};
+    sa.qkv = bf.qkv;
+    sa.M = M;
+    sa.H = H;
+    sa.Hkv = Hkv;
+    sa.seq = bf.seq;
+    sa.pos = bf.pos;
+    sa.vcol = bf.vcol;
+    sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+    sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+    sa.qk_norm = c->qk_norm;
+    sa.eps = c->norm_eps;
+    sa.q_out = bf.q;
+    sa.k_out = bf.k;
+    sa.vt_out = bf.vt;
+    sa.ldvt = bf.ldvt;
+    sa.kv = pv;
+    sa.layer = l;
+    sa.use_cache = kv != nullptr;
+    sa.head_dim = dh;
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)M * qkv_n * 4 + (double)M * qkv_n * (bf16p ? 2 : 4));
+      if (bf16p) launch_rope_norm_scatter_bf16(sa, s);
+      else launch_qkv_scatter_f32(sa, s);
+    }
+    {
+      Timed t(GPT_PROF_ATTN, s, attn_flops, (double)M * (H + 2 * Hkv + H) * dh * (bf16p ? 2 : 4));
+      if (bf16p) {
+        AttnPrefillArgs aa{};
+        aa.q = (const bf16 *)bf.q;
+        aa.k = (const bf16 *)bf.k;
+        aa.vt = (const bf16 *)bf.vt;
+        aa.ldvt = bf.ldvt;
+        aa.cu = bf.cu;
+        aa.cu_pad = bf.cu_pad;
+        aa.H = H;
+        int max_len = 0;
+        for (int b = 0; b < n_seqs; ++b) max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
+        aa.n_seqs = n_seqs;
+        aa.max_wg = (max_len * H + 255) / 256;
+        aa.o = (bf16 *)bf.o;
+        launch_attn_prefill_bf16(aa, s);
+      } else {
+        AttnF32Args aa{};
+        aa.q = (const float *)bf.q;
+        aa.k = (const float *)bf.k;
+        aa.v = (const float *)bf.vt;
+        aa.seq = bf.seq;
+        aa.pos = bf.pos;
+        aa.M = M;
+        aa.H = H;
+        aa.Hkv = Hkv;
+        aa.dh = dh;
+        aa.o = (float *)bf.o;
+        launch_attn_prefill_f32(aa, s);
+      }
+    }
+    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
+      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
+      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, M, d, c->norm_eps, s);
+    }
+    run_gemm(c, gemm(bf.h, d, w->w1[l], M, F, d, bf.u, F,
+                     bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
+             GPT_PROF_GEMM, s);
+    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+  }
+  {
+    Timed t(GPT_PROF_NORM, s, 0, (double)rows * d * (4 + (bf16p ? 2 : 4)));
+    const int *sel = logits_rows == GPT_ROWS_ALL ? nullptr : bf.lastrows;
+    if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, sel, rows, d, c->norm_eps, s);
+    else launch_rmsnorm_f32(bf.x, (float *)bf.h, sel, rows, d, c->norm_eps, s);
+  }
+  run_gemm(c, gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, EPI_F32), GPT_PROF_LMHEAD, s);
+  if (lse || probs) {
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * V * 4 * (probs ? 3 : 1));
+    launch_softmax_lse(logits, rows, V, lse ? lse : bf.lse_tmp, probs, s);
+  }
+  if (kv) launch_lens_set(pv.lens, bf.cu, n_seqs, s);
+  if ((st = hip_check("gpt_prefill launch"))) return st;
+  if (kv)
+    for (int b = 0; b < n_seqs; ++b) kv->lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+  return GPT_OK;
+}
+
+gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                           const float *rope_sin, gpt_kv_cache *kv, const int32_t *tokens_in,
+                           float temperature, const float *uniforms, int32_t *tokens_out, float *logits,
+                           void *workspace, size_t workspace_bytes, gpt_stream_t stream) {
+  gpt_status st = check_config(c);
+  if (st) return st;
+  if ((st = check_weights(c, w))) return st;
+  if (!kv || !tokens_in || !tokens_out || !workspace) return fail(GPT_ERR_ARG, "NULL required pointer");
+  if (temperature > 0.f && !uniforms) return fail(GPT_ERR_ARG, "uniforms are required when temperature > 0");
+  if (!(temperature == temperature)) return fail(GPT_ERR_ARG, "temperature is NaN");
+  if (c->pos_kind == GPT_POS_ROPE && (!rope_cos || !rope_sin)) return fail(GPT_ERR_ARG, "RoPE tables required");
+  if (kv->cfg.n_layer != c->n_layer || kv->cfg.dtype != c->dtype || kv->cfg.n_kv_head != c->n_kv_head ||
+      kv->cfg.head_dim != c->head_dim)
+    return fail(GPT_ERR_ARG, "kv cache was made for another config");
+  const int n = kv->n_seqs;
+  for (int b = 0; b < n; ++b)
+    if (kv->lens[b] + 1 > kv->capacity)
+      return fail(GPT_ERR_CAPACITY, "sequence %d: length %d + 1 exceeds capacity %d", b, kv->lens[b], kv->capacity);
+  const size_t need = carve(c, n, n, nullptr, nullptr);
+  if (workspace_bytes < need) return fail(GPT_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GPT_ERR_ARG, "workspace must be 256-byte aligned");
+  if (logits && !aligned16(logits)) return fail(GPT_ERR_ARG, "logits must be 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();
+  Bufs bf;
+  carve(c, n, n, (char *)workspace, &bf);
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
+  const int qkv_n = (H + 2 * Hkv) * dh;
+  PagedKV pv = paged_view(kv);
+  float *lg = logits ? logits : bf.dlogits;
+  double kv_bytes = 0;
+  for (int b = 0; b < n; ++b) kv_bytes += (double)(kv->lens[b] + 1) * 2 * Hkv * dh * (bf16p ? 2 : 4);
+  {
+    Timed t(GPT_PROF_NORM, s, 0, (double)n * d * (4 + (bf16p ? 2 : 4)));
+    if (bf16p) launch_embed_bf16(tokens_in, (const bf16 *)w->wte, bf.x, n, d, s);
+    else launch_embed_f32(tokens_in, (const float *)w->wte, (const float *)w->wpe, pv.lens, bf.x, n, d, s);
+  }
+  for (int l = 0; l < c->n_layer; ++l) {
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
+      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
+      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+    }
+    GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+    g.W1 = w->wk[l];
+    g.W2 = w->wv[l];
+    g.n1 = H * dh;
+    g.n2 = (H + Hkv) * dh;
+    run_gemm(c, g, GPT_PROF_GEMM, s);
+    ScatterArgs sa{};
+    sa.qkv = bf.qkv;
+    sa.M = n;
+    sa.H = H;
+    sa.Hkv = Hkv;
+    sa.seq = nullptr;
+    sa.pos = pv.lens;
+    sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+    sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+    sa.qk_norm = c->qk_norm;
+    sa.eps = c->norm_eps;
+    sa.q_out = bf.q;
+    sa.kv = pv;
+    sa.layer = l;
+    sa.use_cache = 1;
+    sa.head_dim = dh;
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)n * qkv_n * 6);
+      if (bf16p) launch_rope_norm_scatter_bf16(sa, s);
+      else launch_qkv_scatter_f32(sa, s);
+    }
+    {
+      Timed t(GPT_PROF_DECODE_ATTN, s, 4.0 * H * dh * (kv_bytes / (2.0 * Hkv * dh * (bf16p ? 2 : 4))),
+              kv_bytes + (double)n * H * dh * 2 * (bf16p ? 2 : 4));
+      if (bf16p) {
+        AttnDecodeArgs aa{};
+        aa.q = (const bf16 *)bf.q;
+        aa.kv = pv;
+        aa.layer = l;
+        aa.n = n;
+        aa.H = H;
+        aa.max_splits = (kv->capacity + kDecodeChunk - 1) / kDecodeChunk;
+        aa.o_part = bf.opart;
+        aa.ml_part = bf.mlpart;
+        aa.o = (bf16 *)bf.o;
+        launch_attn_decode_bf16(aa, s);
+      } else {
+        AttnF32Args aa{};
+        aa.q = (const float *)bf.q;
+        aa.M = n;
+        aa.H = H;
+        aa.Hkv = Hkv;
+        aa.dh = dh;
+        aa.kv = pv;
+        aa.layer = l;
+        aa.o = (float *)bf.o;
+        launch_attn_decode_f32(aa, s);
+      }
+    }
+    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], n, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
+      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
+      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+    }
+    run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F,
+                     bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
+             GPT_PROF_GEMM, s);
+    run_gemm(c, gemm(bf.u, F, w->w2[l], n, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+  }
+  {
+    Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
+    if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
+    else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+  }
+  run_gemm(c, gemm(bf.h, d, w->lm_head, n, V, d, lg, V, EPI_F32), GPT_PROF_LMHEAD, s);
+  {
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)n * V * 4);
+    if (temperature > 0.f) launch_sample(lg, n, V, temperature, uniforms, tokens_out, s);
+    else launch_argmax(lg, n, V, tokens_out, s);
+  }
+  launch_lens_inc(pv.lens, n, s);
+  if ((st = hip_check("gpt_decode_step launch"))) return st;
+  for (int b = 0; b < n; ++b) kv->lens[b] += 1;
+  return GPT_OK;
+}
+
+gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, float temperature,
+                             const float *uniforms, int32_t *tokens_out, gpt_stream_t stream) {
+  if (!logits || !tokens_out) return fail(GPT_ERR_ARG, "NULL required pointer");
+  if (rows <= 0 || vocab <= 0) return fail(GPT_ERR_ARG, "rows and vocab must be positive");
+  if (temperature > 0.f && !uniforms) return fail(GPT_ERR_ARG, "uniforms are required when temperature > 0");
+  if (!(temperature == temperature)) return fail(GPT_ERR_ARG, "temperature is NaN");
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();
+  {
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * vocab * 4);
+    if (temperature > 0.f) launch_sample(logits, rows, vocab, temperature, uniforms, tokens_out, s);
+    else launch_argmax(logits, rows, vocab, tokens_out, s);
+  }
+  return hip_check("gpt_select_tokens launch");
+}
+
+gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, int32_t K, void *C,
+                          int32_t epi, gpt_stream_t stream) {
+  if (!A || !W || !C) return fail(GPT_ERR_ARG, "NULL pointer");
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64 || N % 128) return fail(GPT_ERR_ARG, "bad GEMM shape");
+  if (epi < 0 || epi > 3) return fail(GPT_ERR_ARG, "bad epilogue");
+  if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return fail(GPT_ERR_ARG, "pointers must be 16-byte aligned");
+  hipGetLastError();
+  gpt_config c{};
+  c.dtype = GPT_DTYPE_BF16;
+  run_gemm(&c, gemm(A, K, W, M, N, K, C, N, epi), GPT_PROF_GEMM, (hipStream_t)stream);
+  return hip_check("gpt_debug_gemm");
+}
+
+gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, int64_t ldvt,
+                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head,
+                                  int32_t *cu_dev, void *o, gpt_stream_t stream) {
+  if (!q || !k || !vt || !cu_seqlens || !cu_dev || !o) return fail(GPT_ERR_ARG, "NULL pointer");
+  if (n_seqs <= 0 || n_seqs > kMaxPrefillSeqs || n_head <= 0 || n_head > 16) return fail(GPT_ERR_ARG, "bad sizes");
+  if (cu_seqlens[0] != 0) return fail(GPT_ERR_ARG, "cu_seqlens[0] must be 0");
+  long long pad = 0;
+  int max_len = 0;
+  for (int b = 0; b < n_seqs; ++b) {
+    int len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (len <= 0) return fail(GPT_ERR_ARG, "empty sequence");
+    pad += (len + 63) / 64 * 64;
+    max_len = std::max(max_len, len);
+  }
+  if (ldvt < pad || ldvt % 64) return fail(GPT_ERR_ARG, "ldvt too small or not a multiple of 64");
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();
+  PrefillMeta meta;
+  meta.n = n_seqs;
+  for (int b = 0; b <= n_seqs; ++b) meta.cu[b] = cu_seqlens[b];
+  prefill_meta_kernel<<<1, 256, 0, s>>>(meta, cu_dev, cu_dev + n_seqs + 1, nullptr);
+  AttnPrefillArgs aa{};
+  aa.q = (const bf16 *)q;
+  aa.k = (const bf16 *)k;
+  aa.vt = (const bf16 *)vt;
+  aa.ldvt = ldvt;
+  aa.cu = cu_dev;
+  aa.cu_pad = cu_dev + n_seqs + 1;
+  aa.n_seqs = n_seqs;
+  aa.max_wg = (max_len * n_head + 255) / 256;
+  aa.H = n_head;
+  aa.o = (bf16 *)o;
+  launch_attn_prefill_bf16(aa, s);
+  return hip_check("gpt_debug_attn_prefill");
+}
+
+gpt_status gpt_profile_enable(uint32_t mask) {
+  g_prof.reset();
+  g_prof.mask = mask;
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_read(int32_t cls, double *ms, int64_t *launches, double *flops, double *bytes) {
+  if (cls < 0 || cls >= GPT_PROF_NCLASSES) return fail(GPT_ERR_ARG, "bad class");
+  double tot = 0, fl = 0, by = 0;
+  int64_t n = 0;
+  for (auto &r : g_prof.recs) {
+    if (r.cls != cls) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return hip_check("profile sync");
+    float t = 0;
+    hipEventElapsedTime(&t, r.a, r.b);
+    tot += t;
+    fl += r.flops;
+    by += r.bytes;
+    ++n;
+  }
+  if (ms) *ms = tot;
+  if (launches) *launches = n;
+  if (flops) *flops = fl;
+  if (bytes) *bytes = by;
+  return GPT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,387 @@
+// Causal multi-query attention for gfx950 (one K/V head shared by all query
+// heads, head width 128, bf16 operands, fp32 softmax and accumulation).
+//
+// Prefill: the H query heads of a sequence are flattened into rows
+// r = position * H + head, which is exactly the memory order of q.  Row r
+// sees keys 0 .. r / H.  A 256-thread workgroup owns 256 consecutive rows
+// (4 waves x 64); every 64-key K tile and transposed V tile is staged once
+// in LDS and serves all of them, so the single K/V head is read once per
+// workgroup rather than once per query head.  Scores are formed transposed,
+// S^T = K Q^T, so each lane's accumulators hold one row and its softmax
+// statistics stay lane-local (one cross-lane exchange per 32 keys); the
+// exponentiated scores are already laid out as the B operand of
+// O^T = V^T P^T.  Online softmax in the base-2 domain.
+//
+// Decode: one workgroup per (sequence, 256-position chunk), one 64-position
+// page per wave, K and V^T fragments loaded straight from the paged cache,
+// v_mfma_f32_16x16x32_bf16 with the (<= 16) query heads as the N side.
+// Waves merge through LDS; chunks merge in a small log-sum-exp combine.
+#include "kernels.h"
+
+namespace {
+
+constexpr int DH = 128;
+constexpr int KT = 64;  // keys per tile
+
+// K tile [64 keys][128 dims], 16-byte chunks XOR-swizzled by key.
+DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
+// V^T tile [128 dims][64 keys], 8-byte units XOR-swizzled by dim.
+DEV int vidx(int dim, int unit) { return dim * KT + ((unit ^ (dim & 15)) << 2); }
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
+  __shared__ bf16 sk[2][KT * DH];
+  __shared__ bf16 sv[2][DH * KT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, g = lane >> 5;
+  // blockIdx.y counts row blocks from the last one, so the blocks that see
+  // the most keys are dispatched first.
+  const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * 256;
+  const int H = a.H;
+  const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
+  const long long col0 = a.cu_pad[b];
+  const int rows_total = len * H;
+  if (R0 >= rows_total) return;
+  const int Rw = R0 + 64 * wave;
+
+  // Q fragments (B operand of S^T = K Q^T): row r, dims 16 s + 8 g .. +8.
+  int prow[2];
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    int r = min(Rw + 32 * rb + c32, rows_total - 1);
+    prow[rb] = r / H;
+    const bf16 *qp = a.q + ((long long)tok0 * H + r) * DH + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[rb][s] = *(const bf16x8 *)(qp + 16 * s);
+  }
+  const int last_row = min(R0 + 255, rows_total - 1);
+  const int n_kt = (last_row / H) / KT + 1;
+  const int pw_max = Rw < rows_total ? min(Rw + 63, rows_total - 1) / H : -1;
+  const int pw_min = Rw / H;
+
+  // staging: K rows key = tid/16 + 16 p, chunk tid%16; V^T rows dim = tid/8 + 32 p, keys 8*(tid%8)..
+  bf16x8 rk[4], rv[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int key = min(kt * KT + (tid >> 4) + 16 * p, len - 1);
+      rk[p] = *(const bf16x8 *)(a.k + (long long)(tok0 + key) * DH + (tid & 15) * 8);
+    }
+    const int kb0 = kt * KT + (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int dim = (tid >> 3) + 32 * p;
+      rv[p] = *(const bf16x8 *)(a.vt + (long long)dim * a.ldvt + col0 + kb0);
+      if (kb0 + 8 > len) {  // padding columns past the sequence hold no data
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kb0 + e >= len) rv[p][e] = (bf16)0.f;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int key = (tid >> 4) + 16 * p;
+      *(bf16x8 *)&sk[buf][kidx(key, tid & 15)] = rk[p];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int dim = (tid >> 3) + 32 * p, u = (tid & 7) * 2;
+      bf16x4 lo = {rv[p][0], rv[p][1], rv[p][2], rv[p][3]};
+      bf16x4 hi4 = {rv[p][4], rv[p][5], rv[p][6], rv[p][7]};
+      *(bf16x4 *)&sv[buf][vidx(dim, u)] = lo;
+      *(bf16x4 *)&sv[buf][vidx(dim, u + 1)] = hi4;
+    }
+  };
+
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) oacc[d][rb] = (f32x16){};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  const float sc = kLog2e / sqrtf((float)DH);
+
+  auto tile = [&](int kt, int buf) {
+    if (kt * KT > pw_max) return;  // every key of the tile is in this wave's future
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 kf = *(const bf16x8 *)&sk[buf][kidx(32 * kb + c32, 2 * s + g)];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
+      }
+    }
+    const bool need_mask = kt * KT + KT - 1 > pw_min;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[kb][rb][r] * sc;
+          if (need_mask) {
+            int key = kt * KT + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > prow[rb]) v = -INFINITY;
+          }
+          sacc[kb][rb][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrow[rb], mx);
+      const float alpha = fast_exp2(mrow[rb] - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(sacc[kb][rb][r] - mnew);
+          sacc[kb][rb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      lrow[rb] = lrow[rb] * alpha + rs;
+      mrow[rb] = mnew;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d][rb] *= alpha;
+    }
+    // O^T += V^T P^T, 16 keys per MFMA; k slot 8g+j <-> key 16h + 8(j/4) + 4g + j%4
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, h = st & 1;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[rb][j] = f2bf(sacc[kb][rb][8 * h + j]);
+      const int u0 = 8 * kb + 4 * h + g;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int dim = 32 * d + c32;
+        bf16x4 lo = *(const bf16x4 *)&sv[buf][vidx(dim, u0)];
+        bf16x4 hi4 = *(const bf16x4 *)&sv[buf][vidx(dim, u0 + 2)];
+        bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          oacc[d][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt - 1; ++kt) {
+    gload(kt + 1);
+    tile(kt, kt & 1);
+    sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+  tile(n_kt - 1, (n_kt - 1) & 1);
+
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = Rw + 32 * rb + c32;
+    if (r >= rows_total) continue;
+    const float inv = 1.0f / lrow[rb];
+    bf16 *op = a.o + ((long long)tok0 * H + r) * DH + 4 * g;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x4 o = {f2bf(oacc[d][rb][4 * c] * inv), f2bf(oacc[d][rb][4 * c + 1] * inv),
+                    f2bf(oacc[d][rb][4 * c + 2] * inv), f2bf(oacc[d][rb][4 * c + 3] * inv)};
+        *(bf16x4 *)(op + 32 * d + 8 * c) = o;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ decode
+
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
+  __shared__ float so[4][16][DH + 4];
+  __shared__ float sml[4][16][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane & 15, q4 = lane >> 4;
+  const int b = blockIdx.y, split = blockIdx.x;
+  const PagedKV &kv = a.kv;
+  const int len = kv.lens[b] + 1;  // the new position is already in the cache
+  const int start = split * kDecodeChunk;
+  if (start >= len) return;
+  const int H = a.H;
+  const int kpos0 = start + 64 * wave;
+  float mw = -INFINITY, lw = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
+  if (kpos0 < len) {
+    const int page = kv.table[b * kv.pages_per_seq + kpos0 / 64];
+    const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+    const bf16 *K = (const bf16 *)pg;
+    const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
+    bf16x4 vlo[8][2], vhi[8][2];
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
+        vlo[d][h] = *(const bf16x4 *)vp;
+        vhi[d][h] = *(const bf16x4 *)(vp + 16);
+      }
+    bf16x8 qf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
+      else qf[s] = (bf16x8){};
+    }
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = (f32x4){};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
+    }
+    const float sc = kLog2e / sqrtf((float)DH);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kpos0 + 16 * kb + 4 * q4 + r;
+        float v = key < len ? sacc[kb][r] * sc : -INFINITY;
+        sacc[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = fast_exp2(sacc[kb][r] - mx);
+        sacc[kb][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    mw = mx;
+    lw = rs;
+    // keys past the end hold stale data: zero them so 0 * garbage cannot appear
+    if (kpos0 + 64 > len) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
+            if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
+          }
+    }
+    // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = f2bf(sacc[2 * h][e]);
+        pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
+                     vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds head hl, dims 16 d + 4 q4 + r
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[wave][hl][16 * d + 4 * q4 + r] = oacc[d][r];
+  if (q4 == 0) {
+    sml[wave][hl][0] = mw;
+    sml[wave][hl][1] = lw;
+  }
+  __syncthreads();
+  const int h = tid >> 4, d0 = (tid & 15) * 8;
+  if (h >= H) return;
+  float M = sml[0][h][0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, sml[w][h][0]);
+  float f[4], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = fast_exp2(sml[w][h][0] - M);
+    L += f[w] * sml[w][h][1];
+  }
+  float *op = a.o_part + (((long long)b * a.max_splits + split) * H + h) * DH + d0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += f[w] * so[w][h][d0 + e];
+    op[e] = v;
+  }
+  if ((tid & 15) == 0) {
+    float *ml = a.ml_part + (((long long)b * a.max_splits + split) * H + h) * 2;
+    ml[0] = M;
+    ml[1] = L;
+  }
+}
+
+// Merge the chunks of each (sequence, head): one wave, two dims per lane.
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(AttnDecodeArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= a.n * a.H) return;
+  const int b = item / a.H, h = item - b * a.H;
+  const int len = a.kv.lens[b] + 1;
+  const int ns = (len + kDecodeChunk - 1) / kDecodeChunk;
+  const float *ml = a.ml_part + ((long long)b * a.max_splits * a.H + h) * 2;
+  const long long mstride = (long long)a.H * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * mstride]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const float *op = a.o_part + ((long long)b * a.max_splits * a.H + h) * DH;
+  const long long ostride = (long long)a.H * DH;
+  for (int s = 0; s < ns; ++s) {
+    const float f = fast_exp2(ml[s * mstride] - M);
+    L += f * ml[s * mstride + 1];
+    o0 += f * op[s * ostride + lane];
+    o1 += f * op[s * ostride + lane + 64];
+  }
+  const float inv = 1.0f / L;
+  bf16 *o = a.o + ((long long)b * a.H + h) * DH;
+  o[lane] = f2bf(o0 * inv);
+  o[lane + 64] = f2bf(o1 * inv);
+}
+
+}  // namespace
+
+void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
+  if (a.n_seqs > 0 && a.max_wg > 0) attn_prefill_kernel<<<dim3(a.n_seqs, a.max_wg), 256, 0, s>>>(a);
+}
+
+void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
+  if (a.n <= 0) return;
+  attn_decode_kernel<<<dim3(a.max_splits, a.n), 256, 0, s>>>(a);
+  attn_decode_combine_kernel<<<(a.n * a.H + 3) / 4, 256, 0, s>>>(a);
+}

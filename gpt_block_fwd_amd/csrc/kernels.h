@@ -1,0 +1,105 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher enqueues on the
+// given stream and does no validation: the C-ABI layer (api.cpp) checks
+// shapes before calling them.
+#pragma once
+#include "common.h"
+
+// ------------------------------------------------------------ small kernels
+void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq, int *pos,
+                    int *vcol, hipStream_t s);
+void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s);
+void launch_embed_f32(const int *tok, const float *wte, const float *wpe, const int *pos, float *x,
+                      int M, int d, hipStream_t s);
+void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d, float eps,
+                         hipStream_t s);
+void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d, float eps,
+                        hipStream_t s);
+
+// RoPE + QK-norm of the fp32 q/k head vectors of `qkv` ([M][(H+2Hkv)*128]),
+// then bf16 scatter: q -> q_out [M][H*128]; k -> k_out [M][Hkv*128] and/or
+// the paged cache; v -> vt_out [Hkv*128][ldvt] at column vcol[m] and/or the
+// cache.  seq == NULL means row m is sequence m (decode).
+struct ScatterArgs {
+  const float *qkv;
+  int M, H, Hkv;
+  const int *seq, *pos, *vcol;
+  const float *cos, *sin;  // [max_seq][64] or NULL (no RoPE)
+  int qk_norm;
+  float eps;
+  void *q_out, *k_out, *vt_out;  // bf16 (or fp32 on the small path)
+  long long ldvt;
+  PagedKV kv;
+  int layer;
+  int use_cache;
+  int head_dim;  // small path only
+};
+void launch_rope_norm_scatter_bf16(const ScatterArgs &a, hipStream_t s);
+void launch_qkv_scatter_f32(const ScatterArgs &a, hipStream_t s);
+
+void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float *probs,
+                        hipStream_t s);
+void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s);
+void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
+                   int *out, hipStream_t s);
+void launch_lens_set(int *lens, const int *cu, int n, hipStream_t s);
+void launch_lens_inc(int *lens, int n, hipStream_t s);
+void launch_gather_rows_bf16(const bf16 *src, bf16 *dst, const int *rows, int n, int d,
+                             hipStream_t s);
+
+// ------------------------------------------------------------ GEMMs
+enum Epi { EPI_BF16 = 0, EPI_RELU2_BF16 = 1, EPI_RESID = 2, EPI_F32 = 3, EPI_RELU_F32 = 4 };
+
+// C[m][n] = sum_k A[m][k] * W[n][k]; W rows come from up to three segments
+// ([0,n1) from W0, [n1,n2) from W1, [n2,N) from W2) so separate Q/K/V
+// weights feed one GEMM without a copy.
+struct GemmArgs {
+  const void *A;
+  long long lda;
+  const void *W0, *W1, *W2;
+  int n1, n2;
+  long long ldw;
+  int M, N, K;
+  void *C;
+  long long ldc;
+  int epi;
+};
+void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M
+void launch_gemm_bf16_skinny(const GemmArgs &g, hipStream_t s);  // MFMA, M <= 64
+void launch_gemm_f32(const GemmArgs &g, hipStream_t s);          // small fp32 path
+
+// ------------------------------------------------------------ attention
+struct AttnPrefillArgs {
+  const bf16 *q;   // [M][H*128]
+  const bf16 *k;   // [M][128]
+  const bf16 *vt;  // [128][ldvt]
+  long long ldvt;
+  const int *cu, *cu_pad;
+  int n_seqs, max_wg;  // grid: (sequence, 256-row block counted from the end)
+  int H;
+  bf16 *o;  // [M][H*128]
+};
+void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
+
+struct AttnDecodeArgs {
+  const bf16 *q;  // [n][H*128]
+  PagedKV kv;
+  int layer;
+  int n, H, max_splits;
+  float *o_part;  // [n][max_splits][H][128]
+  float *ml_part; // [n][max_splits][H][2]
+  bf16 *o;        // [n][H*128]
+};
+void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
+
+struct AttnF32Args {
+  const float *q, *k, *v;  // prefill: [M][H*dh], [M][Hkv*dh]
+  const int *seq, *pos;
+  int M, H, Hkv, dh;
+  PagedKV kv;  // decode
+  int layer;
+  float *o;
+};
+void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
+void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
+
+constexpr int kDecodeChunk = 256;  // positions per decode-attention workgroup

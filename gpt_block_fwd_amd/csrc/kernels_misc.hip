@@ -1,0 +1,540 @@
+// Row-wise and element-wise kernels of the decoder-block forward for gfx950:
+// row metadata, embedding gather, weightless RMSNorm, RoPE + QK-norm +
+// K/V scatter, vocabulary softmax / log-sum-exp, token selection, and the
+// fp32 small-model GEMM and attention.
+#include "kernels.h"
+
+// ---------------------------------------------------------------- row info
+
+__global__ void rowinfo_kernel(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq,
+                               int *pos, int *vcol) {
+  int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  int lo = 0, hi = n_seqs - 1;  // last b with cu[b] <= m
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  seq[m] = lo;
+  int p = m - cu[lo];
+  pos[m] = p;
+  if (vcol) vcol[m] = cu_pad[lo] + p;
+}
+
+void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq, int *pos,
+                    int *vcol, hipStream_t s) {
+  rowinfo_kernel<<<(M + 255) / 256, 256, 0, s>>>(cu, cu_pad, n_seqs, M, seq, pos, vcol);
+}
+
+// ---------------------------------------------------------------- embedding
+// Token embedding (plus learned position embedding on the small path) into
+// the fp32 residual stream.
+
+__global__ void embed_bf16_kernel(const int *tok, const bf16 *wte, float *x, int M, int d) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // 8 elements each
+  long long total = (long long)M * d / 8;
+  if (i >= total) return;
+  long long m = i * 8 / d;
+  int c = (int)(i * 8 - m * d);
+  const bf16x8 v = *(const bf16x8 *)(wte + (long long)tok[m] * d + c);
+  float4 a = make_float4(bf2f(v[0]), bf2f(v[1]), bf2f(v[2]), bf2f(v[3]));
+  float4 b = make_float4(bf2f(v[4]), bf2f(v[5]), bf2f(v[6]), bf2f(v[7]));
+  float4 *dst = (float4 *)(x + m * d + c);
+  dst[0] = a;
+  dst[1] = b;
+}
+
+void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s) {
+  long long total = (long long)M * d / 8;
+  embed_bf16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(tok, wte, x, M, d);
+}
+
+__global__ void embed_f32_kernel(const int *tok, const float *wte, const float *wpe,
+                                 const int *pos, float *x, int M, int d) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)M * d) return;
+  long long m = i / d;
+  int c = (int)(i - m * d);
+  float v = wte[(long long)tok[m] * d + c];
+  if (wpe) v += wpe[(long long)pos[m] * d + c];
+  x[i] = v;
+}
+
+void launch_embed_f32(const int *tok, const float *wte, const float *wpe, const int *pos, float *x,
+                      int M, int d, hipStream_t s) {
+  long long total = (long long)M * d;
+  embed_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(tok, wte, wpe, pos, x, M, d);
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// y = x / sqrt(mean(x^2) + eps), no gain.  One 64-lane wave per row, fp32
+// sum of squares reduced across the wave.  `rows` optionally selects source
+// rows (the last position of each sequence).
+
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, TO *y, const int *rows,
+                                                      int M, int d, float eps) {
+  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int r = blockIdx.x * 4 + wave;
+  if (r >= M) return;
+  long long src = rows ? rows[r] : r;
+  const float *xr = x + src * d;
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += 256) {
+    float4 v = *(const float4 *)(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  TO *yr = y + (long long)r * d;
+  for (int c = lane * 4; c < d; c += 256) {
+    float4 v = *(const float4 *)(xr + c);
+    if constexpr (sizeof(TO) == 2) {
+      bf16x4 o = {f2bf(v.x * rs), f2bf(v.y * rs), f2bf(v.z * rs), f2bf(v.w * rs)};
+      *(bf16x4 *)(yr + c) = o;
+    } else {
+      *(float4 *)(yr + c) = make_float4(v.x * rs, v.y * rs, v.z * rs, v.w * rs);
+    }
+  }
+}
+
+void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d, float eps,
+                         hipStream_t s) {
+  rmsnorm_kernel<bf16><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+}
+void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d, float eps,
+                        hipStream_t s) {
+  rmsnorm_kernel<float><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+}
+
+// ---------------------------------------------------------------- RoPE + QK-norm + scatter
+// One wave per (row, head slot) of a 128-wide head.  Lane l owns the rotary
+// pair (l, l + 64): half-split rotation by the tabled angle, then a
+// weightless RMSNorm over the head (sum of squares reduced across the wave).
+
+__global__ __launch_bounds__(256) void rope_norm_scatter_bf16_kernel(ScatterArgs a) {
+  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int slots = a.H + 2 * a.Hkv;
+  long long item = (long long)blockIdx.x * 4 + wave;
+  if (item >= (long long)a.M * slots) return;
+  int m = (int)(item / slots), j = (int)(item - (long long)m * slots);
+  const float *u = a.qkv + (long long)m * slots * 128 + j * 128;
+  float x0 = u[lane], x1 = u[lane + 64];
+  int p = a.pos[m];
+  int b = a.seq ? a.seq[m] : m;
+  bool is_v = j >= a.H + a.Hkv;
+  if (!is_v) {
+    if (a.cos) {
+      float c = a.cos[p * 64 + lane], s = a.sin[p * 64 + lane];
+      float r0 = x0 * c - x1 * s, r1 = x0 * s + x1 * c;
+      x0 = r0;
+      x1 = r1;
+    }
+    if (a.qk_norm) {
+      float ss = wave_sum(x0 * x0 + x1 * x1);
+      float rs = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+      x0 *= rs;
+      x1 *= rs;
+    }
+  }
+  bf16 y0 = f2bf(x0), y1 = f2bf(x1);
+  if (j < a.H) {
+    bf16 *q = (bf16 *)a.q_out + (long long)m * a.H * 128 + j * 128;
+    q[lane] = y0;
+    q[lane + 64] = y1;
+    return;
+  }
+  int g = is_v ? j - a.H - a.Hkv : j - a.H;
+  int kvd = a.Hkv * 128;
+  if (!is_v) {
+    if (a.k_out) {
+      bf16 *k = (bf16 *)a.k_out + (long long)m * kvd + g * 128;
+      k[lane] = y0;
+      k[lane + 64] = y1;
+    }
+  } else if (a.vt_out) {
+    bf16 *vt = (bf16 *)a.vt_out;
+    long long col = a.vcol ? a.vcol[m] : m;
+    vt[(long long)(g * 128 + lane) * a.ldvt + col] = y0;
+    vt[(long long)(g * 128 + lane + 64) * a.ldvt + col] = y1;
+  }
+  if (a.use_cache) {
+    const PagedKV &kv = a.kv;
+    int page = kv.table[b * kv.pages_per_seq + p / kv.page_size];
+    int slot = p % kv.page_size;
+    char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+    if (!is_v) {
+      bf16 *k = (bf16 *)pg + (long long)slot * kvd + g * 128;
+      k[lane] = y0;
+      k[lane + 64] = y1;
+    } else {
+      bf16 *vt = (bf16 *)(pg + kv.half_bytes);
+      vt[(long long)(g * 128 + lane) * kv.page_size + slot] = y0;
+      vt[(long long)(g * 128 + lane + 64) * kv.page_size + slot] = y1;
+    }
+  }
+}
+
+void launch_rope_norm_scatter_bf16(const ScatterArgs &a, hipStream_t s) {
+  long long items = (long long)a.M * (a.H + 2 * a.Hkv);
+  rope_norm_scatter_bf16_kernel<<<(unsigned)((items + 3) / 4), 256, 0, s>>>(a);
+}
+
+// fp32 small path: one thread per (row, head slot), any even head_dim <= 64.
+__global__ void qkv_scatter_f32_kernel(ScatterArgs a) {
+  int slots = a.H + 2 * a.Hkv;
+  long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (long long)a.M * slots) return;
+  int m = (int)(item / slots), j = (int)(item - (long long)m * slots);
+  int dh = a.head_dim, half = dh / 2;
+  const float *u = a.qkv + (long long)m * slots * dh + j * dh;
+  float y[64];
+  for (int i = 0; i < dh; ++i) y[i] = u[i];
+  int p = a.pos[m];
+  int b = a.seq ? a.seq[m] : m;
+  bool is_v = j >= a.H + a.Hkv;
+  if (!is_v) {
+    if (a.cos) {
+      for (int i = 0; i < half; ++i) {
+        float c = a.cos[p * half + i], s = a.sin[p * half + i];
+        float r0 = y[i] * c - y[i + half] * s, r1 = y[i] * s + y[i + half] * c;
+        y[i] = r0;
+        y[i + half] = r1;
+      }
+    }
+    if (a.qk_norm) {
+      float ss = 0.f;
+      for (int i = 0; i < dh; ++i) ss += y[i] * y[i];
+      float rs = 1.0f / sqrtf(ss / (float)dh + a.eps);
+      for (int i = 0; i < dh; ++i) y[i] *= rs;
+    }
+  }
+  int kvd = a.Hkv * dh;
+  float *dst = nullptr;
+  if (j < a.H) {
+    dst = (float *)a.q_out + (long long)m * a.H * dh + j * dh;
+  } else if (!is_v) {
+    if (a.k_out) dst = (float *)a.k_out + (long long)m * kvd + (j - a.H) * dh;
+  } else {
+    if (a.vt_out) dst = (float *)a.vt_out + (long long)m * kvd + (j - a.H - a.Hkv) * dh;
+  }
+  if (dst)
+    for (int i = 0; i < dh; ++i) dst[i] = y[i];
+  if (a.use_cache && j >= a.H) {
+    const PagedKV &kv = a.kv;
+    int g = is_v ? j - a.H - a.Hkv : j - a.H;
+    int page = kv.table[b * kv.pages_per_seq + p / kv.page_size];
+    int slot = p % kv.page_size;
+    char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+    float *c = (float *)(pg + (is_v ? kv.half_bytes : 0)) + (long long)slot * kvd + g * dh;
+    for (int i = 0; i < dh; ++i) c[i] = y[i];
+  }
+}
+
+void launch_qkv_scatter_f32(const ScatterArgs &a, hipStream_t s) {
+  long long items = (long long)a.M * (a.H + 2 * a.Hkv);
+  qkv_scatter_f32_kernel<<<(unsigned)((items + 127) / 128), 128, 0, s>>>(a);
+}
+
+// ---------------------------------------------------------------- softmax / LSE
+// One 256-thread workgroup per row: running (max, sum of exp) per thread,
+// merged across the workgroup; lse = max + log(sum).  Optionally a second
+// pass writes p = exp(logit - lse).
+
+DEV void ms_merge(float &m, float &s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * fast_exp2((m - mn) * kLog2e) + s2 * fast_exp2((m2 - mn) * kLog2e);
+  m = mn;
+}
+
+__global__ __launch_bounds__(256) void softmax_lse_kernel(const float *logits, int V, float *lse,
+                                                          float *probs) {
+  __shared__ float sm[4], ss[4];
+  const float *row = logits + (long long)blockIdx.x * V;
+  float m = -INFINITY, s = 0.f;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    float x = row[i];
+    if (x > m) {
+      s = s * fast_exp2((m - x) * kLog2e) + 1.f;
+      m = x;
+    } else {
+      s += fast_exp2((x - m) * kLog2e);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+  }
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[w] = m;
+    ss[w] = s;
+  }
+  __syncthreads();
+  m = sm[0];
+  s = ss[0];
+  for (int i = 1; i < 4; ++i) ms_merge(m, s, sm[i], ss[i]);
+  float l = m + logf(s);
+  if (threadIdx.x == 0 && lse) lse[blockIdx.x] = l;
+  if (probs) {
+    float *pr = probs + (long long)blockIdx.x * V;
+    for (int i = threadIdx.x; i < V; i += 256) pr[i] = fast_exp2((row[i] - l) * kLog2e);
+  }
+}
+
+void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float *probs,
+                        hipStream_t s) {
+  if (rows <= 0) return;
+  softmax_lse_kernel<<<rows, 256, 0, s>>>(logits, V, lse, probs);
+}
+
+// ---------------------------------------------------------------- greedy
+// Argmax per row; among equal maxima the lowest index wins.
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int V, int *out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const float *row = logits + (long long)blockIdx.x * V;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    float x = row[i];
+    if (x > best) {  // indices visited in increasing order: keep the first
+      best = x;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(best, o, 64);
+    int i2 = __shfl_xor(bi, o, 64);
+    if (v2 > best || (v2 == best && i2 < bi)) {
+      best = v2;
+      bi = i2;
+    }
+  }
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = best;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k)
+      if (sv[k] > best || (sv[k] == best && si[k] < bi)) {
+        best = sv[k];
+        bi = si[k];
+      }
+    out[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s) {
+  if (rows <= 0) return;
+  argmax_kernel<<<rows, 256, 0, s>>>(logits, V, out);
+}
+
+// ---------------------------------------------------------------- sampling
+// Inverse-CDF temperature sampling, one 1024-thread workgroup per row.
+// Thread t owns the contiguous chunk [t*C, (t+1)*C).  Weights are
+// e_i = exp((x_i - max)/T); the block scan of the chunk sums gives each
+// chunk's starting cumulative weight, and the token is the first i whose
+// cumulative weight exceeds u * total.
+
+__global__ __launch_bounds__(1024) void sample_kernel(const float *logits, int V, float inv_t,
+                                                      const float *uniforms, int *out) {
+  __shared__ float red[16];
+  __shared__ float scan[16];
+  __shared__ int answer, lastpos;
+  const float *row = logits + (long long)blockIdx.x * V;
+  int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int C = (V + 1023) / 1024;
+  int i0 = t * C, i1 = min(V, i0 + C);
+  // row max
+  float m = -INFINITY;
+  for (int i = i0; i < i1; ++i) m = fmaxf(m, row[i]);
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  if (t == 0) {
+    answer = -1;
+    lastpos = -1;
+  }
+  __syncthreads();
+  m = red[0];
+  for (int k = 1; k < 16; ++k) m = fmaxf(m, red[k]);
+  float sc = inv_t * kLog2e;
+  float local = 0.f;
+  int lastp = -1;
+  for (int i = i0; i < i1; ++i) {
+    float e = fast_exp2((row[i] - m) * sc);
+    local += e;
+    if (e > 0.f) lastp = i;
+  }
+  // inclusive scan across the workgroup
+  float incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  __syncthreads();
+  if (lane == 63) scan[w] = incl;
+  __syncthreads();
+  float base = 0.f, total = 0.f;
+  for (int k = 0; k < 16; ++k) {
+    if (k < w) base += scan[k];
+    total += scan[k];
+  }
+  incl += base;
+  float excl = incl - local;
+  float target = uniforms[blockIdx.x] * total;
+  if (lastp >= 0) atomicMax(&lastpos, lastp);
+  if (excl <= target && target < incl) {
+    float run = excl;
+    int pick = -1, lastpos_here = -1;
+    for (int i = i0; i < i1; ++i) {
+      float e = fast_exp2((row[i] - m) * sc);
+      run += e;
+      if (e > 0.f) lastpos_here = i;
+      if (run > target) {
+        pick = i;
+        break;
+      }
+    }
+    if (pick < 0) pick = lastpos_here;
+    atomicMax(&answer, pick);  // at most one thread qualifies
+  }
+  __syncthreads();
+  if (t == 0) out[blockIdx.x] = answer >= 0 ? answer : (lastpos >= 0 ? lastpos : 0);
+}
+
+void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
+                   int *out, hipStream_t s) {
+  if (rows <= 0) return;
+  sample_kernel<<<rows, 1024, 0, s>>>(logits, V, 1.0f / temperature, u, out);
+}
+
+// ---------------------------------------------------------------- KV lengths
+
+__global__ void lens_set_kernel(int *lens, const int *cu, int n) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < n) lens[b] = cu[b + 1] - cu[b];
+}
+__global__ void lens_inc_kernel(int *lens, int n) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < n) lens[b] += 1;
+}
+void launch_lens_set(int *lens, const int *cu, int n, hipStream_t s) {
+  lens_set_kernel<<<(n + 255) / 256, 256, 0, s>>>(lens, cu, n);
+}
+void launch_lens_inc(int *lens, int n, hipStream_t s) {
+  lens_inc_kernel<<<(n + 255) / 256, 256, 0, s>>>(lens, n);
+}
+
+__global__ void gather_rows_bf16_kernel(const bf16 *src, bf16 *dst, const int *rows, int d) {
+  const bf16 *s = src + (long long)rows[blockIdx.x] * d;
+  bf16 *o = dst + (long long)blockIdx.x * d;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) *(bf16x8 *)(o + c) = *(const bf16x8 *)(s + c);
+}
+void launch_gather_rows_bf16(const bf16 *src, bf16 *dst, const int *rows, int n, int d,
+                             hipStream_t s) {
+  if (n > 0) gather_rows_bf16_kernel<<<n, 64, 0, s>>>(src, dst, rows, d);
+}
+
+// ---------------------------------------------------------------- fp32 small path
+
+__global__ void gemm_f32_kernel(GemmArgs g) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)g.M * g.N) return;
+  int m = (int)(i / g.N), n = (int)(i - (long long)m * g.N);
+  const float *w;
+  if (n < g.n1) w = (const float *)g.W0 + (long long)n * g.ldw;
+  else if (n < g.n2) w = (const float *)g.W1 + (long long)(n - g.n1) * g.ldw;
+  else w = (const float *)g.W2 + (long long)(n - g.n2) * g.ldw;
+  const float *a = (const float *)g.A + (long long)m * g.lda;
+  float acc = 0.f;
+  for (int k = 0; k < g.K; ++k) acc = fmaf(a[k], w[k], acc);
+  float *c = (float *)g.C + (long long)m * g.ldc + n;
+  if (g.epi == EPI_RESID) *c += acc;
+  else if (g.epi == EPI_RELU_F32) *c = fmaxf(acc, 0.f);
+  else if (g.epi == EPI_RELU2_BF16) { float r = fmaxf(acc, 0.f); *c = r * r; }  // fp32 output here
+  else *c = acc;
+}
+
+void launch_gemm_f32(const GemmArgs &g, hipStream_t s) {
+  long long total = (long long)g.M * g.N;
+  if (total > 0) gemm_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(g);
+}
+
+// Causal attention, one thread per (row, head), online softmax in fp32.
+__global__ void attn_prefill_f32_kernel(AttnF32Args a) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)a.M * a.H) return;
+  int m = (int)(i / a.H), h = (int)(i - (long long)m * a.H);
+  int g = h * a.Hkv / a.H, dh = a.dh, kvd = a.Hkv * dh;
+  int p = a.pos[m];
+  int r0 = m - p;
+  const float *q = a.q + (long long)m * a.H * dh + h * dh;
+  float acc[64];
+  for (int c = 0; c < dh; ++c) acc[c] = 0.f;
+  float mx = -INFINITY, l = 0.f, scale = 1.0f / sqrtf((float)dh);
+  for (int j = 0; j <= p; ++j) {
+    const float *k = a.k + (long long)(r0 + j) * kvd + g * dh;
+    const float *v = a.v + (long long)(r0 + j) * kvd + g * dh;
+    float s = 0.f;
+    for (int c = 0; c < dh; ++c) s = fmaf(q[c], k[c], s);
+    s *= scale;
+    float mn = fmaxf(mx, s);
+    float alpha = expf(mx - mn), e = expf(s - mn);
+    l = l * alpha + e;
+    for (int c = 0; c < dh; ++c) acc[c] = acc[c] * alpha + e * v[c];
+    mx = mn;
+  }
+  float *o = a.o + (long long)m * a.H * dh + h * dh;
+  for (int c = 0; c < dh; ++c) o[c] = acc[c] / l;
+}
+
+void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s) {
+  long long total = (long long)a.M * a.H;
+  if (total > 0) attn_prefill_f32_kernel<<<(unsigned)((total + 127) / 128), 128, 0, s>>>(a);
+}
+
+// Decode: row b is sequence b at position lens[b]; keys 0..lens[b] from the
+// fp32 paged cache.
+__global__ void attn_decode_f32_kernel(AttnF32Args a) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)a.M * a.H) return;
+  int b = (int)(i / a.H), h = (int)(i - (long long)b * a.H);
+  int g = h * a.Hkv / a.H, dh = a.dh, kvd = a.Hkv * dh;
+  const PagedKV &kv = a.kv;
+  int p = kv.lens[b];
+  const float *q = a.q + (long long)b * a.H * dh + h * dh;
+  float acc[64];
+  for (int c = 0; c < dh; ++c) acc[c] = 0.f;
+  float mx = -INFINITY, l = 0.f, scale = 1.0f / sqrtf((float)dh);
+  const char *lay = kv.base + (long long)a.layer * kv.layer_stride;
+  for (int j = 0; j <= p; ++j) {
+    int page = kv.table[b * kv.pages_per_seq + j / kv.page_size];
+    const char *pg = lay + (long long)page * kv.page_stride;
+    int slot = j % kv.page_size;
+    const float *k = (const float *)pg + (long long)slot * kvd + g * dh;
+    const float *v = (const float *)(pg + kv.half_bytes) + (long long)slot * kvd + g * dh;
+    float s = 0.f;
+    for (int c = 0; c < dh; ++c) s = fmaf(q[c], k[c], s);
+    s *= scale;
+    float mn = fmaxf(mx, s);
+    float alpha = expf(mx - mn), e = expf(s - mn);
+    l = l * alpha + e;
+    for (int c = 0; c < dh; ++c) acc[c] = acc[c] * alpha + e * v[c];
+    mx = mn;
+  }
+  float *o = a.o + (long long)b * a.H * dh + h * dh;
+  for (int c = 0; c < dh; ++c) o[c] = acc[c] / l;
+}
+
+void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s) {
+  long long total = (long long)a.M * a.H;
+  if (total > 0) attn_decode_f32_kernel<<<(unsigned)((total + 127) / 128), 128, 0, s>>>(a);
+}

@@ -1,0 +1,226 @@
+/*
+ * gpt.h -- C ABI of the MI355X (gfx950) decoder-block forward library, libgpt.so.
+ *
+ * The library runs the forward pass of the nanochat-style GPT decoder block as
+ * a full-sequence prefill and as a KV-cache decode step, ending in the LM-head
+ * logits, the vocabulary softmax and token selection.  Every step runs in
+ * hand-written HIP kernels; the host side only validates arguments, carves
+ * the caller's workspace and enqueues kernels on the caller's stream.
+ *
+ * Sources of the method (titles of the pages; sections named per entry point):
+ *   [nanochat-launch]  "復刻 ChatGPT 有多難？" news article on nanochat's launch,
+ *                      section on Karpathy's tricks (為什么可以訓練如此之快).
+ *   [nanochat-forum]   hongdingcd.com thread on nanochat, paragraphs on the model
+ *                      architecture (rotary positions, QK norm, MQA, KV cache).
+ *   [nanochat-csdn]    CSDN walkthrough of the nanochat speedrun (base-model
+ *                      section: Engine class with KV cache, prefill and decode).
+ *   [microgpt]         Hacker News summary of microgpt, sections "Tokenizer",
+ *                      "Model parameters", "Core architecture", "Inference".
+ *
+ * Conventions
+ *   - All device pointers are allocated and owned by the caller.  The library
+ *     never allocates device memory; it owns only small host-side handles.
+ *   - Linear weights are row-major [out, in] (y = W x), dtype per config:
+ *     bf16 (GPT_DTYPE_BF16) or fp32 (GPT_DTYPE_F32).  The residual stream,
+ *     every accumulator, the softmax and the logits are fp32.
+ *   - Calls are asynchronous and stream-ordered: a call returns after
+ *     enqueueing its kernels on `stream`.  Host arrays passed in (cu_seqlens)
+ *     may be reused as soon as the call returns.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Every call validates its arguments on the host before touching the
+ *     device.  On failure it returns a non-zero gpt_status, enqueues nothing,
+ *     and gpt_last_error() describes the problem.  No C++ exception crosses the
+ *     ABI.  Calls that share one gpt_kv_cache are not thread-safe.
+ */
+#ifndef GPT_BLOCK_FWD_GPT_H
+#define GPT_BLOCK_FWD_GPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *gpt_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  GPT_OK = 0,
+  GPT_ERR_ARG = 1,         /* a pointer, size or layout argument is invalid */
+  GPT_ERR_CAPACITY = 2,    /* a sequence would outgrow its KV-cache capacity */
+  GPT_ERR_UNSUPPORTED = 3, /* a valid configuration this build has no kernels for */
+  GPT_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+} gpt_status;
+
+enum { GPT_POS_LEARNED = 0, GPT_POS_ROPE = 1 };
+enum { GPT_ACT_RELU = 0, GPT_ACT_RELU2 = 1 };
+enum { GPT_DTYPE_F32 = 0, GPT_DTYPE_BF16 = 1 };
+enum { GPT_ROWS_ALL = 0, GPT_ROWS_LAST = 1 };
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char *gpt_last_error(void);
+
+/*
+ * Model shape.  [microgpt "Core architecture"]: pre-norm blocks with a
+ * weightless RMSNorm (x / sqrt(mean(x^2) + norm_eps)), no biases, residual
+ * connections, a two-layer MLP, an untied output projection.
+ * [nanochat-launch tricks]: rotary positions, ReLU^2 MLP, separate Q/K/V.
+ * [nanochat-forum]: QK normalisation and multi-query attention.
+ *
+ *   pos_kind  GPT_POS_LEARNED: x = WTE[id] + WPE[t]  (microgpt layout)
+ *             GPT_POS_ROPE:    x = WTE[id]; q, k rotated by half-split RoPE
+ *   act       GPT_ACT_RELU (max(z,0)) or GPT_ACT_RELU2 (max(z,0)^2)
+ *   qk_norm   1: weightless RMSNorm of every q and k head vector after RoPE
+ *   max_seq   rows of the RoPE tables / WPE; upper bound on any position
+ *
+ * Supported: bf16 needs head_dim == 128, pos_kind ROPE, d_model % 128 == 0,
+ * d_ff % 128 == 0, n_head % n_kv_head == 0; fp32 needs head_dim <= 64 and
+ * d_model <= 1024 (a small-model path).  Anything else is GPT_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  int32_t vocab, n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, max_seq;
+  float rope_base, norm_eps;
+  int32_t pos_kind, act, qk_norm, dtype;
+} gpt_config;
+
+/*
+ * Weights.  wte [vocab, d_model]; wpe [max_seq, d_model] (NULL unless
+ * pos_kind == GPT_POS_LEARNED); lm_head [vocab, d_model].  Per layer l
+ * (host arrays of n_layer device pointers): wq[l] [n_head*head_dim, d_model],
+ * wk[l], wv[l] [n_kv_head*head_dim, d_model], wo[l] [d_model, n_head*head_dim],
+ * w1[l] [d_ff, d_model], w2[l] [d_model, d_ff].  All device, row-major, in
+ * the config dtype, 16-byte aligned.
+ */
+typedef struct {
+  const void *wte, *wpe, *lm_head;
+  const void *const *wq, *const *wk, *const *wv, *const *wo, *const *w1, *const *w2;
+} gpt_weights;
+
+/*
+ * rope_tables -- [nanochat-launch tricks]: rotary cos/sin values depend on no
+ * trained parameter, so they are computed once and kept in GPU memory.
+ * Writes cos_out[t*(head_dim/2) + i] = cos(t * base^(-2i/head_dim)) and the
+ * same for sin, t < max_seq, i < head_dim/2, fp32 device arrays.  Angles and
+ * cos/sin are evaluated in fp64 on the host and rounded once to fp32, then
+ * copied with one stream-ordered transfer each.
+ * Errors: GPT_ERR_ARG for max_seq <= 0, odd or non-positive head_dim,
+ * base <= 0, NULL outputs; GPT_ERR_HIP if the copy cannot be enqueued.
+ */
+gpt_status rope_tables(int32_t max_seq, int32_t head_dim, float base, float *cos_out,
+                       float *sin_out, gpt_stream_t stream);
+
+/*
+ * Paged KV cache -- [nanochat-launch tricks] and [microgpt "Core
+ * architecture", item 7]: keys and values of earlier positions are kept so a
+ * decode step only computes the new position.
+ *
+ * Layout of the caller's device buffer (offsets 256-byte aligned):
+ *   pages   [n_layer][n_pages][2][page]   n_pages = n_seqs * ceil(capacity/page_size)
+ *           K half: [page_size][n_kv_head*head_dim], row per position
+ *           V half: bf16: [n_kv_head*head_dim][page_size] (transposed, so the
+ *                   decode kernel's P*V operand is contiguous along positions);
+ *                   fp32: [page_size][n_kv_head*head_dim]
+ *           keys are stored after RoPE and QK-norm, as attention reads them.
+ *   table   int32 [n_seqs][pages_per_seq]  page index of each logical page;
+ *           sequence s owns pages s*pages_per_seq .. (s+1)*pages_per_seq-1.
+ *   lens    int32 [n_seqs]  cached positions per sequence (device copy; the
+ *           handle keeps a host mirror so capacity checks need no sync).
+ *
+ * kv_cache_alloc: with device_buf == NULL, stores the required byte count in
+ * *bytes_inout and returns GPT_OK (out may be NULL).  With a buffer, checks
+ * *bytes_inout >= required, writes the page table and zero lengths with
+ * blocking copies, and returns a new handle in *out.  page_size must be 64.
+ * Errors: GPT_ERR_ARG (NULL config/bytes_inout/out, n_seqs or capacity <= 0,
+ * capacity > max_seq, buffer too small), GPT_ERR_UNSUPPORTED (page_size),
+ * GPT_ERR_HIP.
+ * kv_cache_free releases the handle only; the device buffer stays the
+ * caller's.  kv_cache_lengths copies the host mirror of the lengths.
+ */
+typedef struct gpt_kv_cache gpt_kv_cache;
+gpt_status kv_cache_alloc(const gpt_config *c, int32_t n_seqs, int32_t capacity_per_seq,
+                          int32_t page_size, void *device_buf, size_t *bytes_inout,
+                          gpt_kv_cache **out);
+gpt_status kv_cache_free(gpt_kv_cache *kv);
+gpt_status kv_cache_lengths(const gpt_kv_cache *kv, int32_t *lens_out);
+
+/*
+ * gpt_workspace_bytes -- bytes of device scratch that gpt_prefill and
+ * gpt_decode_step need for up to max_tokens packed rows (prefill: total
+ * prompt tokens; decode: number of sequences) and up to max_seqs sequences.
+ * Returns 0 for an invalid or unsupported config.
+ */
+size_t gpt_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_seqs);
+
+/*
+ * gpt_prefill -- full-sequence forward of packed, variable-length prompts.
+ * [microgpt "Core architecture"], [nanochat-launch tricks], [nanochat-forum]:
+ *   x = WTE[id] (+ WPE[t]); per layer: h = rms(x); q,k,v = Wq h, Wk h, Wv h;
+ *   q,k rotated (RoPE) and normalised (QK-norm); causal attention of every
+ *   query head against the K/V head floor(h*Hkv/H) with scale 1/sqrt(dh);
+ *   x += Wo o; x += W2 act(W1 rms(x)).  logits = W_lm rms(x); lse = log sum
+ *   exp(logits); probs = exp(logits - lse)  [microgpt "Core architecture" 2].
+ *
+ *   tokens      device int32 [total], sequences packed back to back
+ *   cu_seqlens  HOST int32 [n_seqs+1], cu_seqlens[0] = 0, non-decreasing,
+ *               every sequence non-empty, total = cu_seqlens[n_seqs] <= the
+ *               workspace's max_tokens, every length <= max_seq
+ *   kv          NULL: no cache.  Otherwise the sequences' K/V (positions
+ *               0..len-1) are written into it and its lengths set to len
+ *               (n_seqs must equal the handle's; GPT_ERR_CAPACITY if a length
+ *               exceeds its capacity).  [nanochat-launch tricks]: the forward
+ *               branches on whether a cache is present.
+ *   logits_rows GPT_ROWS_ALL: logits/lse/probs have `total` rows in packed
+ *               order; GPT_ROWS_LAST: one row per sequence (its last position)
+ *   logits      device fp32 [rows, vocab] (required)
+ *   lse, probs  device fp32 [rows] and [rows, vocab], each may be NULL
+ *   rope_cos/rope_sin  tables from rope_tables() with >= max_seq rows
+ *               (may be NULL when pos_kind == GPT_POS_LEARNED)
+ *   workspace   device, >= gpt_workspace_bytes(c, total, n_seqs) bytes,
+ *               256-byte aligned; clobbered
+ */
+gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                       const float *rope_sin, const int32_t *tokens, const int32_t *cu_seqlens,
+                       int32_t n_seqs, gpt_kv_cache *kv, int32_t logits_rows, float *logits,
+                       float *lse, float *probs, void *workspace, size_t workspace_bytes,
+                       gpt_stream_t stream);
+
+/*
+ * gpt_decode_step -- one KV-cache decode step for every sequence of `kv`
+ * ([nanochat-csdn] Engine with KV cache, prefill and decode; [microgpt
+ * "Inference"] feed the previous token back).  Sequence s embeds
+ * tokens_in[s] at position t = len_s, appends its K/V at t, attends over
+ * positions 0..t, and its length becomes t+1.  Then the next token is chosen
+ * from its logits:
+ *   temperature <= 0: greedy, the lowest index among the maxima;
+ *   temperature  > 0: p = softmax(logits / temperature), token = the smallest
+ *                     i with sum_{j<=i} p_j > uniforms[s]; if rounding leaves
+ *                     the total <= u, the last index with p > 0
+ *                     ([microgpt "Inference"]: lower temperature sharpens).
+ *   tokens_in   device int32 [n_seqs]; tokens_out device int32 [n_seqs]
+ *               (may alias tokens_in)
+ *   uniforms    device fp32 [n_seqs] in [0,1), required iff temperature > 0
+ *   logits      device fp32 [n_seqs, vocab] or NULL (then kept in workspace)
+ *   workspace   >= gpt_workspace_bytes(c, n_seqs, n_seqs) bytes
+ * Errors: GPT_ERR_CAPACITY if some len_s + 1 > capacity (checked on the host
+ * mirror, nothing enqueued), GPT_ERR_ARG, GPT_ERR_UNSUPPORTED, GPT_ERR_HIP.
+ */
+gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                           const float *rope_sin, gpt_kv_cache *kv, const int32_t *tokens_in,
+                           float temperature, const float *uniforms, int32_t *tokens_out,
+                           float *logits, void *workspace, size_t workspace_bytes,
+                           gpt_stream_t stream);
+
+/*
+ * gpt_select_tokens -- token choice on rows of given logits, with the same
+ * rule as gpt_decode_step (greedy or inverse-CDF temperature sampling).
+ * Used for the first token after a prefill.  logits device fp32 [rows, vocab];
+ * uniforms device fp32 [rows] (required iff temperature > 0); tokens_out
+ * device int32 [rows].  No workspace.
+ */
+gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, float temperature,
+                             const float *uniforms, int32_t *tokens_out, gpt_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_BLOCK_FWD_GPT_H */

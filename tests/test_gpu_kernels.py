@@ -1,0 +1,105 @@
+"""Single-kernel parity on the GPU: the MFMA GEMMs (every epilogue, ragged
+tiles, the decode-row kernel) and prefill attention on ragged packed
+batches, each against a plain float64 definition on the same bf16 inputs."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import bf16_round, to_dev_bf16, torch
+
+pytestmark = pytest.mark.gpu
+
+B = pytest.importorskip("gpt_block_fwd_amd.binding")
+
+GEMM_SHAPES = [
+    # (M, N, K): several 256x256 tiles with ragged M, N = 4.5 tiles, odd tile counts
+    (300, 384, 192),
+    (1000, 1152, 768),
+    (513, 1920, 1664),
+    # decode-row kernel (M <= 64)
+    (1, 128, 64),
+    (33, 768, 768),
+    (64, 1024, 3072),
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+def test_gemm_matches_float64(M, N, K, epi):
+    t = torch()
+    rng = np.random.default_rng(M * 7 + N + K + epi)
+    A = bf16_round(rng.standard_normal((M, K)))
+    W = bf16_round(rng.standard_normal((N, K)) * 0.05)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    dA, dW = to_dev_bf16(A), to_dev_bf16(W)
+    if epi in (0, 1):
+        C = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+    else:
+        init = rng.standard_normal((M, N)).astype(np.float32) if epi == 2 else np.zeros((M, N), np.float32)
+        C = t.from_numpy(init).cuda()
+    B.gpt_debug_gemm(dA, dW, M, N, K, C, epi)
+    t.cuda.synchronize()
+    out = C.float().cpu().numpy().astype(np.float64)
+    scale = np.sqrt(K) * 0.05
+    if epi == 0:
+        np.testing.assert_allclose(out, ref, rtol=2 ** -8, atol=1e-5 * scale)
+    elif epi == 1:
+        r2 = np.maximum(ref, 0) ** 2
+        np.testing.assert_allclose(out, r2, rtol=2 ** -7, atol=1e-5 * scale ** 2)
+    elif epi == 2:
+        np.testing.assert_allclose(out, init + ref, rtol=1e-5, atol=1e-5 * scale)
+    else:
+        np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-5 * scale)
+
+
+def test_gemm_is_deterministic():
+    t = torch()
+    rng = np.random.default_rng(3)
+    M, N, K = 777, 1024, 768
+    dA = to_dev_bf16(bf16_round(rng.standard_normal((M, K))))
+    dW = to_dev_bf16(bf16_round(rng.standard_normal((N, K)) * 0.05))
+    outs = []
+    for _ in range(2):
+        C = t.empty((M, N), dtype=t.float32, device="cuda")
+        B.gpt_debug_gemm(dA, dW, M, N, K, C, 3)
+        outs.append(C.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def _attn_case(lens, H, seed):
+    rng = np.random.default_rng(seed)
+    total = int(np.sum(lens))
+    # unit-RMS q and k, as QK-norm leaves them
+    q = oracle.rmsnorm(rng.standard_normal((total, H, 128)), 1e-6)
+    k = oracle.rmsnorm(rng.standard_normal((total, 1, 128)), 1e-6)
+    v = rng.standard_normal((total, 1, 128)) * 0.5
+    return bf16_round(q), bf16_round(k), bf16_round(v)
+
+
+@pytest.mark.parametrize("lens,H", [([1, 63, 64, 65, 300], 6), ([2048], 6), ([129, 7, 1000], 13),
+                                    ([256], 1)])
+def test_prefill_attention_matches_oracle(lens, H):
+    t = torch()
+    q, k, v = _attn_case(lens, H, seed=sum(lens) + H)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pads = [(L + 63) // 64 * 64 for L in lens]
+    cu_pad = np.concatenate([[0], np.cumsum(pads)]).astype(np.int64)
+    ldvt = int(cu_pad[-1])
+    vt = np.full((128, ldvt), np.nan, np.float32)  # padding must never be read as data
+    for b, L in enumerate(lens):
+        vt[:, cu_pad[b]:cu_pad[b] + L] = v[cu[b]:cu[b + 1], 0, :].T
+    dq = to_dev_bf16(q.reshape(len(q), -1))
+    dk = to_dev_bf16(k.reshape(len(k), -1))
+    dvt = to_dev_bf16(vt)
+    cu_dev = t.zeros(2 * (len(lens) + 1), dtype=t.int32, device="cuda")
+    o = t.empty((len(q), H * 128), dtype=t.bfloat16, device="cuda")
+    B.gpt_debug_attn_prefill(dq, dk, dvt, ldvt, cu, len(lens), H, cu_dev, o)
+    t.cuda.synchronize()
+    got = o.float().cpu().numpy().reshape(len(q), H, 128)
+    assert np.isfinite(got).all()
+    for b in range(len(lens)):
+        s = slice(cu[b], cu[b + 1])
+        ref = oracle.causal_attention(q[s].astype(np.float64), k[s].astype(np.float64),
+                                      v[s].astype(np.float64), 0)
+        # error budget: P rounded to bf16 (2^-9 relative) and the bf16 output
+        np.testing.assert_allclose(got[s], ref, atol=1.5e-2, rtol=1e-2)
