@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the decoder-block forward on one MI355X.
+
+One step = one prefill of the depth-12 workload (8 sequences x 2048
+uniform tokens) through every layer, the LM head over all positions and the
+vocabulary softmax (LSE); ``value`` is prefill tokens/s with inputs and
+weights resident in HBM.  The same run also reports:
+
+* decode: depth-12, 32 prompts of 512 prefilled, then 256 greedy steps
+  (tokens/s over the step loop);
+* depth-26 prefill (16 x 2048) and depth-26 serving (64 prompts of
+  U[64, 2048] tokens, 512 temperature-0.7 steps), unless --skip-d26;
+* roofline: the bf16 GEMM kernel (all block GEMMs + LM head of the timed
+  prefills), algorithmic FLOPs / kernel time from HIP events recorded by the
+  library on its launch stream, against the 2.5 PFLOP/s dense bf16 peak;
+  decode attention bytes / time against 8 TB/s;
+* cpu_baseline: the oracle (numpy, fp32 BLAS) on the depth-12 prefill
+  workload, timed on the host cores; its logits also give a parity sample.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill tokens/s + decode tokens/s (depth 12/26, 1 GPU); % MFMA / HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prof_read(B, names):
+    out = {"ms": 0.0, "launches": 0, "flops": 0.0, "bytes": 0.0}
+    for n in names:
+        r = B.gpt_profile_read(B.PROF_CLASSES[n])
+        for k in out:
+            out[k] += r[k]
+    return out
+
+
+def bench_prefill(B, torch, dm, w, steps, warmup, prof_mask=0):
+    n = w.n_seqs
+    cu = w.cu_seqlens
+    M = int(cu[-1])
+    rows = M if w.logits_rows == "all" else n
+    logits = torch.empty((rows, dm.model.vocab), dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    tokens = torch.from_numpy(w.tokens).cuda()
+    ws = dm.workspace(M, n)
+    mode = B.ROWS_ALL if w.logits_rows == "all" else B.ROWS_LAST
+    for _ in range(warmup):
+        dm.prefill(tokens, cu, logits, lse, logits_rows=mode, workspace=ws)
+    torch.cuda.synchronize()
+    B.gpt_profile_enable(prof_mask)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dm.prefill(tokens, cu, logits, lse, logits_rows=mode, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return dt, logits, lse
+
+
+def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
+    """Prefill the prompts into a fresh cache, pick the first token, then time
+    `steps` decode steps (selection included)."""
+    n = w.n_seqs
+    cu = w.cu_seqlens
+    cap = int(w.seqlens.max()) + steps
+    kv = B.DeviceKV(dm, n, cap)
+    tokens = torch.from_numpy(w.tokens).cuda()
+    logits = torch.empty((n, dm.model.vocab), dtype=torch.float32, device="cuda")
+    pws = dm.workspace(int(cu[-1]), n)
+    dws = dm.workspace(n, n)
+    toks = torch.empty(n, dtype=torch.int32, device="cuda")
+    U = torch.from_numpy(w.uniforms).cuda() if w.uniforms is not None else None
+
+    def start():
+        dm.prefill(tokens, cu, logits, kv=kv.handle, logits_rows=B.ROWS_LAST, workspace=pws)
+        B.gpt_select_tokens(logits, n, dm.model.vocab, temperature,
+                            U[0] if U is not None else None, toks)
+
+    start()
+    for s in range(warm_steps):
+        dm.decode_step(kv.handle, toks, toks, temperature=temperature,
+                       uniforms=U[s + 1] if U is not None else None, workspace=dws)
+    start()  # re-prefill resets the cached lengths
+    torch.cuda.synchronize()
+    B.gpt_profile_enable(1 << B.PROF_CLASSES["decode_attn"] | 1 << B.PROF_CLASSES["skinny"]
+                         | 1 << B.PROF_CLASSES["lmhead"])
+    t0 = time.perf_counter()
+    for s in range(steps):
+        dm.decode_step(kv.handle, toks, toks, temperature=temperature,
+                       uniforms=U[s + 1] if U is not None else None, workspace=dws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    att = prof_read(B, ["decode_attn"])
+    sk = prof_read(B, ["skinny", "lmhead"])
+    kv.close()
+    return dt, att, sk
+
+
+def cpu_baseline(w, W, gpu_logits):
+    """Time the oracle (fp32 BLAS) over every sequence of the workload on the
+    host cores, and compare its logits with the GPU's (parity sample)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    cu = w.cu_seqlens
+    total, maxd, agree, rows = 0.0, 0.0, 0, 0
+    for b in range(w.n_seqs):
+        t0 = time.perf_counter()
+        ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[b])
+        total += time.perf_counter() - t0
+        g = gpu_logits[cu[b]:cu[b + 1]]
+        maxd = max(maxd, float(np.max(np.abs(g.astype(np.float64) - ref[0]))))
+        agree += int(np.sum(np.argmax(g, -1) == np.argmax(ref[0], -1)))
+        rows += len(g)
+        del ref
+    out = {"value": round(rows / total, 2), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"all {w.n_seqs} depth-12 sequences ({rows} tokens), numpy fp32 BLAS, "
+                     f"{total:.1f} s"}
+    parity = {"rows": rows, "max_abs": maxd, "top1": agree / rows}
+    return out, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--skip-d26", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decoder-block path has no multi-GPU "
+              "sharding in this build (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gpt_block_fwd_amd import binding as B
+    B.lib()
+    torch.cuda.set_device(0)
+
+    # ---------------- depth-12 prefill (the headline)
+    w2 = wl.d12_prefill()
+    log("generating depth-12 weights")
+    W12 = wl.make_weights(w2.model)
+    dm12 = B.DeviceModel(w2.model, W12)
+    gemm_mask = 1 << B.PROF_CLASSES["gemm"] | 1 << B.PROF_CLASSES["lmhead"] | \
+        1 << B.PROF_CLASSES["attn"] | 1 << B.PROF_CLASSES["norm"] | 1 << B.PROF_CLASSES["softmax"]
+    log("timing depth-12 prefill")
+    dt, logits, lse = bench_prefill(B, torch, dm12, w2, args.steps, args.warmup, gemm_mask)
+    M = int(w2.cu_seqlens[-1])
+    value = args.steps * M / dt
+    g = prof_read(B, ["gemm", "lmhead"])
+    attn = prof_read(B, ["attn"])
+    norm = prof_read(B, ["norm"])
+    smx = prof_read(B, ["softmax"])
+    gemm_tfs = g["flops"] / (g["ms"] * 1e-3) / 1e12
+    attn_tfs = attn["flops"] / (attn["ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_bf16 (block GEMMs + LM head)",
+                "achieved": round(gemm_tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
+                "flops_per_launch": g["flops"] / max(g["launches"], 1)}
+    breakdown = {
+        "gemm_ms_per_step": round(g["ms"] / args.steps, 3),
+        "attention": {"ms_per_step": round(attn["ms"] / args.steps, 3),
+                      "achieved_tflops": round(attn_tfs, 1),
+                      "frac": round(attn_tfs / PEAK_BF16_TFLOPS, 4)},
+        "norm_rope_embed_ms_per_step": round(norm["ms"] / args.steps, 3),
+        "softmax_ms_per_step": round(smx["ms"] / args.steps, 3),
+    }
+    log(f"d12 prefill: {value:,.0f} tok/s, gemm {gemm_tfs:.0f} TFLOP/s, attn {attn_tfs:.0f} TFLOP/s")
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(dt / args.steps * 1e3, 3), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "d12_prefill", "batch": 8, "seq_len": 2048, "layers": 12,
+                      "d_model": 768, "heads": 6, "kv_heads": 1, "vocab": 65536,
+                      "logits": "all rows + lse"},
+           "roofline": roofline, "prefill_breakdown": breakdown}
+
+    g0 = logits.cpu().numpy() if not args.skip_cpu else None
+    del logits, lse
+    torch.cuda.empty_cache()
+
+    # ---------------- depth-12 decode
+    if not args.skip_decode:
+        w3 = wl.d12_decode(steps=args.decode_steps)
+        log("timing depth-12 decode")
+        ddt, att, sk = bench_decode(B, torch, dm12, w3, args.decode_steps, 0.0)
+        att_gbs = att["bytes"] / (att["ms"] * 1e-3) / 1e9 if att["ms"] else 0.0
+        sk_gbs = sk["bytes"] / (sk["ms"] * 1e-3) / 1e9 if sk["ms"] else 0.0
+        out["decode"] = {"workload": "d12_decode", "batch": 32, "prompt": 512,
+                         "steps": args.decode_steps,
+                         "tokens_per_s": round(32 * args.decode_steps / ddt, 1),
+                         "ms_per_step": round(ddt / args.decode_steps * 1e3, 4),
+                         "decode_attention": {"achieved_gbs": round(att_gbs, 1),
+                                              "frac": round(att_gbs / PEAK_HBM_GBS, 4),
+                                              "us_per_launch": round(att["ms"] * 1e3 / max(att["launches"], 1), 2)},
+                         "decode_gemms": {"achieved_gbs": round(sk_gbs, 1),
+                                          "frac": round(sk_gbs / PEAK_HBM_GBS, 4)}}
+        log(f"d12 decode: {out['decode']['tokens_per_s']:,.0f} tok/s")
+
+    # ---------------- CPU oracle on one sequence
+    if not args.skip_cpu:
+        log("timing the oracle on the host")
+        cb, parity = cpu_baseline(w2, W12, g0)
+        out["cpu_baseline"] = cb
+        out["parity_sample"] = parity
+    del dm12
+    torch.cuda.empty_cache()
+
+    # ---------------- depth 26
+    if not args.skip_d26:
+        w4 = wl.d26_prefill()
+        log("generating depth-26 weights")
+        W26 = wl.make_weights(w4.model)
+        dm26 = B.DeviceModel(w4.model, W26)
+        del W26
+        log("timing depth-26 prefill")
+        s26 = max(2, args.steps // 3)
+        dt4, lg4, _ = bench_prefill(B, torch, dm26, w4, s26, 1,
+                                    1 << B.PROF_CLASSES["gemm"] | 1 << B.PROF_CLASSES["lmhead"]
+                                    | 1 << B.PROF_CLASSES["attn"])
+        del lg4
+        torch.cuda.empty_cache()
+        g4 = prof_read(B, ["gemm", "lmhead"])
+        a4 = prof_read(B, ["attn"])
+        M4 = int(w4.cu_seqlens[-1])
+        out["d26_prefill"] = {"workload": "d26_prefill", "batch": 16, "seq_len": 2048,
+                              "tokens_per_s": round(s26 * M4 / dt4, 1),
+                              "ms_per_step": round(dt4 / s26 * 1e3, 3),
+                              "gemm_tflops": round(g4["flops"] / (g4["ms"] * 1e-3) / 1e12, 1),
+                              "attn_tflops": round(a4["flops"] / (a4["ms"] * 1e-3) / 1e12, 1)}
+        log(f"d26 prefill: {out['d26_prefill']['tokens_per_s']:,.0f} tok/s")
+        if not args.skip_decode:
+            w5 = wl.d26_serving(steps=512)
+            log("timing depth-26 serving decode")
+            ddt5, att5, sk5 = bench_decode(B, torch, dm26, w5, 512, 0.7)
+            att_gbs = att5["bytes"] / (att5["ms"] * 1e-3) / 1e9 if att5["ms"] else 0.0
+            out["d26_serving"] = {"workload": "d26_serving", "batch": 64,
+                                  "prompt": "U[64,2048]", "steps": 512, "temperature": 0.7,
+                                  "tokens_per_s": round(64 * 512 / ddt5, 1),
+                                  "ms_per_step": round(ddt5 / 512 * 1e3, 4),
+                                  "decode_attention": {"achieved_gbs": round(att_gbs, 1),
+                                                       "frac": round(att_gbs / PEAK_HBM_GBS, 4)}}
+            log(f"d26 serving: {out['d26_serving']['tokens_per_s']:,.0f} tok/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
