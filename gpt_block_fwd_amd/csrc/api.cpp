@@ -129,7 +129,7 @@ gpt_status check_config(const gpt_config *c) {
 
 struct Bufs {
   int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
-  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits;
+  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart;
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
   int max_splits;
@@ -167,6 +167,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
+  t.lpart = (float *)take(M * (long long)((c->vocab + 127) / 128) * 2 * 4);
   if (b) *b = t;
   return align256(off);
 }
@@ -232,7 +233,8 @@ GemmArgs gemm(const void *A, long long lda, const void *W, int M, int N, int K, 
 
 void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
   const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
-  double out_b = g.epi == EPI_RESID ? 8.0 : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16) ? es : 4.0;
+  double out_b = g.epi == EPI_RESID ? 8.0
+                 : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV) ? es : 4.0;
   bool skinny = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
   Timed t(skinny && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
           es * ((double)g.M * g.K + (double)g.N * g.K) + out_b * g.M * g.N);
@@ -432,33 +434,53 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
       if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
       else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, M, d, c->norm_eps, s);
     }
-    GemmArgs g = gemm(bf.h, d, w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+    const bool fused_qkv = bf16p && M > 64;
+    GemmArgs g = gemm(bf.h, d, w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, fused_qkv ? EPI_QKV : EPI_F32);
     g.W1 = w->wk[l];
     g.W2 = w->wv[l];
     g.n1 = H * dh;
     g.n2 = (H + Hkv) * dh;
+    if (fused_qkv) {
+      QkvEpi &e = g.qkv;
+      e.seq = bf.seq;
+      e.pos = bf.pos;
+      e.vcol = bf.vcol;
+      e.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+      e.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+      e.eps = c->norm_eps;
+      e.qk_norm = c->qk_norm;
+      e.H = H;
+      e.Hkv = Hkv;
+      e.q_out = (bf16 *)bf.q;
+      e.k_out = (bf16 *)bf.k;
+      e.vt_out = (bf16 *)bf.vt;
+      e.ldvt = bf.ldvt;
+      e.kv = pv;
+      e.layer = l;
+      e.use_cache = kv != nullptr;
+    }
     run_gemm(c, g, GPT_PROF_GEMM, s);
-    ScatterArgs sa{};
-    sa.qkv = bf.qkv;
-    sa.M = M;
-    sa.H = H;
-    sa.Hkv = Hkv;
-    sa.seq = bf.seq;
-    sa.pos = bf.pos;
-    sa.vcol = bf.vcol;
-    sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
-    sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
-    sa.qk_norm = c->qk_norm;
-    sa.eps = c->norm_eps;
-    sa.q_out = bf.q;
-    sa.k_out = bf.k;
-    sa.vt_out = bf.vt;
-    sa.ldvt = bf.ldvt;
-    sa.kv = pv;
-    sa.layer = l;
-    sa.use_cache = kv != nullptr;
-    sa.head_dim = dh;
-    {
+    if (!fused_qkv) {
+      ScatterArgs sa{};
+      sa.qkv = bf.qkv;
+      sa.M = M;
+      sa.H = H;
+      sa.Hkv = Hkv;
+      sa.seq = bf.seq;
+      sa.pos = bf.pos;
+      sa.vcol = bf.vcol;
+      sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+      sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+      sa.qk_norm = c->qk_norm;
+      sa.eps = c->norm_eps;
+      sa.q_out = bf.q;
+      sa.k_out = bf.k;
+      sa.vt_out = bf.vt;
+      sa.ldvt = bf.ldvt;
+      sa.kv = pv;
+      sa.layer = l;
+      sa.use_cache = kv != nullptr;
+      sa.head_dim = dh;
       Timed t(GPT_PROF_NORM, s, 0, (double)M * qkv_n * 4 + (double)M * qkv_n * (bf16p ? 2 : 4));
       if (bf16p) launch_rope_norm_scatter_bf16(sa, s);
       else launch_qkv_scatter_f32(sa, s);
@@ -512,8 +534,15 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
     if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, sel, rows, d, c->norm_eps, s);
     else launch_rmsnorm_f32(bf.x, (float *)bf.h, sel, rows, d, c->norm_eps, s);
   }
-  run_gemm(c, gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, EPI_F32), GPT_PROF_LMHEAD, s);
-  if (lse || probs) {
+  const bool want_lse = lse || probs;
+  const bool fused_lse = want_lse && bf16p && rows > 64;
+  GemmArgs lg = gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
+  lg.part = bf.lpart;
+  run_gemm(c, lg, GPT_PROF_LMHEAD, s);
+  if (fused_lse) {
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * (V / 128) * 8 + (probs ? (double)rows * V * 8 : 0.0));
+    launch_lse_combine(bf.lpart, V / 128, rows, lse ? lse : bf.lse_tmp, logits, V, probs, s);
+  } else if (want_lse) {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * V * 4 * (probs ? 3 : 1));
     launch_softmax_lse(logits, rows, V, lse ? lse : bf.lse_tmp, probs, s);
   }

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   __syncthreads();
   for (int kt = 0; kt < n_kt - 1; ++kt) {
     gload(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the tile's MFMAs
     tile(kt, kt & 1);
     sstore((kt + 1) & 1);
     __syncthreads();

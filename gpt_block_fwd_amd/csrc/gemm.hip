@@ -14,13 +14,19 @@
 // Skinny kernel (decode, M <= 64): one workgroup per 16 output columns, the
 // K range split across 8 waves, v_mfma_f32_16x16x32_bf16 fed straight from
 // global memory, partial sums reduced through LDS.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace {
 
 constexpr int BK = 64;
 
-DEV int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// LDS tile [rows][64 bf16]: 16-byte chunk c of row r is stored in slot
+// c ^ ((r / 2) % 8), so the 16 rows one ds_read_b128 phase touches (lanes
+// 0-15 of a fragment read) land in 16 distinct 16-byte bank groups.
+DEV int swz_key(int row) { return (row >> 1) & 7; }
+DEV int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 3); }
 
 DEV const bf16 *wrow(const GemmArgs &g, int n) {
   if (n < g.n1) return (const bf16 *)g.W0 + (long long)n * g.ldw;
@@ -50,11 +56,109 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
   }
 }
 
+// QKV epilogue.  The wave's 128 columns are one head: a query head, the K
+// head or the V head.  Lane (c32, hi) holds, for row m, the columns
+// 32 i + 8 c + 4 hi + e (i, c, e < 4), so the rotary partners (p, p + 64) are
+// acc[i] and acc[i + 2] of the same lane.  q and k are rotated by the tabled
+// angle of their position, then divided by their RMS over the head (the
+// partner lane l ^ 32 holds the other 64 columns), and stored as bf16; v is
+// stored transposed for the attention kernels.
+template <int TM>
+DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int c32, int hi) {
+  const QkvEpi &e = g.qkv;
+  const int head = nw0 / 128;
+  const bool is_q = head < e.H, is_k = !is_q && head < e.H + e.Hkv;
+  const int kvh = is_q ? 0 : (is_k ? head - e.H : head - e.H - e.Hkv);
+  const int kvd = e.Hkv * 128;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    __builtin_amdgcn_sched_barrier(0);  // one row block at a time (register pressure)
+    const int m = mw0 + 32 * j + c32;
+    const int mm = min(m, g.M - 1);
+    const int p = e.pos[mm];
+    if (!(is_q || is_k)) {
+      // V: transposed store v^T[dim][column of the row]
+      if (m < g.M) {
+        const long long col = e.vcol ? e.vcol[m] : m;
+        bf16 *cv = nullptr;
+        int slot = 0;
+        if (e.use_cache) {
+          const int b = e.seq ? e.seq[m] : m;
+          const int page = e.kv.table[b * e.kv.pages_per_seq + p / e.kv.page_size];
+          slot = p % e.kv.page_size;
+          cv = (bf16 *)(e.kv.base + (long long)e.layer * e.kv.layer_stride +
+                        (long long)page * e.kv.page_stride + e.kv.half_bytes);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dim = kvh * 128 + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bf16 y = f2bf(acc[i][j][r]);
+            if (e.vt_out) e.vt_out[(long long)dim * e.ldvt + col] = y;
+            if (cv) cv[(long long)dim * e.kv.page_size + slot] = y;
+          }
+      }
+      continue;
+    }
+    if (e.cos) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int pi = 32 * i + 8 * c + 4 * hi;
+          const float4 cs = *(const float4 *)(e.cos + (long long)p * 64 + pi);
+          const float4 sn = *(const float4 *)(e.sin + (long long)p * 64 + pi);
+          const float cc[4] = {cs.x, cs.y, cs.z, cs.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a = acc[i][j][4 * c + q], b = acc[i + 2][j][4 * c + q];
+            acc[i][j][4 * c + q] = a * cc[q] - b * ss[q];
+            acc[i + 2][j][4 * c + q] = a * ss[q] + b * cc[q];
+          }
+        }
+    }
+    float rs = 1.0f;
+    if (e.qk_norm) {
+      float ssum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ssum += acc[i][j][r] * acc[i][j][r];
+      ssum += __shfl_xor(ssum, 32, 64);
+      rs = 1.0f / sqrtf(ssum * (1.0f / 128.0f) + e.eps);
+    }
+    if (m >= g.M) continue;
+    bf16 *dst = is_q ? e.q_out + (long long)m * e.H * 128 + head * 128
+                     : (e.k_out ? e.k_out + (long long)m * kvd + kvh * 128 : nullptr);
+    bf16 *ck = nullptr;
+    if (is_k && e.use_cache) {
+      const int b = e.seq ? e.seq[m] : m;
+      const int page = e.kv.table[b * e.kv.pages_per_seq + p / e.kv.page_size];
+      ck = (bf16 *)(e.kv.base + (long long)e.layer * e.kv.layer_stride + (long long)page * e.kv.page_stride) +
+           (long long)(p % e.kv.page_size) * kvd + kvh * 128;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = 32 * i + 8 * c + 4 * hi;
+        bf16x4 o = {f2bf(acc[i][j][4 * c] * rs), f2bf(acc[i][j][4 * c + 1] * rs),
+                    f2bf(acc[i][j][4 * c + 2] * rs), f2bf(acc[i][j][4 * c + 3] * rs)};
+        if (dst) *(bf16x4 *)(dst + col) = o;
+        if (ck) *(bf16x4 *)(ck + col) = o;
+      }
+  }
+}
+
+#define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
+#define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LA = BM / 32, LB = BN / 32;
+  constexpr int PA = BM / 32, PB = BN / 32;  // 1 KB direct-to-LDS loads per wave per k-tile
   __shared__ bf16 sa[2][BM * BK];
   __shared__ bf16 sb[2][BN * BK];
 
@@ -79,43 +183,44 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   const int tn = (pid % group_size) / gsize_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Global loads: thread t moves 16 bytes of row (t/8 + 32 i), chunk t%8.
-  // Row groups of 32 never straddle a weight segment (segment boundaries
-  // are multiples of 128), so each group's base pointer is wave-uniform and
-  // only a 32-bit offset lives in a lane register.
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const bf16 *abase = (const bf16 *)g.A;
-  int aoff[LA];
-  const bf16 *bbase[LB];
-  int boff[LB];
+  // Direct global->LDS loads (global_load_lds_dwordx4): one instruction of a
+  // wave fills 1 KB of LDS = 8 rows of 64 bf16, lane i landing at row i/8,
+  // 16-byte slot i%8.  The slot holds logical k-chunk (i%8) ^ swz_key(row),
+  // so the lane loads that chunk: the XOR swizzle costs nothing.  Instruction p of
+  // wave w covers rows (4p + w)*8 .. +8; 8-row groups never straddle a
+  // weight segment (segment boundaries are multiples of 128), so the row
+  // base is wave-uniform and a lane keeps a 32-bit offset.
+  const int lr = lane >> 3;
+  int aoff[PA], boff[PB];
+  const bf16 *bbase[PB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    int r = min(m0 + lrow + 32 * i, g.M - 1);
-    aoff[i] = r * (int)g.lda + lchunk * 8;
+  for (int p = 0; p < PA; ++p) {
+    const int lrow = (4 * p + wave) * 8 + lr;  // row within the tile
+    const int r = min(m0 + lrow, g.M - 1);
+    aoff[p] = r * (int)g.lda + (((lane & 7) ^ swz_key(lrow)) << 3);
   }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int nb = min(n0 + 32 * i, g.N - 32);
+  for (int p = 0; p < PB; ++p) {
+    const int nb = min(n0 + (4 * p + wave) * 8, g.N - 8);
     const bf16 *base;
     int first;
     if (nb < g.n1) { base = (const bf16 *)g.W0; first = 0; }
     else if (nb < g.n2) { base = (const bf16 *)g.W1; first = g.n1; }
     else { base = (const bf16 *)g.W2; first = g.n2; }
-    bbase[i] = base;
-    boff[i] = (nb - first + lrow) * (int)g.ldw + lchunk * 8;
+    bbase[p] = base;
+    const int lrow = (4 * p + wave) * 8 + lr;
+    boff[p] = (nb - first + lr) * (int)g.ldw + (((lane & 7) ^ swz_key(lrow)) << 3);
   }
-  bf16x8 ra[LA], rb[LB];
-  auto gload = [&](int kt) {
+  const bf16 *abase = (const bf16 *)g.A;
+  auto dma = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *(const bf16x8 *)(abase + aoff[i] + kt * BK);
+    for (int p = 0; p < PA; ++p)
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(abase + aoff[p] + kt * BK),
+                                       LDS_PTR(&sa[buf][(4 * p + wave) * 8 * BK]), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *(const bf16x8 *)(bbase[i] + boff[i] + kt * BK);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) *(bf16x8 *)&sa[buf][swz(lrow + 32 * i, lchunk)] = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) *(bf16x8 *)&sb[buf][swz(lrow + 32 * i, lchunk)] = rb[i];
+    for (int p = 0; p < PB; ++p)
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(bbase[p] + boff[p] + kt * BK),
+                                       LDS_PTR(&sb[buf][(4 * p + wave) * 8 * BK]), 16, 0, 0);
   };
 
   f32x16 acc[TN][TM];
@@ -126,49 +231,108 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
   const int KT = g.K / BK;
   const int c32 = lane & 31, hi = lane >> 5;
-  auto compute = [&](int buf) {
+  // MFMA operand fragments, double-buffered across the 16-deep k substeps
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto lfrag = [&](int f, int buf, int s) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 fa[TM], fb[TN];
+    for (int j = 0; j < TM; ++j) fa[f][j] = *(const bf16x8 *)&sa[buf][swz(wm * WM + 32 * j + c32, 2 * s + hi)];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) fa[j] = *(const bf16x8 *)&sa[buf][swz(wm * WM + 32 * j + c32, 2 * s + hi)];
-#pragma unroll
-      for (int i = 0; i < TN; ++i) fb[i] = *(const bf16x8 *)&sb[buf][swz(wn * WN + 32 * i + c32, 2 * s + hi)];
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
-    }
+    for (int i = 0; i < TN; ++i) fb[f][i] = *(const bf16x8 *)&sb[buf][swz(wn * WN + 32 * i + c32, 2 * s + hi)];
   };
-  // Double-buffered main loop: the next stage's global loads are in flight
-  // while the current stage feeds the MFMAs; one barrier per stage.
-  gload(0);
-  sstore(0);
+  auto mfmas = [&](int f) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][i], fa[f][j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // MFMA / LDS-read pairs, then the remaining MFMAs
+#pragma unroll
+    for (int q = 0; q < TM + TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
+  };
+
+  // Main loop over k-tiles.  LDS buffer kt&1 holds k-tile kt; the DMA of
+  // k-tile kt+1 into the other buffer is issued first and overlaps the four
+  // MFMA substeps of k-tile kt.  Fragments of substep s+1 are read while the
+  // MFMAs of substep s run.  The single barrier of a k-tile sits after
+  // substep 2: by then every wave has read all of buffer kt&1 and (after its
+  // vmcnt wait) landed its share of k-tile kt+1, so substep 3's MFMAs overlap
+  // the first fragment reads of k-tile kt+1.
+  dma(0, 0);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < KT - 1; ++kt) {
-    gload(kt + 1);
-    compute(kt & 1);
-    sstore((kt + 1) & 1);
+  lfrag(0, 0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) dma(kt + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lfrag(1, buf, 1);
+    mfmas(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    lfrag(0, buf, 2);
+    mfmas(1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    lfrag(1, buf, 3);
+    mfmas(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (more) lfrag(0, buf ^ 1, 0);
+    mfmas(1);
+    if (more) interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
-  compute((KT - 1) & 1);
   // A wave whose 128 columns lie beyond N computed on clamped rows; drop it.
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
+  const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of 128)
+  if constexpr (EPI == EPI_QKV) {
+    static_assert(WN == 128, "the QKV epilogue needs one head per wave");
+    epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi);
+    return;
+  } else {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int m = m0 + wm * WM + 32 * j + c32;
-      if (m >= g.M) continue;
+      const bool ok = m < g.M;
+      if constexpr (EPI == EPI_LOGITS) {
+        // partial softmax statistics of this row over the wave's 128 columns
+        float mx = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int n = n0 + wn * WN + 32 * i + 8 * c + 4 * hi;
-        epi_store4<EPI>(g, m, n, acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
-                        acc[i][j][4 * c + 3]);
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float se = 0.f;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
+        se += __shfl_xor(se, 32, 64);
+        if (ok && hi == 0) {
+          float *pp = g.part + ((long long)m * (g.N / 128) + nw0 / 128) * 2;
+          *(float2 *)pp = make_float2(mx, se);
+        }
       }
+      if (!ok) continue;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = nw0 + 32 * i + 8 * c + 4 * hi;
+          epi_store4<EPI == EPI_LOGITS ? EPI_F32 : EPI>(g, m, n, acc[i][j][4 * c], acc[i][j][4 * c + 1],
+                                                        acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]);
+        }
     }
+  }
 }
 
 // ------------------------------------------------------------------ skinny
@@ -258,6 +422,8 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
     case EPI_BF16: launch_big<EPI_BF16>(g, s); break;
     case EPI_RELU2_BF16: launch_big<EPI_RELU2_BF16>(g, s); break;
     case EPI_RESID: launch_big<EPI_RESID>(g, s); break;
+    case EPI_LOGITS: launch_big<EPI_LOGITS>(g, s); break;
+    case EPI_QKV: launch_big<EPI_QKV>(g, s); break;
     default: launch_big<EPI_F32>(g, s); break;
   }
 }

@@ -38,6 +38,9 @@ void launch_qkv_scatter_f32(const ScatterArgs &a, hipStream_t s);
 
 void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float *probs,
                         hipStream_t s);
+// lse[r] from the LM-head epilogue's per-block partials; then optional probs.
+void launch_lse_combine(const float *part, int nparts, int rows, float *lse, const float *logits,
+                        int V, float *probs, hipStream_t s);
 void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s);
 void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
                    int *out, hipStream_t s);
@@ -47,7 +50,27 @@ void launch_gather_rows_bf16(const bf16 *src, bf16 *dst, const int *rows, int n,
                              hipStream_t s);
 
 // ------------------------------------------------------------ GEMMs
-enum Epi { EPI_BF16 = 0, EPI_RELU2_BF16 = 1, EPI_RESID = 2, EPI_F32 = 3, EPI_RELU_F32 = 4 };
+enum Epi {
+  EPI_BF16 = 0,
+  EPI_RELU2_BF16 = 1,
+  EPI_RESID = 2,
+  EPI_F32 = 3,
+  EPI_RELU_F32 = 4,
+  EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each 128-column block
+  EPI_QKV = 6      // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
+};
+
+// Extra operands of the EPI_QKV epilogue (column block = one 128-wide head).
+struct QkvEpi {
+  const int *seq, *pos, *vcol;
+  const float *cos, *sin;  // [max_seq][64]
+  float eps;
+  int qk_norm, H, Hkv;
+  bf16 *q_out, *k_out, *vt_out;
+  long long ldvt;
+  PagedKV kv;
+  int layer, use_cache;
+};
 
 // C[m][n] = sum_k A[m][k] * W[n][k]; W rows come from up to three segments
 // ([0,n1) from W0, [n1,n2) from W1, [n2,N) from W2) so separate Q/K/V
@@ -62,6 +85,8 @@ struct GemmArgs {
   void *C;
   long long ldc;
   int epi;
+  float *part;  // EPI_LOGITS: [M][N/128][2] partial (max, sum exp)
+  QkvEpi qkv;   // EPI_QKV
 };
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M
 void launch_gemm_bf16_skinny(const GemmArgs &g, hipStream_t s);  // MFMA, M <= 64

@@ -290,6 +290,49 @@ void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float 
   softmax_lse_kernel<<<rows, 256, 0, s>>>(logits, V, lse, probs);
 }
 
+// lse of each row from per-block partials (max_k, sum_k) written by the
+// LM-head GEMM epilogue: lse = M + log(sum_k sum_k * exp(max_k - M)).  One
+// wave per row.  With `probs`, one 256-thread workgroup per row then writes
+// p = exp(logit - lse).
+
+__global__ __launch_bounds__(256) void lse_combine_kernel(const float *part, int nparts, int rows,
+                                                          float *lse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const float2 *pp = (const float2 *)part + (long long)r * nparts;
+  float m = -INFINITY, s = 0.f;
+  for (int i = lane; i < nparts; i += 64) {
+    float2 v = pp[i];
+    ms_merge(m, s, v.x, v.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+  }
+  if (lane == 0) lse[r] = m + logf(s);
+}
+
+__global__ __launch_bounds__(256) void probs_kernel(const float *logits, const float *lse, int V,
+                                                    float *probs) {
+  const float l = lse[blockIdx.x];
+  const float4 *row = (const float4 *)(logits + (long long)blockIdx.x * V);
+  float4 *pr = (float4 *)(probs + (long long)blockIdx.x * V);
+  for (int i = threadIdx.x; i < V / 4; i += 256) {
+    float4 x = row[i];
+    pr[i] = make_float4(fast_exp2((x.x - l) * kLog2e), fast_exp2((x.y - l) * kLog2e),
+                        fast_exp2((x.z - l) * kLog2e), fast_exp2((x.w - l) * kLog2e));
+  }
+}
+
+void launch_lse_combine(const float *part, int nparts, int rows, float *lse, const float *logits,
+                        int V, float *probs, hipStream_t s) {
+  if (rows <= 0) return;
+  lse_combine_kernel<<<(rows + 3) / 4, 256, 0, s>>>(part, nparts, rows, lse);
+  if (probs) probs_kernel<<<rows, 256, 0, s>>>(logits, lse, V, probs);
+}
+
 // ---------------------------------------------------------------- greedy
 // Argmax per row; among equal maxima the lowest index wins.
 

@@ -100,7 +100,7 @@ def test_small_bf16_prefill(n_layer, n_head, lens):
     cfg = wl.small_model(n_layer, n_head, vocab=4096)
     w = wl.ragged_prefill(cfg, lens, seed=n_layer + n_head)
     W, dm = device_model(cfg)
-    logits, lse = gpu_prefill(dm, w.tokens, w.seqlens)
+    logits, lse, probs = gpu_prefill(dm, w.tokens, w.seqlens, want_probs=True)
     ref, _ = oracle.prefill(cfg, W, w.tokens, w.seqlens)
     ref = np.concatenate(ref)
     st = logit_stats(logits, ref)
@@ -108,6 +108,11 @@ def test_small_bf16_prefill(n_layer, n_head, lens):
     assert st["max_abs"] <= 3e-2
     assert st["disagree_explained"]
     np.testing.assert_allclose(lse, oracle.logsumexp(ref), atol=3e-2)
+    # the softmax outputs are distributions consistent with the GPU's own logits
+    lg = logits.astype(np.float64)
+    np.testing.assert_allclose(lse, oracle.logsumexp(lg), atol=2e-5)
+    np.testing.assert_allclose(probs, oracle.softmax(lg), atol=2e-6)
+    np.testing.assert_allclose(probs.sum(-1), 1.0, atol=1e-4)
 
 
 def test_small_bf16_prefill_last_rows_and_cache():
