@@ -353,7 +353,8 @@ def param_count(W) -> int:
 
 def run_serving(cfg, W, tokens, seqlens, steps: int, temperature: float = 0.0,
                 uniforms: Optional[np.ndarray] = None, forced: Optional[np.ndarray] = None,
-                dtype=np.float64, seqs: Optional[Sequence[int]] = None):
+                dtype=np.float64, seqs: Optional[Sequence[int]] = None,
+                bf16_points: bool = False):
     """Prefill each prompt into a cache, then decode ``steps`` tokens.
 
     The first new token comes from the last prompt position's logits; each
@@ -363,7 +364,8 @@ def run_serving(cfg, W, tokens, seqlens, steps: int, temperature: float = 0.0,
     comparable with another implementation after a near-tie.
 
     Returns ``(chosen [steps+1, n], logits [steps+1, n, V])`` for the
-    selected sequences.
+    selected sequences.  ``bf16_points`` (noise-floor probe only) rounds at the
+    bf16 storage points as in ``block``.
     """
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
     idx = list(range(len(seqlens)) if seqs is None else seqs)
@@ -374,7 +376,7 @@ def run_serving(cfg, W, tokens, seqlens, steps: int, temperature: float = 0.0,
     last = []
     for b in idx:
         c = KVCache(cfg.n_layer)
-        last.append(forward(cfg, W, tokens[cu[b]:cu[b + 1]], c, dtype, rows="last",
+        last.append(forward(cfg, W, tokens[cu[b]:cu[b + 1]], c, dtype, bf16_points, rows="last",
                             tables=tables)[0])
         caches.append(c)
     chosen = np.zeros((steps + 1, len(idx)), np.int64)
@@ -390,6 +392,6 @@ def run_serving(cfg, W, tokens, seqlens, steps: int, temperature: float = 0.0,
         if s == steps:
             break
         feed = chosen[s] if forced is None else forced[s, idx]
-        cur = np.stack([forward(cfg, W, [int(feed[j])], caches[j], dtype, rows="last",
+        cur = np.stack([forward(cfg, W, [int(feed[j])], caches[j], dtype, bf16_points, rows="last",
                                 tables=tables)[0] for j in range(len(idx))])
     return chosen, all_logits
