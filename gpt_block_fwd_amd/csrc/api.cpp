@@ -37,6 +37,8 @@ gpt_status hip_check(const char *what) {
 }
 
 constexpr int kMaxPrefillSeqs = 512;
+constexpr int kAttnCounters = 4096;  // decode-attention page counters (one per sequence)
+constexpr int kCounters = kSkinnyCounters + kAttnCounters;
 constexpr int kPage = 64;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -129,7 +131,8 @@ gpt_status check_config(const gpt_config *c) {
 
 struct Bufs {
   int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
-  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart;
+  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart, *sel, *skpart;
+  unsigned *ctr;  // completion counters of the fused decode kernels
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
   int max_splits;
@@ -167,7 +170,10 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
-  t.lpart = (float *)take(M * (long long)((c->vocab + 127) / 128) * 2 * 4);
+  t.skpart = (float *)take(kSkinnyPartFloats * 4);
+  t.ctr = (unsigned *)take((size_t)kCounters * 4);
+  t.sel = (float *)take((size_t)argmax_scratch_floats((int)nseq, c->vocab) * 4);
+  t.lpart = (float *)take(M * (long long)((c->vocab + kLogitsPartCols - 1) / kLogitsPartCols) * 2 * 4);
   if (b) *b = t;
   return align256(off);
 }
@@ -200,7 +206,12 @@ struct PrefillMeta {
   int cu[kMaxPrefillSeqs + 1];
 };
 
-__global__ void prefill_meta_kernel(PrefillMeta m, int *cu, int *cu_pad, int *lastrows) {
+// One workgroup: device copies of cu_seqlens, the 64-padded offsets of the
+// transposed-V columns, each sequence's last row; clears the counters.
+__global__ void prefill_meta_kernel(PrefillMeta m, int *cu, int *cu_pad, int *lastrows,
+                                    unsigned *ctr, int nctr) {
+  if (ctr)
+    for (int i = threadIdx.x; i < nctr; i += blockDim.x) ctr[i] = 0u;
   for (int i = threadIdx.x; i <= m.n; i += blockDim.x) cu[i] = m.cu[i];
   if (lastrows)
     for (int i = threadIdx.x; i < m.n; i += blockDim.x) lastrows[i] = m.cu[i + 1] - 1;
@@ -231,7 +242,8 @@ GemmArgs gemm(const void *A, long long lda, const void *W, int M, int N, int K, 
   return g;
 }
 
-void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
+void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s,
+              const SkinnyFuse *fuse = nullptr) {
   const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
   double out_b = g.epi == EPI_RESID ? 8.0
                  : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV) ? es : 4.0;
@@ -239,11 +251,20 @@ void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
   Timed t(skinny && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
           es * ((double)g.M * g.K + (double)g.N * g.K) + out_b * g.M * g.N);
   if (c->dtype == GPT_DTYPE_F32) launch_gemm_f32(g, s);
-  else if (skinny) launch_gemm_bf16_skinny(g, s);
+  else if (skinny) launch_gemm_bf16_skinny(g, fuse ? *fuse : SkinnyFuse{}, s);
   else launch_gemm_bf16(g, s);
 }
 
 PagedKV paged_view(const gpt_kv_cache *kv);
+
+SkinnyFuse split_only(const Bufs &bf) {
+  SkinnyFuse f{};
+  f.part = bf.skpart;
+  f.tile_ctr = bf.ctr;
+  f.grp_ctr = bf.ctr + 4096;
+  f.mode = SK_PLAIN;
+  return f;
+}
 
 }  // namespace
 
@@ -403,6 +424,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   hipGetLastError();  // clear any stale error from unrelated work
   Bufs bf;
   carve(c, M, n_seqs, (char *)workspace, &bf);
+  const SkinnyFuse spl = split_only(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;
@@ -413,7 +435,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   for (int b = 0; b <= n_seqs; ++b) meta.cu[b] = cu_seqlens[b];
   {
     Timed t(GPT_PROF_NORM, s, 0, 0);
-    prefill_meta_kernel<<<1, 256, 0, s>>>(meta, bf.cu, bf.cu_pad, bf.lastrows);
+    prefill_meta_kernel<<<1, 256, 0, s>>>(meta, bf.cu, bf.cu_pad, bf.lastrows, bf.ctr, kCounters);
     launch_rowinfo(bf.cu, bf.cu_pad, n_seqs, M, bf.seq, bf.pos, bf.vcol, s);
   }
   PagedKV pv{};
@@ -459,7 +481,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
       e.layer = l;
       e.use_cache = kv != nullptr;
     }
-    run_gemm(c, g, GPT_PROF_GEMM, s);
+    run_gemm(c, g, GPT_PROF_GEMM, s, &spl);
     if (!fused_qkv) {
       ScatterArgs sa{};
       sa.qkv = bf.qkv;
@@ -517,7 +539,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
         launch_attn_prefill_f32(aa, s);
       }
     }
-    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &spl);
     {
       Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
       if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
@@ -525,8 +547,8 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
     }
     run_gemm(c, gemm(bf.h, d, w->w1[l], M, F, d, bf.u, F,
                      bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
-             GPT_PROF_GEMM, s);
-    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+             GPT_PROF_GEMM, s, &spl);
+    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &spl);
   }
   {
     Timed t(GPT_PROF_NORM, s, 0, (double)rows * d * (4 + (bf16p ? 2 : 4)));
@@ -538,10 +560,10 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   const bool fused_lse = want_lse && bf16p && rows > 64;
   GemmArgs lg = gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
   lg.part = bf.lpart;
-  run_gemm(c, lg, GPT_PROF_LMHEAD, s);
+  run_gemm(c, lg, GPT_PROF_LMHEAD, s, &spl);
   if (fused_lse) {
-    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * (V / 128) * 8 + (probs ? (double)rows * V * 8 : 0.0));
-    launch_lse_combine(bf.lpart, V / 128, rows, lse ? lse : bf.lse_tmp, logits, V, probs, s);
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * (V / kLogitsPartCols) * 8 + (probs ? (double)rows * V * 8 : 0.0));
+    launch_lse_combine(bf.lpart, V / kLogitsPartCols, rows, lse ? lse : bf.lse_tmp, logits, V, probs, s);
   } else if (want_lse) {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * V * 4 * (probs ? 3 : 1));
     launch_softmax_lse(logits, rows, V, lse ? lse : bf.lse_tmp, probs, s);
@@ -580,6 +602,7 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   hipGetLastError();
   Bufs bf;
   carve(c, n, n, (char *)workspace, &bf);
+  const SkinnyFuse spl = split_only(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;
@@ -587,48 +610,49 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   float *lg = logits ? logits : bf.dlogits;
   double kv_bytes = 0;
   for (int b = 0; b < n; ++b) kv_bytes += (double)(kv->lens[b] + 1) * 2 * Hkv * dh * (bf16p ? 2 : 4);
-  {
-    Timed t(GPT_PROF_NORM, s, 0, (double)n * d * (4 + (bf16p ? 2 : 4)));
-    if (bf16p) launch_embed_bf16(tokens_in, (const bf16 *)w->wte, bf.x, n, d, s);
-    else launch_embed_f32(tokens_in, (const float *)w->wte, (const float *)w->wpe, pv.lens, bf.x, n, d, s);
-  }
-  for (int l = 0; l < c->n_layer; ++l) {
+  ScatterArgs sa{};
+  sa.qkv = bf.qkv;
+  sa.M = n;
+  sa.H = H;
+  sa.Hkv = Hkv;
+  sa.seq = nullptr;
+  sa.pos = pv.lens;
+  sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+  sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+  sa.qk_norm = c->qk_norm;
+  sa.eps = c->norm_eps;
+  sa.q_out = bf.q;
+  sa.kv = pv;
+  sa.use_cache = 1;
+  sa.head_dim = dh;
+  const double att_flops = 4.0 * H * dh * (kv_bytes / (2.0 * Hkv * dh * (bf16p ? 2 : 4)));
+  const double att_bytes = kv_bytes + (double)n * H * dh * 2 * (bf16p ? 2 : 4);
+
+  if (bf16p) {
+    // Five fused kernels per layer: QKV (+ RoPE, QK-norm, cache append),
+    // attention (+ page merge), O (+ residual, RMSNorm), W1 (+ ReLU^2),
+    // W2 (+ residual, RMSNorm).
     {
-      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
-      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
-      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 8);
+      launch_embed_norm_bf16(tokens_in, (const bf16 *)w->wte, bf.x, (bf16 *)bf.h, n, d, c->norm_eps,
+                             bf.ctr, kCounters, s);
     }
-    GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
-    g.W1 = w->wk[l];
-    g.W2 = w->wv[l];
-    g.n1 = H * dh;
-    g.n2 = (H + Hkv) * dh;
-    run_gemm(c, g, GPT_PROF_GEMM, s);
-    ScatterArgs sa{};
-    sa.qkv = bf.qkv;
-    sa.M = n;
-    sa.H = H;
-    sa.Hkv = Hkv;
-    sa.seq = nullptr;
-    sa.pos = pv.lens;
-    sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
-    sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
-    sa.qk_norm = c->qk_norm;
-    sa.eps = c->norm_eps;
-    sa.q_out = bf.q;
-    sa.kv = pv;
-    sa.layer = l;
-    sa.use_cache = 1;
-    sa.head_dim = dh;
-    {
-      Timed t(GPT_PROF_NORM, s, 0, (double)n * qkv_n * 6);
-      if (bf16p) launch_rope_norm_scatter_bf16(sa, s);
-      else launch_qkv_scatter_f32(sa, s);
-    }
-    {
-      Timed t(GPT_PROF_DECODE_ATTN, s, 4.0 * H * dh * (kv_bytes / (2.0 * Hkv * dh * (bf16p ? 2 : 4))),
-              kv_bytes + (double)n * H * dh * 2 * (bf16p ? 2 : 4));
-      if (bf16p) {
+    SkinnyFuse fq = spl, fn = spl;
+    fq.mode = SK_QKV;
+    fn.mode = SK_NORM;
+    fn.eps = c->norm_eps;
+    fn.norm_out = (bf16 *)bf.h;
+    for (int l = 0; l < c->n_layer; ++l) {
+      GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+      g.W1 = w->wk[l];
+      g.W2 = w->wv[l];
+      g.n1 = H * dh;
+      g.n2 = (H + Hkv) * dh;
+      fq.sc = sa;
+      fq.sc.layer = l;
+      run_gemm(c, g, GPT_PROF_GEMM, s, &fq);
+      {
+        Timed t(GPT_PROF_DECODE_ATTN, s, att_flops, att_bytes);
         AttnDecodeArgs aa{};
         aa.q = (const bf16 *)bf.q;
         aa.kv = pv;
@@ -639,8 +663,31 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         aa.o_part = bf.opart;
         aa.ml_part = bf.mlpart;
         aa.o = (bf16 *)bf.o;
+        aa.ctr = bf.ctr + kSkinnyCounters;
         launch_attn_decode_bf16(aa, s);
-      } else {
+      }
+      run_gemm(c, gemm(bf.o, H * dh, w->wo[l], n, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &fn);
+      run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F, EPI_RELU2_BF16), GPT_PROF_GEMM, s, &spl);
+      run_gemm(c, gemm(bf.u, F, w->w2[l], n, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &fn);
+    }
+  } else {
+    {
+      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 8);
+      launch_embed_f32(tokens_in, (const float *)w->wte, (const float *)w->wpe, pv.lens, bf.x, n, d, s);
+    }
+    for (int l = 0; l < c->n_layer; ++l) {
+      launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+      GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+      g.W1 = w->wk[l];
+      g.W2 = w->wv[l];
+      g.n1 = H * dh;
+      g.n2 = (H + Hkv) * dh;
+      run_gemm(c, g, GPT_PROF_GEMM, s);
+      ScatterArgs sl = sa;
+      sl.layer = l;
+      launch_qkv_scatter_f32(sl, s);
+      {
+        Timed t(GPT_PROF_DECODE_ATTN, s, att_flops, att_bytes);
         AttnF32Args aa{};
         aa.q = (const float *)bf.q;
         aa.M = n;
@@ -652,30 +699,21 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         aa.o = (float *)bf.o;
         launch_attn_decode_f32(aa, s);
       }
+      run_gemm(c, gemm(bf.o, H * dh, w->wo[l], n, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+      launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
+      run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F, c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16),
+               GPT_PROF_GEMM, s);
+      run_gemm(c, gemm(bf.u, F, w->w2[l], n, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
     }
-    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], n, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
-    {
-      Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
-      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
-      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
-    }
-    run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F,
-                     bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
-             GPT_PROF_GEMM, s);
-    run_gemm(c, gemm(bf.u, F, w->w2[l], n, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+    launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
   }
-  {
-    Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
-    if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
-    else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
-  }
-  run_gemm(c, gemm(bf.h, d, w->lm_head, n, V, d, lg, V, EPI_F32), GPT_PROF_LMHEAD, s);
+  // h holds the final RMSNorm of x here (fused into the last W2 on bf16)
+  run_gemm(c, gemm(bf.h, d, w->lm_head, n, V, d, lg, V, EPI_F32), GPT_PROF_LMHEAD, s, &spl);
   {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)n * V * 4);
-    if (temperature > 0.f) launch_sample(lg, n, V, temperature, uniforms, tokens_out, s);
-    else launch_argmax(lg, n, V, tokens_out, s);
+    if (temperature > 0.f) launch_sample(lg, n, V, temperature, uniforms, tokens_out, pv.lens, s);
+    else launch_argmax(lg, n, V, tokens_out, bf.sel, pv.lens, s);
   }
-  launch_lens_inc(pv.lens, n, s);
   if ((st = hip_check("gpt_decode_step launch"))) return st;
   for (int b = 0; b < n; ++b) kv->lens[b] += 1;
   return GPT_OK;
@@ -691,14 +729,16 @@ gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, f
   hipGetLastError();
   {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * vocab * 4);
-    if (temperature > 0.f) launch_sample(logits, rows, vocab, temperature, uniforms, tokens_out, s);
-    else launch_argmax(logits, rows, vocab, tokens_out, s);
+    if (temperature > 0.f) launch_sample(logits, rows, vocab, temperature, uniforms, tokens_out, nullptr, s);
+    else launch_argmax_rows(logits, rows, vocab, tokens_out, s);
   }
   return hip_check("gpt_select_tokens launch");
 }
 
+size_t gpt_debug_split_floats(void) { return (size_t)kSkinnyPartFloats + kSkinnyCounters; }
+
 gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, int32_t K, void *C,
-                          int32_t epi, gpt_stream_t stream) {
+                          int32_t epi, float *split_scratch, gpt_stream_t stream) {
   if (!A || !W || !C) return fail(GPT_ERR_ARG, "NULL pointer");
   if (M <= 0 || N <= 0 || K <= 0 || K % 64 || N % 128) return fail(GPT_ERR_ARG, "bad GEMM shape");
   if (epi < 0 || epi > 3) return fail(GPT_ERR_ARG, "bad epilogue");
@@ -706,7 +746,15 @@ gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, in
   hipGetLastError();
   gpt_config c{};
   c.dtype = GPT_DTYPE_BF16;
-  run_gemm(&c, gemm(A, K, W, M, N, K, C, N, epi), GPT_PROF_GEMM, (hipStream_t)stream);
+  SkinnyFuse f{};
+  if (split_scratch) {
+    f.part = split_scratch;
+    f.tile_ctr = (unsigned *)(split_scratch + kSkinnyPartFloats);
+    f.grp_ctr = f.tile_ctr + 4096;
+    if (hipMemsetAsync(f.tile_ctr, 0, kSkinnyCounters * 4, (hipStream_t)stream) != hipSuccess)
+      return hip_check("gpt_debug_gemm counters");
+  }
+  run_gemm(&c, gemm(A, K, W, M, N, K, C, N, epi), GPT_PROF_GEMM, (hipStream_t)stream, &f);
   return hip_check("gpt_debug_gemm");
 }
 
@@ -730,7 +778,7 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
   PrefillMeta meta;
   meta.n = n_seqs;
   for (int b = 0; b <= n_seqs; ++b) meta.cu[b] = cu_seqlens[b];
-  prefill_meta_kernel<<<1, 256, 0, s>>>(meta, cu_dev, cu_dev + n_seqs + 1, nullptr);
+  prefill_meta_kernel<<<1, 256, 0, s>>>(meta, cu_dev, cu_dev + n_seqs + 1, nullptr, nullptr, 0);
   AttnPrefillArgs aa{};
   aa.q = (const bf16 *)q;
   aa.k = (const bf16 *)k;

@@ -12,10 +12,11 @@
 // exponentiated scores are already laid out as the B operand of
 // O^T = V^T P^T.  Online softmax in the base-2 domain.
 //
-// Decode: one workgroup per (sequence, 256-position chunk), one 64-position
-// page per wave, K and V^T fragments loaded straight from the paged cache,
+// Decode: one single-wave workgroup per (sequence, 64-position page), so
+// even a small batch spreads over many CUs; K and V^T fragments are loaded
+// straight from the paged cache (every load issued before the first MFMA),
 // v_mfma_f32_16x16x32_bf16 with the (<= 16) query heads as the N side.
-// Waves merge through LDS; chunks merge in a small log-sum-exp combine.
+// The last page of a sequence to finish merges the pages (log-sum-exp).
 #include "kernels.h"
 
 namespace {
@@ -208,171 +209,143 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 // ------------------------------------------------------------------ decode
 
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
-  __shared__ float so[4][16][DH + 4];
-  __shared__ float sml[4][16][2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(64) void attn_decode_kernel(AttnDecodeArgs a) {
+  const int lane = threadIdx.x;
   const int hl = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, split = blockIdx.x;
   const PagedKV &kv = a.kv;
   const int len = kv.lens[b] + 1;  // the new position is already in the cache
-  const int start = split * kDecodeChunk;
-  if (start >= len) return;
+  const int kpos0 = split * kDecodeChunk;
+  if (kpos0 >= len) return;
   const int H = a.H;
-  const int kpos0 = start + 64 * wave;
-  float mw = -INFINITY, lw = 0.f;
-  f32x4 oacc[8];
+  const int page = kv.table[b * kv.pages_per_seq + kpos0 / kv.page_size];
+  const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+  const bf16 *K = (const bf16 *)pg;
+  const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
+  // every load of the page is issued before the first MFMA
+  bf16x8 kf[4][4];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
-  if (kpos0 < len) {
-    const int page = kv.table[b * kv.pages_per_seq + kpos0 / 64];
-    const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
-    const bf16 *K = (const bf16 *)pg;
-    const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
-    bf16x8 kf[4][4];
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
-    bf16x4 vlo[8][2], vhi[8][2];
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
-        vlo[d][h] = *(const bf16x4 *)vp;
-        vhi[d][h] = *(const bf16x4 *)(vp + 16);
-      }
-    bf16x8 qf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
-      else qf[s] = (bf16x8){};
-    }
-    f32x4 sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = (f32x4){};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
-    }
-    const float sc = kLog2e / sqrtf((float)DH);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kpos0 + 16 * kb + 4 * q4 + r;
-        float v = key < len ? sacc[kb][r] * sc : -INFINITY;
-        sacc[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float p = fast_exp2(sacc[kb][r] - mx);
-        sacc[kb][r] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    mw = mx;
-    lw = rs;
-    // keys past the end hold stale data: zero them so 0 * garbage cannot appear
-    if (kpos0 + 64 > len) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
-            if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
-          }
-    }
-    // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = f2bf(sacc[2 * h][e]);
-        pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
-                     vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
-      }
-    }
-  }
-  // lane holds head hl, dims 16 d + 4 q4 + r
+    for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
+  bf16x4 vlo[8][2], vhi[8][2];
 #pragma unroll
   for (int d = 0; d < 8; ++d)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) so[wave][hl][16 * d + 4 * q4 + r] = oacc[d][r];
-  if (q4 == 0) {
-    sml[wave][hl][0] = mw;
-    sml[wave][hl][1] = lw;
-  }
-  __syncthreads();
-  const int h = tid >> 4, d0 = (tid & 15) * 8;
-  if (h >= H) return;
-  float M = sml[0][h][0];
+    for (int h = 0; h < 2; ++h) {
+      const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
+      vlo[d][h] = *(const bf16x4 *)vp;
+      vhi[d][h] = *(const bf16x4 *)(vp + 16);
+    }
+  bf16x8 qf[4];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) M = fmaxf(M, sml[w][h][0]);
-  float f[4], L = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    f[w] = fast_exp2(sml[w][h][0] - M);
-    L += f[w] * sml[w][h][1];
+  for (int s = 0; s < 4; ++s) {
+    if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
+    else qf[s] = (bf16x8){};
   }
-  float *op = a.o_part + (((long long)b * a.max_splits + split) * H + h) * DH + d0;
+  // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
+  f32x4 sacc[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float v = 0.f;
+  for (int kb = 0; kb < 4; ++kb) {
+    sacc[kb] = (f32x4){};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v += f[w] * so[w][h][d0 + e];
-    op[e] = v;
+    for (int s = 0; s < 4; ++s)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
   }
-  if ((tid & 15) == 0) {
-    float *ml = a.ml_part + (((long long)b * a.max_splits + split) * H + h) * 2;
-    ml[0] = M;
-    ml[1] = L;
+  const float sc = kLog2e / sqrtf((float)DH);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = kpos0 + 16 * kb + 4 * q4 + r;
+      const float v = key < len ? sacc[kb][r] * sc : -INFINITY;
+      sacc[kb][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(sacc[kb][r] - mx);
+      sacc[kb][r] = p;
+      rs += p;
+    }
+  rs += __shfl_xor(rs, 16, 64);
+  rs += __shfl_xor(rs, 32, 64);
+  // positions past the end hold stale data: zero them so 0 * garbage cannot appear
+  if (kpos0 + 64 > len) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
+          if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
+        }
   }
-}
-
-// Merge the chunks of each (sequence, head): one wave, two dims per lane.
-__global__ __launch_bounds__(256) void attn_decode_combine_kernel(AttnDecodeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= a.n * a.H) return;
-  const int b = item / a.H, h = item - b * a.H;
-  const int len = a.kv.lens[b] + 1;
+  // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
+  f32x4 oacc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pf[e] = f2bf(sacc[2 * h][e]);
+      pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
+                   vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
+      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
+    }
+  }
+  if (hl < H) {
+    // lane holds head hl, dims 16 d + 4 q4 + r: unnormalised partial output
+    float *op = a.o_part + (((long long)b * a.max_splits + split) * H + hl) * DH;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) *(f32x4 *)(op + 16 * d + 4 * q4) = oacc[d];
+    if (q4 == 0) {
+      float *ml = a.ml_part + (((long long)b * a.max_splits + split) * H + hl) * 2;
+      ml[0] = mx;
+      ml[1] = rs;
+    }
+  }
+  // The last page of the sequence to finish merges all pages (log-sum-exp)
+  // for every head.  The agent-scope acquire-release counter publishes the
+  // other pages' partials; it resets itself for the next layer.
   const int ns = (len + kDecodeChunk - 1) / kDecodeChunk;
-  const float *ml = a.ml_part + ((long long)b * a.max_splits * a.H + h) * 2;
-  const long long mstride = (long long)a.H * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * mstride]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  const float *op = a.o_part + ((long long)b * a.max_splits * a.H + h) * DH;
-  const long long ostride = (long long)a.H * DH;
-  for (int s = 0; s < ns; ++s) {
-    const float f = fast_exp2(ml[s * mstride] - M);
-    L += f * ml[s * mstride + 1];
-    o0 += f * op[s * ostride + lane];
-    o1 += f * op[s * ostride + lane + 64];
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&a.ctr[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);  // one arrival per workgroup, seen by every lane
+  if (prev != (unsigned)(ns - 1)) return;
+  if (lane == 0) a.ctr[b] = 0u;
+  for (int h = 0; h < H; ++h) {
+    const float *ml = a.ml_part + ((long long)b * a.max_splits * H + h) * 2;
+    const long long mstride = (long long)H * 2;
+    float M = -INFINITY;
+    for (int p = 0; p < ns; ++p) M = fmaxf(M, ml[p * mstride]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    const float *opp = a.o_part + ((long long)b * a.max_splits * H + h) * DH;
+    const long long ostride = (long long)H * DH;
+    for (int p = 0; p < ns; ++p) {
+      const float fct = fast_exp2(ml[p * mstride] - M);
+      L += fct * ml[p * mstride + 1];
+      o0 += fct * opp[p * ostride + lane];
+      o1 += fct * opp[p * ostride + lane + 64];
+    }
+    const float inv = 1.0f / L;
+    bf16 *o = a.o + ((long long)b * H + h) * DH;
+    o[lane] = f2bf(o0 * inv);
+    o[lane + 64] = f2bf(o1 * inv);
   }
-  const float inv = 1.0f / L;
-  bf16 *o = a.o + ((long long)b * a.H + h) * DH;
-  o[lane] = f2bf(o0 * inv);
-  o[lane + 64] = f2bf(o1 * inv);
 }
 
 }  // namespace
@@ -383,6 +356,5 @@ void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  attn_decode_kernel<<<dim3(a.max_splits, a.n), 256, 0, s>>>(a);
-  attn_decode_combine_kernel<<<(a.n * a.H + 3) / 4, 256, 0, s>>>(a);
+  attn_decode_kernel<<<dim3(a.max_splits, a.n), 64, 0, s>>>(a);
 }

@@ -16,7 +16,7 @@
 // global memory, partial sums reduced through LDS.
 #include <type_traits>
 
-#include "kernels.h"
+#include "scatter.h"
 
 namespace {
 
@@ -154,11 +154,16 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
 #define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
 #define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+// NWN waves along N and 2 along M: NWN = 2 gives 4 waves (one per SIMD)
+// with 128x128 wave tiles; NWN = 4 gives 8 waves (two per SIMD) with
+// 128x64 wave tiles, so one wave's LDS and DMA traffic overlaps the other's
+// MFMAs.
+template <int BM, int BN, int NWN, int EPI>
+__global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int NW = 2 * NWN;
+  constexpr int WM = BM / 2, WN = BN / NWN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int PA = BM / 32, PB = BN / 32;  // 1 KB direct-to-LDS loads per wave per k-tile
+  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
   __shared__ bf16 sa[2][BM * BK];
   __shared__ bf16 sb[2][BN * BK];
 
@@ -189,26 +194,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   // so the lane loads that chunk: the XOR swizzle costs nothing.  Instruction p of
   // wave w covers rows (4p + w)*8 .. +8; 8-row groups never straddle a
   // weight segment (segment boundaries are multiples of 128), so the row
-  // base is wave-uniform and a lane keeps a 32-bit offset.
+  // base is wave-uniform and a lane keeps a 32-bit offset.  Instruction p of
+  // wave w covers rows (NW p + w)*8 .. +8.
   const int lr = lane >> 3;
   int aoff[PA], boff[PB];
   const bf16 *bbase[PB];
 #pragma unroll
   for (int p = 0; p < PA; ++p) {
-    const int lrow = (4 * p + wave) * 8 + lr;  // row within the tile
+    const int lrow = (NW * p + wave) * 8 + lr;  // row within the tile
     const int r = min(m0 + lrow, g.M - 1);
     aoff[p] = r * (int)g.lda + (((lane & 7) ^ swz_key(lrow)) << 3);
   }
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
-    const int nb = min(n0 + (4 * p + wave) * 8, g.N - 8);
+    const int nb = min(n0 + (NW * p + wave) * 8, g.N - 8);
     const bf16 *base;
     int first;
     if (nb < g.n1) { base = (const bf16 *)g.W0; first = 0; }
     else if (nb < g.n2) { base = (const bf16 *)g.W1; first = g.n1; }
     else { base = (const bf16 *)g.W2; first = g.n2; }
     bbase[p] = base;
-    const int lrow = (4 * p + wave) * 8 + lr;
+    const int lrow = (NW * p + wave) * 8 + lr;
     boff[p] = (nb - first + lr) * (int)g.ldw + (((lane & 7) ^ swz_key(lrow)) << 3);
   }
   const bf16 *abase = (const bf16 *)g.A;
@@ -216,11 +222,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < PA; ++p)
       __builtin_amdgcn_global_load_lds(GLOBAL_PTR(abase + aoff[p] + kt * BK),
-                                       LDS_PTR(&sa[buf][(4 * p + wave) * 8 * BK]), 16, 0, 0);
+                                       LDS_PTR(&sa[buf][(NW * p + wave) * 8 * BK]), 16, 0, 0);
 #pragma unroll
     for (int p = 0; p < PB; ++p)
       __builtin_amdgcn_global_load_lds(GLOBAL_PTR(bbase[p] + boff[p] + kt * BK),
-                                       LDS_PTR(&sb[buf][(4 * p + wave) * 8 * BK]), 16, 0, 0);
+                                       LDS_PTR(&sb[buf][(NW * p + wave) * 8 * BK]), 16, 0, 0);
   };
 
   f32x16 acc[TN][TM];
@@ -290,10 +296,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     if (more) interleave();
     __builtin_amdgcn_sched_barrier(0);
   }
-  // A wave whose 128 columns lie beyond N computed on clamped rows; drop it.
+  // A wave whose columns lie beyond N computed on clamped rows; drop it.
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
-  const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of 128)
+  const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of WN)
   if constexpr (EPI == EPI_QKV) {
     static_assert(WN == 128, "the QKV epilogue needs one head per wave");
     epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
       const int m = m0 + wm * WM + 32 * j + c32;
       const bool ok = m < g.M;
       if constexpr (EPI == EPI_LOGITS) {
-        // partial softmax statistics of this row over the wave's 128 columns
+        // partial softmax statistics of this row over the wave's WN columns
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < TN; ++i)
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
           for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
         se += __shfl_xor(se, 32, 64);
         if (ok && hi == 0) {
-          float *pp = g.part + ((long long)m * (g.N / 128) + nw0 / 128) * 2;
+          float *pp = g.part + ((long long)m * (g.N / WN) + nw0 / WN) * 2;
           *(float2 *)pp = make_float2(mx, se);
         }
       }
@@ -337,27 +343,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ skinny
 
-constexpr int SK_WAVES = 8;
+constexpr int SK_WAVES = 4;
+constexpr int SK_KSTEP = 32 * SK_WAVES;  // k per round of the four waves
+
+// Workgroup (nb, kz): output columns nb*16 .. +16, k range kz*KS .. +KS.
+// Wave w takes k-steps of 32 at w, w+4, ... of that range, four in flight.
+// The fusions of SkinnyFuse are done by the last workgroup to finish.
+DEV bool last_arrival(unsigned *ctr, unsigned total) {
+  // release this workgroup's stores, acquire the others'
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+}
 
 template <int EPI, int MB>
-__global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g, int ksplit, SkinnyFuse f) {
   __shared__ f32x4 red[SK_WAVES][MB][64];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const bf16 *w = wrow(g, n0 + l16) + 8 * q4;
+  const int n0 = blockIdx.x * 16, kz = blockIdx.y;
+  const int KS = g.K / ksplit;
+  const int kbeg = kz * KS;
+  const bf16 *w = wrow(g, n0 + l16) + 8 * q4 + kbeg;
   const bf16 *x[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     int m = min(mb * 16 + l16, g.M - 1);
-    x[mb] = (const bf16 *)g.A + (long long)m * g.lda + 8 * q4;
+    x[mb] = (const bf16 *)g.A + (long long)m * g.lda + 8 * q4 + kbeg;
   }
   f32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4){};
-  const int steps = g.K / 32;
+  const int steps = KS / 32;
   int st = wave;
-  // four k-steps per round so that several weight loads are in flight
   for (; st + 3 * SK_WAVES < steps; st += 4 * SK_WAVES) {
     bf16x8 wf[4], xf[4][MB];
 #pragma unroll
@@ -385,33 +402,75 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g) 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
   __syncthreads();
-  if (wave >= MB) return;
-  const int mb = wave;
-  f32x4 s = red[0][mb][lane];
+  // wave mb < MB owns rows mb*16 + l16, columns n0 + 4 q4 .. +4
+  const int m = wave * 16 + l16;
+  const bool own = wave < MB && m < g.M;
+  f32x4 sum = {};
+  if (wave < MB) {
+    sum = red[0][wave][lane];
 #pragma unroll
-  for (int k = 1; k < SK_WAVES; ++k) s += red[k][mb][lane];
-  const int m = mb * 16 + l16;
-  if (m >= g.M) return;
-  epi_store4<EPI>(g, m, n0 + 4 * q4, s[0], s[1], s[2], s[3]);
+    for (int k = 1; k < SK_WAVES; ++k) sum += red[k][wave][lane];
+  }
+  if (ksplit > 1) {
+    if (own) *(f32x4 *)(f.part + ((long long)kz * g.M + m) * g.N + n0 + 4 * q4) = sum;
+    __syncthreads();
+    if (tid == 0) s_last = last_arrival(&f.tile_ctr[blockIdx.x], (unsigned)ksplit);
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) f.tile_ctr[blockIdx.x] = 0u;
+    if (own) {
+      sum = *(const f32x4 *)(f.part + (long long)m * g.N + n0 + 4 * q4);
+      for (int k = 1; k < ksplit; ++k) sum += *(const f32x4 *)(f.part + ((long long)k * g.M + m) * g.N + n0 + 4 * q4);
+    }
+  }
+  if (own) epi_store4<EPI>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
+  if (f.mode == SK_PLAIN) return;
+  // group completion: the whole GEMM (SK_NORM) or one 128-wide head slot (SK_QKV)
+  const int gid = f.mode == SK_QKV ? n0 / 128 : 0;
+  const unsigned total = f.mode == SK_QKV ? 8u : gridDim.x;
+  __syncthreads();
+  if (tid == 0) s_last = last_arrival(&f.grp_ctr[gid], total);
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) f.grp_ctr[gid] = 0u;
+  const float *C = (const float *)g.C;
+  for (int r = wave; r < g.M; r += SK_WAVES) {
+    if (f.mode == SK_NORM) rmsnorm_row_bf16(C + (long long)r * g.ldc, f.norm_out + (long long)r * g.N, g.N, f.eps, lane);
+    else rope_norm_scatter_row(f.sc, C + (long long)r * g.ldc + gid * 128, r, gid, lane);
+  }
+}
+
+// Number of k splits: the largest divisor of K / 128 that keeps the grid at
+// or below 1024 workgroups (about four per CU).
+int skinny_ksplit(int N, int K) {
+  const int units = K / SK_KSTEP, nb = N / 16;
+  int best = 1;
+  for (int d = 1; d <= units; ++d)
+    if (units % d == 0 && nb * d <= 1024) best = d;
+  return best;
+}
+
+template <int EPI>
+void launch_sk(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s) {
+  const int ks = f.part ? skinny_ksplit(g.N, g.K) : 1;
+  const dim3 grid(g.N / 16, ks);
+  const int mb = (g.M + 15) / 16;
+  switch (mb) {
+    case 1: gemm_skinny_kernel<EPI, 1><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
+    case 2: gemm_skinny_kernel<EPI, 2><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
+    case 3: gemm_skinny_kernel<EPI, 3><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
+    default: gemm_skinny_kernel<EPI, 4><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
+  }
 }
 
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = 256, BN = 256;
+  // the QKV epilogue needs a whole 128-wide head per wave
+  constexpr int NWN = EPI == EPI_QKV ? 2 : 4;
+  static_assert(EPI != EPI_LOGITS || BN / NWN == kLogitsPartCols, "partial width");
   int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  gemm_bf16_kernel<BM, BN, EPI><<<tiles, 256, 0, s>>>(g);
-}
-
-template <int EPI>
-void launch_sk(const GemmArgs &g, hipStream_t s) {
-  int blocks = g.N / 16;
-  int mb = (g.M + 15) / 16;
-  switch (mb) {
-    case 1: gemm_skinny_kernel<EPI, 1><<<blocks, 64 * SK_WAVES, 0, s>>>(g); break;
-    case 2: gemm_skinny_kernel<EPI, 2><<<blocks, 64 * SK_WAVES, 0, s>>>(g); break;
-    case 3: gemm_skinny_kernel<EPI, 3><<<blocks, 64 * SK_WAVES, 0, s>>>(g); break;
-    default: gemm_skinny_kernel<EPI, 4><<<blocks, 64 * SK_WAVES, 0, s>>>(g); break;
-  }
+  gemm_bf16_kernel<BM, BN, NWN, EPI><<<tiles, 128 * NWN, 0, s>>>(g);
 }
 
 }  // namespace
@@ -428,12 +487,12 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
   }
 }
 
-void launch_gemm_bf16_skinny(const GemmArgs &g, hipStream_t s) {
+void launch_gemm_bf16_skinny(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s) {
   if (g.M <= 0) return;
   switch (g.epi) {
-    case EPI_BF16: launch_sk<EPI_BF16>(g, s); break;
-    case EPI_RELU2_BF16: launch_sk<EPI_RELU2_BF16>(g, s); break;
-    case EPI_RESID: launch_sk<EPI_RESID>(g, s); break;
-    default: launch_sk<EPI_F32>(g, s); break;
+    case EPI_BF16: launch_sk<EPI_BF16>(g, f, s); break;
+    case EPI_RELU2_BF16: launch_sk<EPI_RELU2_BF16>(g, f, s); break;
+    case EPI_RESID: launch_sk<EPI_RESID>(g, f, s); break;
+    default: launch_sk<EPI_F32>(g, f, s); break;
   }
 }

@@ -8,6 +8,8 @@
 void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq, int *pos,
                     int *vcol, hipStream_t s);
 void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s);
+void launch_embed_norm_bf16(const int *tok, const bf16 *wte, float *x, bf16 *h, int M, int d,
+                            float eps, unsigned *ctr, int nctr, hipStream_t s);
 void launch_embed_f32(const int *tok, const float *wte, const float *wpe, const int *pos, float *x,
                       int M, int d, hipStream_t s);
 void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d, float eps,
@@ -41,9 +43,14 @@ void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float 
 // lse[r] from the LM-head epilogue's per-block partials; then optional probs.
 void launch_lse_combine(const float *part, int nparts, int rows, float *lse, const float *logits,
                         int V, float *probs, hipStream_t s);
-void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s);
+// scratch: argmax_scratch_floats(rows, V) floats of device memory
+// lens (optional): decode lengths, incremented once the token is chosen
+void launch_argmax(const float *logits, int rows, int V, int *out, float *scratch, int *lens,
+                   hipStream_t s);
+int argmax_scratch_floats(int rows, int V);
+void launch_argmax_rows(const float *logits, int rows, int V, int *out, hipStream_t s);
 void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
-                   int *out, hipStream_t s);
+                   int *out, int *lens, hipStream_t s);
 void launch_lens_set(int *lens, const int *cu, int n, hipStream_t s);
 void launch_lens_inc(int *lens, int n, hipStream_t s);
 void launch_gather_rows_bf16(const bf16 *src, bf16 *dst, const int *rows, int n, int d,
@@ -56,7 +63,7 @@ enum Epi {
   EPI_RESID = 2,
   EPI_F32 = 3,
   EPI_RELU_F32 = 4,
-  EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each 128-column block
+  EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each kLogitsPartCols columns
   EPI_QKV = 6      // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
 };
 
@@ -85,11 +92,31 @@ struct GemmArgs {
   void *C;
   long long ldc;
   int epi;
-  float *part;  // EPI_LOGITS: [M][N/128][2] partial (max, sum exp)
+  float *part;  // EPI_LOGITS: [M][N/kLogitsPartCols][2] partial (max, sum exp)
   QkvEpi qkv;   // EPI_QKV
 };
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M
-void launch_gemm_bf16_skinny(const GemmArgs &g, hipStream_t s);  // MFMA, M <= 64
+// Fusions of the decode-row GEMM (M <= 64), done by the last workgroup to
+// finish (agent-scope acquire-release counters that reset themselves):
+//  * k split: workgroups write fp32 partials; the last of a column tile sums
+//    them in k order and applies the epilogue;
+//  * SK_NORM: after the last column tile, RMSNorm of every row of the fp32
+//    output C into bf16 norm_out (the next projection's input);
+//  * SK_QKV: after the last tile of a 128-wide head slot, RoPE + QK-norm +
+//    bf16 scatter of that slot for every row (ScatterArgs).
+enum { SK_PLAIN = 0, SK_NORM = 1, SK_QKV = 2 };
+struct SkinnyFuse {
+  float *part;        // kSkinnyPartFloats floats, or NULL: no k split
+  unsigned *tile_ctr; // kSkinnyCounters counters (zero before first use)
+  unsigned *grp_ctr;
+  int mode;
+  float eps;
+  bf16 *norm_out;
+  ScatterArgs sc;
+};
+constexpr long long kSkinnyPartFloats = 1024LL * 16 * 64;  // grid <= 1024 x 16 columns, M <= 64
+constexpr int kSkinnyCounters = 4096 + 64;                 // tile counters + group counters
+void launch_gemm_bf16_skinny(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s);
 void launch_gemm_f32(const GemmArgs &g, hipStream_t s);          // small fp32 path
 
 // ------------------------------------------------------------ attention
@@ -110,9 +137,10 @@ struct AttnDecodeArgs {
   PagedKV kv;
   int layer;
   int n, H, max_splits;
-  float *o_part;  // [n][max_splits][H][128]
+  float *o_part;  // [n][max_splits][H][128], one split per 64-position page
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
+  unsigned *ctr;  // [n] page-completion counters, zero before first use
 };
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
@@ -127,4 +155,5 @@ struct AttnF32Args {
 void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
 void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
 
-constexpr int kDecodeChunk = 256;  // positions per decode-attention workgroup
+constexpr int kDecodeChunk = 64;     // positions per decode-attention workgroup (one page)
+constexpr int kLogitsPartCols = 64;  // columns per LM-head softmax partial (one wave's width)

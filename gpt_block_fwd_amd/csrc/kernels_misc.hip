@@ -2,7 +2,7 @@
 // row metadata, embedding gather, weightless RMSNorm, RoPE + QK-norm +
 // K/V scatter, vocabulary softmax / log-sum-exp, token selection, and the
 // fp32 small-model GEMM and attention.
-#include "kernels.h"
+#include "scatter.h"
 
 // ---------------------------------------------------------------- row info
 
@@ -42,6 +42,32 @@ __global__ void embed_bf16_kernel(const int *tok, const bf16 *wte, float *x, int
   float4 *dst = (float4 *)(x + m * d + c);
   dst[0] = a;
   dst[1] = b;
+}
+
+// Decode rows: x = WTE[token] (fp32), h = rms(x) (bf16), one wave per row.
+// Block 0 also clears the completion counters the fused kernels of the step
+// use (they reset what they use, so this only matters for a fresh workspace).
+__global__ __launch_bounds__(256) void embed_norm_bf16_kernel(const int *tok, const bf16 *wte, float *x,
+                                                              bf16 *h, int M, int d, float eps,
+                                                              unsigned *ctr, int nctr) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nctr; i += blockDim.x) ctr[i] = 0u;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + wave;
+  if (m >= M) return;
+  const bf16 *er = wte + (long long)tok[m] * d;
+  float *xr = x + (long long)m * d;
+  for (int c = lane * 8; c < d; c += 512) {
+    const bf16x8 v = *(const bf16x8 *)(er + c);
+    *(float4 *)(xr + c) = make_float4(bf2f(v[0]), bf2f(v[1]), bf2f(v[2]), bf2f(v[3]));
+    *(float4 *)(xr + c + 4) = make_float4(bf2f(v[4]), bf2f(v[5]), bf2f(v[6]), bf2f(v[7]));
+  }
+  rmsnorm_row_bf16(xr, h + (long long)m * d, d, eps, lane);
+}
+
+void launch_embed_norm_bf16(const int *tok, const bf16 *wte, float *x, bf16 *h, int M, int d,
+                            float eps, unsigned *ctr, int nctr, hipStream_t s) {
+  embed_norm_bf16_kernel<<<(M + 3) / 4, 256, 0, s>>>(tok, wte, x, h, M, d, eps, ctr, nctr);
 }
 
 void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s) {
@@ -113,66 +139,12 @@ void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d,
 // weightless RMSNorm over the head (sum of squares reduced across the wave).
 
 __global__ __launch_bounds__(256) void rope_norm_scatter_bf16_kernel(ScatterArgs a) {
-  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int slots = a.H + 2 * a.Hkv;
-  long long item = (long long)blockIdx.x * 4 + wave;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slots = a.H + 2 * a.Hkv;
+  const long long item = (long long)blockIdx.x * 4 + wave;
   if (item >= (long long)a.M * slots) return;
-  int m = (int)(item / slots), j = (int)(item - (long long)m * slots);
-  const float *u = a.qkv + (long long)m * slots * 128 + j * 128;
-  float x0 = u[lane], x1 = u[lane + 64];
-  int p = a.pos[m];
-  int b = a.seq ? a.seq[m] : m;
-  bool is_v = j >= a.H + a.Hkv;
-  if (!is_v) {
-    if (a.cos) {
-      float c = a.cos[p * 64 + lane], s = a.sin[p * 64 + lane];
-      float r0 = x0 * c - x1 * s, r1 = x0 * s + x1 * c;
-      x0 = r0;
-      x1 = r1;
-    }
-    if (a.qk_norm) {
-      float ss = wave_sum(x0 * x0 + x1 * x1);
-      float rs = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
-      x0 *= rs;
-      x1 *= rs;
-    }
-  }
-  bf16 y0 = f2bf(x0), y1 = f2bf(x1);
-  if (j < a.H) {
-    bf16 *q = (bf16 *)a.q_out + (long long)m * a.H * 128 + j * 128;
-    q[lane] = y0;
-    q[lane + 64] = y1;
-    return;
-  }
-  int g = is_v ? j - a.H - a.Hkv : j - a.H;
-  int kvd = a.Hkv * 128;
-  if (!is_v) {
-    if (a.k_out) {
-      bf16 *k = (bf16 *)a.k_out + (long long)m * kvd + g * 128;
-      k[lane] = y0;
-      k[lane + 64] = y1;
-    }
-  } else if (a.vt_out) {
-    bf16 *vt = (bf16 *)a.vt_out;
-    long long col = a.vcol ? a.vcol[m] : m;
-    vt[(long long)(g * 128 + lane) * a.ldvt + col] = y0;
-    vt[(long long)(g * 128 + lane + 64) * a.ldvt + col] = y1;
-  }
-  if (a.use_cache) {
-    const PagedKV &kv = a.kv;
-    int page = kv.table[b * kv.pages_per_seq + p / kv.page_size];
-    int slot = p % kv.page_size;
-    char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
-    if (!is_v) {
-      bf16 *k = (bf16 *)pg + (long long)slot * kvd + g * 128;
-      k[lane] = y0;
-      k[lane + 64] = y1;
-    } else {
-      bf16 *vt = (bf16 *)(pg + kv.half_bytes);
-      vt[(long long)(g * 128 + lane) * kv.page_size + slot] = y0;
-      vt[(long long)(g * 128 + lane + 64) * kv.page_size + slot] = y1;
-    }
-  }
+  const int m = (int)(item / slots), j = (int)(item - (long long)m * slots);
+  rope_norm_scatter_row(a, a.qkv + (long long)m * slots * 128 + j * 128, m, j, lane);
 }
 
 void launch_rope_norm_scatter_bf16(const ScatterArgs &a, hipStream_t s) {
@@ -334,49 +306,110 @@ void launch_lse_combine(const float *part, int nparts, int rows, float *lse, con
 }
 
 // ---------------------------------------------------------------- greedy
-// Argmax per row; among equal maxima the lowest index wins.
+// Argmax per row; among equal maxima the lowest index wins.  Two phases so
+// that a few rows still spread over many CUs: phase 1 reduces chunks of
+// kArgChunk columns (grid rows x chunks), phase 2 merges a row's chunks.
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int V, int *out) {
+constexpr int kArgChunk = 2048;
+
+DEV void arg_merge(float &best, int &bi, float v2, int i2) {
+  if (v2 > best || (v2 == best && i2 < bi)) {
+    best = v2;
+    bi = i2;
+  }
+}
+
+// Partials are (float bits of the value, index) pairs of ints, so the index
+// never passes through a float register (small integers are denormals).
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const float *logits, int V,
+                                                             int2 *part) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  const float *row = logits + (long long)blockIdx.x * V;
+  const int row = blockIdx.y, chunk = blockIdx.x;
+  const float *r = logits + (long long)row * V;
+  const int i0 = chunk * kArgChunk, i1 = min(V, i0 + kArgChunk);
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) {
-    float x = row[i];
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
+    const float x = r[i];
     if (x > best) {  // indices visited in increasing order: keep the first
       best = x;
       bi = i;
     }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float v2 = __shfl_xor(best, o, 64);
-    int i2 = __shfl_xor(bi, o, 64);
-    if (v2 > best || (v2 == best && i2 < bi)) {
-      best = v2;
-      bi = i2;
-    }
-  }
-  int w = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) arg_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sv[w] = best;
     si[w] = bi;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 1; k < 4; ++k)
-      if (sv[k] > best || (sv[k] == best && si[k] < bi)) {
-        best = sv[k];
-        bi = si[k];
-      }
+    for (int k = 1; k < 4; ++k) arg_merge(best, bi, sv[k], si[k]);
+    part[(long long)row * gridDim.x + chunk] = make_int2(__float_as_int(best), bi);
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_final_kernel(const int2 *part, int nchunks,
+                                                           int rows, int *out, int *lens) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int c = lane; c < nchunks; c += 64) {
+    const int2 v = part[(long long)row * nchunks + c];
+    arg_merge(best, bi, __int_as_float(v.x), v.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) arg_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+  if (lane == 0) {
+    out[row] = bi == 0x7fffffff ? 0 : bi;
+    if (lens) lens[row] += 1;  // decode: the step's position is now cached
+  }
+}
+
+// Single-pass variant without scratch: one workgroup per row.
+__global__ __launch_bounds__(256) void argmax_rows_kernel(const float *logits, int V, int *out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const float *r = logits + (long long)blockIdx.x * V;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float x = r[i];
+    if (x > best) {
+      best = x;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) arg_merge(best, bi, __shfl_xor(best, o, 64), __shfl_xor(bi, o, 64));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = best;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k) arg_merge(best, bi, sv[k], si[k]);
     out[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
   }
 }
 
-void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s) {
+void launch_argmax_rows(const float *logits, int rows, int V, int *out, hipStream_t s) {
+  if (rows > 0) argmax_rows_kernel<<<rows, 256, 0, s>>>(logits, V, out);
+}
+
+int argmax_scratch_floats(int rows, int V) { return 2 * rows * ((V + kArgChunk - 1) / kArgChunk); }
+
+void launch_argmax(const float *logits, int rows, int V, int *out, float *scratch, int *lens,
+                   hipStream_t s) {
   if (rows <= 0) return;
-  argmax_kernel<<<rows, 256, 0, s>>>(logits, V, out);
+  const int nchunks = (V + kArgChunk - 1) / kArgChunk;
+  argmax_partial_kernel<<<dim3(nchunks, rows), 256, 0, s>>>(logits, V, (int2 *)scratch);
+  argmax_final_kernel<<<(rows + 3) / 4, 256, 0, s>>>((const int2 *)scratch, nchunks, rows, out, lens);
 }
 
 // ---------------------------------------------------------------- sampling
@@ -387,7 +420,7 @@ void launch_argmax(const float *logits, int rows, int V, int *out, hipStream_t s
 // cumulative weight exceeds u * total.
 
 __global__ __launch_bounds__(1024) void sample_kernel(const float *logits, int V, float inv_t,
-                                                      const float *uniforms, int *out) {
+                                                      const float *uniforms, int *out, int *lens) {
   __shared__ float red[16];
   __shared__ float scan[16];
   __shared__ int answer, lastpos;
@@ -450,13 +483,16 @@ __global__ __launch_bounds__(1024) void sample_kernel(const float *logits, int V
     atomicMax(&answer, pick);  // at most one thread qualifies
   }
   __syncthreads();
-  if (t == 0) out[blockIdx.x] = answer >= 0 ? answer : (lastpos >= 0 ? lastpos : 0);
+  if (t == 0) {
+    out[blockIdx.x] = answer >= 0 ? answer : (lastpos >= 0 ? lastpos : 0);
+    if (lens) lens[blockIdx.x] += 1;  // decode: the step's position is now cached
+  }
 }
 
 void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
-                   int *out, hipStream_t s) {
+                   int *out, int *lens, hipStream_t s) {
   if (rows <= 0) return;
-  sample_kernel<<<rows, 1024, 0, s>>>(logits, V, 1.0f / temperature, u, out);
+  sample_kernel<<<rows, 1024, 0, s>>>(logits, V, 1.0f / temperature, u, out, lens);
 }
 
 // ---------------------------------------------------------------- KV lengths

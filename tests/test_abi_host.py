@@ -131,6 +131,6 @@ def test_select_and_rope_validation():
 
 
 def test_debug_entry_validation():
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 100, 64, 0x3000, 0, 0), B.GPT_ERR_ARG)
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 60, 0x3000, 0, 0), B.GPT_ERR_ARG)
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 64, 0x3000, 9, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 100, 64, 0x3000, 0, None, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 60, 0x3000, 0, None, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 64, 0x3000, 9, None, 0), B.GPT_ERR_ARG)

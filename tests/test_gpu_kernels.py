@@ -20,13 +20,18 @@ GEMM_SHAPES = [
     (1, 128, 64),
     (33, 768, 768),
     (64, 1024, 3072),
+    (64, 1920, 1664),
+    (17, 6656, 1664),
 ]
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-def test_gemm_matches_float64(M, N, K, epi):
+def test_gemm_matches_float64(M, N, K, epi, split):
     t = torch()
+    if split and M > 64:
+        pytest.skip("k splitting applies to the decode-row kernel only")
     rng = np.random.default_rng(M * 7 + N + K + epi)
     A = bf16_round(rng.standard_normal((M, K)))
     W = bf16_round(rng.standard_normal((N, K)) * 0.05)
@@ -37,7 +42,8 @@ def test_gemm_matches_float64(M, N, K, epi):
     else:
         init = rng.standard_normal((M, N)).astype(np.float32) if epi == 2 else np.zeros((M, N), np.float32)
         C = t.from_numpy(init).cuda()
-    B.gpt_debug_gemm(dA, dW, M, N, K, C, epi)
+    scratch = t.empty(B.gpt_debug_split_floats(), dtype=t.float32, device="cuda") if split else None
+    B.gpt_debug_gemm(dA, dW, M, N, K, C, epi, scratch)
     t.cuda.synchronize()
     out = C.float().cpu().numpy().astype(np.float64)
     scale = np.sqrt(K) * 0.05
