@@ -131,7 +131,7 @@ gpt_status check_config(const gpt_config *c) {
 
 struct Bufs {
   int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
-  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart, *sel, *skpart;
+  float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart, *sel;
   unsigned *ctr;  // completion counters of the fused decode kernels
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
@@ -170,7 +170,6 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
-  t.skpart = (float *)take(kSkinnyPartFloats * 4);
   t.ctr = (unsigned *)take((size_t)kCounters * 4);
   t.sel = (float *)take((size_t)argmax_scratch_floats((int)nseq, c->vocab) * 4);
   t.lpart = (float *)take(M * (long long)((c->vocab + kLogitsPartCols - 1) / kLogitsPartCols) * 2 * 4);
@@ -257,9 +256,11 @@ void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s,
 
 PagedKV paged_view(const gpt_kv_cache *kv);
 
-SkinnyFuse split_only(const Bufs &bf) {
+// Decode-row GEMMs keep each output tile in one workgroup (no split of k
+// across workgroups: an exchange between XCDs costs about as much as a
+// kernel boundary); the counters serve the fused epilogues.
+SkinnyFuse skinny_plain(const Bufs &bf) {
   SkinnyFuse f{};
-  f.part = bf.skpart;
   f.tile_ctr = bf.ctr;
   f.grp_ctr = bf.ctr + 4096;
   f.mode = SK_PLAIN;
@@ -330,6 +331,9 @@ gpt_status kv_cache_alloc(const gpt_config *c, int32_t n_seqs, int32_t capacity_
   if (!bytes_inout) return fail(GPT_ERR_ARG, "bytes_inout is NULL");
   if (n_seqs <= 0 || capacity_per_seq <= 0) return fail(GPT_ERR_ARG, "n_seqs and capacity must be positive");
   if (capacity_per_seq > c->max_seq) return fail(GPT_ERR_ARG, "capacity exceeds max_seq");
+  if (c->dtype == GPT_DTYPE_BF16 && capacity_per_seq > kMaxDecodeChunks * kDecodeChunk)
+    return fail(GPT_ERR_UNSUPPORTED, "bf16 decode supports at most %d cached positions per sequence",
+                kMaxDecodeChunks * kDecodeChunk);
   if (page_size != kPage) return fail(GPT_ERR_UNSUPPORTED, "page_size must be 64");
   const long long pps = (capacity_per_seq + page_size - 1) / page_size;
   const long long n_pages = pps * n_seqs;
@@ -424,7 +428,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   hipGetLastError();  // clear any stale error from unrelated work
   Bufs bf;
   carve(c, M, n_seqs, (char *)workspace, &bf);
-  const SkinnyFuse spl = split_only(bf);
+  const SkinnyFuse spl = skinny_plain(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;
@@ -602,7 +606,7 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   hipGetLastError();
   Bufs bf;
   carve(c, n, n, (char *)workspace, &bf);
-  const SkinnyFuse spl = split_only(bf);
+  const SkinnyFuse spl = skinny_plain(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;

@@ -209,142 +209,207 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 // ------------------------------------------------------------------ decode
 
-__global__ __launch_bounds__(64) void attn_decode_kernel(AttnDecodeArgs a) {
-  const int lane = threadIdx.x;
+// One workgroup per chunk of kDecodePages pages of one sequence; wave w
+// takes page w of the chunk.  Each wave scores its 64 cached positions for
+// all query heads at once (MQA: one K/V page serves every head), the four
+// pages are merged in LDS by log-sum-exp, and the chunk's unnormalised
+// output with its (max, sum) per head goes to the partial buffers.  The last
+// chunk of the sequence to finish merges all chunks and writes o.
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
+  __shared__ float o_s[kDecodePages][16 * DH];  // per-page unnormalised outputs; reused by the final merge
+  __shared__ float ml_s[kDecodePages][16][2];   // per-page (max, sum) per head
+  __shared__ unsigned s_prev;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hl = lane & 15, q4 = lane >> 4;
-  const int b = blockIdx.y, split = blockIdx.x;
+  const int b = blockIdx.y, chunk = blockIdx.x;
   const PagedKV &kv = a.kv;
   const int len = kv.lens[b] + 1;  // the new position is already in the cache
-  const int kpos0 = split * kDecodeChunk;
-  if (kpos0 >= len) return;
+  const int c0 = chunk * kDecodeChunk;
+  if (c0 >= len) return;
   const int H = a.H;
-  const int page = kv.table[b * kv.pages_per_seq + kpos0 / kv.page_size];
-  const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
-  const bf16 *K = (const bf16 *)pg;
-  const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
-  // every load of the page is issued before the first MFMA
-  bf16x8 kf[4][4];
+  const int kpos0 = c0 + wave * 64;
+  if (kpos0 < len) {
+    const int page = kv.table[b * kv.pages_per_seq + kpos0 / kv.page_size];
+    const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+    const bf16 *K = (const bf16 *)pg;
+    const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
+    // every load of the page is issued before the first MFMA
+    bf16x8 kf[4][4];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
-  bf16x4 vlo[8][2], vhi[8][2];
-#pragma unroll
-  for (int d = 0; d < 8; ++d)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
-      vlo[d][h] = *(const bf16x4 *)vp;
-      vhi[d][h] = *(const bf16x4 *)(vp + 16);
-    }
-  bf16x8 qf[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
-    else qf[s] = (bf16x8){};
-  }
-  // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
-  f32x4 sacc[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    sacc[kb] = (f32x4){};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
-  }
-  const float sc = kLog2e / sqrtf((float)DH);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kpos0 + 16 * kb + 4 * q4 + r;
-      const float v = key < len ? sacc[kb][r] * sc : -INFINITY;
-      sacc[kb][r] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  float rs = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(sacc[kb][r] - mx);
-      sacc[kb][r] = p;
-      rs += p;
-    }
-  rs += __shfl_xor(rs, 16, 64);
-  rs += __shfl_xor(rs, 32, 64);
-  // positions past the end hold stale data: zero them so 0 * garbage cannot appear
-  if (kpos0 + 64 > len) {
+      for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
+    bf16x4 vlo[8][2], vhi[8][2];
 #pragma unroll
     for (int d = 0; d < 8; ++d)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
+        vlo[d][h] = *(const bf16x4 *)vp;
+        vhi[d][h] = *(const bf16x4 *)(vp + 16);
+      }
+    bf16x8 qf[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
-          if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
-        }
-  }
-  // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
-  f32x4 oacc[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pf[e] = f2bf(sacc[2 * h][e]);
-      pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+    for (int s = 0; s < 4; ++s) {
+      if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
+      else qf[s] = (bf16x8){};
     }
+    // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
+    f32x4 sacc[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
-                   vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
-      oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = (f32x4){};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
+    }
+    const float sc = kLog2e / sqrtf((float)DH);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kpos0 + 16 * kb + 4 * q4 + r;
+        const float v = key < len ? sacc[kb][r] * sc : -INFINITY;
+        sacc[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(sacc[kb][r] - mx);
+        sacc[kb][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    // positions past the end hold stale data: zero them so 0 * garbage cannot appear
+    if (kpos0 + 64 > len) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
+            if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
+          }
+    }
+    // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
+    f32x4 oacc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = f2bf(sacc[2 * h][e]);
+        pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
+                     vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
+      }
+    }
+    if (hl < H) {
+      // lane holds head hl, dims 16 d + 4 q4 + r
+#pragma unroll
+      for (int d = 0; d < 8; ++d) *(f32x4 *)&o_s[wave][hl * DH + 16 * d + 4 * q4] = oacc[d];
+      if (q4 == 0) {
+        ml_s[wave][hl][0] = mx;
+        ml_s[wave][hl][1] = rs;
+      }
     }
   }
-  if (hl < H) {
-    // lane holds head hl, dims 16 d + 4 q4 + r: unnormalised partial output
-    float *op = a.o_part + (((long long)b * a.max_splits + split) * H + hl) * DH;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) *(f32x4 *)(op + 16 * d + 4 * q4) = oacc[d];
-    if (q4 == 0) {
-      float *ml = a.ml_part + (((long long)b * a.max_splits + split) * H + hl) * 2;
-      ml[0] = mx;
-      ml[1] = rs;
+  __syncthreads();
+  const int nw = min(kDecodePages, (len - c0 + 63) / 64);  // pages of this chunk
+  const int S = (len + kDecodeChunk - 1) / kDecodeChunk;   // chunks of this sequence
+  const long long obase = ((long long)b * a.max_splits + chunk) * H * DH;
+  for (int idx = tid; idx < H * DH; idx += 256) {
+    const int h = idx >> 7;
+    float M = ml_s[0][h][0];
+    for (int w = 1; w < nw; ++w) M = fmaxf(M, ml_s[w][h][0]);
+    float L = 0.f, O = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float f = fast_exp2(ml_s[w][h][0] - M);
+      L += f * ml_s[w][h][1];
+      O += f * o_s[w][idx];
+    }
+    if (S == 1) {
+      a.o[(long long)b * H * DH + idx] = f2bf(O / L);
+    } else {
+      xst(a.o_part + obase + idx, O);
+      if ((idx & (DH - 1)) == 0) {
+        float *ml = a.ml_part + (((long long)b * a.max_splits + chunk) * H + h) * 2;
+        xst(ml, M);
+        xst(ml + 1, L);
+      }
     }
   }
-  // The last page of the sequence to finish merges all pages (log-sum-exp)
-  // for every head.  The agent-scope acquire-release counter publishes the
-  // other pages' partials; it resets itself for the next layer.
-  const int ns = (len + kDecodeChunk - 1) / kDecodeChunk;
-  unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&a.ctr[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, 64);  // one arrival per workgroup, seen by every lane
-  if (prev != (unsigned)(ns - 1)) return;
-  if (lane == 0) a.ctr[b] = 0u;
-  for (int h = 0; h < H; ++h) {
-    const float *ml = a.ml_part + ((long long)b * a.max_splits * H + h) * 2;
-    const long long mstride = (long long)H * 2;
+  if (S == 1) return;
+  // Publish the chunk: its partials travel through sc1 stores and loads and
+  // it is counted once they have completed.  The counter resets itself for
+  // the next layer.
+  stores_done();
+  __syncthreads();
+  if (tid == 0) s_prev = arrive(&a.ctr[b]);
+  __syncthreads();
+  if (s_prev != (unsigned)(S - 1)) return;
+  if (tid == 0) a.ctr[b] = 0u;
+  // Final merge over the S chunks.  (max, sum) of every chunk and head into
+  // LDS, then one factor per (chunk, head) with 1/sum folded in, then every
+  // output with all of its chunk loads in flight together.
+  float *mlg = &o_s[0][0];                   // [S][16][2]
+  float *fct = &o_s[0][0] + kMaxDecodeChunks * 32;  // [S][16]
+  for (int i = tid; i < S * H; i += 256) {
+    const int c = i / H, h = i - c * H;
+    const float *ml = a.ml_part + (((long long)b * a.max_splits + c) * H + h) * 2;
+    mlg[(c * 16 + h) * 2] = xld(ml);
+    mlg[(c * 16 + h) * 2 + 1] = xld(ml + 1);
+  }
+  __syncthreads();
+  if (tid < H) {
     float M = -INFINITY;
-    for (int p = 0; p < ns; ++p) M = fmaxf(M, ml[p * mstride]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    const float *opp = a.o_part + ((long long)b * a.max_splits * H + h) * DH;
-    const long long ostride = (long long)H * DH;
-    for (int p = 0; p < ns; ++p) {
-      const float fct = fast_exp2(ml[p * mstride] - M);
-      L += fct * ml[p * mstride + 1];
-      o0 += fct * opp[p * ostride + lane];
-      o1 += fct * opp[p * ostride + lane + 64];
-    }
+    for (int c = 0; c < S; ++c) M = fmaxf(M, mlg[(c * 16 + tid) * 2]);
+    float L = 0.f;
+    for (int c = 0; c < S; ++c) L += fast_exp2(mlg[(c * 16 + tid) * 2] - M) * mlg[(c * 16 + tid) * 2 + 1];
     const float inv = 1.0f / L;
-    bf16 *o = a.o + ((long long)b * H + h) * DH;
-    o[lane] = f2bf(o0 * inv);
-    o[lane + 64] = f2bf(o1 * inv);
+    for (int c = 0; c < S; ++c) fct[c * 16 + tid] = fast_exp2(mlg[(c * 16 + tid) * 2] - M) * inv;
+  }
+  __syncthreads();
+  constexpr int OPT = 16 * DH / 256;  // outputs per thread at most
+  const float *ob = a.o_part + (long long)b * a.max_splits * H * DH;
+  float acc[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
+  for (int c0c = 0; c0c < S; c0c += 4) {
+    float v[4][OPT];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) {
+        const int idx = tid + 256 * j;
+        v[cc][j] = (c0c + cc < S && idx < H * DH) ? xld(ob + (long long)(c0c + cc) * H * DH + idx) : 0.f;
+      }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) {
+        const int idx = tid + 256 * j;
+        if (c0c + cc < S && idx < H * DH) acc[j] += fct[(c0c + cc) * 16 + (idx >> 7)] * v[cc][j];
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int idx = tid + 256 * j;
+    if (idx < H * DH) a.o[(long long)b * H * DH + idx] = f2bf(acc[j]);
   }
 }
 
@@ -356,5 +421,5 @@ void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  attn_decode_kernel<<<dim3(a.max_splits, a.n), 64, 0, s>>>(a);
+  attn_decode_kernel<<<dim3(a.max_splits, a.n), 256, 0, s>>>(a);
 }

@@ -31,6 +31,47 @@ DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---------------------------------------------------------------- exchange between workgroups
+// Within one kernel, values that one workgroup hands to another (split-K
+// partials, the rows a last-arriving workgroup normalises, per-page attention
+// partials) are written and read with relaxed agent-scope atomic accesses,
+// which compile to sc1 loads and stores.  Each XCD has its own L2, and for
+// ordinary device memory the eight are not kept coherent with one another;
+// sc1 accesses are coherent across them by themselves.  Publishing therefore
+// only needs the workgroup's own stores to have completed before its arrival
+// is counted.  An acquire-release counter atomic would instead write back and
+// invalidate the whole L2 of the XCD at every arrival, which costs tens of
+// microseconds per launch.
+DEV void xst(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DEV float xld(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Four consecutive floats, 16-byte aligned, as two 8-byte accesses.
+DEV void xst4(float *p, f32x4 v) {
+  unsigned long long *q = (unsigned long long *)p;
+  const unsigned long long lo = (unsigned long long)__float_as_uint(v[0]) |
+                                ((unsigned long long)__float_as_uint(v[1]) << 32);
+  const unsigned long long hi = (unsigned long long)__float_as_uint(v[2]) |
+                                ((unsigned long long)__float_as_uint(v[3]) << 32);
+  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV f32x4 xld4(const float *p) {
+  unsigned long long *q = (unsigned long long *)const_cast<float *>(p);
+  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (f32x4){__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)),
+                 __uint_as_float((unsigned)hi), __uint_as_float((unsigned)(hi >> 32))};
+}
+// Wait until this wave's stores have completed (and keep the compiler from
+// moving memory accesses across the wait).
+DEV void stores_done() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Count one arrival on *ctr (called by one lane, after every wave of the
+// workgroup has passed stores_done and a barrier); returns the count before.
+DEV unsigned arrive(unsigned *ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Row metadata shared by the prefill kernels: for packed row m, its
 // sequence, its 0-based position and its column in the per-sequence padded
 // transposed-V buffer.

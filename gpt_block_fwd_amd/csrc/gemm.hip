@@ -34,8 +34,9 @@ DEV const bf16 *wrow(const GemmArgs &g, int n) {
   return (const bf16 *)g.W2 + (long long)(n - g.n2) * g.ldw;
 }
 
-// Store 4 consecutive outputs of row m starting at column n.
-template <int EPI>
+// Store 4 consecutive outputs of row m starting at column n.  XWG: fp32
+// results are read back by another workgroup of the same kernel.
+template <int EPI, bool XWG = false>
 DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v2, float v3) {
   if constexpr (EPI == EPI_BF16 || EPI == EPI_RELU2_BF16) {
     if constexpr (EPI == EPI_RELU2_BF16) {
@@ -47,12 +48,15 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     bf16x4 o = {f2bf(v0), f2bf(v1), f2bf(v2), f2bf(v3)};
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_RESID) {
-    float4 *p = (float4 *)((float *)g.C + (long long)m * g.ldc + n);
-    float4 x = *p;
-    x.x += v0; x.y += v1; x.z += v2; x.w += v3;
-    *p = x;
+    float *p = (float *)g.C + (long long)m * g.ldc + n;
+    f32x4 x = *(const f32x4 *)p;
+    x[0] += v0; x[1] += v1; x[2] += v2; x[3] += v3;
+    if constexpr (XWG) xst4(p, x);
+    else *(f32x4 *)p = x;
   } else {
-    *(float4 *)((float *)g.C + (long long)m * g.ldc + n) = make_float4(v0, v1, v2, v3);
+    float *p = (float *)g.C + (long long)m * g.ldc + n;
+    if constexpr (XWG) xst4(p, (f32x4){v0, v1, v2, v3});
+    else *(f32x4 *)p = (f32x4){v0, v1, v2, v3};
   }
 }
 
@@ -343,20 +347,30 @@ __global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ skinny
 
-constexpr int SK_WAVES = 4;
-constexpr int SK_KSTEP = 32 * SK_WAVES;  // k per round of the four waves
+constexpr int SK_KSTEP = 128;  // k granularity of a split (four steps of 32)
 
-// Workgroup (nb, kz): output columns nb*16 .. +16, k range kz*KS .. +KS.
-// Wave w takes k-steps of 32 at w, w+4, ... of that range, four in flight.
-// The fusions of SkinnyFuse are done by the last workgroup to finish.
-DEV bool last_arrival(unsigned *ctr, unsigned total) {
-  // release this workgroup's stores, acquire the others'
-  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+// The fusions of SkinnyFuse are done by the last workgroup to finish: what
+// the others hand over is stored and loaded with sc1 accesses, and arrival
+// is counted only after the workgroup's stores have completed.  Called by
+// every thread; the answer is broadcast through *flag.
+DEV bool last_arrival(unsigned *ctr, unsigned total, int *flag) {
+  stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = arrive(ctr) == total - 1;
+  __syncthreads();
+  return *flag;
 }
 
-template <int EPI, int MB>
-__global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g, int ksplit, SkinnyFuse f) {
-  __shared__ f32x4 red[SK_WAVES][MB][64];
+// Workgroup (nb, kz): output columns nb*16 .. +16 for all M <= 16 MB rows,
+// k range kz*KS .. +KS (KS = K without a split).  Its NW waves share that
+// range: wave w takes the k-steps of 32 at w, w + NW, ..., UNR loads in
+// flight before their MFMAs, and the waves' sums meet in LDS.  Lane l of an
+// MFMA holds weight row n0 + l%16 and activation row 16 mb + l%16, k
+// elements 8 (l/16) .. +8 of the step.
+template <int EPI, int MB, int NW>
+__global__ __launch_bounds__(64 * NW, 4) void gemm_skinny_kernel(GemmArgs g, int ksplit, SkinnyFuse f) {
+  constexpr int UNR = MB <= 2 ? 8 : 4;
+  __shared__ f32x4 red[NW][MB][64];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
@@ -374,30 +388,23 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g, 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4){};
   const int steps = KS / 32;
-  int st = wave;
-  for (; st + 3 * SK_WAVES < steps; st += 4 * SK_WAVES) {
-    bf16x8 wf[4], xf[4][MB];
+  for (int st = wave; st < steps; st += UNR * NW) {
+    bf16x8 wf[UNR], xf[UNR][MB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = (st + u * SK_WAVES) * 32;
-      wf[u] = *(const bf16x8 *)(w + k);
+    for (int u = 0; u < UNR; ++u) {
+      if (st + u * NW < steps) {  // wave-uniform
+        const int k = (st + u * NW) * 32;
+        wf[u] = *(const bf16x8 *)(w + k);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) xf[u][mb] = *(const bf16x8 *)(x[mb] + k);
+        for (int mb = 0; mb < MB; ++mb) xf[u][mb] = *(const bf16x8 *)(x[mb] + k);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < UNR; ++u)
+      if (st + u * NW < steps)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][mb], acc[mb], 0, 0, 0);
-  }
-  for (; st < steps; st += SK_WAVES) {
-    const int k = st * 32;
-    bf16x8 wf = *(const bf16x8 *)(w + k);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      bf16x8 xf = *(const bf16x8 *)(x[mb] + k);
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[mb], 0, 0, 0);
-    }
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][mb], acc[mb], 0, 0, 0);
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
@@ -409,39 +416,44 @@ __global__ __launch_bounds__(64 * SK_WAVES) void gemm_skinny_kernel(GemmArgs g, 
   if (wave < MB) {
     sum = red[0][wave][lane];
 #pragma unroll
-    for (int k = 1; k < SK_WAVES; ++k) sum += red[k][wave][lane];
+    for (int k = 1; k < NW; ++k) sum += red[k][wave][lane];
   }
   if (ksplit > 1) {
-    if (own) *(f32x4 *)(f.part + ((long long)kz * g.M + m) * g.N + n0 + 4 * q4) = sum;
-    __syncthreads();
-    if (tid == 0) s_last = last_arrival(&f.tile_ctr[blockIdx.x], (unsigned)ksplit);
-    __syncthreads();
-    if (!s_last) return;
+    if (own) xst4(f.part + ((long long)kz * g.M + m) * g.N + n0 + 4 * q4, sum);
+    if (!last_arrival(&f.tile_ctr[blockIdx.x], (unsigned)ksplit, &s_last)) return;
     if (tid == 0) f.tile_ctr[blockIdx.x] = 0u;
     if (own) {
-      sum = *(const f32x4 *)(f.part + (long long)m * g.N + n0 + 4 * q4);
-      for (int k = 1; k < ksplit; ++k) sum += *(const f32x4 *)(f.part + ((long long)k * g.M + m) * g.N + n0 + 4 * q4);
+      sum = xld4(f.part + (long long)m * g.N + n0 + 4 * q4);
+      for (int k = 1; k < ksplit; ++k) sum += xld4(f.part + ((long long)k * g.M + m) * g.N + n0 + 4 * q4);
     }
   }
-  if (own) epi_store4<EPI>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
-  if (f.mode == SK_PLAIN) return;
+  if (f.mode == SK_PLAIN) {
+    if (own) epi_store4<EPI>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
+    return;
+  }
+  if (own) epi_store4<EPI, true>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
   // group completion: the whole GEMM (SK_NORM) or one 128-wide head slot (SK_QKV)
   const int gid = f.mode == SK_QKV ? n0 / 128 : 0;
   const unsigned total = f.mode == SK_QKV ? 8u : gridDim.x;
-  __syncthreads();
-  if (tid == 0) s_last = last_arrival(&f.grp_ctr[gid], total);
-  __syncthreads();
-  if (!s_last) return;
+  if (!last_arrival(&f.grp_ctr[gid], total, &s_last)) return;
   if (tid == 0) f.grp_ctr[gid] = 0u;
   const float *C = (const float *)g.C;
-  for (int r = wave; r < g.M; r += SK_WAVES) {
-    if (f.mode == SK_NORM) rmsnorm_row_bf16(C + (long long)r * g.ldc, f.norm_out + (long long)r * g.N, g.N, f.eps, lane);
-    else rope_norm_scatter_row(f.sc, C + (long long)r * g.ldc + gid * 128, r, gid, lane);
+  if (f.mode == SK_QKV) {
+    rope_norm_scatter_rows_xwg(f.sc, C + gid * 128, g.ldc, g.M, gid, wave, NW, lane);
+    return;
+  }
+  switch ((g.N + 255) / 256) {
+#define NORM_CASE(k) \
+  case k: rmsnorm_rows_xwg<k>(C, g.ldc, f.norm_out, g.N, g.M, g.N, f.eps, wave, NW, lane); break;
+    NORM_CASE(1) NORM_CASE(2) NORM_CASE(3) NORM_CASE(4) NORM_CASE(5) NORM_CASE(6) NORM_CASE(7) NORM_CASE(8)
+#undef NORM_CASE
+    default: break;  // unreachable: the bf16 path has d_model = n_head * 128 <= 2048
   }
 }
 
-// Number of k splits: the largest divisor of K / 128 that keeps the grid at
-// or below 1024 workgroups (about four per CU).
+// Number of k splits across workgroups (only when a split scratch is given):
+// the largest divisor of K / 128 that keeps the grid at or below 1024
+// workgroups.
 int skinny_ksplit(int N, int K) {
   const int units = K / SK_KSTEP, nb = N / 16;
   int best = 1;
@@ -450,16 +462,34 @@ int skinny_ksplit(int N, int K) {
   return best;
 }
 
+// Waves per workgroup: many column blocks (the LM head) keep four; few
+// blocks with a long k range take eight or sixteen so that the range is
+// covered by more loads in flight instead of a split across workgroups.
+int skinny_waves(int N, int K, int ks) {
+  const int nb = N / 16, steps = K / ks / 32;
+  if (nb >= 512 || steps < 16) return 4;
+  return steps < 48 ? 8 : 16;
+}
+
+template <int EPI, int MB>
+void launch_sk_mb(const GemmArgs &g, const SkinnyFuse &f, int ks, int nw, hipStream_t s) {
+  const dim3 grid(g.N / 16, ks);
+  switch (nw) {
+    case 4: gemm_skinny_kernel<EPI, MB, 4><<<grid, 256, 0, s>>>(g, ks, f); break;
+    case 8: gemm_skinny_kernel<EPI, MB, 8><<<grid, 512, 0, s>>>(g, ks, f); break;
+    default: gemm_skinny_kernel<EPI, MB, 16><<<grid, 1024, 0, s>>>(g, ks, f); break;
+  }
+}
+
 template <int EPI>
 void launch_sk(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s) {
   const int ks = f.part ? skinny_ksplit(g.N, g.K) : 1;
-  const dim3 grid(g.N / 16, ks);
-  const int mb = (g.M + 15) / 16;
-  switch (mb) {
-    case 1: gemm_skinny_kernel<EPI, 1><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
-    case 2: gemm_skinny_kernel<EPI, 2><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
-    case 3: gemm_skinny_kernel<EPI, 3><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
-    default: gemm_skinny_kernel<EPI, 4><<<grid, 64 * SK_WAVES, 0, s>>>(g, ks, f); break;
+  const int nw = skinny_waves(g.N, g.K, ks);
+  switch ((g.M + 15) / 16) {
+    case 1: launch_sk_mb<EPI, 1>(g, f, ks, nw, s); break;
+    case 2: launch_sk_mb<EPI, 2>(g, f, ks, nw, s); break;
+    case 3: launch_sk_mb<EPI, 3>(g, f, ks, nw, s); break;
+    default: launch_sk_mb<EPI, 4>(g, f, ks, nw, s); break;
   }
 }
 

@@ -137,10 +137,10 @@ struct AttnDecodeArgs {
   PagedKV kv;
   int layer;
   int n, H, max_splits;
-  float *o_part;  // [n][max_splits][H][128], one split per 64-position page
+  float *o_part;  // [n][max_splits][H][128], one split per kDecodeChunk positions
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
-  unsigned *ctr;  // [n] page-completion counters, zero before first use
+  unsigned *ctr;  // [n] chunk-completion counters, zero before first use
 };
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
@@ -155,5 +155,7 @@ struct AttnF32Args {
 void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
 void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
 
-constexpr int kDecodeChunk = 64;     // positions per decode-attention workgroup (one page)
+constexpr int kDecodePages = 4;                      // pages per decode-attention workgroup
+constexpr int kDecodeChunk = 64 * kDecodePages;      // cached positions per decode-attention workgroup
+constexpr int kMaxDecodeChunks = 64;                 // chunks per sequence the final merge holds in LDS
 constexpr int kLogitsPartCols = 64;  // columns per LM-head softmax partial (one wave's width)

@@ -131,7 +131,8 @@ gpt_status rope_tables(int32_t max_seq, int32_t head_dim, float base, float *cos
  * *bytes_inout >= required, writes the page table and zero lengths with
  * blocking copies, and returns a new handle in *out.  page_size must be 64.
  * Errors: GPT_ERR_ARG (NULL config/bytes_inout/out, n_seqs or capacity <= 0,
- * capacity > max_seq, buffer too small), GPT_ERR_UNSUPPORTED (page_size),
+ * capacity > max_seq, buffer too small), GPT_ERR_UNSUPPORTED (page_size other
+ * than 64, or a bf16 model with capacity above 16384 positions per sequence),
  * GPT_ERR_HIP.
  * kv_cache_free releases the handle only; the device buffer stays the
  * caller's.  kv_cache_lengths copies the host mirror of the lengths.
