@@ -28,7 +28,7 @@ PROF_CLASSES = {"gemm": 0, "lmhead": 1, "attn": 2, "decode_attn": 3, "skinny": 4
 EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_decode_step",
            "gpt_select_tokens", "gpt_profile_enable", "gpt_profile_read",
-           "gpt_debug_gemm", "gpt_debug_split_floats", "gpt_debug_attn_prefill")
+           "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
 class GptError(RuntimeError):
@@ -84,12 +84,10 @@ def lib() -> ctypes.CDLL:
     L.gpt_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double)]
-    L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, vp]
-    L.gpt_debug_split_floats.argtypes = []
-    L.gpt_debug_split_floats.restype = sz
+    L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp]
     L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
     for name in EXPORTS:
-        if name not in ("gpt_last_error", "gpt_workspace_bytes", "gpt_debug_split_floats"):
+        if name not in ("gpt_last_error", "gpt_workspace_bytes"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -198,13 +196,8 @@ def gpt_profile_read(cls: int):
     return {"ms": ms.value, "launches": n.value, "flops": fl.value, "bytes": by.value}
 
 
-def gpt_debug_gemm(A, W, M: int, N: int, K: int, C, epi: int, split_scratch=None, stream=None):
-    _check(lib().gpt_debug_gemm(_ptr(A), _ptr(W), M, N, K, _ptr(C), epi, _ptr(split_scratch),
-                                _stream(stream)))
-
-
-def gpt_debug_split_floats() -> int:
-    return int(lib().gpt_debug_split_floats())
+def gpt_debug_gemm(A, W, M: int, N: int, K: int, C, epi: int, ksplit: int = 1, stream=None):
+    _check(lib().gpt_debug_gemm(_ptr(A), _ptr(W), M, N, K, _ptr(C), epi, ksplit, _stream(stream)))
 
 
 def gpt_debug_attn_prefill(q, k, vt, ldvt: int, cu_seqlens, n_seqs: int, n_head: int, cu_dev, o,

@@ -37,8 +37,7 @@ gpt_status hip_check(const char *what) {
 }
 
 constexpr int kMaxPrefillSeqs = 512;
-constexpr int kAttnCounters = 4096;  // decode-attention page counters (one per sequence)
-constexpr int kCounters = kSkinnyCounters + kAttnCounters;
+constexpr int kCounters = 4096;  // decode-attention chunk counters (one per sequence)
 constexpr int kPage = 64;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -132,7 +131,8 @@ gpt_status check_config(const gpt_config *c) {
 struct Bufs {
   int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
   float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart, *sel;
-  unsigned *ctr;  // completion counters of the fused decode kernels
+  float *slabs;   // partial products of split decode-row GEMMs
+  unsigned *ctr;  // completion counters of decode attention
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
   int max_splits;
@@ -171,6 +171,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
   t.ctr = (unsigned *)take((size_t)kCounters * 4);
+  t.slabs = (float *)take((size_t)kMaxRowSplit * std::min(M, 64LL) * std::max(d, (H + 2 * Hkv) * dh) * 4);
   t.sel = (float *)take((size_t)argmax_scratch_floats((int)nseq, c->vocab) * 4);
   t.lpart = (float *)take(M * (long long)((c->vocab + kLogitsPartCols - 1) / kLogitsPartCols) * 2 * 4);
   if (b) *b = t;
@@ -241,31 +242,28 @@ GemmArgs gemm(const void *A, long long lda, const void *W, int M, int N, int K, 
   return g;
 }
 
-void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s,
-              const SkinnyFuse *fuse = nullptr) {
+void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
   const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
   double out_b = g.epi == EPI_RESID ? 8.0
                  : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV) ? es : 4.0;
-  bool skinny = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
-  Timed t(skinny && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
+  bool rows = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
+  Timed t(rows && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
           es * ((double)g.M * g.K + (double)g.N * g.K) + out_b * g.M * g.N);
   if (c->dtype == GPT_DTYPE_F32) launch_gemm_f32(g, s);
-  else if (skinny) launch_gemm_bf16_skinny(g, fuse ? *fuse : SkinnyFuse{}, s);
+  else if (rows) launch_gemm_bf16_rows(g, 1, 0, s);
   else launch_gemm_bf16(g, s);
 }
 
-PagedKV paged_view(const gpt_kv_cache *kv);
-
-// Decode-row GEMMs keep each output tile in one workgroup (no split of k
-// across workgroups: an exchange between XCDs costs about as much as a
-// kernel boundary); the counters serve the fused epilogues.
-SkinnyFuse skinny_plain(const Bufs &bf) {
-  SkinnyFuse f{};
-  f.tile_ctr = bf.ctr;
-  f.grp_ctr = bf.ctr + 4096;
-  f.mode = SK_PLAIN;
-  return f;
+// Decode-row GEMM (bf16, M <= 64) with its k range split ks ways into fp32
+// slabs `slab` floats apart (EPI_F32); bytes counted are the algorithmic
+// ones (operands and one fp32 output).
+void run_gemm_rows(const GemmArgs &g, int ks, long long slab, int cls, hipStream_t s) {
+  Timed t(cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
+          2.0 * ((double)g.M * g.K + (double)g.N * g.K) + 4.0 * g.M * g.N);
+  launch_gemm_bf16_rows(g, ks, slab, s);
 }
+
+PagedKV paged_view(const gpt_kv_cache *kv);
 
 }  // namespace
 
@@ -428,7 +426,6 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   hipGetLastError();  // clear any stale error from unrelated work
   Bufs bf;
   carve(c, M, n_seqs, (char *)workspace, &bf);
-  const SkinnyFuse spl = skinny_plain(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;
@@ -485,7 +482,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
       e.layer = l;
       e.use_cache = kv != nullptr;
     }
-    run_gemm(c, g, GPT_PROF_GEMM, s, &spl);
+    run_gemm(c, g, GPT_PROF_GEMM, s);
     if (!fused_qkv) {
       ScatterArgs sa{};
       sa.qkv = bf.qkv;
@@ -543,7 +540,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
         launch_attn_prefill_f32(aa, s);
       }
     }
-    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &spl);
+    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
     {
       Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
       if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
@@ -551,8 +548,8 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
     }
     run_gemm(c, gemm(bf.h, d, w->w1[l], M, F, d, bf.u, F,
                      bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
-             GPT_PROF_GEMM, s, &spl);
-    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &spl);
+             GPT_PROF_GEMM, s);
+    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
   }
   {
     Timed t(GPT_PROF_NORM, s, 0, (double)rows * d * (4 + (bf16p ? 2 : 4)));
@@ -564,7 +561,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   const bool fused_lse = want_lse && bf16p && rows > 64;
   GemmArgs lg = gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
   lg.part = bf.lpart;
-  run_gemm(c, lg, GPT_PROF_LMHEAD, s, &spl);
+  run_gemm(c, lg, GPT_PROF_LMHEAD, s);
   if (fused_lse) {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * (V / kLogitsPartCols) * 8 + (probs ? (double)rows * V * 8 : 0.0));
     launch_lse_combine(bf.lpart, V / kLogitsPartCols, rows, lse ? lse : bf.lse_tmp, logits, V, probs, s);
@@ -594,6 +591,7 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
       kv->cfg.head_dim != c->head_dim)
     return fail(GPT_ERR_ARG, "kv cache was made for another config");
   const int n = kv->n_seqs;
+  if (n > kCounters) return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences per decode step", kCounters);
   for (int b = 0; b < n; ++b)
     if (kv->lens[b] + 1 > kv->capacity)
       return fail(GPT_ERR_CAPACITY, "sequence %d: length %d + 1 exceeds capacity %d", b, kv->lens[b], kv->capacity);
@@ -606,7 +604,6 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   hipGetLastError();
   Bufs bf;
   carve(c, n, n, (char *)workspace, &bf);
-  const SkinnyFuse spl = skinny_plain(bf);
   const bool bf16p = c->dtype == GPT_DTYPE_BF16;
   const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
   const int qkv_n = (H + 2 * Hkv) * dh;
@@ -633,28 +630,55 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   const double att_bytes = kv_bytes + (double)n * H * dh * 2 * (bf16p ? 2 : 4);
 
   if (bf16p) {
-    // Five fused kernels per layer: QKV (+ RoPE, QK-norm, cache append),
-    // attention (+ page merge), O (+ residual, RMSNorm), W1 (+ ReLU^2),
-    // W2 (+ residual, RMSNorm).
+    // Per layer: QKV projection (k split into fp32 slabs) -> RoPE, QK-norm,
+    // cache append (sums the slabs) -> attention -> O projection (slabs) ->
+    // residual + RMSNorm -> W1 + ReLU^2 -> W2 (slabs) -> residual + RMSNorm.
+    // Above 64 rows the large-M GEMMs write x and the norms run on their own.
+    const bool rows = n <= 64;
     {
       Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 8);
       launch_embed_norm_bf16(tokens_in, (const bf16 *)w->wte, bf.x, (bf16 *)bf.h, n, d, c->norm_eps,
                              bf.ctr, kCounters, s);
     }
-    SkinnyFuse fq = spl, fn = spl;
-    fq.mode = SK_QKV;
-    fn.mode = SK_NORM;
-    fn.eps = c->norm_eps;
-    fn.norm_out = (bf16 *)bf.h;
+    // x += A W^T, then h = RMSNorm(x)
+    auto proj_resid_norm = [&](const void *A, int K, const void *Wt) {
+      if (rows) {
+        const int ks = gemm_rows_ksplit(d, K);
+        run_gemm_rows(gemm(A, K, Wt, n, d, K, bf.slabs, d, EPI_F32), ks, (long long)n * d, GPT_PROF_GEMM, s);
+        Timed t(GPT_PROF_NORM, s, 0, (double)n * d * (4.0 * ks + 10.0));
+        launch_resid_norm_bf16(bf.slabs, ks, (long long)n * d, bf.x, (bf16 *)bf.h, n, d, c->norm_eps, s);
+      } else {
+        run_gemm(c, gemm(A, K, Wt, n, d, K, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+        Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 6);
+        launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, n, d, c->norm_eps, s);
+      }
+    };
     for (int l = 0; l < c->n_layer; ++l) {
-      GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
-      g.W1 = w->wk[l];
-      g.W2 = w->wv[l];
-      g.n1 = H * dh;
-      g.n2 = (H + Hkv) * dh;
-      fq.sc = sa;
-      fq.sc.layer = l;
-      run_gemm(c, g, GPT_PROF_GEMM, s, &fq);
+      ScatterArgs sl = sa;
+      sl.layer = l;
+      if (rows) {
+        const int ks = gemm_rows_ksplit(qkv_n, d);
+        GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.slabs, qkv_n, EPI_F32);
+        g.W1 = w->wk[l];
+        g.W2 = w->wv[l];
+        g.n1 = H * dh;
+        g.n2 = (H + Hkv) * dh;
+        run_gemm_rows(g, ks, (long long)n * qkv_n, GPT_PROF_GEMM, s);
+        sl.qkv = bf.slabs;
+        sl.nslab = ks;
+        sl.slab = (long long)n * qkv_n;
+      } else {
+        GemmArgs g = gemm(bf.h, d, w->wq[l], n, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+        g.W1 = w->wk[l];
+        g.W2 = w->wv[l];
+        g.n1 = H * dh;
+        g.n2 = (H + Hkv) * dh;
+        run_gemm(c, g, GPT_PROF_GEMM, s);
+      }
+      {
+        Timed t(GPT_PROF_NORM, s, 0, (double)n * qkv_n * (4.0 * std::max(sl.nslab, 1) + 2.0));
+        launch_rope_norm_scatter_bf16(sl, s);
+      }
       {
         Timed t(GPT_PROF_DECODE_ATTN, s, att_flops, att_bytes);
         AttnDecodeArgs aa{};
@@ -667,12 +691,12 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         aa.o_part = bf.opart;
         aa.ml_part = bf.mlpart;
         aa.o = (bf16 *)bf.o;
-        aa.ctr = bf.ctr + kSkinnyCounters;
+        aa.ctr = bf.ctr;
         launch_attn_decode_bf16(aa, s);
       }
-      run_gemm(c, gemm(bf.o, H * dh, w->wo[l], n, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &fn);
-      run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F, EPI_RELU2_BF16), GPT_PROF_GEMM, s, &spl);
-      run_gemm(c, gemm(bf.u, F, w->w2[l], n, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s, &fn);
+      proj_resid_norm(bf.o, H * dh, w->wo[l]);
+      run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F, EPI_RELU2_BF16), GPT_PROF_GEMM, s);
+      proj_resid_norm(bf.u, F, w->w2[l]);
     }
   } else {
     {
@@ -711,8 +735,8 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
     }
     launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, n, d, c->norm_eps, s);
   }
-  // h holds the final RMSNorm of x here (fused into the last W2 on bf16)
-  run_gemm(c, gemm(bf.h, d, w->lm_head, n, V, d, lg, V, EPI_F32), GPT_PROF_LMHEAD, s, &spl);
+  // h holds the final RMSNorm of x here
+  run_gemm(c, gemm(bf.h, d, w->lm_head, n, V, d, lg, V, EPI_F32), GPT_PROF_LMHEAD, s);
   {
     Timed t(GPT_PROF_SOFTMAX, s, 0, (double)n * V * 4);
     if (temperature > 0.f) launch_sample(lg, n, V, temperature, uniforms, tokens_out, pv.lens, s);
@@ -739,26 +763,24 @@ gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, f
   return hip_check("gpt_select_tokens launch");
 }
 
-size_t gpt_debug_split_floats(void) { return (size_t)kSkinnyPartFloats + kSkinnyCounters; }
-
 gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, int32_t K, void *C,
-                          int32_t epi, float *split_scratch, gpt_stream_t stream) {
+                          int32_t epi, int32_t ksplit, gpt_stream_t stream) {
   if (!A || !W || !C) return fail(GPT_ERR_ARG, "NULL pointer");
   if (M <= 0 || N <= 0 || K <= 0 || K % 64 || N % 128) return fail(GPT_ERR_ARG, "bad GEMM shape");
   if (epi < 0 || epi > 3) return fail(GPT_ERR_ARG, "bad epilogue");
+  if (ksplit < 1 || ksplit > kMaxRowSplit || ksplit > K / 64) return fail(GPT_ERR_ARG, "bad ksplit");
+  if (ksplit > 1 && (M > 64 || epi != EPI_F32))
+    return fail(GPT_ERR_ARG, "ksplit > 1 needs M <= 64 and the fp32 epilogue");
   if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return fail(GPT_ERR_ARG, "pointers must be 16-byte aligned");
   hipGetLastError();
-  gpt_config c{};
-  c.dtype = GPT_DTYPE_BF16;
-  SkinnyFuse f{};
-  if (split_scratch) {
-    f.part = split_scratch;
-    f.tile_ctr = (unsigned *)(split_scratch + kSkinnyPartFloats);
-    f.grp_ctr = f.tile_ctr + 4096;
-    if (hipMemsetAsync(f.tile_ctr, 0, kSkinnyCounters * 4, (hipStream_t)stream) != hipSuccess)
-      return hip_check("gpt_debug_gemm counters");
+  const GemmArgs g = gemm(A, K, W, M, N, K, C, N, epi);
+  if (ksplit > 1) {
+    run_gemm_rows(g, ksplit, (long long)M * N, GPT_PROF_GEMM, (hipStream_t)stream);
+  } else {
+    gpt_config c{};
+    c.dtype = GPT_DTYPE_BF16;
+    run_gemm(&c, g, GPT_PROF_GEMM, (hipStream_t)stream);
   }
-  run_gemm(&c, gemm(A, K, W, M, N, K, C, N, epi), GPT_PROF_GEMM, (hipStream_t)stream, &f);
   return hip_check("gpt_debug_gemm");
 }
 

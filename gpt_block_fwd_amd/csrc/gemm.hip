@@ -11,12 +11,14 @@
 // so consecutive tiles share an XCD (8 XCDs, round-robin dispatch) and
 // grouped 8 tile-rows at a time for L2 reuse.
 //
-// Skinny kernel (decode, M <= 64): one workgroup per 16 output columns, the
-// K range split across 8 waves, v_mfma_f32_16x16x32_bf16 fed straight from
-// global memory, partial sums reduced through LDS.
+// Decode-row kernel (M <= 64): one workgroup per 64 output columns (and k
+// range, when k is split), weight and activation chunks staged through a
+// multi-stage LDS ring by whole-line direct-to-LDS loads, then
+// v_mfma_f32_16x16x32_bf16 from LDS.
+#include <algorithm>
 #include <type_traits>
 
-#include "scatter.h"
+#include "kernels.h"
 
 namespace {
 
@@ -34,9 +36,8 @@ DEV const bf16 *wrow(const GemmArgs &g, int n) {
   return (const bf16 *)g.W2 + (long long)(n - g.n2) * g.ldw;
 }
 
-// Store 4 consecutive outputs of row m starting at column n.  XWG: fp32
-// results are read back by another workgroup of the same kernel.
-template <int EPI, bool XWG = false>
+// Store 4 consecutive outputs of row m starting at column n.
+template <int EPI>
 DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v2, float v3) {
   if constexpr (EPI == EPI_BF16 || EPI == EPI_RELU2_BF16) {
     if constexpr (EPI == EPI_RELU2_BF16) {
@@ -51,12 +52,9 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     float *p = (float *)g.C + (long long)m * g.ldc + n;
     f32x4 x = *(const f32x4 *)p;
     x[0] += v0; x[1] += v1; x[2] += v2; x[3] += v3;
-    if constexpr (XWG) xst4(p, x);
-    else *(f32x4 *)p = x;
+    *(f32x4 *)p = x;
   } else {
-    float *p = (float *)g.C + (long long)m * g.ldc + n;
-    if constexpr (XWG) xst4(p, (f32x4){v0, v1, v2, v3});
-    else *(f32x4 *)p = (f32x4){v0, v1, v2, v3};
+    *(f32x4 *)((float *)g.C + (long long)m * g.ldc + n) = (f32x4){v0, v1, v2, v3};
   }
 }
 
@@ -345,152 +343,119 @@ __global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// ------------------------------------------------------------------ skinny
+// ------------------------------------------------------------------ decode rows
 
-constexpr int SK_KSTEP = 128;  // k granularity of a split (four steps of 32)
-
-// The fusions of SkinnyFuse are done by the last workgroup to finish: what
-// the others hand over is stored and loaded with sc1 accesses, and arrival
-// is counted only after the workgroup's stores have completed.  Called by
-// every thread; the answer is broadcast through *flag.
-DEV bool last_arrival(unsigned *ctr, unsigned total, int *flag) {
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = arrive(ctr) == total - 1;
-  __syncthreads();
-  return *flag;
+template <int N>
+DEV void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup (nb, kz): output columns nb*16 .. +16 for all M <= 16 MB rows,
-// k range kz*KS .. +KS (KS = K without a split).  Its NW waves share that
-// range: wave w takes the k-steps of 32 at w, w + NW, ..., UNR loads in
-// flight before their MFMAs, and the waves' sums meet in LDS.  Lane l of an
-// MFMA holds weight row n0 + l%16 and activation row 16 mb + l%16, k
-// elements 8 (l/16) .. +8 of the step.
-template <int EPI, int MB, int NW>
-__global__ __launch_bounds__(64 * NW, 4) void gemm_skinny_kernel(GemmArgs g, int ksplit, SkinnyFuse f) {
-  constexpr int UNR = MB <= 2 ? 8 : 4;
-  __shared__ f32x4 red[NW][MB][64];
-  __shared__ int s_last;
+// Wait until at most min(ahead, MAXA) chunks of NI loads each are in flight.
+template <int NI, int MAXA>
+DEV void wait_ahead(int ahead) {
+  if constexpr (MAXA == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= MAXA) wait_vm<MAXA * NI>();
+    else wait_ahead<NI, MAXA - 1>(ahead);
+  }
+}
+
+// Decode-row kernel (M <= 64): one workgroup of 4 waves per 64 output
+// columns and k range kz of ks.  The k range streams in chunks of 64 through
+// an S-stage LDS ring holding the 64 weight rows and the activation rows
+// (padded to an even number of 16-row blocks), each chunk filled by
+// direct-to-LDS loads that read whole 128-byte lines: a wave instruction
+// covers 8 rows x 128 B.  Every wave issues the same number NI of those per
+// chunk, so "chunk c has landed" is a fixed vmcnt.  Wave w then multiplies
+// weight rows 16w .. +16 (output columns) by all activation rows with
+// v_mfma_f32_16x16x32_bf16 (lane l: weight row l%16 / activation row
+// 16 mb + l%16, k elements 8 (l/16) .. +8 of the 32-deep step).
+template <int EPI, int MB, bool DEEP>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long long slab) {
+  constexpr int MBE = (MB + 1) & ~1;      // activation 16-row blocks loaded
+  constexpr int ROWS = 64 + 16 * MBE;     // LDS tile rows: weights, then activations
+  constexpr int NI = (ROWS / 8) / 4;      // DMA instructions per wave per chunk
+  // Stages: two workgroups per CU (64-72 KB each), or one workgroup with
+  // twice the ring (128-144 KB) when the grid is too small to fill the chip.
+  constexpr int S = (MBE <= 2 ? 6 : 4) * (DEEP ? 2 : 1);
+  __shared__ bf16 lds[S][ROWS * BK];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int n0 = blockIdx.x * 16, kz = blockIdx.y;
-  const int KS = g.K / ksplit;
-  const int kbeg = kz * KS;
-  const bf16 *w = wrow(g, n0 + l16) + 8 * q4 + kbeg;
-  const bf16 *x[MB];
+  const int n0 = blockIdx.x * 64, kz = blockIdx.y;
+  const int nck = g.K / BK;
+  const int c0 = (int)((long long)kz * nck / ks), c1 = (int)((long long)(kz + 1) * nck / ks);
+  const int nch = c1 - c0;
+
+  // DMA slot j of this wave fills tile rows 8 (w + 4 j) .. +8; lane i lands
+  // in row i/8, 16-byte slot i%8, which holds logical chunk (i%8) ^ key.
+  const bf16 *src[NI];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    int m = min(mb * 16 + l16, g.M - 1);
-    x[mb] = (const bf16 *)g.A + (long long)m * g.lda + 8 * q4 + kbeg;
+  for (int j = 0; j < NI; ++j) {
+    const int slot = wave + 4 * j;
+    const int r = 8 * slot + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_key(r);
+    if (r < 64) src[j] = wrow(g, n0 + r) + lc * 8 + c0 * BK;
+    else src[j] = (const bf16 *)g.A + (long long)min(r - 64, g.M - 1) * g.lda + lc * 8 + c0 * BK;
   }
+  auto dma = [&](int c, int st) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(src[j] + c * BK), LDS_PTR(&lds[st][8 * (wave + 4 * j) * BK]),
+                                       16, 0, 0);
+  };
+
   f32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4){};
-  const int steps = KS / 32;
-  for (int st = wave; st < steps; st += UNR * NW) {
-    bf16x8 wf[UNR], xf[UNR][MB];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (st + u * NW < steps) {  // wave-uniform
-        const int k = (st + u * NW) * 32;
-        wf[u] = *(const bf16x8 *)(w + k);
+  for (int j = 0; j < S - 1; ++j)
+    if (j < nch) dma(j, j);
+  for (int c = 0; c < nch; ++c) {
+    wait_ahead<NI, S - 2>(nch - 1 - c);  // chunks still allowed in flight after chunk c
+    // Chunk c is in LDS and every wave is done with chunk c - 1's stage (its
+    // MFMAs consumed those reads).  A bare s_barrier: __syncthreads() would
+    // add a workgroup fence, and with it a wait for every load in flight.
+    asm volatile("s_barrier" ::: "memory");
+    if (c + S - 1 < nch) dma(c + S - 1, (c + S - 1) % S);
+    const bf16 *t = lds[c % S];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) xf[u][mb] = *(const bf16x8 *)(x[mb] + k);
+    for (int ksub = 0; ksub < 2; ++ksub) {
+      const bf16x8 wf = *(const bf16x8 *)&t[swz(16 * wave + l16, 4 * ksub + q4)];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 xf = *(const bf16x8 *)&t[swz(64 + 16 * mb + l16, 4 * ksub + q4)];
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[mb], 0, 0, 0);
       }
     }
+  }
+  // lane holds output columns n0 + 16 w + 4 q4 .. +4 of row 16 mb + l16
+  GemmArgs go = g;
+  if (ks > 1) go.C = (float *)g.C + kz * slab;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
-      if (st + u * NW < steps)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][mb], acc[mb], 0, 0, 0);
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
-  __syncthreads();
-  // wave mb < MB owns rows mb*16 + l16, columns n0 + 4 q4 .. +4
-  const int m = wave * 16 + l16;
-  const bool own = wave < MB && m < g.M;
-  f32x4 sum = {};
-  if (wave < MB) {
-    sum = red[0][wave][lane];
-#pragma unroll
-    for (int k = 1; k < NW; ++k) sum += red[k][wave][lane];
-  }
-  if (ksplit > 1) {
-    if (own) xst4(f.part + ((long long)kz * g.M + m) * g.N + n0 + 4 * q4, sum);
-    if (!last_arrival(&f.tile_ctr[blockIdx.x], (unsigned)ksplit, &s_last)) return;
-    if (tid == 0) f.tile_ctr[blockIdx.x] = 0u;
-    if (own) {
-      sum = xld4(f.part + (long long)m * g.N + n0 + 4 * q4);
-      for (int k = 1; k < ksplit; ++k) sum += xld4(f.part + ((long long)k * g.M + m) * g.N + n0 + 4 * q4);
-    }
-  }
-  if (f.mode == SK_PLAIN) {
-    if (own) epi_store4<EPI>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
-    return;
-  }
-  if (own) epi_store4<EPI, true>(g, m, n0 + 4 * q4, sum[0], sum[1], sum[2], sum[3]);
-  // group completion: the whole GEMM (SK_NORM) or one 128-wide head slot (SK_QKV)
-  const int gid = f.mode == SK_QKV ? n0 / 128 : 0;
-  const unsigned total = f.mode == SK_QKV ? 8u : gridDim.x;
-  if (!last_arrival(&f.grp_ctr[gid], total, &s_last)) return;
-  if (tid == 0) f.grp_ctr[gid] = 0u;
-  const float *C = (const float *)g.C;
-  if (f.mode == SK_QKV) {
-    rope_norm_scatter_rows_xwg(f.sc, C + gid * 128, g.ldc, g.M, gid, wave, NW, lane);
-    return;
-  }
-  switch ((g.N + 255) / 256) {
-#define NORM_CASE(k) \
-  case k: rmsnorm_rows_xwg<k>(C, g.ldc, f.norm_out, g.N, g.M, g.N, f.eps, wave, NW, lane); break;
-    NORM_CASE(1) NORM_CASE(2) NORM_CASE(3) NORM_CASE(4) NORM_CASE(5) NORM_CASE(6) NORM_CASE(7) NORM_CASE(8)
-#undef NORM_CASE
-    default: break;  // unreachable: the bf16 path has d_model = n_head * 128 <= 2048
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = 16 * mb + l16;
+    if (m < g.M) epi_store4<EPI>(go, m, n0 + 16 * wave + 4 * q4, acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
   }
 }
 
-// Number of k splits across workgroups (only when a split scratch is given):
-// the largest divisor of K / 128 that keeps the grid at or below 1024
-// workgroups.
-int skinny_ksplit(int N, int K) {
-  const int units = K / SK_KSTEP, nb = N / 16;
-  int best = 1;
-  for (int d = 1; d <= units; ++d)
-    if (units % d == 0 && nb * d <= 1024) best = d;
-  return best;
-}
-
-// Waves per workgroup: many column blocks (the LM head) keep four; few
-// blocks with a long k range take eight or sixteen so that the range is
-// covered by more loads in flight instead of a split across workgroups.
-int skinny_waves(int N, int K, int ks) {
-  const int nb = N / 16, steps = K / ks / 32;
-  if (nb >= 512 || steps < 16) return 4;
-  return steps < 48 ? 8 : 16;
-}
-
-template <int EPI, int MB>
-void launch_sk_mb(const GemmArgs &g, const SkinnyFuse &f, int ks, int nw, hipStream_t s) {
-  const dim3 grid(g.N / 16, ks);
-  switch (nw) {
-    case 4: gemm_skinny_kernel<EPI, MB, 4><<<grid, 256, 0, s>>>(g, ks, f); break;
-    case 8: gemm_skinny_kernel<EPI, MB, 8><<<grid, 512, 0, s>>>(g, ks, f); break;
-    default: gemm_skinny_kernel<EPI, MB, 16><<<grid, 1024, 0, s>>>(g, ks, f); break;
+template <int EPI, bool DEEP>
+void launch_rows_d(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
+  const dim3 grid(g.N / 64, ks);
+  switch ((g.M + 15) / 16) {
+    case 1: gemm_rows_kernel<EPI, 1, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 2: gemm_rows_kernel<EPI, 2, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 3: gemm_rows_kernel<EPI, 3, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    default: gemm_rows_kernel<EPI, 4, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
   }
 }
 
 template <int EPI>
-void launch_sk(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s) {
-  const int ks = f.part ? skinny_ksplit(g.N, g.K) : 1;
-  const int nw = skinny_waves(g.N, g.K, ks);
-  switch ((g.M + 15) / 16) {
-    case 1: launch_sk_mb<EPI, 1>(g, f, ks, nw, s); break;
-    case 2: launch_sk_mb<EPI, 2>(g, f, ks, nw, s); break;
-    case 3: launch_sk_mb<EPI, 3>(g, f, ks, nw, s); break;
-    default: launch_sk_mb<EPI, 4>(g, f, ks, nw, s); break;
-  }
+void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
+  // 256 CUs: a grid that leaves CUs without a second workgroup gets the deep ring
+  if ((long long)(g.N / 64) * ks <= 256) launch_rows_d<EPI, true>(g, ks, slab, s);
+  else launch_rows_d<EPI, false>(g, ks, slab, s);
 }
 
 template <int EPI>
@@ -517,12 +482,22 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
   }
 }
 
-void launch_gemm_bf16_skinny(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s) {
+void launch_gemm_bf16_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
   if (g.M <= 0) return;
   switch (g.epi) {
-    case EPI_BF16: launch_sk<EPI_BF16>(g, f, s); break;
-    case EPI_RELU2_BF16: launch_sk<EPI_RELU2_BF16>(g, f, s); break;
-    case EPI_RESID: launch_sk<EPI_RESID>(g, f, s); break;
-    default: launch_sk<EPI_F32>(g, f, s); break;
+    case EPI_BF16: launch_rows<EPI_BF16>(g, ks, slab, s); break;
+    case EPI_RELU2_BF16: launch_rows<EPI_RELU2_BF16>(g, ks, slab, s); break;
+    case EPI_RESID: launch_rows<EPI_RESID>(g, ks, slab, s); break;
+    default: launch_rows<EPI_F32>(g, ks, slab, s); break;
   }
+}
+
+// About 320 workgroups (the chip holds two per CU), at least two 64-deep
+// chunks per k range, at most kMaxRowSplit ranges.
+int gemm_rows_ksplit(int N, int K) {
+  const int tiles = N / 64, chunks = K / BK;
+  int ks = (320 + tiles / 2) / tiles;
+  ks = std::min(ks, chunks / 2);
+  ks = std::min(ks, kMaxRowSplit);
+  return std::max(ks, 1);
 }

@@ -16,6 +16,11 @@ void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d,
                          hipStream_t s);
 void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d, float eps,
                         hipStream_t s);
+// Residual add of a split GEMM's partial slabs, then RMSNorm: for every row,
+// x += part[0] + part[1] + ... (nslab slabs `slab` floats apart, in order)
+// and h = bf16(rmsnorm(x)).  d <= 2048.
+void launch_resid_norm_bf16(const float *part, int nslab, long long slab, float *x, bf16 *h, int M, int d,
+                            float eps, hipStream_t s);
 
 // RoPE + QK-norm of the fp32 q/k head vectors of `qkv` ([M][(H+2Hkv)*128]),
 // then bf16 scatter: q -> q_out [M][H*128]; k -> k_out [M][Hkv*128] and/or
@@ -23,6 +28,8 @@ void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d,
 // cache.  seq == NULL means row m is sequence m (decode).
 struct ScatterArgs {
   const float *qkv;
+  int nslab;       // qkv holds nslab fp32 partial slabs (k ranges of a split GEMM) ...
+  long long slab;  // ... `slab` floats apart, summed in order; nslab <= 1: one slab
   int M, H, Hkv;
   const int *seq, *pos, *vcol;
   const float *cos, *sin;  // [max_seq][64] or NULL (no RoPE)
@@ -96,27 +103,13 @@ struct GemmArgs {
   QkvEpi qkv;   // EPI_QKV
 };
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M
-// Fusions of the decode-row GEMM (M <= 64), done by the last workgroup to
-// finish (agent-scope acquire-release counters that reset themselves):
-//  * k split: workgroups write fp32 partials; the last of a column tile sums
-//    them in k order and applies the epilogue;
-//  * SK_NORM: after the last column tile, RMSNorm of every row of the fp32
-//    output C into bf16 norm_out (the next projection's input);
-//  * SK_QKV: after the last tile of a 128-wide head slot, RoPE + QK-norm +
-//    bf16 scatter of that slot for every row (ScatterArgs).
-enum { SK_PLAIN = 0, SK_NORM = 1, SK_QKV = 2 };
-struct SkinnyFuse {
-  float *part;        // kSkinnyPartFloats floats, or NULL: no k split
-  unsigned *tile_ctr; // kSkinnyCounters counters (zero before first use)
-  unsigned *grp_ctr;
-  int mode;
-  float eps;
-  bf16 *norm_out;
-  ScatterArgs sc;
-};
-constexpr long long kSkinnyPartFloats = 1024LL * 16 * 64;  // grid <= 1024 x 16 columns, M <= 64
-constexpr int kSkinnyCounters = 4096 + 64;                 // tile counters + group counters
-void launch_gemm_bf16_skinny(const GemmArgs &g, const SkinnyFuse &f, hipStream_t s);
+// Decode-row GEMM (M <= 64, N % 64 == 0, K % 64 == 0).  With ks > 1 the k
+// range is split over ks workgroups per column tile and range kz writes its
+// fp32 partial product to C + kz * slab (EPI_F32 only); the consumer sums
+// the slabs in order.
+void launch_gemm_bf16_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s);
+constexpr int kMaxRowSplit = 16;
+int gemm_rows_ksplit(int N, int K);  // k ranges for a decode-row GEMM whose consumer sums slabs
 void launch_gemm_f32(const GemmArgs &g, hipStream_t s);          // small fp32 path
 
 // ------------------------------------------------------------ attention

@@ -70,6 +70,60 @@ void launch_embed_norm_bf16(const int *tok, const bf16 *wte, float *x, bf16 *h, 
   embed_norm_bf16_kernel<<<(M + 3) / 4, 256, 0, s>>>(tok, wte, x, h, M, d, eps, ctr, nctr);
 }
 
+// One workgroup per row; d <= 2048, so a thread holds at most two
+// four-float chunks (columns 4 t and 4 t + 1024).  All slab loads of both
+// chunks are issued before the first add; the sum runs x + slab 0 + slab 1
+// + ... in that order.
+__global__ __launch_bounds__(256) void resid_norm_bf16_kernel(const float *part, int nslab, long long slab,
+                                                              float *x, bf16 *h, int M, int d, float eps) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, t = threadIdx.x;
+  float *xr = x + (long long)m * d;
+  const float *pr = part + (long long)m * d;
+  f32x4 v[2], p[2][kMaxRowSplit];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int col = 4 * (t + 256 * i);
+    if (col < d) {
+      v[i] = *(const f32x4 *)(xr + col);
+#pragma unroll
+      for (int k = 0; k < kMaxRowSplit; ++k)
+        if (k < nslab) p[i][k] = *(const f32x4 *)(pr + k * slab + col);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int col = 4 * (t + 256 * i);
+    if (col < d) {
+#pragma unroll
+      for (int k = 0; k < kMaxRowSplit; ++k)
+        if (k < nslab) v[i] += p[i][k];
+      *(f32x4 *)(xr + col) = v[i];
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
+  }
+  ss = wave_sum(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+  bf16 *hr = h + (long long)m * d;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int col = 4 * (t + 256 * i);
+    if (col < d) {
+      bf16x4 o = {f2bf(v[i][0] * rs), f2bf(v[i][1] * rs), f2bf(v[i][2] * rs), f2bf(v[i][3] * rs)};
+      *(bf16x4 *)(hr + col) = o;
+    }
+  }
+}
+
+void launch_resid_norm_bf16(const float *part, int nslab, long long slab, float *x, bf16 *h, int M, int d,
+                            float eps, hipStream_t s) {
+  resid_norm_bf16_kernel<<<M, 256, 0, s>>>(part, nslab, slab, x, h, M, d, eps);
+}
+
 void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s) {
   long long total = (long long)M * d / 8;
   embed_bf16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(tok, wte, x, M, d);

@@ -1,6 +1,6 @@
-// RoPE + QK-norm + bf16 scatter of one 128-wide head slot of one row, for
-// one 64-lane wave.  Shared by the standalone scatter kernel and by the
-// fused decode QKV GEMM.
+// Per-row device helpers of the bf16 path, each run by one 64-lane wave:
+// RoPE + QK-norm + bf16 scatter of one 128-wide head slot, and RMSNorm of
+// one fp32 row into bf16.
 #pragma once
 #include "kernels.h"
 
@@ -69,9 +69,24 @@ DEV int scatter_page(const ScatterArgs &a, int m, int p) {
   return a.kv.table[b * a.kv.pages_per_seq + p / a.kv.page_size];
 }
 
-// One row, values read from u (written by an earlier kernel).
+// One row, values read from u (written by an earlier kernel), summed over
+// the partial slabs of a split GEMM.
 DEV void rope_norm_scatter_row(const ScatterArgs &a, const float *u, int m, int j, int lane) {
-  const float x0 = u[lane], x1 = u[lane + 64];
+  // every slab load in flight before the first add; sum in slab order
+  float p0[kMaxRowSplit], p1[kMaxRowSplit];
+#pragma unroll
+  for (int k = 0; k < kMaxRowSplit; ++k)
+    if (k == 0 || k < a.nslab) {
+      p0[k] = u[k * a.slab + lane];
+      p1[k] = u[k * a.slab + lane + 64];
+    }
+  float x0 = p0[0], x1 = p1[0];
+#pragma unroll
+  for (int k = 1; k < kMaxRowSplit; ++k)
+    if (k < a.nslab) {
+      x0 += p0[k];
+      x1 += p1[k];
+    }
   const int p = a.pos[m];
   float c = 0.f, s = 0.f;
   if (a.cos && j < a.H + a.Hkv) {
@@ -79,46 +94,6 @@ DEV void rope_norm_scatter_row(const ScatterArgs &a, const float *u, int m, int 
     s = a.sin[p * 64 + lane];
   }
   rope_norm_scatter_vals(a, x0, x1, c, s, p, scatter_page(a, m, p), m, j, lane);
-}
-
-// Rows r0, r0 + rstep, ... < M of head slot j, values at U + r * ldu
-// written by other workgroups of the same kernel.  Four rows at a time, the
-// loads of every row are issued together, in two dependent rounds (values
-// and positions, then table factors and pages), before any row is finished.
-DEV void rope_norm_scatter_rows_xwg(const ScatterArgs &a, const float *U, int ldu, int M, int j, int r0,
-                                    int rstep, int lane) {
-  constexpr int R = 4;
-  for (; r0 < M; r0 += R * rstep) {
-    float x0[R], x1[R], c[R], s[R];
-  int p[R], page[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = r0 + i * rstep;
-    if (r < M) {
-      x0[i] = xld(U + (long long)r * ldu + lane);
-      x1[i] = xld(U + (long long)r * ldu + lane + 64);
-      p[i] = a.pos[r];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = r0 + i * rstep;
-    c[i] = s[i] = 0.f;
-    page[i] = 0;
-    if (r < M) {
-      if (a.cos && j < a.H + a.Hkv) {
-        c[i] = a.cos[p[i] * 64 + lane];
-        s[i] = a.sin[p[i] * 64 + lane];
-      }
-      if (j >= a.H) page[i] = scatter_page(a, r, p[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = r0 + i * rstep;
-    if (r < M) rope_norm_scatter_vals(a, x0[i], x1[i], c[i], s[i], p[i], page[i], r, j, lane);
-  }
-  }
 }
 
 // Weightless RMSNorm of one fp32 row of width d into bf16, by one wave.
@@ -134,45 +109,5 @@ DEV void rmsnorm_row_bf16(const float *xr, bf16 *yr, int d, float eps, int lane)
     const f32x4 v = *(const f32x4 *)(xr + c);
     bf16x4 o = {f2bf(v[0] * rs), f2bf(v[1] * rs), f2bf(v[2] * rs), f2bf(v[3] * rs)};
     *(bf16x4 *)(yr + c) = o;
-  }
-}
-
-// The same normalisation for rows r0, r0 + rstep, ... < M of X (row stride
-// ldx, written by other workgroups of the same kernel) into Y (row stride
-// ldy), by one wave.  CPL = ceil(d / 256) four-float chunks per lane and
-// row; the loads of R rows are all issued before the first is reduced.
-// The per-lane order of the sum of squares is that of rmsnorm_row_bf16.
-template <int CPL>
-DEV void rmsnorm_rows_xwg(const float *X, int ldx, bf16 *Y, int ldy, int M, int d, float eps, int r0,
-                          int rstep, int lane) {
-  constexpr int R = CPL >= 12 ? 1 : 12 / CPL;
-  for (int rb = r0; rb < M; rb += R * rstep) {
-    f32x4 v[R][CPL];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int r = rb + i * rstep, col = (c * 64 + lane) * 4;
-        v[i][c] = (r < M && col < d) ? xld4(X + (long long)r * ldx + col) : (f32x4){};
-      }
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) ss += v[i][c][0] * v[i][c][0] + v[i][c][1] * v[i][c][1] +
-                                          v[i][c][2] * v[i][c][2] + v[i][c][3] * v[i][c][3];
-      ss = wave_sum(ss);
-      const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-      const int r = rb + i * rstep;
-      if (r >= M) continue;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int col = (c * 64 + lane) * 4;
-        if (col < d) {
-          bf16x4 o = {f2bf(v[i][c][0] * rs), f2bf(v[i][c][1] * rs), f2bf(v[i][c][2] * rs), f2bf(v[i][c][3] * rs)};
-          *(bf16x4 *)(Y + (long long)r * ldy + col) = o;
-        }
-      }
-    }
   }
 }

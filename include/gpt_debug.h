@@ -21,14 +21,16 @@ enum { GPT_EPI_BF16 = 0, GPT_EPI_RELU2_BF16 = 1, GPT_EPI_RESID = 2, GPT_EPI_F32 
  * decoder block, [microgpt "Core architecture"] linear layers), fp32
  * accumulation, then the epilogue: store bf16, ReLU^2 then bf16
  * ([nanochat-launch tricks]), add into fp32 C (residual), or store fp32.
- * M <= 64 runs the decode (skinny) kernel, larger M the tiled kernel.
- * split_scratch: NULL, or device fp32 scratch of gpt_debug_split_floats()
- * floats that lets the decode kernel split K across workgroups.
+ * M <= 64 runs the decode-row kernel, larger M the tiled kernel.
+ * ksplit: 1, or (M <= 64 and GPT_EPI_F32 only) 2 .. 16 and at most K / 64:
+ * the k range is split over ksplit workgroups per column tile and C then
+ * holds ksplit fp32 slabs [ksplit, M, N] of partial products whose sum is
+ * A W^T (the form the decode step's consumers read).
  * Needs K % 64 == 0, N % 128 == 0, 16-byte aligned pointers.
+ * Errors: GPT_ERR_ARG for NULL pointers, bad shapes, epilogue or ksplit.
  */
 gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, int32_t K, void *C,
-                          int32_t epi, float *split_scratch, gpt_stream_t stream);
-size_t gpt_debug_split_floats(void);
+                          int32_t epi, int32_t ksplit, gpt_stream_t stream);
 
 /*
  * Causal MQA attention of packed sequences ([nanochat-forum]: multi-query

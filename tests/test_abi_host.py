@@ -131,6 +131,12 @@ def test_select_and_rope_validation():
 
 
 def test_debug_entry_validation():
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 100, 64, 0x3000, 0, None, 0), B.GPT_ERR_ARG)
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 60, 0x3000, 0, None, 0), B.GPT_ERR_ARG)
-    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 64, 0x3000, 9, None, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 100, 64, 0x3000, 0, 1, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 60, 0x3000, 0, 1, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 64, 0x3000, 9, 1, 0), B.GPT_ERR_ARG)
+    # k split: fp32 slabs only, M <= 64, 2 .. 16 ranges of at least 64
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 256, 0x3000, 0, 2, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 100, 128, 256, 0x3000, 3, 2, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 256, 0x3000, 3, 5, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 64 * 32, 0x3000, 3, 17, 0), B.GPT_ERR_ARG)
+    _bad(lambda: B.gpt_debug_gemm(0x1000, 0x2000, 10, 128, 256, 0x3000, 3, 0, 0), B.GPT_ERR_ARG)

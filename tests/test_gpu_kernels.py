@@ -16,22 +16,20 @@ GEMM_SHAPES = [
     (300, 384, 192),
     (1000, 1152, 768),
     (513, 1920, 1664),
-    # decode-row kernel (M <= 64)
+    # decode-row kernel (M <= 64): 1, 2, 3 and 4 row blocks, ragged M, 64-column tiles
     (1, 128, 64),
     (33, 768, 768),
     (64, 1024, 3072),
     (64, 1920, 1664),
     (17, 6656, 1664),
+    (40, 384, 1152),
 ]
 
 
-@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-def test_gemm_matches_float64(M, N, K, epi, split):
+def test_gemm_matches_float64(M, N, K, epi):
     t = torch()
-    if split and M > 64:
-        pytest.skip("k splitting applies to the decode-row kernel only")
     rng = np.random.default_rng(M * 7 + N + K + epi)
     A = bf16_round(rng.standard_normal((M, K)))
     W = bf16_round(rng.standard_normal((N, K)) * 0.05)
@@ -42,8 +40,7 @@ def test_gemm_matches_float64(M, N, K, epi, split):
     else:
         init = rng.standard_normal((M, N)).astype(np.float32) if epi == 2 else np.zeros((M, N), np.float32)
         C = t.from_numpy(init).cuda()
-    scratch = t.empty(B.gpt_debug_split_floats(), dtype=t.float32, device="cuda") if split else None
-    B.gpt_debug_gemm(dA, dW, M, N, K, C, epi, scratch)
+    B.gpt_debug_gemm(dA, dW, M, N, K, C, epi)
     t.cuda.synchronize()
     out = C.float().cpu().numpy().astype(np.float64)
     scale = np.sqrt(K) * 0.05
@@ -56,6 +53,30 @@ def test_gemm_matches_float64(M, N, K, epi, split):
         np.testing.assert_allclose(out, init + ref, rtol=1e-5, atol=1e-5 * scale)
     else:
         np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-5 * scale)
+
+
+@pytest.mark.parametrize("M,N,K,ks", [(32, 768, 768, 6), (64, 1664, 6656, 12), (17, 1024, 320, 2),
+                                      (5, 128, 1024, 16), (64, 1920, 1664, 11)])
+def test_gemm_rows_split_slabs(M, N, K, ks):
+    """k split over workgroups: the slabs are partial products over disjoint k
+    ranges (ragged: ranges differ by one 64-deep chunk) that sum to A W^T."""
+    t = torch()
+    rng = np.random.default_rng(M + N + K + ks)
+    A = bf16_round(rng.standard_normal((M, K)))
+    W = bf16_round(rng.standard_normal((N, K)) * 0.05)
+    C = t.full((ks, M, N), float("nan"), dtype=t.float32, device="cuda")
+    B.gpt_debug_gemm(to_dev_bf16(A), to_dev_bf16(W), M, N, K, C, 3, ks)
+    t.cuda.synchronize()
+    slabs = C.cpu().numpy().astype(np.float64)
+    assert np.isfinite(slabs).all()  # every slab element written
+    chunks = K // 64
+    bounds = [kz * chunks // ks * 64 for kz in range(ks + 1)]
+    for kz in range(ks):  # each slab is exactly its own k range
+        k0, k1 = bounds[kz], bounds[kz + 1]
+        ref = A[:, k0:k1].astype(np.float64) @ W[:, k0:k1].astype(np.float64).T
+        np.testing.assert_allclose(slabs[kz], ref, rtol=1e-5, atol=1e-5 * np.sqrt(k1 - k0) * 0.05)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    np.testing.assert_allclose(slabs.sum(0), ref, rtol=1e-5, atol=1e-5 * np.sqrt(K) * 0.05)
 
 
 def test_gemm_is_deterministic():
