@@ -133,6 +133,108 @@ def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     return dt, att, sk
 
 
+# ---------------------------------------------------------------- HBM traffic of the GEMM kernel
+# Two rocprofv3 counter passes over `--traffic-pass` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) are reduced by `--summarize-traffic` into
+# TRAFFIC_FILE.  Each counter is scaled by what it reads for a plain 1 GiB
+# copy in the same process.  The figure is reported only while the GEMM
+# sources hash to the value recorded with it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_d12_prefill.json")
+GEMM_SOURCES = ["gpt_block_fwd_amd/csrc/gemm.hip", "gpt_block_fwd_amd/csrc/kernels.h",
+                "gpt_block_fwd_amd/csrc/common.h"]
+COPY_BYTES = 1 << 30
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_pass():
+    """One warm-up and one counted depth-12 prefill, then a 1 GiB copy."""
+    import torch
+    from gpt_block_fwd_amd import binding as B
+    B.lib()
+    w = wl.d12_prefill()
+    dm = B.DeviceModel(w.model, wl.make_weights(w.model))
+    M = int(w.cu_seqlens[-1])
+    logits = torch.empty((M, dm.model.vocab), dtype=torch.float32, device="cuda")
+    lse = torch.empty(M, dtype=torch.float32, device="cuda")
+    tokens = torch.from_numpy(w.tokens).cuda()
+    ws = dm.workspace(M, w.n_seqs)
+    for _ in range(2):
+        dm.prefill(tokens, w.cu_seqlens, logits, lse, workspace=ws)
+        torch.cuda.synchronize()
+    del logits
+    torch.cuda.empty_cache()
+    # calibration: a plain elementwise copy (fp16 -> fp32: reads COPY_BYTES / 2,
+    # writes COPY_BYTES), then the runtime's blit copy (COPY_BYTES each way)
+    xh = torch.ones(COPY_BYTES // 4, dtype=torch.float16, device="cuda")
+    y = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    y.copy_(xh)
+    torch.cuda.synchronize()
+    del xh
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    log("traffic pass done")
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_traffic(fetch_csv, write_csv, out_path):
+    """GEMM HBM bytes per launch of the counted prefill (the second of the
+    two), each counter scaled by its reading for the final 1 GiB copy."""
+    res = {}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _counter_rows(path, "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE")
+        # the elementwise fp16 -> fp32 copy, then the runtime's blit copy
+        elem = [r for r in rows if "tofloat32_copy_kernel" in r[1]][-1]
+        blit = [r for r in rows if "copyBuffer" in r[1]][-1]
+        known = COPY_BYTES / 2 if name == "fetch" else COPY_BYTES
+        factor = known / 1024.0 / elem[2]
+        gemm = [r for r in rows if "gemm_bf16_kernel" in r[1]]
+        counted = gemm[len(gemm) // 2:]
+        res[name] = {"copy_kernel": elem[1][:80], "copy_kib": elem[2], "copy_known_kib": known / 1024.0,
+                     "factor": factor, "blit_kib": blit[2], "blit_known_kib": COPY_BYTES / 1024.0,
+                     "launches": len(counted), "kib_per_launch": sum(r[2] for r in counted) / len(counted)}
+    per_launch = (res["fetch"]["kib_per_launch"] * res["fetch"]["factor"] +
+                  res["write"]["kib_per_launch"] * res["write"]["factor"]) * 1024.0
+    out = {"kernel": "gemm_bf16_kernel (depth-12 prefill: block GEMMs + LM head)",
+           "bytes_per_launch": per_launch, "fetch": res["fetch"], "write": res["write"],
+           "gemm_sources_sha256": gemm_source_hash()}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic():
+    """Bytes per GEMM launch from TRAFFIC_FILE, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_sources_sha256") != gemm_source_hash():
+        return None
+    return round(float(t["bytes_per_launch"]), 0)
+
+
 def cpu_baseline(w, W, gpu_logits):
     """Time the oracle (fp32 BLAS) over every sequence of the workload on the
     host cores, and compare its logits with the GPU's (parity sample)."""
@@ -170,7 +272,16 @@ def main():
     ap.add_argument("--skip-d26", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="one counted depth-12 prefill and a 1 GiB copy, for rocprofv3 --pmc")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.traffic_pass:
+        traffic_pass()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder-block path has no multi-GPU "
               "sharding in this build (run with --gpus 1)", file=sys.stderr)
@@ -200,9 +311,10 @@ def main():
     attn_tfs = attn["flops"] / (attn["ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "gemm_bf16 (block GEMMs + LM head)",
                 "achieved": round(gemm_tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(gemm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
-                "flops_per_launch": g["flops"] / max(g["launches"], 1)}
+                "flops_per_launch": g["flops"] / max(g["launches"], 1),
+                "algorithmic_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1), 0)}
     breakdown = {
         "gemm_ms_per_step": round(g["ms"] / args.steps, 3),
         "attention": {"ms_per_step": round(attn["ms"] / args.steps, 3),
