@@ -522,7 +522,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
         int max_len = 0;
         for (int b = 0; b < n_seqs; ++b) max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
         aa.n_seqs = n_seqs;
-        aa.max_wg = (max_len * H + 255) / 256;
+        aa.max_wg = (max_len * H + kAttnPrefillRows - 1) / kAttnPrefillRows;
         aa.o = (bf16 *)bf.o;
         launch_attn_prefill_bf16(aa, s);
       } else {
@@ -813,7 +813,7 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
   aa.cu = cu_dev;
   aa.cu_pad = cu_dev + n_seqs + 1;
   aa.n_seqs = n_seqs;
-  aa.max_wg = (max_len * n_head + 255) / 256;
+  aa.max_wg = (max_len * n_head + kAttnPrefillRows - 1) / kAttnPrefillRows;
   aa.H = n_head;
   aa.o = (bf16 *)o;
   launch_attn_prefill_bf16(aa, s);

@@ -3,10 +3,10 @@
 //
 // Prefill: the H query heads of a sequence are flattened into rows
 // r = position * H + head, which is exactly the memory order of q.  Row r
-// sees keys 0 .. r / H.  A 256-thread workgroup owns 256 consecutive rows
-// (4 waves x 64); every 64-key K tile and transposed V tile is staged once
-// in LDS and serves all of them, so the single K/V head is read once per
-// workgroup rather than once per query head.  Scores are formed transposed,
+// sees keys 0 .. r / H.  A workgroup owns 64 * kAttnPrefillWaves
+// consecutive rows (64 per wave); every 64-key K tile and transposed V tile
+// is staged once in LDS and serves all of them, so the single K/V head is
+// read once per workgroup rather than once per query head.  Scores are formed transposed,
 // S^T = K Q^T, so each lane's accumulators hold one row and its softmax
 // statistics stay lane-local (one cross-lane exchange per 32 keys); the
 // exponentiated scores are already laid out as the B operand of
@@ -29,14 +29,18 @@ DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3);
 // V^T tile [128 dims][64 keys], 8-byte units XOR-swizzled by dim.
 DEV int vidx(int dim, int unit) { return dim * KT + ((unit ^ (dim & 15)) << 2); }
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
+// NWV waves per workgroup, 64 rows each.
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs a) {
+  constexpr int NT = 64 * NWV, ROWS = 64 * NWV;
+  constexpr int SP = 4 * 4 / NWV;  // 16-byte staging loads per thread for each of K and V^T
   __shared__ bf16 sk[2][KT * DH];
   __shared__ bf16 sv[2][DH * KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
   // blockIdx.y counts row blocks from the last one, so the blocks that see
   // the most keys are dispatched first.
-  const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * 256;
+  const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * ROWS;
   const int H = a.H;
   const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
   const long long col0 = a.cu_pad[b];
@@ -55,23 +59,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[rb][s] = *(const bf16x8 *)(qp + 16 * s);
   }
-  const int last_row = min(R0 + 255, rows_total - 1);
+  const int last_row = min(R0 + ROWS - 1, rows_total - 1);
   const int n_kt = (last_row / H) / KT + 1;
   const int pw_max = Rw < rows_total ? min(Rw + 63, rows_total - 1) / H : -1;
   const int pw_min = Rw / H;
 
-  // staging: K rows key = tid/16 + 16 p, chunk tid%16; V^T rows dim = tid/8 + 32 p, keys 8*(tid%8)..
-  bf16x8 rk[4], rv[4];
+  // staging: K rows key = tid/16 + (NT/16) p, chunk tid%16; V^T rows
+  // dim = tid/8 + (NT/8) p, keys 8*(tid%8) ..
+  bf16x8 rk[SP], rv[SP];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int key = min(kt * KT + (tid >> 4) + 16 * p, len - 1);
+    for (int p = 0; p < SP; ++p) {
+      int key = min(kt * KT + (tid >> 4) + (NT / 16) * p, len - 1);
       rk[p] = *(const bf16x8 *)(a.k + (long long)(tok0 + key) * DH + (tid & 15) * 8);
     }
     const int kb0 = kt * KT + (tid & 7) * 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int dim = (tid >> 3) + 32 * p;
+    for (int p = 0; p < SP; ++p) {
+      int dim = (tid >> 3) + (NT / 8) * p;
       rv[p] = *(const bf16x8 *)(a.vt + (long long)dim * a.ldvt + col0 + kb0);
       if (kb0 + 8 > len) {  // padding columns past the sequence hold no data
 #pragma unroll
@@ -82,13 +87,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int key = (tid >> 4) + 16 * p;
+    for (int p = 0; p < SP; ++p) {
+      int key = (tid >> 4) + (NT / 16) * p;
       *(bf16x8 *)&sk[buf][kidx(key, tid & 15)] = rk[p];
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int dim = (tid >> 3) + 32 * p, u = (tid & 7) * 2;
+    for (int p = 0; p < SP; ++p) {
+      int dim = (tid >> 3) + (NT / 8) * p, u = (tid & 7) * 2;
       bf16x4 lo = {rv[p][0], rv[p][1], rv[p][2], rv[p][3]};
       bf16x4 hi4 = {rv[p][4], rv[p][5], rv[p][6], rv[p][7]};
       *(bf16x4 *)&sv[buf][vidx(dim, u)] = lo;
@@ -209,15 +214,38 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
 
 // ------------------------------------------------------------------ decode
 
+#define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
+#define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
+
+// Page staging in LDS.  K [64 keys][128 dims]: 16-byte chunk c of key r at
+// slot c ^ (r % 16), so the 16 keys of a fragment read hit 16 bank groups.
+// V^T [128 dims][64 keys]: 16-byte chunk c of dim r at slot c ^ ((r / 2) % 8);
+// fragments read it in 8-byte units.
+DEV int kdx(int key, int chunk) { return key * DH + ((chunk ^ (key & 15)) << 3); }
+DEV int vdx(int dim, int unit) { return dim * 64 + (((unit >> 1) ^ ((dim >> 1) & 7)) << 3) + ((unit & 1) << 2); }
+
 // One workgroup per chunk of kDecodePages pages of one sequence; wave w
-// takes page w of the chunk.  Each wave scores its 64 cached positions for
-// all query heads at once (MQA: one K/V page serves every head), the four
-// pages are merged in LDS by log-sum-exp, and the chunk's unnormalised
-// output with its (max, sum) per head goes to the partial buffers.  The last
-// chunk of the sequence to finish merges all chunks and writes o.
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
-  __shared__ float o_s[kDecodePages][16 * DH];  // per-page unnormalised outputs; reused by the final merge
-  __shared__ float ml_s[kDecodePages][16][2];   // per-page (max, sum) per head
+// takes page w of the chunk and scores its 64 cached positions for all
+// query heads at once (MQA: one K/V page serves every head).  STAGE: the
+// wave first copies its page (K and V^T, 32 KB) into LDS with
+// direct-to-LDS loads that read whole 128-byte lines and takes its MFMA
+// fragments from there; this costs 128 KB of LDS, one workgroup per CU, so
+// it pays only when the grid does not fill the chip.  Otherwise the
+// fragments are loaded from the cache straight into registers and four
+// workgroups fit a CU.  The pages of a chunk are merged in LDS by
+// log-sum-exp, and the chunk's unnormalised output with its (max, sum) per
+// head goes to the partial buffers.  The last chunk of the sequence to
+// finish merges all chunks and writes o.
+template <bool STAGE>
+__global__ __launch_bounds__(64 * kDecodePages) void attn_decode_kernel(AttnDecodeArgs a) {
+  constexpr int NT = 64 * kDecodePages;
+  // STAGE: per wave a K page and a V^T page; otherwise per wave the fp32
+  // partial output (16 heads x 128).  The partials (and the final merge's
+  // scratch) use the first 8 KB of each wave's area.
+  constexpr int WAVE_BYTES = STAGE ? 2 * 64 * DH * 2 : 16 * DH * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kDecodePages * WAVE_BYTES];
+  __shared__ float ml_s[kDecodePages][16][2];  // per-page (max, sum) per head
+  auto wave_area = [&](int w) { return smem + w * WAVE_BYTES; };
   __shared__ unsigned s_prev;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hl = lane & 15, q4 = lane >> 4;
@@ -233,26 +261,60 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
     const bf16 *K = (const bf16 *)pg;
     const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
-    // every load of the page is issued before the first MFMA
+    bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
     bf16x8 kf[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
     bf16x4 vlo[8][2], vhi[8][2];
+    if constexpr (STAGE) {
+      // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims
+      // x 128 B each; lane i fills slot i of the instruction's kilobyte and
+      // so loads the logical chunk that slot holds.
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
-        vlo[d][h] = *(const bf16x4 *)vp;
-        vhi[d][h] = *(const bf16x4 *)(vp + 16);
+      for (int j = 0; j < 16; ++j) {
+        const int key = 4 * j + (lane >> 4), pc = lane & 15;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * DH + ((pc ^ (key & 15)) << 3)),
+                                         LDS_PTR(Ks + j * 512), 16, 0, 0);
       }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(Vt + dim * 64 + ((pc ^ ((dim >> 1) & 7)) << 3)),
+                                         LDS_PTR(Vs + j * 512), 16, 0, 0);
+      }
+    } else {
+      // every load of the page is issued before the first MFMA
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
+          vlo[d][h] = *(const bf16x4 *)vp;
+          vhi[d][h] = *(const bf16x4 *)(vp + 16);
+        }
+    }
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
       else qf[s] = (bf16x8){};
+    }
+    if constexpr (STAGE) {
+      // this wave's page has landed (each wave reads only its own staging area)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)&Ks[kdx(16 * kb + hl, 4 * s + q4)];
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          vlo[d][h] = *(const bf16x4 *)&Vs[vdx(16 * d + hl, 8 * h + q4)];
+          vhi[d][h] = *(const bf16x4 *)&Vs[vdx(16 * d + hl, 8 * h + q4 + 4)];
+        }
     }
     // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
     f32x4 sacc[4];
@@ -319,9 +381,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
       }
     }
     if (hl < H) {
-      // lane holds head hl, dims 16 d + 4 q4 + r
+      // lane holds head hl, dims 16 d + 4 q4 + r; with STAGE the partial
+      // overwrites this wave's K staging area, whose reads the MFMAs above
+      // have consumed
+      float *o_w = (float *)wave_area(wave);
 #pragma unroll
-      for (int d = 0; d < 8; ++d) *(f32x4 *)&o_s[wave][hl * DH + 16 * d + 4 * q4] = oacc[d];
+      for (int d = 0; d < 8; ++d) *(f32x4 *)&o_w[hl * DH + 16 * d + 4 * q4] = oacc[d];
       if (q4 == 0) {
         ml_s[wave][hl][0] = mx;
         ml_s[wave][hl][1] = rs;
@@ -332,7 +397,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   const int nw = min(kDecodePages, (len - c0 + 63) / 64);  // pages of this chunk
   const int S = (len + kDecodeChunk - 1) / kDecodeChunk;   // chunks of this sequence
   const long long obase = ((long long)b * a.max_splits + chunk) * H * DH;
-  for (int idx = tid; idx < H * DH; idx += 256) {
+  for (int idx = tid; idx < H * DH; idx += NT) {
     const int h = idx >> 7;
     float M = ml_s[0][h][0];
     for (int w = 1; w < nw; ++w) M = fmaxf(M, ml_s[w][h][0]);
@@ -340,7 +405,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     for (int w = 0; w < nw; ++w) {
       const float f = fast_exp2(ml_s[w][h][0] - M);
       L += f * ml_s[w][h][1];
-      O += f * o_s[w][idx];
+      O += f * ((const float *)wave_area(w))[idx];
     }
     if (S == 1) {
       a.o[(long long)b * H * DH + idx] = f2bf(O / L);
@@ -366,9 +431,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
   // Final merge over the S chunks.  (max, sum) of every chunk and head into
   // LDS, then one factor per (chunk, head) with 1/sum folded in, then every
   // output with all of its chunk loads in flight together.
-  float *mlg = &o_s[0][0];                   // [S][16][2]
-  float *fct = &o_s[0][0] + kMaxDecodeChunks * 32;  // [S][16]
-  for (int i = tid; i < S * H; i += 256) {
+  // the per-wave areas are free by now
+  static_assert(kMaxDecodeChunks * 48 * 4 <= kDecodePages * WAVE_BYTES, "merge scratch exceeds LDS");
+  float *mlg = (float *)smem;                              // [S][16][2]
+  float *fct = (float *)smem + kMaxDecodeChunks * 32;      // [S][16]
+  for (int i = tid; i < S * H; i += NT) {
     const int c = i / H, h = i - c * H;
     const float *ml = a.ml_part + (((long long)b * a.max_splits + c) * H + h) * 2;
     mlg[(c * 16 + h) * 2] = xld(ml);
@@ -384,7 +451,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     for (int c = 0; c < S; ++c) fct[c * 16 + tid] = fast_exp2(mlg[(c * 16 + tid) * 2] - M) * inv;
   }
   __syncthreads();
-  constexpr int OPT = 16 * DH / 256;  // outputs per thread at most
+  constexpr int OPT = 16 * DH / NT;  // outputs per thread at most
   const float *ob = a.o_part + (long long)b * a.max_splits * H * DH;
   float acc[OPT];
 #pragma unroll
@@ -395,20 +462,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int j = 0; j < OPT; ++j) {
-        const int idx = tid + 256 * j;
+        const int idx = tid + NT * j;
         v[cc][j] = (c0c + cc < S && idx < H * DH) ? xld(ob + (long long)(c0c + cc) * H * DH + idx) : 0.f;
       }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int j = 0; j < OPT; ++j) {
-        const int idx = tid + 256 * j;
+        const int idx = tid + NT * j;
         if (c0c + cc < S && idx < H * DH) acc[j] += fct[(c0c + cc) * 16 + (idx >> 7)] * v[cc][j];
       }
   }
 #pragma unroll
   for (int j = 0; j < OPT; ++j) {
-    const int idx = tid + 256 * j;
+    const int idx = tid + NT * j;
     if (idx < H * DH) a.o[(long long)b * H * DH + idx] = f2bf(acc[j]);
   }
 }
@@ -416,10 +483,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnDecodeArgs a) {
 }  // namespace
 
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
-  if (a.n_seqs > 0 && a.max_wg > 0) attn_prefill_kernel<<<dim3(a.n_seqs, a.max_wg), 256, 0, s>>>(a);
+  if (a.n_seqs > 0 && a.max_wg > 0)
+    attn_prefill_kernel<kAttnPrefillWaves><<<dim3(a.n_seqs, a.max_wg), 64 * kAttnPrefillWaves, 0, s>>>(a);
 }
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  attn_decode_kernel<<<dim3(a.max_splits, a.n), 256, 0, s>>>(a);
+  // staging through LDS holds one workgroup per CU: use it only when the
+  // grid is at most one workgroup per CU (256)
+  const dim3 grid(a.max_splits, a.n);
+  if ((long long)a.max_splits * a.n <= 256) attn_decode_kernel<true><<<grid, 64 * kDecodePages, 0, s>>>(a);
+  else attn_decode_kernel<false><<<grid, 64 * kDecodePages, 0, s>>>(a);
 }
