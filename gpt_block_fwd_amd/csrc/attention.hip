@@ -236,15 +236,15 @@ DEV int vdx(int dim, int unit) { return dim * 64 + (((unit >> 1) ^ ((dim >> 1) &
 // log-sum-exp, and the chunk's unnormalised output with its (max, sum) per
 // head goes to the partial buffers.  The last chunk of the sequence to
 // finish merges all chunks and writes o.
-template <bool STAGE>
-__global__ __launch_bounds__(64 * kDecodePages) void attn_decode_kernel(AttnDecodeArgs a) {
-  constexpr int NT = 64 * kDecodePages;
+template <bool STAGE, int NP>
+__global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) {
+  constexpr int NT = 64 * NP, CH = 64 * NP;  // threads; cached positions per chunk
   // STAGE: per wave a K page and a V^T page; otherwise per wave the fp32
   // partial output (16 heads x 128).  The partials (and the final merge's
   // scratch) use the first 8 KB of each wave's area.
   constexpr int WAVE_BYTES = STAGE ? 2 * 64 * DH * 2 : 16 * DH * 4;
-  __shared__ __attribute__((aligned(16))) char smem[kDecodePages * WAVE_BYTES];
-  __shared__ float ml_s[kDecodePages][16][2];  // per-page (max, sum) per head
+  __shared__ __attribute__((aligned(16))) char smem[NP * WAVE_BYTES];
+  __shared__ float ml_s[NP][16][2];  // per-page (max, sum) per head
   auto wave_area = [&](int w) { return smem + w * WAVE_BYTES; };
   __shared__ unsigned s_prev;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * kDecodePages) void attn_decode_kernel(AttnDeco
   const int b = blockIdx.y, chunk = blockIdx.x;
   const PagedKV &kv = a.kv;
   const int len = kv.lens[b] + 1;  // the new position is already in the cache
-  const int c0 = chunk * kDecodeChunk;
+  const int c0 = chunk * CH;
   if (c0 >= len) return;
   const int H = a.H;
   const int kpos0 = c0 + wave * 64;
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(64 * kDecodePages) void attn_decode_kernel(AttnDeco
     }
   }
   __syncthreads();
-  const int nw = min(kDecodePages, (len - c0 + 63) / 64);  // pages of this chunk
-  const int S = (len + kDecodeChunk - 1) / kDecodeChunk;   // chunks of this sequence
+  const int nw = min(NP, (len - c0 + 63) / 64);  // pages of this chunk
+  const int S = (len + CH - 1) / CH;   // chunks of this sequence
   const long long obase = ((long long)b * a.max_splits + chunk) * H * DH;
   for (int idx = tid; idx < H * DH; idx += NT) {
     const int h = idx >> 7;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * kDecodePages) void attn_decode_kernel(AttnDeco
   // LDS, then one factor per (chunk, head) with 1/sum folded in, then every
   // output with all of its chunk loads in flight together.
   // the per-wave areas are free by now
-  static_assert(kMaxDecodeChunks * 48 * 4 <= kDecodePages * WAVE_BYTES, "merge scratch exceeds LDS");
+  static_assert(kMaxDecodeChunks * 48 * 4 <= NP * WAVE_BYTES, "merge scratch exceeds LDS");
   float *mlg = (float *)smem;                              // [S][16][2]
   float *fct = (float *)smem + kMaxDecodeChunks * 32;      // [S][16]
   for (int i = tid; i < S * H; i += NT) {
@@ -489,9 +489,15 @@ void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  // staging through LDS holds one workgroup per CU: use it only when the
-  // grid is at most one workgroup per CU (256)
-  const dim3 grid(a.max_splits, a.n);
-  if ((long long)a.max_splits * a.n <= 256) attn_decode_kernel<true><<<grid, 64 * kDecodePages, 0, s>>>(a);
-  else attn_decode_kernel<false><<<grid, 64 * kDecodePages, 0, s>>>(a);
+  // Staging through LDS holds one workgroup per CU: use it (chunks of
+  // kDecodePages pages) only when the grid is at most one workgroup per CU.
+  // Otherwise twice the pages per chunk, so each sequence's final merge has
+  // half the chunks; the partial buffers, sized for kDecodeChunk, hold them.
+  if ((long long)a.max_splits * a.n <= 256) {
+    attn_decode_kernel<true, kDecodePages><<<dim3(a.max_splits, a.n), 64 * kDecodePages, 0, s>>>(a);
+  } else {
+    AttnDecodeArgs b = a;
+    b.max_splits = (a.max_splits + 1) / 2;
+    attn_decode_kernel<false, 2 * kDecodePages><<<dim3(b.max_splits, b.n), 128 * kDecodePages, 0, s>>>(b);
+  }
 }
