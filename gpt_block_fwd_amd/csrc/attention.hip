@@ -19,15 +19,21 @@
 // The last page of a sequence to finish merges the pages (log-sum-exp).
 #include "kernels.h"
 
+#define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
+#define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
+
 namespace {
 
 constexpr int DH = 128;
 constexpr int KT = 64;  // keys per tile
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazy softmax reference
 
 // K tile [64 keys][128 dims], 16-byte chunks XOR-swizzled by key.
 DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
-// V^T tile [128 dims][64 keys], 8-byte units XOR-swizzled by dim.
-DEV int vidx(int dim, int unit) { return dim * KT + ((unit ^ (dim & 15)) << 2); }
+// V^T tile [128 dims][64 keys], 16-byte chunks XOR-swizzled by dim pair, read
+// in 8-byte units.  Both swizzles move whole 16-byte chunks, so direct-to-LDS
+// loads can apply them by choosing each lane's source.
+DEV int vidx(int dim, int unit) { return dim * KT + ((((unit >> 1) ^ ((dim >> 1) & 7)) << 3) | ((unit & 1) << 2)); }
 
 // NWV waves per workgroup, 64 rows each.
 template <int NWV>
@@ -64,40 +70,38 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   const int pw_max = Rw < rows_total ? min(Rw + 63, rows_total - 1) / H : -1;
   const int pw_min = Rw / H;
 
-  // staging: K rows key = tid/16 + (NT/16) p, chunk tid%16; V^T rows
-  // dim = tid/8 + (NT/8) p, keys 8*(tid%8) ..
-  bf16x8 rk[SP], rv[SP];
-  auto gload = [&](int kt) {
+  // Direct-to-LDS staging: a tile is 16 KB of K (4 keys x 256 B per wave
+  // instruction) and 16 KB of V^T (8 dims x 128 B per instruction); wave w
+  // issues instructions j = w, w + NWV, ...  Lane i fills 16-byte slot i of
+  // the instruction's kilobyte and so loads the logical chunk that slot
+  // holds.  Keys past the sequence are clamped to its last key (they are
+  // masked); V^T columns past it are zeroed once the tile has landed.
+  constexpr int DJ = 16 / NWV;  // instructions per wave for each of K and V^T
+  auto dma = [&](int kt, int buf) {
 #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      int key = min(kt * KT + (tid >> 4) + (NT / 16) * p, len - 1);
-      rk[p] = *(const bf16x8 *)(a.k + (long long)(tok0 + key) * DH + (tid & 15) * 8);
+    for (int jj = 0; jj < DJ; ++jj) {
+      const int j = wave + NWV * jj;
+      const int key = 4 * j + (lane >> 4), pc = lane & 15;
+      const int gkey = min(kt * KT + key, len - 1);
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * DH + ((pc ^ (key & 7)) << 3)),
+                                       LDS_PTR(&sk[buf][j * 512]), 16, 0, 0);
     }
-    const int kb0 = kt * KT + (tid & 7) * 8;
 #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      int dim = (tid >> 3) + (NT / 8) * p;
-      rv[p] = *(const bf16x8 *)(a.vt + (long long)dim * a.ldvt + col0 + kb0);
-      if (kb0 + 8 > len) {  // padding columns past the sequence hold no data
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (kb0 + e >= len) rv[p][e] = (bf16)0.f;
-      }
+    for (int jj = 0; jj < DJ; ++jj) {
+      const int j = wave + NWV * jj;
+      const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+      __builtin_amdgcn_global_load_lds(
+          GLOBAL_PTR(a.vt + (long long)dim * a.ldvt + col0 + kt * KT + ((pc ^ ((dim >> 1) & 7)) << 3)),
+          LDS_PTR(&sv[buf][j * 512]), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      int key = (tid >> 4) + (NT / 16) * p;
-      *(bf16x8 *)&sk[buf][kidx(key, tid & 15)] = rk[p];
-    }
-#pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      int dim = (tid >> 3) + (NT / 8) * p, u = (tid & 7) * 2;
-      bf16x4 lo = {rv[p][0], rv[p][1], rv[p][2], rv[p][3]};
-      bf16x4 hi4 = {rv[p][4], rv[p][5], rv[p][6], rv[p][7]};
-      *(bf16x4 *)&sv[buf][vidx(dim, u)] = lo;
-      *(bf16x4 *)&sv[buf][vidx(dim, u + 1)] = hi4;
+  // After a tile has landed (and a barrier): zero its V^T columns past the
+  // sequence; the caller puts another barrier before the tile is read.
+  auto zero_tail = [&](int kt, int buf) {
+    const int valid = len - kt * KT;  // 1 .. 63 here
+    for (int i = tid; i < DH * KT; i += NT) {
+      const int dim = i / KT, key = i % KT;
+      if (key >= valid) sv[buf][vidx(dim, key >> 2) + (key & 3)] = (bf16)0.f;
     }
   };
 
@@ -126,39 +130,49 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
           sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
       }
     }
+    // Online softmax in the base-2 domain with a lazy reference: a row's
+    // reference max moves (and its output and sum are rescaled) only when a
+    // tile's max exceeds it by more than kLazy, so the probabilities formed
+    // against it stay below 2^kLazy and most tiles skip the rescale.
+    // Causal masking is needed only on tiles that reach past the wave's
+    // first row position (a wave-uniform test).
     const bool need_mask = kt * KT + KT - 1 > pw_min;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int key = kt * KT + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > prow[rb]) sacc[kb][rb][r] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sacc[kb][rb][r] * sc;
-          if (need_mask) {
-            int key = kt * KT + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > prow[rb]) v = -INFINITY;
-          }
-          sacc[kb][rb][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[rb], mx);
-      const float alpha = fast_exp2(mrow[rb] - mnew);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][rb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sc;  // scaled tile max of the row
+      if (mx > mrow[rb] + kLazy) {
+        const float alpha = fast_exp2(mrow[rb] - mx);
+        lrow[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) oacc[d][rb] *= alpha;
+        mrow[rb] = mx;
+      }
+      const float mref = mrow[rb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sacc[kb][rb][r] - mnew);
+          float p = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], sc, -mref));
           sacc[kb][rb][r] = p;
           rs += p;
         }
       rs += __shfl_xor(rs, 32, 64);
-      lrow[rb] = lrow[rb] * alpha + rs;
-      mrow[rb] = mnew;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) oacc[d][rb] *= alpha;
+      lrow[rb] += rs;
     }
     // O^T += V^T P^T, 16 keys per MFMA; k slot 8g+j <-> key 16h + 8(j/4) + 4g + j%4
 #pragma unroll
@@ -183,15 +197,21 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  auto land = [&](int kt, int buf) {  // wait for tile kt's loads (all waves)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt * KT + KT > len) {
+      zero_tail(kt, buf);
+      __syncthreads();
+    }
+  };
+  dma(0, 0);
+  land(0, 0);
   for (int kt = 0; kt < n_kt - 1; ++kt) {
-    gload(kt + 1);
+    dma(kt + 1, (kt + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the tile's MFMAs
     tile(kt, kt & 1);
-    sstore((kt + 1) & 1);
-    __syncthreads();
+    land(kt + 1, (kt + 1) & 1);
   }
   tile(n_kt - 1, (n_kt - 1) & 1);
 
@@ -213,9 +233,6 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
 }
 
 // ------------------------------------------------------------------ decode
-
-#define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
-#define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
 
 // Page staging in LDS.  K [64 keys][128 dims]: 16-byte chunk c of key r at
 // slot c ^ (r % 16), so the 16 keys of a fragment read hit 16 bank groups.
