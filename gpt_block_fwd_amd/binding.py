@@ -85,7 +85,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double)]
     L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp]
-    L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, vp, vp, vp]
+    L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
     for name in EXPORTS:
         if name not in ("gpt_last_error", "gpt_workspace_bytes"):
             getattr(L, name).restype = ctypes.c_int
@@ -201,10 +201,10 @@ def gpt_debug_gemm(A, W, M: int, N: int, K: int, C, epi: int, ksplit: int = 1, s
 
 
 def gpt_debug_attn_prefill(q, k, vt, ldvt: int, cu_seqlens, n_seqs: int, n_head: int, cu_dev, o,
-                           stream=None):
+                           qk_norm: int = 1, stream=None):
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     _check(lib().gpt_debug_attn_prefill(_ptr(q), _ptr(k), _ptr(vt), ldvt, cu.ctypes.data, n_seqs,
-                                        n_head, _ptr(cu_dev), _ptr(o), _stream(stream)))
+                                        n_head, qk_norm, _ptr(cu_dev), _ptr(o), _stream(stream)))
 
 
 # ------------------------------------------------------------------ device weights

@@ -519,6 +519,7 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
         aa.cu = bf.cu;
         aa.cu_pad = bf.cu_pad;
         aa.H = H;
+        aa.qk_norm = c->qk_norm;
         int max_len = 0;
         for (int b = 0; b < n_seqs; ++b) max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
         aa.n_seqs = n_seqs;
@@ -785,7 +786,7 @@ gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, in
 }
 
 gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, int64_t ldvt,
-                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head,
+                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head, int32_t qk_norm,
                                   int32_t *cu_dev, void *o, gpt_stream_t stream) {
   if (!q || !k || !vt || !cu_seqlens || !cu_dev || !o) return fail(GPT_ERR_ARG, "NULL pointer");
   if (n_seqs <= 0 || n_seqs > kMaxPrefillSeqs || n_head <= 0 || n_head > 16) return fail(GPT_ERR_ARG, "bad sizes");
@@ -815,6 +816,7 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
   aa.n_seqs = n_seqs;
   aa.max_wg = (max_len * n_head + kAttnPrefillRows - 1) / kAttnPrefillRows;
   aa.H = n_head;
+  aa.qk_norm = qk_norm != 0;
   aa.o = (bf16 *)o;
   launch_attn_prefill_bf16(aa, s);
   return hip_check("gpt_debug_attn_prefill");

@@ -27,6 +27,11 @@ namespace {
 constexpr int DH = 128;
 constexpr int KT = 64;  // keys per tile
 constexpr float kLazy = 8.0f;  // log2 headroom of the lazy softmax reference
+// With QK-norm, q and k have RMS <= 1 per head, so |q.k| <= 128 (1 + 2^-9)^2
+// after bf16 rounding and a scaled score |q.k| log2(e) / sqrt(128) stays
+// below 16.4: a fixed reference of 16.5 keeps every 2^(score - ref) in
+// (2^-33, 1), far from fp32 overflow and underflow.
+constexpr float kScoreBound = 16.5f;
 
 // K tile [64 keys][128 dims], 16-byte chunks XOR-swizzled by key.
 DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
@@ -35,8 +40,10 @@ DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3);
 // loads can apply them by choosing each lane's source.
 DEV int vidx(int dim, int unit) { return dim * KT + ((((unit >> 1) ^ ((dim >> 1) & 7)) << 3) | ((unit & 1) << 2)); }
 
-// NWV waves per workgroup, 64 rows each.
-template <int NWV>
+// NWV waves per workgroup, 64 rows each.  FIXREF: q and k are QK-normalised,
+// so the softmax runs against the fixed reference kScoreBound (no running
+// max, no rescale of the output accumulators).
+template <int NWV, bool FIXREF>
 __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs a) {
   constexpr int NT = 64 * NWV, ROWS = 64 * NWV;
   constexpr int SP = 4 * 4 / NWV;  // 16-byte staging loads per thread for each of K and V^T
@@ -137,6 +144,31 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     // Causal masking is needed only on tiles that reach past the wave's
     // first row position (a wave-uniform test).
     const bool need_mask = kt * KT + KT - 1 > pw_min;
+    if constexpr (FIXREF) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              int key = kt * KT + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+              if (key > prow[rb]) sacc[kb][rb][r] = -INFINITY;
+            }
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], sc, -kScoreBound));
+            sacc[kb][rb][r] = p;
+            rs += p;
+          }
+        rs += __shfl_xor(rs, 32, 64);
+        lrow[rb] += rs;
+      }
+    } else
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -INFINITY;
@@ -500,8 +532,10 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 }  // namespace
 
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
-  if (a.n_seqs > 0 && a.max_wg > 0)
-    attn_prefill_kernel<kAttnPrefillWaves><<<dim3(a.n_seqs, a.max_wg), 64 * kAttnPrefillWaves, 0, s>>>(a);
+  if (a.n_seqs <= 0 || a.max_wg <= 0) return;
+  const dim3 grid(a.n_seqs, a.max_wg);
+  if (a.qk_norm) attn_prefill_kernel<kAttnPrefillWaves, true><<<grid, 64 * kAttnPrefillWaves, 0, s>>>(a);
+  else attn_prefill_kernel<kAttnPrefillWaves, false><<<grid, 64 * kAttnPrefillWaves, 0, s>>>(a);
 }
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {

@@ -125,6 +125,7 @@ struct AttnPrefillArgs {
   const int *cu, *cu_pad;
   int n_seqs, max_wg;  // grid: (sequence, kAttnPrefillRows-row block counted from the end)
   int H;
+  int qk_norm;  // q and k are QK-normalised (RMS <= 1 per head): fixed softmax reference
   bf16 *o;  // [M][H*128]
 };
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);

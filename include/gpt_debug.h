@@ -40,9 +40,12 @@ gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, in
  * 64 (ldvt >= cu_pad[n_seqs], multiple of 64); o bf16 [total, H*128].
  * cu_seqlens is a host array [n_seqs + 1]; cu_dev is a device int32 buffer
  * of 2*(n_seqs + 1) entries the call fills with cu_seqlens and cu_pad.
+ * qk_norm != 0 promises QK-normalised q and k (RMS <= 1 per head, as the
+ * forward pass leaves them): the softmax then runs against a fixed bound on
+ * the scores instead of a running maximum; with qk_norm == 0 any q and k.
  */
 gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, int64_t ldvt,
-                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head,
+                                  const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head, int32_t qk_norm,
                                   int32_t *cu_dev, void *o, gpt_stream_t stream);
 
 #ifdef __cplusplus

@@ -93,21 +93,25 @@ def test_gemm_is_deterministic():
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
-def _attn_case(lens, H, seed):
+def _attn_case(lens, H, seed, qk_norm):
     rng = np.random.default_rng(seed)
     total = int(np.sum(lens))
-    # unit-RMS q and k, as QK-norm leaves them
-    q = oracle.rmsnorm(rng.standard_normal((total, H, 128)), 1e-6)
-    k = oracle.rmsnorm(rng.standard_normal((total, 1, 128)), 1e-6)
+    if qk_norm:  # unit-RMS q and k, as QK-norm leaves them
+        q = oracle.rmsnorm(rng.standard_normal((total, H, 128)), 1e-6)
+        k = oracle.rmsnorm(rng.standard_normal((total, 1, 128)), 1e-6)
+    else:  # larger scores, and a drift along the sequence that keeps raising the row maxima
+        q = rng.standard_normal((total, H, 128)) * 2.0
+        k = rng.standard_normal((total, 1, 128)) * 2.0 + np.linspace(0, 3, total)[:, None, None]
     v = rng.standard_normal((total, 1, 128)) * 0.5
     return bf16_round(q), bf16_round(k), bf16_round(v)
 
 
+@pytest.mark.parametrize("qk_norm", [1, 0])
 @pytest.mark.parametrize("lens,H", [([1, 63, 64, 65, 300], 6), ([2048], 6), ([129, 7, 1000], 13),
                                     ([256], 1)])
-def test_prefill_attention_matches_oracle(lens, H):
+def test_prefill_attention_matches_oracle(lens, H, qk_norm):
     t = torch()
-    q, k, v = _attn_case(lens, H, seed=sum(lens) + H)
+    q, k, v = _attn_case(lens, H, seed=sum(lens) + H, qk_norm=qk_norm)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     pads = [(L + 63) // 64 * 64 for L in lens]
     cu_pad = np.concatenate([[0], np.cumsum(pads)]).astype(np.int64)
@@ -120,7 +124,7 @@ def test_prefill_attention_matches_oracle(lens, H):
     dvt = to_dev_bf16(vt)
     cu_dev = t.zeros(2 * (len(lens) + 1), dtype=t.int32, device="cuda")
     o = t.empty((len(q), H * 128), dtype=t.bfloat16, device="cuda")
-    B.gpt_debug_attn_prefill(dq, dk, dvt, ldvt, cu, len(lens), H, cu_dev, o)
+    B.gpt_debug_attn_prefill(dq, dk, dvt, ldvt, cu, len(lens), H, cu_dev, o, qk_norm=qk_norm)
     t.cuda.synchronize()
     got = o.float().cpu().numpy().reshape(len(q), H, 128)
     assert np.isfinite(got).all()
