@@ -24,6 +24,10 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags (none at present).
+EXTRA: dict = {}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -31,7 +35,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c"]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c"]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += [src, "-o", obj]

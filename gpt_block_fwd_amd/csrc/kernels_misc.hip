@@ -467,78 +467,123 @@ void launch_argmax(const float *logits, int rows, int V, int *out, float *scratc
 }
 
 // ---------------------------------------------------------------- sampling
-// Inverse-CDF temperature sampling, one 1024-thread workgroup per row.
-// Thread t owns the contiguous chunk [t*C, (t+1)*C).  Weights are
-// e_i = exp((x_i - max)/T); the block scan of the chunk sums gives each
-// chunk's starting cumulative weight, and the token is the first i whose
-// cumulative weight exceeds u * total.
+// Inverse-CDF temperature sampling, one 1024-thread workgroup per row:
+// weights e_i = 2^((x_i - max) log2(e) / T); the token is the first i whose
+// cumulative weight exceeds u * total.  The row is walked in super-tiles of
+// 8192 entries; thread t owns entries 8t .. 8t + 8 of each (32 contiguous
+// bytes, so a wave's loads are contiguous).  Pass 1: the row max.  Pass 2:
+// the total.  Pass 3: super-tile by super-tile, an inclusive scan of the
+// threads' sums finds the super-tile, then the thread, then the entry where
+// the running sum passes the target.  If rounding leaves the target at or
+// above the last running sum, the last entry of positive weight is taken.
 
-__global__ __launch_bounds__(1024) void sample_kernel(const float *logits, int V, float inv_t,
-                                                      const float *uniforms, int *out, int *lens) {
-  __shared__ float red[16];
-  __shared__ float scan[16];
-  __shared__ int answer, lastpos;
+constexpr int kSampThreads = 1024, kSampPer = 8, kSampTile = kSampThreads * kSampPer;
+
+DEV void samp_load(const float *row, int V, int base, int t, float (&x)[kSampPer]) {
+  const int i0 = base + kSampPer * t;
+  if (i0 + kSampPer <= V && (V & 3) == 0) {
+    const f32x4 lo = *(const f32x4 *)(row + i0), hi = *(const f32x4 *)(row + i0 + 4);
+    x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+    x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) x[j] = i0 + j < V ? row[i0 + j] : -INFINITY;
+  }
+}
+
+// Block-wide sum (fixed tree: per-wave reduction, then the 16 wave sums in order).
+DEV float samp_block_sum(float v, float *red) {
+  v = wave_sum(v);
+  const int t = threadIdx.x;
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int k = 0; k < kSampThreads / 64; ++k) s += red[k];
+  return s;
+}
+
+__global__ __launch_bounds__(kSampThreads) void sample_kernel(const float *logits, int V, float inv_t,
+                                                              const float *uniforms, int *out, int *lens) {
+  __shared__ float red[kSampThreads / 64];
+  __shared__ float wsum[kSampThreads / 64];
+  __shared__ int s_pick, s_last;
   const float *row = logits + (long long)blockIdx.x * V;
-  int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int C = (V + 1023) / 1024;
-  int i0 = t * C, i1 = min(V, i0 + C);
-  // row max
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float x[kSampPer];
+  // pass 1: max
   float m = -INFINITY;
-  for (int i = i0; i < i1; ++i) m = fmaxf(m, row[i]);
+  for (int base = 0; base < V; base += kSampTile) {
+    samp_load(row, V, base, t, x);
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) m = fmaxf(m, x[j]);
+  }
   m = wave_max(m);
   if (lane == 0) red[w] = m;
   if (t == 0) {
-    answer = -1;
-    lastpos = -1;
+    s_pick = -1;
+    s_last = -1;
   }
   __syncthreads();
   m = red[0];
-  for (int k = 1; k < 16; ++k) m = fmaxf(m, red[k]);
-  float sc = inv_t * kLog2e;
+  for (int k = 1; k < kSampThreads / 64; ++k) m = fmaxf(m, red[k]);
+  const float sc = inv_t * kLog2e;
+  // pass 2: total weight
   float local = 0.f;
-  int lastp = -1;
-  for (int i = i0; i < i1; ++i) {
-    float e = fast_exp2((row[i] - m) * sc);
-    local += e;
-    if (e > 0.f) lastp = i;
-  }
-  // inclusive scan across the workgroup
-  float incl = local;
+  for (int base = 0; base < V; base += kSampTile) {
+    samp_load(row, V, base, t, x);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    float v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
+    for (int j = 0; j < kSampPer; ++j) local += fast_exp2((x[j] - m) * sc);
   }
-  __syncthreads();
-  if (lane == 63) scan[w] = incl;
-  __syncthreads();
-  float base = 0.f, total = 0.f;
-  for (int k = 0; k < 16; ++k) {
-    if (k < w) base += scan[k];
-    total += scan[k];
-  }
-  incl += base;
-  float excl = incl - local;
-  float target = uniforms[blockIdx.x] * total;
-  if (lastp >= 0) atomicMax(&lastpos, lastp);
-  if (excl <= target && target < incl) {
-    float run = excl;
-    int pick = -1, lastpos_here = -1;
-    for (int i = i0; i < i1; ++i) {
-      float e = fast_exp2((row[i] - m) * sc);
-      run += e;
-      if (e > 0.f) lastpos_here = i;
-      if (run > target) {
-        pick = i;
-        break;
-      }
+  const float total = samp_block_sum(local, red);
+  const float target = uniforms[blockIdx.x] * total;
+  // pass 3: find the crossing
+  float run = 0.f;  // weight of the super-tiles before this one
+  int last = -1;
+  for (int base = 0; base < V; base += kSampTile) {
+    samp_load(row, V, base, t, x);
+    float e[kSampPer], mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      e[j] = fast_exp2((x[j] - m) * sc);
+      mine += e[j];
+      if (e[j] > 0.f) last = base + kSampPer * t + j;
     }
-    if (pick < 0) pick = lastpos_here;
-    atomicMax(&answer, pick);  // at most one thread qualifies
+    // inclusive scan of the threads' sums in thread order
+    float incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    float before = 0.f, tile_total = 0.f;
+    for (int k = 0; k < kSampThreads / 64; ++k) {
+      if (k < w) before += wsum[k];
+      tile_total += wsum[k];
+    }
+    const float excl = run + before + incl - mine;
+    if (excl <= target && target < excl + mine) {
+      float cum = excl;
+      int pick = -1;
+#pragma unroll
+      for (int j = 0; j < kSampPer; ++j) {
+        cum += e[j];
+        if (pick < 0 && cum > target) pick = base + kSampPer * t + j;
+      }
+      if (pick < 0) pick = last;  // rounding inside the thread's entries
+      atomicMax(&s_pick, pick);
+    }
+    __syncthreads();
+    if (s_pick >= 0) break;  // uniform: every thread reads the same value
+    run += tile_total;
   }
+  if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
   if (t == 0) {
-    out[blockIdx.x] = answer >= 0 ? answer : (lastpos >= 0 ? lastpos : 0);
+    out[blockIdx.x] = s_pick >= 0 ? s_pick : (s_last >= 0 ? s_last : 0);
     if (lens) lens[blockIdx.x] += 1;  // decode: the step's position is now cached
   }
 }
@@ -546,7 +591,7 @@ __global__ __launch_bounds__(1024) void sample_kernel(const float *logits, int V
 void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
                    int *out, int *lens, hipStream_t s) {
   if (rows <= 0) return;
-  sample_kernel<<<rows, 1024, 0, s>>>(logits, V, 1.0f / temperature, u, out, lens);
+  sample_kernel<<<rows, kSampThreads, 0, s>>>(logits, V, 1.0f / temperature, u, out, lens);
 }
 
 // ---------------------------------------------------------------- KV lengths
