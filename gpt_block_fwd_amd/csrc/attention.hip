@@ -312,7 +312,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
     bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
     bf16x8 kf[4][4];
-    bf16x4 vlo[8][2], vhi[8][2];
+    bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
     if constexpr (STAGE) {
       // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims
       // x 128 B each; lane i fills slot i of the instruction's kilobyte and
@@ -338,11 +338,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
       for (int d = 0; d < 8; ++d)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16 *vp = Vt + (16 * d + hl) * 64 + 32 * h + 4 * q4;
-          vlo[d][h] = *(const bf16x4 *)vp;
-          vhi[d][h] = *(const bf16x4 *)(vp + 16);
-        }
+        for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)(Vt + (16 * d + hl) * 64 + 32 * h + 8 * q4);
     }
     bf16x8 qf[4];
 #pragma unroll
@@ -360,10 +356,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
       for (int d = 0; d < 8; ++d)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          vlo[d][h] = *(const bf16x4 *)&Vs[vdx(16 * d + hl, 8 * h + q4)];
-          vhi[d][h] = *(const bf16x4 *)&Vs[vdx(16 * d + hl, 8 * h + q4 + 4)];
-        }
+        for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
     }
     // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
     f32x4 sacc[4];
@@ -405,10 +398,8 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (kpos0 + 32 * h + 4 * q4 + e >= len) vlo[d][h][e] = (bf16)0.f;
-            if (kpos0 + 32 * h + 16 + 4 * q4 + e >= len) vhi[d][h][e] = (bf16)0.f;
-          }
+          for (int j = 0; j < 8; ++j)
+            if (kpos0 + 32 * h + 16 * (j >> 2) + 4 * q4 + (j & 3) >= len) vf[d][h][j] = (bf16)0.f;
     }
     // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
     f32x4 oacc[8];
@@ -423,11 +414,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
         pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
       }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        bf16x8 vf = {vlo[d][h][0], vlo[d][h][1], vlo[d][h][2], vlo[d][h][3],
-                     vhi[d][h][0], vhi[d][h][1], vhi[d][h][2], vhi[d][h][3]};
-        oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
-      }
+      for (int d = 0; d < 8; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d][h], pf, oacc[d], 0, 0, 0);
     }
     if (hl < H) {
       // lane holds head hl, dims 16 d + 4 q4 + r; with STAGE the partial

@@ -81,6 +81,13 @@ struct RowInfo {
   const int *vcol;
 };
 
+// Column of cached position p (0 .. 63) in a page's transposed V rows.
+// Within each 32-position half, position 16 a + 4 q + b (a < 2, q < 4,
+// b < 4) sits at column 8 q + 4 a + b: the order in which the decode
+// kernel's MFMA takes keys (k slot 8 q + j <-> key 16 (j / 4) + 4 q + j % 4),
+// so one 16-byte load yields a lane's eight keys.
+DEV int vslot(int p) { return (p & 32) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3); }
+
 // Paged KV cache addressing (see include/gpt.h for the layout).
 struct PagedKV {
   char *base;             // start of layer 0's pages

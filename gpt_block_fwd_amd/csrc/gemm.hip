@@ -87,7 +87,7 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
         if (e.use_cache) {
           const int b = e.seq ? e.seq[m] : m;
           const int page = e.kv.table[b * e.kv.pages_per_seq + p / e.kv.page_size];
-          slot = p % e.kv.page_size;
+          slot = vslot(p % e.kv.page_size);
           cv = (bf16 *)(e.kv.base + (long long)e.layer * e.kv.layer_stride +
                         (long long)page * e.kv.page_stride + e.kv.half_bytes);
         }

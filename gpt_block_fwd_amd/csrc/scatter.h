@@ -57,8 +57,8 @@ DEV void rope_norm_scatter_vals(const ScatterArgs &a, float x0, float x1, float 
       k[lane + 64] = y1;
     } else {
       bf16 *vt = (bf16 *)(pg + kv.half_bytes);
-      vt[(long long)(g * 128 + lane) * kv.page_size + slot] = y0;
-      vt[(long long)(g * 128 + lane + 64) * kv.page_size + slot] = y1;
+      vt[(long long)(g * 128 + lane) * kv.page_size + vslot(slot)] = y0;
+      vt[(long long)(g * 128 + lane + 64) * kv.page_size + vslot(slot)] = y1;
     }
   }
 }

@@ -118,7 +118,10 @@ gpt_status rope_tables(int32_t max_seq, int32_t head_dim, float base, float *cos
  *   pages   [n_layer][n_pages][2][page]   n_pages = n_seqs * ceil(capacity/page_size)
  *           K half: [page_size][n_kv_head*head_dim], row per position
  *           V half: bf16: [n_kv_head*head_dim][page_size] (transposed, so the
- *                   decode kernel's P*V operand is contiguous along positions);
+ *                   decode kernel's P*V operand is contiguous along positions;
+ *                   within each 32-position half of a page, position
+ *                   16a + 4q + b (a < 2, q < 4, b < 4) is stored at column
+ *                   8q + 4a + b, the order the decode MFMA takes keys in);
  *                   fp32: [page_size][n_kv_head*head_dim]
  *           keys are stored after RoPE and QK-norm, as attention reads them.
  *   table   int32 [n_seqs][pages_per_seq]  page index of each logical page;
