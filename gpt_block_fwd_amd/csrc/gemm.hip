@@ -361,29 +361,34 @@ DEV void wait_ahead(int ahead) {
   }
 }
 
-// Decode-row kernel (M <= 64): one workgroup of 4 waves per 64 output
-// columns and k range kz of ks.  The k range streams in chunks of 64 through
-// an S-stage LDS ring holding the 64 weight rows and the activation rows
-// (padded to an even number of 16-row blocks), each chunk filled by
-// direct-to-LDS loads that read whole 128-byte lines: a wave instruction
-// covers 8 rows x 128 B.  Every wave issues the same number NI of those per
-// chunk, so "chunk c has landed" is a fixed vmcnt.  Wave w then multiplies
-// weight rows 16w .. +16 (output columns) by all activation rows with
-// v_mfma_f32_16x16x32_bf16 (lane l: weight row l%16 / activation row
-// 16 mb + l%16, k elements 8 (l/16) .. +8 of the 32-deep step).
-template <int EPI, int MB, bool DEEP>
+// Decode-row kernel (M <= 64): one workgroup of 4 waves per BNR output
+// columns (64 or 32) and k range kz of ks.  The k range streams in chunks of
+// 64 through an S-stage LDS ring holding the BNR weight rows and the
+// activation rows (padded to an even number of 16-row blocks), each chunk
+// filled by direct-to-LDS loads that read whole 128-byte lines: a wave
+// instruction covers 8 rows x 128 B.  Every wave issues the same number NI
+// of those per chunk, so "chunk c has landed" is a fixed vmcnt.  BNR = 64:
+// wave w multiplies weight rows 16w .. +16 (output columns) by all
+// activation rows for both 32-deep k substeps of a chunk.  BNR = 32 (twice
+// the workgroups, for grids that would leave CUs idle): wave w takes column
+// block w % 2 and substep w / 2, and the two substep halves are added
+// through LDS at the end.  v_mfma_f32_16x16x32_bf16: lane l holds weight row
+// l%16 / activation row 16 mb + l%16, k elements 8 (l/16) .. +8 of the step.
+template <int EPI, int MB, bool DEEP, int BNR>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long long slab) {
   constexpr int MBE = (MB + 1) & ~1;      // activation 16-row blocks loaded
-  constexpr int ROWS = 64 + 16 * MBE;     // LDS tile rows: weights, then activations
+  constexpr int ROWS = BNR + 16 * MBE;    // LDS tile rows: weights, then activations
+  static_assert((ROWS / 8) % 4 == 0, "DMA instructions must split evenly over the waves");
   constexpr int NI = (ROWS / 8) / 4;      // DMA instructions per wave per chunk
-  // Stages: two workgroups per CU (64-72 KB each), or one workgroup with
-  // twice the ring (128-144 KB) when the grid is too small to fill the chip.
-  constexpr int S = (MBE <= 2 ? 6 : 4) * (DEEP ? 2 : 1);
+  // Stages: a 72 KB ring (two workgroups per CU), or 144 KB (one workgroup
+  // per CU) when the grid is too small to fill the chip.
+  constexpr int S = (DEEP ? 147456 : 73728) / (ROWS * BK * 2);
+  static_assert(S >= 3 && (S - 2) * NI < 64, "ring depth");
   __shared__ bf16 lds[S][ROWS * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int n0 = blockIdx.x * 64, kz = blockIdx.y;
+  const int n0 = blockIdx.x * BNR, kz = blockIdx.y;
   const int nck = g.K / BK;
   const int c0 = (int)((long long)kz * nck / ks), c1 = (int)((long long)(kz + 1) * nck / ks);
   const int nch = c1 - c0;
@@ -396,8 +401,8 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long
     const int slot = wave + 4 * j;
     const int r = 8 * slot + (lane >> 3);
     const int lc = (lane & 7) ^ swz_key(r);
-    if (r < 64) src[j] = wrow(g, n0 + r) + lc * 8 + c0 * BK;
-    else src[j] = (const bf16 *)g.A + (long long)min(r - 64, g.M - 1) * g.lda + lc * 8 + c0 * BK;
+    if (r < BNR) src[j] = wrow(g, n0 + r) + lc * 8 + c0 * BK;
+    else src[j] = (const bf16 *)g.A + (long long)min(r - BNR, g.M - 1) * g.lda + lc * 8 + c0 * BK;
   }
   auto dma = [&](int c, int st) {
 #pragma unroll
@@ -406,6 +411,9 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long
                                        16, 0, 0);
   };
 
+  constexpr int NSUB = BNR == 64 ? 2 : 1;          // k substeps per chunk for this wave
+  const int cb = BNR == 64 ? wave : (wave & 1);    // 16-column block of this wave
+  const int sub0 = BNR == 64 ? 0 : (wave >> 1);    // first k substep of this wave
   f32x4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4){};
@@ -421,41 +429,62 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long
     if (c + S - 1 < nch) dma(c + S - 1, (c + S - 1) % S);
     const bf16 *t = lds[c % S];
 #pragma unroll
-    for (int ksub = 0; ksub < 2; ++ksub) {
-      const bf16x8 wf = *(const bf16x8 *)&t[swz(16 * wave + l16, 4 * ksub + q4)];
+    for (int i = 0; i < NSUB; ++i) {
+      const int ksub = sub0 + i;
+      const bf16x8 wf = *(const bf16x8 *)&t[swz(16 * cb + l16, 4 * ksub + q4)];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 xf = *(const bf16x8 *)&t[swz(64 + 16 * mb + l16, 4 * ksub + q4)];
+        const bf16x8 xf = *(const bf16x8 *)&t[swz(BNR + 16 * mb + l16, 4 * ksub + q4)];
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf, acc[mb], 0, 0, 0);
       }
     }
   }
-  // lane holds output columns n0 + 16 w + 4 q4 .. +4 of row 16 mb + l16
+  if constexpr (BNR == 32) {
+    // add the second substep's partial sums (waves 2, 3) into waves 0, 1
+    f32x4 *red = (f32x4 *)&lds[0][0];  // [2 column blocks][MB][64 lanes]
+    __syncthreads();                    // every wave is done reading the ring
+    if (wave >= 2)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red[(cb * MB + mb) * 64 + lane] = acc[mb];
+    __syncthreads();
+    if (wave >= 2) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] += red[(cb * MB + mb) * 64 + lane];
+  }
+  // lane holds output columns n0 + 16 cb + 4 q4 .. +4 of row 16 mb + l16
   GemmArgs go = g;
   if (ks > 1) go.C = (float *)g.C + kz * slab;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = 16 * mb + l16;
-    if (m < g.M) epi_store4<EPI>(go, m, n0 + 16 * wave + 4 * q4, acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+    if (m < g.M) epi_store4<EPI>(go, m, n0 + 16 * cb + 4 * q4, acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
   }
 }
 
-template <int EPI, bool DEEP>
+template <int EPI, bool DEEP, int BNR>
 void launch_rows_d(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
-  const dim3 grid(g.N / 64, ks);
+  const dim3 grid(g.N / BNR, ks);
   switch ((g.M + 15) / 16) {
-    case 1: gemm_rows_kernel<EPI, 1, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    case 2: gemm_rows_kernel<EPI, 2, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    case 3: gemm_rows_kernel<EPI, 3, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    default: gemm_rows_kernel<EPI, 4, DEEP><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 1: gemm_rows_kernel<EPI, 1, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 2: gemm_rows_kernel<EPI, 2, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 3: gemm_rows_kernel<EPI, 3, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    default: gemm_rows_kernel<EPI, 4, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
   }
 }
 
 template <int EPI>
 void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
-  // 256 CUs: a grid that leaves CUs without a second workgroup gets the deep ring
-  if ((long long)(g.N / 64) * ks <= 256) launch_rows_d<EPI, true>(g, ks, slab, s);
-  else launch_rows_d<EPI, false>(g, ks, slab, s);
+  // 256 CUs.  At most 128 tiles of 64 columns: halve the tiles.  A grid
+  // that leaves CUs without a second workgroup gets the deep ring.
+  const long long t64 = (long long)(g.N / 64) * ks;
+  if (t64 <= 128) {
+    if (2 * t64 <= 256) launch_rows_d<EPI, true, 32>(g, ks, slab, s);
+    else launch_rows_d<EPI, false, 32>(g, ks, slab, s);
+  } else if (t64 <= 256) {
+    launch_rows_d<EPI, true, 64>(g, ks, slab, s);
+  } else {
+    launch_rows_d<EPI, false, 64>(g, ks, slab, s);
+  }
 }
 
 template <int EPI>

@@ -23,6 +23,9 @@ GEMM_SHAPES = [
     (64, 1920, 1664),
     (17, 6656, 1664),
     (40, 384, 1152),
+    # 64-column tiles: deep ring (129-256 tiles) and two workgroups per CU (> 256)
+    (48, 10240, 768),
+    (8, 32768, 256),
 ]
 
 
