@@ -40,12 +40,12 @@ DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3);
 // loads can apply them by choosing each lane's source.
 DEV int vidx(int dim, int unit) { return dim * KT + ((((unit >> 1) ^ ((dim >> 1) & 7)) << 3) | ((unit & 1) << 2)); }
 
-// NWV waves per workgroup, 64 rows each.  FIXREF: q and k are QK-normalised,
+// NWV waves per workgroup, 32 RB rows each.  FIXREF: q and k are QK-normalised,
 // so the softmax runs against the fixed reference kScoreBound (no running
 // max, no rescale of the output accumulators).
-template <int NWV, bool FIXREF>
+template <int NWV, int RB, bool FIXREF>
 __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs a) {
-  constexpr int NT = 64 * NWV, ROWS = 64 * NWV;
+  constexpr int NT = 64 * NWV, ROWS = 32 * RB * NWV;
   constexpr int SP = 4 * 4 / NWV;  // 16-byte staging loads per thread for each of K and V^T
   __shared__ bf16 sk[2][KT * DH];
   __shared__ bf16 sv[2][DH * KT];
@@ -59,13 +59,13 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   const long long col0 = a.cu_pad[b];
   const int rows_total = len * H;
   if (R0 >= rows_total) return;
-  const int Rw = R0 + 64 * wave;
+  const int Rw = R0 + 32 * RB * wave;
 
   // Q fragments (B operand of S^T = K Q^T): row r, dims 16 s + 8 g .. +8.
-  int prow[2];
-  bf16x8 qf[2][8];
+  int prow[RB];
+  bf16x8 qf[RB][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     int r = min(Rw + 32 * rb + c32, rows_total - 1);
     prow[rb] = r / H;
     const bf16 *qp = a.q + ((long long)tok0 * H + r) * DH + 8 * g;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   }
   const int last_row = min(R0 + ROWS - 1, rows_total - 1);
   const int n_kt = (last_row / H) / KT + 1;
-  const int pw_max = Rw < rows_total ? min(Rw + 63, rows_total - 1) / H : -1;
+  const int pw_max = Rw < rows_total ? min(Rw + 32 * RB - 1, rows_total - 1) / H : -1;
   const int pw_min = Rw / H;
 
   // Direct-to-LDS staging: a tile is 16 KB of K (4 keys x 256 B per wave
@@ -112,28 +112,33 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     }
   };
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4][RB];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) oacc[d][rb] = (f32x16){};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) oacc[d][rb] = (f32x16){};
+  float mrow[RB], lrow[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mrow[rb] = -INFINITY;
+    lrow[rb] = 0.f;
+  }
   const float sc = kLog2e / sqrtf((float)DH);
 
   auto tile = [&](int kt, int buf) {
     if (kt * KT > pw_max) return;  // every key of the tile is in this wave's future
-    f32x16 sacc[2][2];
+    f32x16 sacc[2][RB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sacc[kb][rb] = (f32x16){};
+      for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = (f32x16){};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         bf16x8 kf = *(const bf16x8 *)&sk[buf][kidx(32 * kb + c32, 2 * s + g)];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
           sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
       }
     }
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     const bool need_mask = kt * KT + KT - 1 > pw_min;
     if constexpr (FIXREF) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
         if (need_mask) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
       }
     } else
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       float mx = -INFINITY;
       if (need_mask) {
 #pragma unroll
@@ -210,9 +215,9 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kb = st >> 1, h = st & 1;
-      bf16x8 pf[2];
+      bf16x8 pf[RB];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[rb][j] = f2bf(sacc[kb][rb][8 * h + j]);
       const int u0 = 8 * kb + 4 * h + g;
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
         bf16x4 hi4 = *(const bf16x4 *)&sv[buf][vidx(dim, u0 + 2)];
         bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
       }
     }
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   tile(n_kt - 1, (n_kt - 1) & 1);
 
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int r = Rw + 32 * rb + c32;
     if (r >= rows_total) continue;
     const float inv = 1.0f / lrow[rb];
@@ -521,8 +526,9 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   if (a.n_seqs <= 0 || a.max_wg <= 0) return;
   const dim3 grid(a.n_seqs, a.max_wg);
-  if (a.qk_norm) attn_prefill_kernel<kAttnPrefillWaves, true><<<grid, 64 * kAttnPrefillWaves, 0, s>>>(a);
-  else attn_prefill_kernel<kAttnPrefillWaves, false><<<grid, 64 * kAttnPrefillWaves, 0, s>>>(a);
+  constexpr int NWV = kAttnPrefillWaves, RB = kAttnPrefillRows / (32 * kAttnPrefillWaves);
+  if (a.qk_norm) attn_prefill_kernel<NWV, RB, true><<<grid, 64 * NWV, 0, s>>>(a);
+  else attn_prefill_kernel<NWV, RB, false><<<grid, 64 * NWV, 0, s>>>(a);
 }
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {

@@ -113,10 +113,11 @@ int gemm_rows_ksplit(int N, int K);  // k ranges for a decode-row GEMM whose con
 void launch_gemm_f32(const GemmArgs &g, hipStream_t s);          // small fp32 path
 
 // ------------------------------------------------------------ attention
-// Waves (64 rows each) per prefill-attention workgroup.  Four: each staged
-// K/V tile then serves 256 rows (two waves measured 10% slower at depth 12).
-constexpr int kAttnPrefillWaves = 4;
-constexpr int kAttnPrefillRows = 64 * kAttnPrefillWaves;
+// Prefill-attention workgroup: kAttnPrefillRows rows over kAttnPrefillWaves
+// waves (32 or 64 rows per wave).  256 rows: each staged K/V tile serves
+// that many (128 rows measured 10% slower at depth 12).
+constexpr int kAttnPrefillWaves = 8;
+constexpr int kAttnPrefillRows = 256;
 struct AttnPrefillArgs {
   const bf16 *q;   // [M][H*128]
   const bf16 *k;   // [M][128]
