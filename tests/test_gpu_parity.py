@@ -177,6 +177,43 @@ def test_small_bf16_decode_teacher_forced(temperature):
     kv.close()
 
 
+def test_small_bf16_decode_many_sequences():
+    """64 sequences with room for 1100 positions each: more than 256 decode
+    attention workgroups, so the register-load variant with 8-page chunks
+    runs; 3 greedy steps, the longest and the shortest sequence
+    teacher-forced through the oracle."""
+    t = torch()
+    cfg = wl.small_model(2, 2, vocab=4096)
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 1090, size=64)
+    lens[0], lens[1] = 1089, 1
+    w = wl.ragged_prefill(cfg, lens, seed=21)
+    W, dm = device_model(cfg)
+    n, steps = len(lens), 3
+    kv = B.DeviceKV(dm, n, 1100)
+    logits0, _ = gpu_prefill(dm, w.tokens, w.seqlens, rows=B.ROWS_LAST, kv=kv.handle)
+    toks = t.empty(n, dtype=t.int32, device="cuda")
+    B.gpt_select_tokens(t.from_numpy(logits0).cuda(), n, cfg.vocab, 0.0, None, toks)
+    ws = dm.workspace(n, n)
+    step_logits = t.empty((n, cfg.vocab), dtype=t.float32, device="cuda")
+    got_tok, got_logits = [toks.cpu().numpy().copy()], [logits0]
+    for _ in range(steps):
+        dm.decode_step(kv.handle, toks, toks, logits=step_logits, workspace=ws)
+        got_tok.append(toks.cpu().numpy().copy())
+        got_logits.append(step_logits.cpu().numpy().copy())
+    np.testing.assert_array_equal(kv.lengths(), w.seqlens + steps)
+    kv.close()
+    got_tok = np.stack(got_tok)
+    sample = [0, 1]
+    _, ref = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok, seqs=sample)
+    st = logit_stats(np.stack(got_logits)[:, sample], ref)
+    print(st)
+    assert st["max_abs"] <= 3e-2
+    assert st["disagree_explained"]
+    for s_ in range(1, steps + 1):  # greedy: every sequence's token is its own argmax
+        np.testing.assert_array_equal(got_tok[s_], np.argmax(got_logits[s_], axis=-1))
+
+
 def test_decode_capacity_error():
     t = torch()
     cfg = wl.small_model(1, 1, vocab=1024)
@@ -204,10 +241,13 @@ def test_argmax_lowest_index_on_ties():
     np.testing.assert_array_equal(out.cpu().numpy(), [5, 0, 65535])
 
 
-def test_sampling_inverse_cdf():
+@pytest.mark.parametrize("V", [65536, 27, 70000, 70001])
+def test_sampling_inverse_cdf(V):
+    """Whole 8192-entry super-tiles, a vocabulary under one tile, a ragged
+    last tile, and a width that is not a multiple of four (scalar loads)."""
     t = torch()
-    rng = np.random.default_rng(8)
-    rows, V = 64, 65536
+    rng = np.random.default_rng(8 + V)
+    rows = 64
     lg = (rng.standard_normal((rows, V)) * 0.8).astype(np.float32)
     U = rng.random(rows).astype(np.float32)
     U[0], U[1] = 0.0, np.float32(1.0 - 2 ** -24)
