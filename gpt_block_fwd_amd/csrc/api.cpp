@@ -631,9 +631,10 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   const double att_bytes = kv_bytes + (double)n * H * dh * 2 * (bf16p ? 2 : 4);
 
   if (bf16p) {
-    // Per layer: QKV projection (k split into fp32 slabs) -> RoPE, QK-norm,
-    // cache append (sums the slabs) -> attention -> O projection (slabs) ->
-    // residual + RMSNorm -> W1 + ReLU^2 -> W2 (slabs) -> residual + RMSNorm.
+    // Per layer: QKV projection (k split into fp32 slabs) -> attention, which
+    // sums the slabs, applies RoPE and QK-norm and appends k, v to the cache
+    // -> O projection (slabs) -> residual + RMSNorm -> W1 + ReLU^2 -> W2
+    // (slabs) -> residual + RMSNorm.
     // Above 64 rows the large-M GEMMs write x and the norms run on their own.
     const bool rows = n <= 64;
     {
@@ -677,17 +678,10 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         run_gemm(c, g, GPT_PROF_GEMM, s);
       }
       {
-        Timed t(GPT_PROF_NORM, s, 0, (double)n * qkv_n * (4.0 * std::max(sl.nslab, 1) + 2.0));
-        launch_rope_norm_scatter_bf16(sl, s);
-      }
-      {
         Timed t(GPT_PROF_DECODE_ATTN, s, att_flops, att_bytes);
         AttnDecodeArgs aa{};
-        aa.q = (const bf16 *)bf.q;
-        aa.kv = pv;
-        aa.layer = l;
+        aa.in = sl;
         aa.n = n;
-        aa.H = H;
         aa.max_splits = (kv->capacity + kDecodeChunk - 1) / kDecodeChunk;
         aa.o_part = bf.opart;
         aa.ml_part = bf.mlpart;

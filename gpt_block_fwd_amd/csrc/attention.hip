@@ -18,6 +18,7 @@
 // v_mfma_f32_16x16x32_bf16 with the (<= 16) query heads as the N side.
 // The last page of a sequence to finish merges the pages (log-sum-exp).
 #include "kernels.h"
+#include "scatter.h"
 
 #define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
 #define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
@@ -278,6 +279,22 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
 DEV int kdx(int key, int chunk) { return key * DH + ((chunk ^ (key & 15)) << 3); }
 DEV int vdx(int dim, int unit) { return dim * 64 + (((unit >> 1) ^ ((dim >> 1) & 7)) << 3) + ((unit & 1) << 2); }
 
+// A wave-uniform int through the scalar cache.  Block-table entries read
+// this way do not occupy the vector-memory counter, so waiting for them does
+// not also wait for the slab loads in flight.
+DEV int sload(const int *p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// The query of the new position: every workgroup builds all H heads into
+// LDS (sum of the split-GEMM slabs, RoPE, QK-norm, bf16), head slots spread
+// over the half-waves of all its waves.  The chunk holding the new position
+// also builds its k and v, stores them to the cache for later steps, and the
+// wave whose page holds that position patches them into its copy of the page
+// (which it may have read before or after the store).
+//
 // One workgroup per chunk of kDecodePages pages of one sequence; wave w
 // takes page w of the chunk and scores its 64 cached positions for all
 // query heads at once (MQA: one K/V page serves every head).  STAGE: the
@@ -285,11 +302,11 @@ DEV int vdx(int dim, int unit) { return dim * 64 + (((unit >> 1) ^ ((dim >> 1) &
 // direct-to-LDS loads that read whole 128-byte lines and takes its MFMA
 // fragments from there; this costs 128 KB of LDS, one workgroup per CU, so
 // it pays only when the grid does not fill the chip.  Otherwise the
-// fragments are loaded from the cache straight into registers and four
-// workgroups fit a CU.  The pages of a chunk are merged in LDS by
-// log-sum-exp, and the chunk's unnormalised output with its (max, sum) per
-// head goes to the partial buffers.  The last chunk of the sequence to
-// finish merges all chunks and writes o.
+// fragments are loaded from the cache straight into registers.  The pages
+// of a chunk are merged in LDS by log-sum-exp, and the chunk's
+// unnormalised output with its (max, sum) per head goes to the partial
+// buffers.  The last chunk of the sequence to finish merges all chunks and
+// writes o.
 template <bool STAGE, int NP>
 __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int NT = 64 * NP, CH = 64 * NP;  // threads; cached positions per chunk
@@ -297,27 +314,39 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   // partial output (16 heads x 128).  The partials (and the final merge's
   // scratch) use the first 8 KB of each wave's area.
   constexpr int WAVE_BYTES = STAGE ? 2 * 64 * DH * 2 : 16 * DH * 4;
+  constexpr int QS = DH + 8;  // q row pitch: the 16 heads of a fragment read start on different banks
   __shared__ __attribute__((aligned(16))) char smem[NP * WAVE_BYTES];
   __shared__ float ml_s[NP][16][2];  // per-page (max, sum) per head
+  __shared__ __attribute__((aligned(16))) bf16 q_s[16 * QS];
+  __shared__ __attribute__((aligned(16))) bf16 kv_s[2 * DH];  // the new position's k and v
   auto wave_area = [&](int w) { return smem + w * WAVE_BYTES; };
   __shared__ unsigned s_prev;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wave index as a scalar, so per-wave addresses and the block-table
+  // lookups are scalar and only the slab and page loads use the vector
+  // memory counter
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane & 15, q4 = lane >> 4;
   const int b = blockIdx.y, chunk = blockIdx.x;
-  const PagedKV &kv = a.kv;
-  const int len = kv.lens[b] + 1;  // the new position is already in the cache
+  const ScatterArgs &in = a.in;
+  const PagedKV &kv = in.kv;
+  const int len = kv.lens[b] + 1;  // positions 0 .. lens[b], the last one new
+  const int pn = len - 1;
   const int c0 = chunk * CH;
   if (c0 >= len) return;
-  const int H = a.H;
+  const int H = in.H;
   const int kpos0 = c0 + wave * 64;
+  const int nw = min(NP, (len - c0 + 63) / 64);  // pages of this chunk
+  const bool owner = pn < c0 + CH;                // the chunk holds the new position
+  const bool pw = pn >= kpos0 && pn < kpos0 + 64;  // this wave's page holds it
+  const int nslot = H + (owner ? 2 : 0);
+  bf16x8 kf[4][4];
+  bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
+  bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
   if (kpos0 < len) {
-    const int page = kv.table[b * kv.pages_per_seq + kpos0 / kv.page_size];
-    const char *pg = kv.base + (long long)a.layer * kv.layer_stride + (long long)page * kv.page_stride;
+    const int page = sload(kv.table + b * kv.pages_per_seq + kpos0 / kv.page_size);
+    const char *pg = kv.base + (long long)in.layer * kv.layer_stride + (long long)page * kv.page_stride;
     const bf16 *K = (const bf16 *)pg;
     const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
-    bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
-    bf16x8 kf[4][4];
-    bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
     if constexpr (STAGE) {
       // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims
       // x 128 B each; lane i fills slot i of the instruction's kilobyte and
@@ -345,15 +374,89 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
         for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)(Vt + (16 * d + hl) * 64 + 32 * h + 8 * q4);
     }
+  }
+  {
+    // Slots are built by half-waves while the page loads are in flight:
+    // lane li of half hw holds dims 4 li .. 4 li + 3 of one slot, so each
+    // slab costs one 16-byte load per lane for two slots.  Half-wave
+    // hh = 2 wave + hw builds slots hh, hh + 2 NP, ...
+    // Slot j < H: query head j into q_s.  j = H: k, j = H + 1: v of the new
+    // position, into kv_s and the cache.  Query heads and k: half-split
+    // rotation (dim i pairs with i + 64, held by lane li ^ 16), then a
+    // weightless RMSNorm over the head.
+    const int li = lane & 31, hw = lane >> 5, hh = 2 * wave + hw;
+    const float *u = in.qkv + (long long)b * (H + 2) * DH;
+    const int st = (int)in.slab;  // slabs of at most 64 rows: far below 2^31 floats
+    f32x4 c4 = {}, s4 = {};
+    if (in.cos && hh < nslot) {
+      c4 = *(const f32x4 *)(in.cos + pn * 64 + 4 * (li & 15));
+      s4 = *(const f32x4 *)(in.sin + pn * 64 + 4 * (li & 15));
+    }
+    const int npage = owner ? sload(kv.table + b * kv.pages_per_seq + pn / kv.page_size) : 0;
+    char *npg = kv.base + (long long)in.layer * kv.layer_stride + (long long)npage * kv.page_stride;
+    const int nsl = pn % kv.page_size;
+    for (int j = hh; j < nslot; j += 2 * NP) {
+      const float *uj = u + j * DH + 4 * li;
+      f32x4 t[kMaxRowSplit];
+#pragma unroll
+      for (int k = 0; k < kMaxRowSplit; ++k)
+        if (k == 0 || k < in.nslab) t[k] = *(const f32x4 *)(uj + k * st);
+      f32x4 x = t[0];
+#pragma unroll
+      for (int k = 1; k < kMaxRowSplit; ++k)
+        if (k < in.nslab) x += t[k];
+      if (j < H + 1) {
+        if (in.cos) {
+          f32x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = __shfl_xor(x[e], 16, 64);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = li < 16 ? x[e] * c4[e] - y[e] * s4[e] : y[e] * s4[e] + x[e] * c4[e];
+        }
+        if (in.qk_norm) {
+          float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+          const float rs = 1.0f / sqrtf(ss * (1.0f / 128.0f) + in.eps);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= rs;
+        }
+      }
+      const bf16x4 y4 = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
+      if (j < H) {
+        *(bf16x4 *)&q_s[j * QS + 4 * li] = y4;
+      } else {
+        *(bf16x4 *)&kv_s[(j - H) * DH + 4 * li] = y4;
+        if (j == H) {
+          *(bf16x4 *)((bf16 *)npg + nsl * DH + 4 * li) = y4;
+        } else {
+          bf16 *vt = (bf16 *)(npg + kv.half_bytes);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vt[(4 * li + e) * kv.page_size + vslot(nsl)] = y4[e];
+        }
+      }
+    }
+  }
+  // q_s and kv_s complete (a bare barrier: the page loads stay in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (kpos0 < len) {
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (hl < H) qf[s] = *(const bf16x8 *)(a.q + ((long long)b * H + hl) * DH + 32 * s + 8 * q4);
+      if (hl < H) qf[s] = *(const bf16x8 *)&q_s[hl * QS + 32 * s + 8 * q4];
       else qf[s] = (bf16x8){};
     }
+    const int nkey = pn - kpos0;  // the new position's slot in this wave's page, if pw
     if constexpr (STAGE) {
       // this wave's page has landed (each wave reads only its own staging area)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (pw) {
+        Ks[kdx(nkey, lane >> 3) + (lane & 7)] = kv_s[lane];
+        Ks[kdx(nkey, (lane + 64) >> 3) + (lane & 7)] = kv_s[lane + 64];
+        const int cc = vslot(nkey);
+        Vs[vdx(lane, cc >> 2) + (cc & 3)] = kv_s[DH + lane];
+        Vs[vdx(lane + 64, cc >> 2) + (cc & 3)] = kv_s[DH + lane + 64];
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -362,6 +465,28 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
       for (int d = 0; d < 8; ++d)
 #pragma unroll
         for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
+    } else if (pw) {
+      bf16x8 kn[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kn[s] = *(const bf16x8 *)&kv_s[32 * s + 8 * q4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        if (16 * kb + hl == nkey) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) kf[kb][s] = kn[s];
+        }
+      const int cc = vslot(nkey), e = cc & 7;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if ((cc >> 3) == 4 * h + q4) {
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            const bf16 v = kv_s[DH + 16 * d + hl];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (i == e) vf[d][h][i] = v;
+          }
+        }
     }
     // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
     f32x4 sacc[4];
@@ -435,7 +560,6 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     }
   }
   __syncthreads();
-  const int nw = min(NP, (len - c0 + 63) / 64);  // pages of this chunk
   const int S = (len + CH - 1) / CH;   // chunks of this sequence
   const long long obase = ((long long)b * a.max_splits + chunk) * H * DH;
   for (int idx = tid; idx < H * DH; idx += NT) {

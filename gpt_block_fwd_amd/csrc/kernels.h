@@ -132,10 +132,12 @@ struct AttnPrefillArgs {
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
 
 struct AttnDecodeArgs {
-  const bf16 *q;  // [n][H*128]
-  PagedKV kv;
-  int layer;
-  int n, H, max_splits;
+  // The new position of each sequence b: its q|k|v projection row b (fp32,
+  // in.nslab partial slabs, H + 2 slots of 128), the RoPE tables and QK-norm
+  // setting, the paged cache, the layer and H.  The kernel builds q, appends
+  // k and v at position lens[b] and attends over positions 0 .. lens[b].
+  ScatterArgs in;
+  int n, max_splits;
   float *o_part;  // [n][max_splits][H][128], one split per kDecodeChunk positions
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
