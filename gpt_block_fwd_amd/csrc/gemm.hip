@@ -2,9 +2,11 @@
 // K-contiguous), fp32 accumulation, fused epilogues (bf16 store, ReLU^2 ->
 // bf16, fp32 residual add, fp32 store).
 //
-// Large-M kernel: 256-thread workgroups (4 waves in 2x2), BM x BN x 64 tiles
-// staged through double-buffered LDS with a 16-byte XOR swizzle, one
-// v_mfma_f32_32x32x16_bf16 per 32x32 block and 16-deep k substep.  The MFMA
+// Large-M kernels: 256x256x64 tiles staged through double-buffered LDS by
+// direct-to-LDS loads with a 16-byte XOR swizzle, one
+// v_mfma_f32_32x32x16_bf16 per 32x32 block and 16-deep k substep; eight waves
+// in two groups that alternate load and compute phases (four waves of
+// 128x128 for the QKV epilogue).  The MFMA
 // A operand is the weight tile and the B operand the activation tile, so a
 // lane's accumulator holds one activation row and runs of 4 consecutive
 // output columns (vector stores in the epilogue).  Workgroup ids are remapped
@@ -156,26 +158,13 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
 #define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
 #define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
 
-// NWN waves along N and 2 along M: NWN = 2 gives 4 waves (one per SIMD)
-// with 128x128 wave tiles; NWN = 4 gives 8 waves (two per SIMD) with
-// 128x64 wave tiles, so one wave's LDS and DMA traffic overlaps the other's
-// MFMAs.
-template <int BM, int BN, int NWN, int EPI>
-__global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NW = 2 * NWN;
-  constexpr int WM = BM / 2, WN = BN / NWN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
-  __shared__ bf16 sa[2][BM * BK];
-  __shared__ bf16 sb[2][BN * BK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+// Tile origin of this workgroup.  XCD-aware remap: the hardware hands
+// workgroup ids to the 8 XCDs round robin; give each XCD a contiguous range
+// of logical tiles, then group 8 tile-rows at a time for L2 reuse.
+template <int BM, int BN>
+DEV void tile_origin(const GemmArgs &g, int &m0, int &n0) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-
-  // XCD-aware remap: the hardware hands workgroup ids to the 8 XCDs round
-  // robin; give each XCD a contiguous range of logical tiles.
   int pid = blockIdx.x;
   {
     const int xcd = pid & 7, idx = pid >> 3;
@@ -188,7 +177,78 @@ __global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
   const int gsize_m = min(tiles_m - first_m, GROUP_M);
   const int tm = first_m + (pid % group_size) % gsize_m;
   const int tn = (pid % group_size) / gsize_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  m0 = tm * BM;
+  n0 = tn * BN;
+}
+
+// Epilogue of a WM x WN wave tile (TM x TN blocks of 32x32) whose first
+// row is m0 + wm WM and first column n0 + wn WN.
+template <int TM, int TN, int WM, int WN, int EPI>
+DEV void tile_epilogue(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, int n0, int wm, int wn, int c32,
+                       int hi) {
+  // A wave whose columns lie beyond N computed on clamped rows; drop it.
+  const bool active = (n0 + wn * WN) < g.N;
+  if (!active) return;
+  const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of WN)
+  if constexpr (EPI == EPI_QKV) {
+    static_assert(WN == 128, "the QKV epilogue needs one head per wave");
+    epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi);
+    return;
+  } else {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * WM + 32 * j + c32;
+      const bool ok = m < g.M;
+      if constexpr (EPI == EPI_LOGITS) {
+        // partial softmax statistics of this row over the wave's WN columns
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float se = 0.f;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
+        se += __shfl_xor(se, 32, 64);
+        if (ok && hi == 0) {
+          float *pp = g.part + ((long long)m * (g.N / WN) + nw0 / WN) * 2;
+          *(float2 *)pp = make_float2(mx, se);
+        }
+      }
+      if (!ok) continue;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = nw0 + 32 * i + 8 * c + 4 * hi;
+          epi_store4<EPI == EPI_LOGITS ? EPI_F32 : EPI>(g, m, n, acc[i][j][4 * c], acc[i][j][4 * c + 1],
+                                                        acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]);
+        }
+    }
+  }
+}
+
+
+// NWN waves along N and 2 along M, each wave software-pipelining its own
+// LDS reads against its MFMAs.  Used with NWN = 2 (4 waves, one per SIMD,
+// 128x128 wave tiles) for the QKV epilogue, which needs a whole 128-wide head
+// per wave; the other epilogues use gemm_pp_kernel.
+template <int BM, int BN, int NWN, int EPI>
+__global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int NW = 2 * NWN;
+  constexpr int WM = BM / 2, WN = BN / NWN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
+  __shared__ bf16 sa[2][BM * BK];
+  __shared__ bf16 sb[2][BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  int m0, n0;
+  tile_origin<BM, BN>(g, m0, n0);
 
   // Direct global->LDS loads (global_load_lds_dwordx4): one instruction of a
   // wave fills 1 KB of LDS = 8 rows of 64 bf16, lane i landing at row i/8,
@@ -298,49 +358,139 @@ __global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
     if (more) interleave();
     __builtin_amdgcn_sched_barrier(0);
   }
-  // A wave whose columns lie beyond N computed on clamped rows; drop it.
-  const bool active = (n0 + wn * WN) < g.N;
-  if (!active) return;
-  const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of WN)
-  if constexpr (EPI == EPI_QKV) {
-    static_assert(WN == 128, "the QKV epilogue needs one head per wave");
-    epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi);
-    return;
-  } else {
+  tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
+}
+
+// Eight waves in two groups of four (one wave per SIMD each); group q owns
+// rows 128 q .. 128 q + 127 of the 256x256 tile, wave w of a group columns
+// 64 w .. 64 w + 63.  The groups alternate between a load phase (the LDS ->
+// register reads of two 16-deep substeps) and a compute phase (their 16
+// MFMAs), group 1 one phase behind group 0, so each SIMD's matrix core runs
+// one group's compute phase while the other group loads.  Every phase ends
+// at a workgroup barrier, and a load phase's reads have completed before it.
+// Each group streams half of every k-tile into LDS by DMA.  Both issue their
+// half of k-tile t+1 in their first load phase of k-tile t, after its reads
+// (the target buffer was last read two phases earlier), and both wait for it
+// three phases later: group 0 after its last compute phase of k-tile t,
+// group 1 before the barrier that ends its last load phase.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
+  constexpr int NW = 8, WM = BM / 2, WN = BN / 4;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
+  // One LDS object per buffer, so the compiler can tell a DMA into one
+  // buffer from reads of the other and adds no wait for it.
+  __shared__ bf16 sa0[BM * BK], sa1[BM * BK];
+  __shared__ bf16 sb0[BN * BK], sb1[BN * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wm = grp, wn = wave & 3;
+  int m0, n0;
+  tile_origin<BM, BN>(g, m0, n0);
+
+  // Direct-to-LDS loads as in gemm_bf16_kernel: instruction p of wave w fills
+  // rows (8 p + w) * 8 .. +8 of the tile.
+  const int lr = lane >> 3;
+  int aoff[PA], boff[PB];
+  const bf16 *bbase[PB];
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int m = m0 + wm * WM + 32 * j + c32;
-      const bool ok = m < g.M;
-      if constexpr (EPI == EPI_LOGITS) {
-        // partial softmax statistics of this row over the wave's WN columns
-        float mx = -INFINITY;
+  for (int p = 0; p < PA; ++p) {
+    const int lrow = (NW * p + wave) * 8 + lr;
+    const int r = min(m0 + lrow, g.M - 1);
+    aoff[p] = r * (int)g.lda + (((lane & 7) ^ swz_key(lrow)) << 3);
+  }
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+  for (int p = 0; p < PB; ++p) {
+    const int nb = min(n0 + (NW * p + wave) * 8, g.N - 8);
+    const bf16 *base;
+    int first;
+    if (nb < g.n1) { base = (const bf16 *)g.W0; first = 0; }
+    else if (nb < g.n2) { base = (const bf16 *)g.W1; first = g.n1; }
+    else { base = (const bf16 *)g.W2; first = g.n2; }
+    bbase[p] = base;
+    const int lrow = (NW * p + wave) * 8 + lr;
+    boff[p] = (nb - first + lr) * (int)g.ldw + (((lane & 7) ^ swz_key(lrow)) << 3);
+  }
+  const bf16 *abase = (const bf16 *)g.A;
+  auto dma = [&](int kt, bf16 *As, bf16 *Bs) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float se = 0.f;
+    for (int p = 0; p < PA; ++p)
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(abase + aoff[p] + kt * BK),
+                                       LDS_PTR(&As[(NW * p + wave) * 8 * BK]), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+    for (int p = 0; p < PB; ++p)
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(bbase[p] + boff[p] + kt * BK),
+                                       LDS_PTR(&Bs[(NW * p + wave) * 8 * BK]), 16, 0, 0);
+  };
+
+  f32x16 acc[TN][TM];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
-        se += __shfl_xor(se, 32, 64);
-        if (ok && hi == 0) {
-          float *pp = g.part + ((long long)m * (g.N / WN) + nw0 / WN) * 2;
-          *(float2 *)pp = make_float2(mx, se);
-        }
-      }
-      if (!ok) continue;
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = (f32x16){};
+
+  const int KT = g.K / BK;
+  const int c32 = lane & 31, hi = lane >> 5;
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto lfrag = [&](int f, const bf16 *As, const bf16 *Bs, int s) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) fa[f][j] = *(const bf16x8 *)&As[swz(wm * WM + 32 * j + c32, 2 * s + hi)];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) fb[f][i] = *(const bf16x8 *)&Bs[swz(wn * WN + 32 * i + c32, 2 * s + hi)];
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int n = nw0 + 32 * i + 8 * c + 4 * hi;
-          epi_store4<EPI == EPI_LOGITS ? EPI_F32 : EPI>(g, m, n, acc[i][j][4 * c], acc[i][j][4 * c + 1],
-                                                        acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]);
-        }
-    }
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][i], fa[f][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Waits the compiler sees (a vmcnt(0) in inline asm would leave its own
+  // tracking of the DMA in flight): vmcnt(0), and lgkmcnt(0).
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  auto wait_lds = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };
+  // Where the compiler cannot tell which group runs, it adds a vmcnt(0)
+  // before a load phase; both groups have waited for their DMA by then.
+  auto ktile = [&](int kt, const bf16 *As, const bf16 *Bs, bf16 *nAs, bf16 *nBs) {
+    lfrag(0, As, Bs, 0);
+    lfrag(1, As, Bs, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < KT) dma(kt + 1, nAs, nBs);
+    wait_lds();
+    bar();
+    compute();
+    bar();
+    lfrag(0, As, Bs, 2);
+    lfrag(1, As, Bs, 3);
+    wait_lds();
+    if (grp == 1) wait_dma();
+    bar();
+    compute();
+    if (grp == 0) wait_dma();
+    // group 1's last compute phase ends the kernel's barriers
+    if (!(grp == 1 && kt == KT - 1)) bar();
+  };
+  dma(0, sa0, sb0);
+  wait_dma();
+  bar();
+  if (grp == 1) bar();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    ktile(kt, sa0, sb0, sa1, sb1);
+    ktile(kt + 1, sa1, sb1, sa0, sb0);
   }
+  if (kt < KT) ktile(kt, sa0, sb0, sa1, sb1);
+  tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
 }
 
 // ------------------------------------------------------------------ decode rows
@@ -494,7 +644,8 @@ void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int NWN = EPI == EPI_QKV ? 2 : 4;
   static_assert(EPI != EPI_LOGITS || BN / NWN == kLogitsPartCols, "partial width");
   int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  gemm_bf16_kernel<BM, BN, NWN, EPI><<<tiles, 128 * NWN, 0, s>>>(g);
+  if constexpr (NWN == 4) gemm_pp_kernel<BM, BN, EPI><<<tiles, 512, 0, s>>>(g);
+  else gemm_bf16_kernel<BM, BN, NWN, EPI><<<tiles, 128 * NWN, 0, s>>>(g);
 }
 
 }  // namespace
