@@ -232,6 +232,64 @@ DEV void tile_epilogue(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, int n0,
 }
 
 
+// Epilogue of gemm_pp_kernel's 128x64 wave tiles through LDS (the operand
+// buffers are free once the main loop is done).  In the accumulator layout a
+// store instruction covers 32 rows x 32 bytes; here each wave writes one
+// 32-row block at a time into its own LDS area and reads it back so that 16
+// lanes cover 64 consecutive columns of one row: every store instruction
+// then writes whole 128-byte lines (bf16: 128-byte halves of 256-byte rows),
+// and a residual add reads whole lines.  The area's row pitch of 68 floats
+// keeps both the block writes and the row reads free of bank conflicts.
+constexpr int kStagePitch = 68;
+template <int TM, int TN, int WM, int WN, int EPI>
+DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, int n0, int wm, int wn,
+                              int c32, int hi, int lane, float *stg) {
+  static_assert(WN == 64 && TN == 2 && EPI != EPI_QKV, "staged epilogue: 64-column wave tiles");
+  const bool active = (n0 + wn * WN) < g.N;
+  if (!active) return;
+  const int nw0 = n0 + wn * WN;
+  if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * WM + 32 * j + c32;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float se = 0.f;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
+      se += __shfl_xor(se, 32, 64);
+      if (m < g.M && hi == 0) {
+        float *pp = g.part + ((long long)m * (g.N / WN) + nw0 / WN) * 2;
+        *(float2 *)pp = make_float2(mx, se);
+      }
+    }
+  }
+  constexpr int EPS = EPI == EPI_LOGITS ? EPI_F32 : EPI;
+  const int rr = lane >> 4, cc = 4 * (lane & 15);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *(f32x4 *)&stg[c32 * kStagePitch + 32 * i + 8 * c + 4 * hi] =
+            (f32x4){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = 4 * q + rr;
+      const f32x4 v = *(const f32x4 *)&stg[r * kStagePitch + cc];
+      const int m = m0 + wm * WM + 32 * j + r;
+      if (m < g.M) epi_store4<EPS>(g, m, nw0 + cc, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
 // NWN waves along N and 2 along M, each wave software-pipelining its own
 // LDS reads against its MFMAs.  Used with NWN = 2 (4 waves, one per SIMD,
 // 128x128 wave tiles) for the QKV epilogue, which needs a whole 128-wide head
@@ -490,7 +548,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     ktile(kt + 1, sa1, sb1, sa0, sb0);
   }
   if (kt < KT) ktile(kt, sa0, sb0, sa1, sb1);
-  tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
+  // Staging areas: 32 x 68 floats per wave, two waves per 32 KB buffer.  A
+  // group reaches its epilogue only after both groups' last LDS reads
+  // (group 0 after the barrier that ends group 1's last load phase), and no
+  // DMA is in flight by then.
+  static_assert(2 * 32 * kStagePitch * 4 <= BM * BK * 2 && 2 * 32 * kStagePitch * 4 <= BN * BK * 2,
+                "staging area");
+  bf16 *const sbuf = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
+  float *stg = (float *)sbuf + (wave & 1) * 32 * kStagePitch;
+  tile_epilogue_staged<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, stg);
 }
 
 // ------------------------------------------------------------------ decode rows
