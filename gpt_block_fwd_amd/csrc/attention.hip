@@ -34,12 +34,15 @@ constexpr float kLazy = 8.0f;  // log2 headroom of the lazy softmax reference
 // (2^-33, 1), far from fp32 overflow and underflow.
 constexpr float kScoreBound = 16.5f;
 
-// K tile [64 keys][128 dims], 16-byte chunks XOR-swizzled by key.
-DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 7)) << 3); }
-// V^T tile [128 dims][64 keys], 16-byte chunks XOR-swizzled by dim pair, read
-// in 8-byte units.  Both swizzles move whole 16-byte chunks, so direct-to-LDS
-// loads can apply them by choosing each lane's source.
-DEV int vidx(int dim, int unit) { return dim * KT + ((((unit >> 1) ^ ((dim >> 1) & 7)) << 3) | ((unit & 1) << 2)); }
+// K tile [64 keys][128 dims]: 16-byte chunk c of key r at slot c ^ (r % 16),
+// so the 16 keys of a fragment read's lane group hit 16 distinct bank groups.
+DEV int kidx(int key, int chunk) { return key * DH + ((chunk ^ (key & 15)) << 3); }
+// V^T tile [128 dims][64 stored key columns] (keys in the vperm16 order of
+// the V^T buffer): 16-byte chunk c of dim r at slot c ^ ((r / 2) % 8), so a
+// fragment read's 16 lanes (dims of both parities) hit 16 distinct bank
+// groups.  Both swizzles move whole 16-byte chunks, so direct-to-LDS loads
+// can apply them by choosing each lane's source.
+DEV int vidx(int dim, int col) { return dim * KT + ((((col >> 3) ^ ((dim >> 1) & 7))) << 3) + (col & 7); }
 
 // NWV waves per workgroup, 32 RB rows each.  FIXREF: q and k are QK-normalised,
 // so the softmax runs against the fixed reference kScoreBound (no running
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
       const int j = wave + NWV * jj;
       const int key = 4 * j + (lane >> 4), pc = lane & 15;
       const int gkey = min(kt * KT + key, len - 1);
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * DH + ((pc ^ (key & 7)) << 3)),
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * DH + ((pc ^ (key & 15)) << 3)),
                                        LDS_PTR(&sk[buf][j * 512]), 16, 0, 0);
     }
 #pragma unroll
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     const int valid = len - kt * KT;  // 1 .. 63 here
     for (int i = tid; i < DH * KT; i += NT) {
       const int dim = i / KT, key = i % KT;
-      if (key >= valid) sv[buf][vidx(dim, key >> 2) + (key & 3)] = (bf16)0.f;
+      if (key >= valid) sv[buf][vidx(dim, vperm16(key))] = (bf16)0.f;
     }
   };
 
@@ -221,13 +224,12 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[rb][j] = f2bf(sacc[kb][rb][8 * h + j]);
-      const int u0 = 8 * kb + 4 * h + g;
+      // the lane's eight keys are stored columns 32 kb + 16 h + 8 g .. +8
+      const int col = 32 * kb + 16 * h + 8 * g;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int dim = 32 * d + c32;
-        bf16x4 lo = *(const bf16x4 *)&sv[buf][vidx(dim, u0)];
-        bf16x4 hi4 = *(const bf16x4 *)&sv[buf][vidx(dim, u0 + 2)];
-        bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        const bf16x8 vf = *(const bf16x8 *)&sv[buf][vidx(dim, col)];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[d][rb], 0, 0, 0);

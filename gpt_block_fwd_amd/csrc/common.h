@@ -88,6 +88,14 @@ struct RowInfo {
 // so one 16-byte load yields a lane's eight keys.
 DEV int vslot(int p) { return (p & 32) | (((p >> 2) & 3) << 3) | (((p >> 4) & 1) << 2) | (p & 3); }
 
+// Column of sequence position p (from the sequence's first column) in the
+// prefill V^T buffer: bits 2 and 3 of p swapped, so within each 16-position
+// group, position 8 a + 4 q + b (a, q < 2, b < 4) sits at column 8 q + 4 a + b.
+// That is the order in which the prefill attention's 32x32x16 MFMA takes
+// keys (k slot 8 q + j <-> key 8 (j / 4) + 4 q + j % 4 of the group), so one
+// 16-byte load yields a lane's eight keys.  The map is its own inverse.
+DEV int vperm16(int p) { return (p & ~15) | (((p >> 2) & 1) << 3) | (((p >> 3) & 1) << 2) | (p & 3); }
+
 // Paged KV cache addressing (see include/gpt.h for the layout).
 struct PagedKV {
   char *base;             // start of layer 0's pages

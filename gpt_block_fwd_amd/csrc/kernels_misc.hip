@@ -18,7 +18,7 @@ __global__ void rowinfo_kernel(const int *cu, const int *cu_pad, int n_seqs, int
   seq[m] = lo;
   int p = m - cu[lo];
   pos[m] = p;
-  if (vcol) vcol[m] = cu_pad[lo] + p;
+  if (vcol) vcol[m] = cu_pad[lo] + vperm16(p);
 }
 
 void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq, int *pos,

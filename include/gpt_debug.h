@@ -35,9 +35,12 @@ gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, in
 /*
  * Causal MQA attention of packed sequences ([nanochat-forum]: multi-query
  * attention): q bf16 [total, H*128], k bf16 [total, 128], vt bf16
- * [128, ldvt] holding V transposed with sequence b's positions starting at
- * column cu_pad[b] = sum over earlier sequences of their length rounded up to
- * 64 (ldvt >= cu_pad[n_seqs], multiple of 64); o bf16 [total, H*128].
+ * [128, ldvt] holding V transposed: position i of sequence b at column
+ * cu_pad[b] + (i with bits 2 and 3 swapped), where cu_pad[b] = sum over
+ * earlier sequences of their length rounded up to 64 (ldvt >= cu_pad[n_seqs],
+ * multiple of 64).  The swap puts each lane's eight keys of the attention
+ * MFMA in one 16-byte run; it is the layout the forward pass itself writes.
+ * o bf16 [total, H*128].
  * cu_seqlens is a host array [n_seqs + 1]; cu_dev is a device int32 buffer
  * of 2*(n_seqs + 1) entries the call fills with cu_seqlens and cu_pad.
  * qk_norm != 0 promises QK-normalised q and k (RMS <= 1 per head, as the

@@ -121,7 +121,10 @@ def test_prefill_attention_matches_oracle(lens, H, qk_norm):
     ldvt = int(cu_pad[-1])
     vt = np.full((128, ldvt), np.nan, np.float32)  # padding must never be read as data
     for b, L in enumerate(lens):
-        vt[:, cu_pad[b]:cu_pad[b] + L] = v[cu[b]:cu[b + 1], 0, :].T
+        # position i at column cu_pad[b] + (i with bits 2 and 3 swapped)
+        i = np.arange(L)
+        col = (i & ~15) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3)
+        vt[:, cu_pad[b] + col] = v[cu[b]:cu[b + 1], 0, :].T
     dq = to_dev_bf16(q.reshape(len(q), -1))
     dk = to_dev_bf16(k.reshape(len(k), -1))
     dvt = to_dev_bf16(vt)
