@@ -208,15 +208,14 @@ def summarize_traffic(fetch_csv, write_csv, out_path):
         blit = [r for r in rows if "copyBuffer" in r[1]][-1]
         known = COPY_BYTES / 2 if name == "fetch" else COPY_BYTES
         factor = known / 1024.0 / elem[2]
-        gemm = [r for r in rows if "gemm_pp_kernel" in r[1] or "gemm_bf16_kernel" in r[1]]
+        gemm = [r for r in rows if "gemm_pp_kernel" in r[1]]
         counted = gemm[len(gemm) // 2:]
         res[name] = {"copy_kernel": elem[1][:80], "copy_kib": elem[2], "copy_known_kib": known / 1024.0,
                      "factor": factor, "blit_kib": blit[2], "blit_known_kib": COPY_BYTES / 1024.0,
                      "launches": len(counted), "kib_per_launch": sum(r[2] for r in counted) / len(counted)}
     per_launch = (res["fetch"]["kib_per_launch"] * res["fetch"]["factor"] +
                   res["write"]["kib_per_launch"] * res["write"]["factor"]) * 1024.0
-    out = {"kernel": "prefill GEMMs: gemm_pp_kernel (O, W1, W2, LM head) and gemm_bf16_kernel (QKV), "
-                     "depth-12 prefill",
+    out = {"kernel": "gemm_pp_kernel (depth-12 prefill: QKV, O, W1, W2, LM head)",
            "bytes_per_launch": per_launch, "fetch": res["fetch"], "write": res["write"],
            "gemm_sources_sha256": gemm_source_hash()}
     with open(out_path, "w") as fh:
@@ -310,7 +309,7 @@ def main():
     smx = prof_read(B, ["softmax"])
     gemm_tfs = g["flops"] / (g["ms"] * 1e-3) / 1e12
     attn_tfs = attn["flops"] / (attn["ms"] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "prefill GEMMs (gemm_pp_kernel + gemm_bf16_kernel for QKV; block GEMMs and LM head)",
+    roofline = {"bound": "mfma", "kernel": "gemm_pp_kernel (block GEMMs + LM head)",
                 "achieved": round(gemm_tfs, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gemm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),

@@ -2,11 +2,10 @@
 // K-contiguous), fp32 accumulation, fused epilogues (bf16 store, ReLU^2 ->
 // bf16, fp32 residual add, fp32 store).
 //
-// Large-M kernels: 256x256x64 tiles staged through double-buffered LDS by
+// Large-M kernel: 256x256x64 tiles staged through double-buffered LDS by
 // direct-to-LDS loads with a 16-byte XOR swizzle, one
 // v_mfma_f32_32x32x16_bf16 per 32x32 block and 16-deep k substep; eight waves
-// in two groups that alternate load and compute phases (four waves of
-// 128x128 for the QKV epilogue).  The MFMA
+// in two groups that alternate load and compute phases.  The MFMA
 // A operand is the weight tile and the B operand the activation tile, so a
 // lane's accumulator holds one activation row and runs of 4 consecutive
 // output columns (vector stores in the epilogue).  Workgroup ids are remapped
@@ -290,138 +289,10 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
   }
 }
 
-// NWN waves along N and 2 along M, each wave software-pipelining its own
-// LDS reads against its MFMAs.  Used with NWN = 2 (4 waves, one per SIMD,
-// 128x128 wave tiles) for the QKV epilogue, which needs a whole 128-wide head
-// per wave; the other epilogues use gemm_pp_kernel.
-template <int BM, int BN, int NWN, int EPI>
-__global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int NW = 2 * NWN;
-  constexpr int WM = BM / 2, WN = BN / NWN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
-  __shared__ bf16 sa[2][BM * BK];
-  __shared__ bf16 sb[2][BN * BK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  int m0, n0;
-  tile_origin<BM, BN>(g, m0, n0);
-
-  // Direct global->LDS loads (global_load_lds_dwordx4): one instruction of a
-  // wave fills 1 KB of LDS = 8 rows of 64 bf16, lane i landing at row i/8,
-  // 16-byte slot i%8.  The slot holds logical k-chunk (i%8) ^ swz_key(row),
-  // so the lane loads that chunk: the XOR swizzle costs nothing.  Instruction p of
-  // wave w covers rows (4p + w)*8 .. +8; 8-row groups never straddle a
-  // weight segment (segment boundaries are multiples of 128), so the row
-  // base is wave-uniform and a lane keeps a 32-bit offset.  Instruction p of
-  // wave w covers rows (NW p + w)*8 .. +8.
-  const int lr = lane >> 3;
-  int aoff[PA], boff[PB];
-  const bf16 *bbase[PB];
-#pragma unroll
-  for (int p = 0; p < PA; ++p) {
-    const int lrow = (NW * p + wave) * 8 + lr;  // row within the tile
-    const int r = min(m0 + lrow, g.M - 1);
-    aoff[p] = r * (int)g.lda + (((lane & 7) ^ swz_key(lrow)) << 3);
-  }
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const int nb = min(n0 + (NW * p + wave) * 8, g.N - 8);
-    const bf16 *base;
-    int first;
-    if (nb < g.n1) { base = (const bf16 *)g.W0; first = 0; }
-    else if (nb < g.n2) { base = (const bf16 *)g.W1; first = g.n1; }
-    else { base = (const bf16 *)g.W2; first = g.n2; }
-    bbase[p] = base;
-    const int lrow = (NW * p + wave) * 8 + lr;
-    boff[p] = (nb - first + lr) * (int)g.ldw + (((lane & 7) ^ swz_key(lrow)) << 3);
-  }
-  const bf16 *abase = (const bf16 *)g.A;
-  auto dma = [&](int kt, int buf) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p)
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(abase + aoff[p] + kt * BK),
-                                       LDS_PTR(&sa[buf][(NW * p + wave) * 8 * BK]), 16, 0, 0);
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(bbase[p] + boff[p] + kt * BK),
-                                       LDS_PTR(&sb[buf][(NW * p + wave) * 8 * BK]), 16, 0, 0);
-  };
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = (f32x16){};
-
-  const int KT = g.K / BK;
-  const int c32 = lane & 31, hi = lane >> 5;
-  // MFMA operand fragments, double-buffered across the 16-deep k substeps
-  bf16x8 fa[2][TM], fb[2][TN];
-  auto lfrag = [&](int f, int buf, int s) {
-#pragma unroll
-    for (int j = 0; j < TM; ++j) fa[f][j] = *(const bf16x8 *)&sa[buf][swz(wm * WM + 32 * j + c32, 2 * s + hi)];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) fb[f][i] = *(const bf16x8 *)&sb[buf][swz(wn * WN + 32 * i + c32, 2 * s + hi)];
-  };
-  auto mfmas = [&](int f) {
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][i], fa[f][j], acc[i][j], 0, 0, 0);
-  };
-  auto interleave = [&]() {  // MFMA / LDS-read pairs, then the remaining MFMAs
-#pragma unroll
-    for (int q = 0; q < TM + TN; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);
-  };
-
-  // Main loop over k-tiles.  LDS buffer kt&1 holds k-tile kt; the DMA of
-  // k-tile kt+1 into the other buffer is issued first and overlaps the four
-  // MFMA substeps of k-tile kt.  Fragments of substep s+1 are read while the
-  // MFMAs of substep s run.  The single barrier of a k-tile sits after
-  // substep 2: by then every wave has read all of buffer kt&1 and (after its
-  // vmcnt wait) landed its share of k-tile kt+1, so substep 3's MFMAs overlap
-  // the first fragment reads of k-tile kt+1.
-  dma(0, 0);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  lfrag(0, 0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) dma(kt + 1, buf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    lfrag(1, buf, 1);
-    mfmas(0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    lfrag(0, buf, 2);
-    mfmas(1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    lfrag(1, buf, 3);
-    mfmas(0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (more) lfrag(0, buf ^ 1, 0);
-    mfmas(1);
-    if (more) interleave();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
-}
-
 // Eight waves in two groups of four (one wave per SIMD each); group q owns
 // rows 128 q .. 128 q + 127 of the 256x256 tile, wave w of a group columns
-// 64 w .. 64 w + 63.  The groups alternate between a load phase (the LDS ->
+// 64 w .. 64 w + 63 (for QKV: rows 64 (w / 2) .. and columns 128 (w % 2) ..
+// of the group's half).  The groups alternate between a load phase (the LDS ->
 // register reads of two 16-deep substeps) and a compute phase (their 16
 // MFMAs), group 1 one phase behind group 0, so each SIMD's matrix core runs
 // one group's compute phase while the other group loads.  Every phase ends
@@ -433,7 +304,11 @@ __global__ __launch_bounds__(128 * NWN) void gemm_bf16_kernel(GemmArgs g) {
 // group 1 before the barrier that ends its last load phase.
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
-  constexpr int NW = 8, WM = BM / 2, WN = BN / 4;
+  // The QKV epilogue needs a whole 128-wide head per wave: there the four
+  // waves of a group split its 128 rows in two and the 256 columns in two
+  // (64x128 wave tiles); otherwise 128x64.
+  constexpr bool WIDE = EPI == EPI_QKV;
+  constexpr int NW = 8, WM = WIDE ? BM / 4 : BM / 2, WN = WIDE ? BN / 2 : BN / 4;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
   // One LDS object per buffer, so the compiler can tell a DMA into one
@@ -442,12 +317,19 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   __shared__ bf16 sb0[BN * BK], sb1[BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wm = grp, wn = wave & 3;
+  const int grp = wave >> 2;
+  const int wm = WIDE ? 2 * grp + ((wave >> 1) & 1) : grp, wn = WIDE ? wave & 1 : wave & 3;
   int m0, n0;
   tile_origin<BM, BN>(g, m0, n0);
 
-  // Direct-to-LDS loads as in gemm_bf16_kernel: instruction p of wave w fills
-  // rows (8 p + w) * 8 .. +8 of the tile.
+  // Direct global->LDS loads (global_load_lds_dwordx4): one instruction of a
+  // wave fills 1 KB of LDS = 8 rows of 64 bf16, lane i landing at row i/8,
+  // 16-byte slot i%8.  The slot holds logical k-chunk (i%8) ^ swz_key(row),
+  // so the lane loads that chunk: the XOR swizzle costs nothing.
+  // Instruction p of wave w fills rows (8 p + w) * 8 .. +8 of the tile;
+  // 8-row groups never straddle a weight segment (segment boundaries are
+  // multiples of 128), so the row base is wave-uniform and a lane keeps a
+  // 32-bit offset.
   const int lr = lane >> 3;
   int aoff[PA], boff[PB];
   const bf16 *bbase[PB];
@@ -554,9 +436,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   // DMA is in flight by then.
   static_assert(2 * 32 * kStagePitch * 4 <= BM * BK * 2 && 2 * 32 * kStagePitch * 4 <= BN * BK * 2,
                 "staging area");
-  bf16 *const sbuf = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
-  float *stg = (float *)sbuf + (wave & 1) * 32 * kStagePitch;
-  tile_epilogue_staged<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, stg);
+  if constexpr (WIDE) {
+    tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
+  } else {
+    bf16 *const sbuf = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
+    float *stg = (float *)sbuf + (wave & 1) * 32 * kStagePitch;
+    tile_epilogue_staged<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, stg);
+  }
 }
 
 // ------------------------------------------------------------------ decode rows
@@ -706,12 +592,9 @@ void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = 256, BN = 256;
-  // the QKV epilogue needs a whole 128-wide head per wave
-  constexpr int NWN = EPI == EPI_QKV ? 2 : 4;
-  static_assert(EPI != EPI_LOGITS || BN / NWN == kLogitsPartCols, "partial width");
+  static_assert(EPI != EPI_LOGITS || BN / 4 == kLogitsPartCols, "partial width");
   int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if constexpr (NWN == 4) gemm_pp_kernel<BM, BN, EPI><<<tiles, 512, 0, s>>>(g);
-  else gemm_bf16_kernel<BM, BN, NWN, EPI><<<tiles, 128 * NWN, 0, s>>>(g);
+  gemm_pp_kernel<BM, BN, EPI><<<tiles, 512, 0, s>>>(g);
 }
 
 }  // namespace
