@@ -51,8 +51,10 @@ template <int NWV, int RB, bool FIXREF>
 __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs a) {
   constexpr int NT = 64 * NWV, ROWS = 32 * RB * NWV;
   constexpr int SP = 4 * 4 / NWV;  // 16-byte staging loads per thread for each of K and V^T
-  __shared__ bf16 sk[2][KT * DH];
-  __shared__ bf16 sv[2][DH * KT];
+  // One LDS object per buffer, so the compiler can tell the DMA into one
+  // buffer from reads of the other and adds no wait for it.
+  __shared__ bf16 sk0[KT * DH], sk1[KT * DH];
+  __shared__ bf16 sv0[DH * KT], sv1[DH * KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
   // blockIdx.y counts row blocks from the last one, so the blocks that see
@@ -88,14 +90,14 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   // holds.  Keys past the sequence are clamped to its last key (they are
   // masked); V^T columns past it are zeroed once the tile has landed.
   constexpr int DJ = 16 / NWV;  // instructions per wave for each of K and V^T
-  auto dma = [&](int kt, int buf) {
+  auto dma = [&](int kt, bf16 *sk, bf16 *sv) {
 #pragma unroll
     for (int jj = 0; jj < DJ; ++jj) {
       const int j = wave + NWV * jj;
       const int key = 4 * j + (lane >> 4), pc = lane & 15;
       const int gkey = min(kt * KT + key, len - 1);
       __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * DH + ((pc ^ (key & 15)) << 3)),
-                                       LDS_PTR(&sk[buf][j * 512]), 16, 0, 0);
+                                       LDS_PTR(&sk[j * 512]), 16, 0, 0);
     }
 #pragma unroll
     for (int jj = 0; jj < DJ; ++jj) {
@@ -103,16 +105,16 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
       const int dim = 8 * j + (lane >> 3), pc = lane & 7;
       __builtin_amdgcn_global_load_lds(
           GLOBAL_PTR(a.vt + (long long)dim * a.ldvt + col0 + kt * KT + ((pc ^ ((dim >> 1) & 7)) << 3)),
-          LDS_PTR(&sv[buf][j * 512]), 16, 0, 0);
+          LDS_PTR(&sv[j * 512]), 16, 0, 0);
     }
   };
   // After a tile has landed (and a barrier): zero its V^T columns past the
   // sequence; the caller puts another barrier before the tile is read.
-  auto zero_tail = [&](int kt, int buf) {
+  auto zero_tail = [&](int kt, bf16 *sv) {
     const int valid = len - kt * KT;  // 1 .. 63 here
     for (int i = tid; i < DH * KT; i += NT) {
       const int dim = i / KT, key = i % KT;
-      if (key >= valid) sv[buf][vidx(dim, vperm16(key))] = (bf16)0.f;
+      if (key >= valid) sv[vidx(dim, vperm16(key))] = (bf16)0.f;
     }
   };
 
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   }
   const float sc = kLog2e / sqrtf((float)DH);
 
-  auto tile = [&](int kt, int buf) {
+  auto tile = [&](int kt, const bf16 *sk, const bf16 *sv) {
     if (kt * KT > pw_max) return;  // every key of the tile is in this wave's future
     f32x16 sacc[2][RB];
 #pragma unroll
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 kf = *(const bf16x8 *)&sk[buf][kidx(32 * kb + c32, 2 * s + g)];
+        bf16x8 kf = *(const bf16x8 *)&sk[kidx(32 * kb + c32, 2 * s + g)];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], sacc[kb][rb], 0, 0, 0);
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int dim = 32 * d + c32;
-        const bf16x8 vf = *(const bf16x8 *)&sv[buf][vidx(dim, col)];
+        const bf16x8 vf = *(const bf16x8 *)&sv[vidx(dim, col)];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           oacc[d][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[d][rb], 0, 0, 0);
@@ -237,23 +239,34 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     }
   };
 
-  auto land = [&](int kt, int buf) {  // wait for tile kt's loads (all waves)
+  auto land = [&](int kt, bf16 *sv) {  // wait for tile kt's loads (all waves)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kt * KT + KT > len) {
-      zero_tail(kt, buf);
+      zero_tail(kt, sv);
       __syncthreads();
     }
   };
-  dma(0, 0);
-  land(0, 0);
-  for (int kt = 0; kt < n_kt - 1; ++kt) {
-    dma(kt + 1, (kt + 1) & 1);
+  // tile kt computes from one buffer while tile kt + 1 streams into the other
+  auto step = [&](int kt, bf16 *sk, bf16 *sv, bf16 *nsk, bf16 *nsv) {
+    dma(kt + 1, nsk, nsv);
     __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the tile's MFMAs
-    tile(kt, kt & 1);
-    land(kt + 1, (kt + 1) & 1);
+    tile(kt, sk, sv);
+    land(kt + 1, nsv);
+  };
+  dma(0, sk0, sv0);
+  land(0, sv0);
+  int kt = 0;
+  for (; kt + 2 < n_kt; kt += 2) {
+    step(kt, sk0, sv0, sk1, sv1);
+    step(kt + 1, sk1, sv1, sk0, sv0);
   }
-  tile(n_kt - 1, (n_kt - 1) & 1);
+  if (kt + 1 < n_kt) {
+    step(kt, sk0, sv0, sk1, sv1);
+    tile(kt + 1, sk1, sv1);
+  } else {
+    tile(kt, sk0, sv0);
+  }
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
