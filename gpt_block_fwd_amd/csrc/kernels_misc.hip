@@ -151,7 +151,9 @@ void launch_embed_f32(const int *tok, const float *wte, const float *wpe, const 
 // sum of squares reduced across the wave.  `rows` optionally selects source
 // rows (the last position of each sequence).
 
-template <typename TO>
+// NC > 0: the row (d <= 256 NC) is loaded into registers with every load in
+// flight at once and written from there; NC == 0: any d, two passes.
+template <typename TO, int NC>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, TO *y, const int *rows,
                                                       int M, int d, float eps) {
   int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -159,32 +161,49 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, TO *y, con
   if (r >= M) return;
   long long src = rows ? rows[r] : r;
   const float *xr = x + src * d;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    float4 v = *(const float4 *)(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  float rs = 1.0f / sqrtf(ss / (float)d + eps);
   TO *yr = y + (long long)r * d;
-  for (int c = lane * 4; c < d; c += 256) {
-    float4 v = *(const float4 *)(xr + c);
+  auto put = [&](int c, f32x4 v, float rs) {
     if constexpr (sizeof(TO) == 2) {
-      bf16x4 o = {f2bf(v.x * rs), f2bf(v.y * rs), f2bf(v.z * rs), f2bf(v.w * rs)};
+      bf16x4 o = {f2bf(v[0] * rs), f2bf(v[1] * rs), f2bf(v[2] * rs), f2bf(v[3] * rs)};
       *(bf16x4 *)(yr + c) = o;
     } else {
-      *(float4 *)(yr + c) = make_float4(v.x * rs, v.y * rs, v.z * rs, v.w * rs);
+      *(f32x4 *)(yr + c) = (f32x4){v[0] * rs, v[1] * rs, v[2] * rs, v[3] * rs};
     }
+  };
+  float ss = 0.f;
+  if constexpr (NC > 0) {
+    f32x4 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane * 4 + 256 * i < d) v[i] = *(const f32x4 *)(xr + lane * 4 + 256 * i);
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane * 4 + 256 * i < d) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane * 4 + 256 * i < d) put(lane * 4 + 256 * i, v[i], rs);
+  } else {
+    for (int c = lane * 4; c < d; c += 256) {
+      const f32x4 v = *(const f32x4 *)(xr + c);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane * 4; c < d; c += 256) put(c, *(const f32x4 *)(xr + c), rs);
   }
 }
 
 void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d, float eps,
                          hipStream_t s) {
-  rmsnorm_kernel<bf16><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+  if (d <= 2048) rmsnorm_kernel<bf16, 8><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+  else rmsnorm_kernel<bf16, 0><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
 }
 void launch_rmsnorm_f32(const float *x, float *y, const int *rows, int M, int d, float eps,
                         hipStream_t s) {
-  rmsnorm_kernel<float><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+  if (d <= 2048) rmsnorm_kernel<float, 8><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
+  else rmsnorm_kernel<float, 0><<<(M + 3) / 4, 256, 0, s>>>(x, y, rows, M, d, eps);
 }
 
 // ---------------------------------------------------------------- RoPE + QK-norm + scatter
