@@ -243,7 +243,7 @@ constexpr int kStagePitch = 68;
 template <int TM, int TN, int WM, int WN, int EPI>
 DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, int n0, int wm, int wn,
                               int c32, int hi, int lane, float *stg) {
-  static_assert(WN == 64 && TN == 2 && EPI != EPI_QKV, "staged epilogue: 64-column wave tiles");
+  static_assert((WN == 64 || WN == 96) && EPI != EPI_QKV, "staged epilogue: 64- or 96-column wave tiles");
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
   const int nw0 = n0 + wn * WN;
@@ -270,27 +270,35 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
     }
   }
   constexpr int EPS = EPI == EPI_LOGITS ? EPI_F32 : EPI;
-  const int rr = lane >> 4, cc = 4 * (lane & 15);
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    // columns 0-63 of the wave tile, then (96-wide tiles) columns 64-95
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+    for (int i0 = 0; i0 < TN; i0 += 2) {
+      const int ni = TN - i0 >= 2 ? 2 : 1;   // 32-column blocks in this pass
+      const int lpr = 8 * ni;                // lanes per 32 ni-column row
+      const int rr = lane / lpr, cc = 4 * (lane % lpr);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *(f32x4 *)&stg[c32 * kStagePitch + 32 * i + 8 * c + 4 * hi] =
-            (f32x4){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+      for (int i = 0; i < ni; ++i)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = 4 * q + rr;
-      const f32x4 v = *(const f32x4 *)&stg[r * kStagePitch + cc];
-      const int m = m0 + wm * WM + 32 * j + r;
-      if (m >= g.M) continue;
-      if constexpr (EPI == EPI_LOGITS) {
-        // nothing in this pass reads the logits again: non-temporal stores
-        // keep them from displacing the operands in L2 (10% on the LM head)
-        __builtin_nontemporal_store(v, (f32x4 *)((float *)g.C + (long long)m * g.ldc + nw0 + cc));
-      } else {
-        epi_store4<EPS>(g, m, nw0 + cc, v[0], v[1], v[2], v[3]);
+        for (int c = 0; c < 4; ++c)
+          *(f32x4 *)&stg[c32 * kStagePitch + 32 * i + 8 * c + 4 * hi] =
+              (f32x4){acc[i0 + i][j][4 * c], acc[i0 + i][j][4 * c + 1], acc[i0 + i][j][4 * c + 2],
+                      acc[i0 + i][j][4 * c + 3]};
+#pragma unroll
+      for (int q = 0; q < 4 * ni; ++q) {
+        const int r = (64 / lpr) * q + rr;
+        const f32x4 v = *(const f32x4 *)&stg[r * kStagePitch + cc];
+        const int m = m0 + wm * WM + 32 * j + r;
+        const int n = nw0 + 32 * i0 + cc;
+        if (m >= g.M) continue;
+        if constexpr (EPI == EPI_LOGITS) {
+          // nothing in this pass reads the logits again: non-temporal stores
+          // keep them from displacing the operands in L2 (10% on the LM head)
+          __builtin_nontemporal_store(v, (f32x4 *)((float *)g.C + (long long)m * g.ldc + n));
+        } else {
+          epi_store4<EPS>(g, m, n, v[0], v[1], v[2], v[3]);
+        }
       }
     }
   }
@@ -311,10 +319,11 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
 // group 1 before the barrier that ends its last load phase.
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
-  // The QKV epilogue needs a whole 128-wide head per wave: there the four
-  // waves of a group split its 128 rows in two and the 256 columns in two
-  // (64x128 wave tiles); otherwise 128x64.
-  constexpr bool WIDE = EPI == EPI_QKV;
+  // The QKV epilogue needs a whole 128-wide head per wave, and 192-column
+  // tiles split into 96-column wave tiles: there the four waves of a group
+  // split its 128 rows in two and the columns in two (64x128 or 64x96 wave
+  // tiles); otherwise 128x64.
+  constexpr bool WIDE = EPI == EPI_QKV || BN == 192;
   constexpr int NW = 8, WM = WIDE ? BM / 4 : BM / 2, WN = WIDE ? BN / 2 : BN / 4;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   // DMA is in flight by then.
   static_assert(2 * 32 * kStagePitch * 4 <= BM * BK * 2 && 2 * 32 * kStagePitch * 4 <= BN * BK * 2,
                 "staging area");
-  if constexpr (WIDE) {
+  if constexpr (EPI == EPI_QKV) {
     tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
   } else {
     bf16 *const sbuf = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
@@ -598,10 +607,20 @@ void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
 
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
-  constexpr int BM = 256, BN = 256;
-  static_assert(EPI != EPI_LOGITS || BN / 4 == kLogitsPartCols, "partial width");
-  int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  gemm_pp_kernel<BM, BN, EPI><<<tiles, 512, 0, s>>>(g);
+  constexpr int BM = 256;
+  static_assert(EPI != EPI_LOGITS || 256 / 4 == kLogitsPartCols, "partial width");
+  const int tm = (g.M + BM - 1) / BM;
+  const int t256 = tm * ((g.N + 255) / 256);
+  if constexpr (EPI == EPI_RESID) {
+    // 192-column tiles when N splits into them and they take fewer
+    // column-rounds over the 256 CUs (d = 768: 256 tiles instead of 192)
+    const int t192 = tm * (g.N / 192);
+    if (g.N % 192 == 0 && (long long)((t192 + 255) / 256) * 192 < (long long)((t256 + 255) / 256) * 256) {
+      gemm_pp_kernel<BM, 192, EPI><<<t192, 512, 0, s>>>(g);
+      return;
+    }
+  }
+  gemm_pp_kernel<BM, 256, EPI><<<t256, 512, 0, s>>>(g);
 }
 
 }  // namespace

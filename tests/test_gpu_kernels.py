@@ -13,9 +13,12 @@ B = pytest.importorskip("gpt_block_fwd_amd.binding")
 
 GEMM_SHAPES = [
     # (M, N, K): several 256x256 tiles with ragged M, N = 4.5 tiles, odd tile counts
+    # (the residual add takes 256x192 tiles where N splits into 192 columns)
     (300, 384, 192),
     (1000, 1152, 768),
     (513, 1920, 1664),
+    # residual add on 192-column tiles (N = 768, 1152, 384), ragged M
+    (700, 768, 3072),
     # decode-row kernel (M <= 64): 1, 2, 3 and 4 row blocks, ragged M, 64-column tiles
     (1, 128, 64),
     (33, 768, 768),
