@@ -18,7 +18,8 @@ __all__ = [
     "READINGS", "rmsnorm", "rope_angles", "rope_tables", "apply_rope",
     "relu", "relu2", "softmax", "logsumexp", "causal_attention", "KVCache",
     "embed", "block", "final_logits", "forward", "prefill", "decode_step",
-    "greedy", "sample", "cross_entropy", "param_count", "round_bf16",
+    "greedy", "sample", "cross_entropy", "token_losses", "mean_loss", "param_count",
+    "round_bf16",
     "run_serving",
 ]
 
@@ -341,6 +342,31 @@ def cross_entropy(logits: np.ndarray, targets: np.ndarray) -> float:
     model is by the real next token."""
     lse = logsumexp(logits, axis=-1)
     return float(np.mean(lse - logits[np.arange(len(targets)), targets]))
+
+
+def token_losses(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Per-row next-token cross-entropy (Microgpt, "Training process", item 2):
+    the negative log-probability the model gives the real next token,
+    ``loss[r] = logsumexp(logits[r]) - logits[r, targets[r]]``, in float64.
+
+    A target outside ``[0, V)`` marks a row with no next token (a sequence's
+    last position); its loss is 0.
+    """
+    lg = np.asarray(logits, np.float64)
+    t = np.asarray(targets, np.int64)
+    V = lg.shape[-1]
+    ok = (t >= 0) & (t < V)
+    out = np.zeros(len(t), np.float64)
+    rows = np.nonzero(ok)[0]
+    out[rows] = logsumexp(lg[rows], axis=-1) - lg[rows, t[rows]]
+    return out
+
+
+def mean_loss(losses: np.ndarray, targets: np.ndarray, vocab: int) -> float:
+    """Mean of ``token_losses`` over the rows that have a target (0 if none)."""
+    t = np.asarray(targets, np.int64)
+    ok = (t >= 0) & (t < vocab)
+    return float(np.mean(np.asarray(losses, np.float64)[ok])) if ok.any() else 0.0
 
 
 def param_count(W) -> int:

@@ -88,6 +88,67 @@ def test_init_loss_near_3_3():
     assert np.mean(losses) > math.log(27) - 0.05
 
 
+# ---------------------------------------------------------------- cross-entropy
+
+def test_token_losses_closed_forms():
+    """Uniform logits cost ln V for any target; shifting a row changes
+    nothing; a target far ahead of the rest costs ~(V-1) e^-gap."""
+    V = 37
+    lg = np.zeros((3, V))
+    np.testing.assert_allclose(oracle.token_losses(lg, [0, 5, 36]), math.log(V), rtol=0, atol=1e-15)
+    rng = np.random.default_rng(11)
+    lg = rng.normal(size=(5, V)) * 4
+    t = rng.integers(0, V, 5)
+    np.testing.assert_allclose(oracle.token_losses(lg + rng.normal(size=(5, 1)) * 50, t),
+                               oracle.token_losses(lg, t), rtol=0, atol=1e-12)
+    one = np.zeros((1, V))
+    one[0, 7] = 30.0
+    # lse - 30 cancels in float64: absolute error ~ 30 * 2^-52
+    np.testing.assert_allclose(oracle.token_losses(one, [7]), (V - 1) * math.exp(-30.0), rtol=0, atol=2e-14)
+    # and the wrong target pays the gap
+    np.testing.assert_allclose(oracle.token_losses(one, [8]), 30.0 + (V - 1) * math.exp(-30.0), rtol=1e-12)
+
+
+def test_token_losses_match_scalar_loop():
+    """-log(softmax) written out with math.exp per entry, on a small vocabulary."""
+    rng = np.random.default_rng(12)
+    V = 9
+    lg = rng.normal(size=(6, V)) * 3
+    t = rng.integers(0, V, 6)
+    ref = []
+    for r in range(6):
+        z = sum(math.exp(float(v)) for v in lg[r])
+        ref.append(-math.log(math.exp(float(lg[r, t[r]])) / z))
+    np.testing.assert_allclose(oracle.token_losses(lg, t), ref, rtol=0, atol=1e-12)
+
+
+def test_ignored_targets_and_mean():
+    rng = np.random.default_rng(13)
+    V = 10
+    lg = rng.normal(size=(5, V))
+    t = np.array([3, -1, 9, 10, 0])   # rows 1 and 3 have no target
+    loss = oracle.token_losses(lg, t)
+    assert loss[1] == 0.0 and loss[3] == 0.0
+    full = oracle.token_losses(lg[[0, 2, 4]], t[[0, 2, 4]])
+    np.testing.assert_array_equal(loss[[0, 2, 4]], full)
+    assert oracle.mean_loss(loss, t, V) == pytest.approx(float(np.mean(full)), abs=1e-15)
+    assert oracle.mean_loss(loss, np.full(5, -1), V) == 0.0
+
+
+def test_init_token_loss_near_3_3():
+    """The per-row losses of the tiny model at init, averaged over every row
+    with a next token, sit near 3.3 (Microgpt, 'Training process')."""
+    w = wl.tiny_workload()
+    W = wl.make_weights(w.model)
+    lg = np.concatenate(oracle.prefill(w.model, W, w.tokens, w.seqlens)[0])
+    t = w.next_token_targets()
+    assert (t.reshape(8, 16)[:, -1] == -1).all()
+    np.testing.assert_array_equal(t.reshape(8, 16)[:, :-1], w.tokens.reshape(8, 16)[:, 1:])
+    m = oracle.mean_loss(oracle.token_losses(lg, t), t, w.model.vocab)
+    g = GOLDEN["init_loss"]
+    assert abs(m - g["value"]) <= g["tol"]
+
+
 # ---------------------------------------------------------------- softmax
 
 def test_vocab_softmax_rows_are_distributions():

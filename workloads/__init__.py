@@ -193,6 +193,15 @@ class Workload:
         cu = self.cu_seqlens
         return self.tokens[cu[b]:cu[b + 1]]
 
+    def next_token_targets(self) -> np.ndarray:
+        """int32 [sum(seqlens)]: the token that follows each position within
+        its sequence, -1 at each sequence's last position."""
+        t = np.full(len(self.tokens), -1, np.int32)
+        cu = self.cu_seqlens
+        for b in range(self.n_seqs):
+            t[cu[b]:cu[b + 1] - 1] = self.tokens[cu[b] + 1:cu[b + 1]]
+        return t
+
 
 def tiny_workload(seed: int = 0) -> Workload:
     """8 sequences of 16: position 0 is BOS (id 26), the rest uniform on [0, 27)."""
