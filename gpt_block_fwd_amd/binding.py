@@ -26,7 +26,8 @@ PROF_CLASSES = {"gemm": 0, "lmhead": 1, "attn": 2, "decode_attn": 3, "skinny": 4
 
 #: every entry point declared by include/gpt.h and include/gpt_profile.h
 EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
-           "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_decode_step",
+           "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
+           "gpt_decode_step",
            "gpt_select_tokens", "gpt_profile_enable", "gpt_profile_read",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.gpt_workspace_bytes.restype = sz
     L.gpt_prefill.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, i32, vp, i32,
                               vp, vp, vp, vp, sz, vp]
+    L.gpt_prefill_loss.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, vp, i32, vp,
+                                   vp, vp, vp, vp, sz, vp]
     L.gpt_decode_step.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, f32, vp, vp,
                                   vp, vp, sz, vp]
     L.gpt_select_tokens.argtypes = [vp, i32, i32, f32, vp, vp, vp]
@@ -167,6 +170,16 @@ def gpt_prefill(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, tokens,
                              _ptr(rope_sin), _ptr(tokens), cu.ctypes.data, n_seqs, kv, logits_rows,
                              _ptr(logits), _ptr(lse), _ptr(probs), _ptr(workspace),
                              workspace_bytes, _stream(stream)))
+
+
+def gpt_prefill_loss(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, tokens, targets,
+                     cu_seqlens: np.ndarray, n_seqs: int, kv: Optional[int], loss, lse, mean,
+                     workspace, workspace_bytes: int, stream=None):
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    _check(lib().gpt_prefill_loss(ctypes.byref(cfg), ctypes.byref(weights), _ptr(rope_cos),
+                                  _ptr(rope_sin), _ptr(tokens), _ptr(targets), cu.ctypes.data,
+                                  n_seqs, kv, _ptr(loss), _ptr(lse), _ptr(mean), _ptr(workspace),
+                                  workspace_bytes, _stream(stream)))
 
 
 def gpt_decode_step(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, kv: int, tokens_in,
@@ -264,6 +277,14 @@ class DeviceModel:
         ws, nb = workspace if workspace is not None else self.workspace(total, n)
         gpt_prefill(self.cfg, self.weights, self.rope_cos, self.rope_sin, tokens, cu_seqlens, n,
                     kv, logits_rows, logits, lse, probs, ws, nb, stream)
+
+    def prefill_loss(self, tokens, targets, cu_seqlens, loss, lse=None, mean=None, kv=None,
+                     workspace=None, stream=None):
+        n = len(cu_seqlens) - 1
+        total = int(cu_seqlens[-1])
+        ws, nb = workspace if workspace is not None else self.workspace(total, n)
+        gpt_prefill_loss(self.cfg, self.weights, self.rope_cos, self.rope_sin, tokens, targets,
+                         cu_seqlens, n, kv, loss, lse, mean, ws, nb, stream)
 
     def decode_step(self, kv: int, tokens_in, tokens_out, temperature=0.0, uniforms=None,
                     logits=None, workspace=None, stream=None):

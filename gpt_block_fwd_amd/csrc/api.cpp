@@ -131,6 +131,8 @@ gpt_status check_config(const gpt_config *c) {
 struct Bufs {
   int *cu, *cu_pad, *lastrows, *seq, *pos, *vcol;
   float *x, *qkv, *lse_tmp, *opart, *mlpart, *dlogits, *lpart, *sel;
+  float *tgt;      // target logits of the fused cross-entropy [M]
+  float *llogits;  // logits for the cross-entropy where the LM head cannot fuse it
   float *slabs;   // partial products of split decode-row GEMMs
   unsigned *ctr;  // completion counters of decode attention
   void *h, *q, *k, *vt, *o, *u;
@@ -174,6 +176,11 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.slabs = (float *)take((size_t)kMaxRowSplit * std::min(M, 64LL) * std::max(d, (H + 2 * Hkv) * dh) * 4);
   t.sel = (float *)take((size_t)argmax_scratch_floats((int)nseq, c->vocab) * 4);
   t.lpart = (float *)take(M * (long long)((c->vocab + kLogitsPartCols - 1) / kLogitsPartCols) * 2 * 4);
+  t.tgt = (float *)take(M * 4);
+  // fp32 models and bf16 prefills of at most 64 rows compute the loss from
+  // materialised logits (sized by min(M, 64) for bf16, so the total grows
+  // with M)
+  t.llogits = (float *)take((c->dtype == GPT_DTYPE_BF16 ? std::min(M, 64LL) : M) * (long long)c->vocab * 4);
   if (b) *b = t;
   return align256(off);
 }
@@ -389,14 +396,22 @@ size_t gpt_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_
   return carve(c, max_tokens, max_seqs, nullptr, nullptr);
 }
 
-gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
-                       const float *rope_sin, const int32_t *tokens, const int32_t *cu_seqlens,
-                       int32_t n_seqs, gpt_kv_cache *kv, int32_t logits_rows, float *logits, float *lse,
-                       float *probs, void *workspace, size_t workspace_bytes, gpt_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// Prefill forward.  Logits mode (targets == NULL): logits of `logits_rows`
+// rows, optional lse and probs.  Loss mode: every row's cross-entropy
+// against targets into loss (optional lse, mean); logits is unused.
+gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin,
+                        const int32_t *tokens, const int32_t *cu_seqlens, int32_t n_seqs, gpt_kv_cache *kv,
+                        int32_t logits_rows, float *logits, float *lse, float *probs, const int32_t *targets,
+                        float *loss, float *mean, void *workspace, size_t workspace_bytes, gpt_stream_t stream) {
   gpt_status st = check_config(c);
   if (st) return st;
   if ((st = check_weights(c, w))) return st;
-  if (!tokens || !cu_seqlens || !logits || !workspace) return fail(GPT_ERR_ARG, "NULL required pointer");
+  const bool loss_mode = targets != nullptr;
+  if (!tokens || !cu_seqlens || !workspace || (loss_mode ? !loss : !logits))
+    return fail(GPT_ERR_ARG, "NULL required pointer");
   if (n_seqs <= 0) return fail(GPT_ERR_ARG, "n_seqs must be positive");
   if (n_seqs > kMaxPrefillSeqs) return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences per prefill", kMaxPrefillSeqs);
   if (logits_rows != GPT_ROWS_ALL && logits_rows != GPT_ROWS_LAST) return fail(GPT_ERR_ARG, "bad logits_rows");
@@ -420,7 +435,8 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   const size_t need = carve(c, M, n_seqs, nullptr, nullptr);
   if (workspace_bytes < need) return fail(GPT_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GPT_ERR_ARG, "workspace must be 256-byte aligned");
-  if (!aligned16(logits) || (probs && !aligned16(probs))) return fail(GPT_ERR_ARG, "logits/probs must be 16-byte aligned");
+  if (!loss_mode && (!aligned16(logits) || (probs && !aligned16(probs))))
+    return fail(GPT_ERR_ARG, "logits/probs must be 16-byte aligned");
 
   hipStream_t s = (hipStream_t)stream;
   hipGetLastError();  // clear any stale error from unrelated work
@@ -558,6 +574,34 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
     if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, sel, rows, d, c->norm_eps, s);
     else launch_rmsnorm_f32(bf.x, (float *)bf.h, sel, rows, d, c->norm_eps, s);
   }
+  if (loss_mode) {
+    // next-token cross-entropy of every row without materialising the
+    // logits when the LM head runs on the large-M kernel
+    if (bf16p && rows > 64) {
+      GemmArgs lg = gemm(bf.h, d, w->lm_head, rows, V, d, nullptr, V, EPI_LOSS);
+      lg.part = bf.lpart;
+      lg.targets = targets;
+      lg.tgt = bf.tgt;
+      {
+        Timed t(GPT_PROF_LMHEAD, s, 2.0 * rows * V * d,
+                2.0 * ((double)rows * d + (double)V * d) + (double)rows * (V / kLogitsPartCols) * 8);
+        launch_gemm_bf16(lg, s);
+      }
+      Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * (V / kLogitsPartCols) * 8 + (double)rows * 12);
+      launch_ce_from_parts(bf.lpart, V / kLogitsPartCols, bf.tgt, targets, V, rows, loss, lse, s);
+    } else {
+      run_gemm(c, gemm(bf.h, d, w->lm_head, rows, V, d, bf.llogits, V, EPI_F32), GPT_PROF_LMHEAD, s);
+      Timed t(GPT_PROF_SOFTMAX, s, 0, (double)rows * V * 4 + (double)rows * 12);
+      launch_softmax_lse(bf.llogits, rows, V, lse ? lse : bf.lse_tmp, nullptr, s);
+      launch_ce_from_logits(bf.llogits, lse ? lse : bf.lse_tmp, targets, V, rows, loss, s);
+    }
+    if (mean) launch_mean_loss(loss, targets, V, rows, mean, s);
+    if (kv) launch_lens_set(pv.lens, bf.cu, n_seqs, s);
+    if ((st = hip_check("gpt_prefill_loss launch"))) return st;
+    if (kv)
+      for (int b = 0; b < n_seqs; ++b) kv->lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+    return GPT_OK;
+  }
   const bool want_lse = lse || probs;
   const bool fused_lse = want_lse && bf16p && rows > 64;
   GemmArgs lg = gemm(bf.h, d, w->lm_head, rows, V, d, logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
@@ -575,6 +619,27 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
   if (kv)
     for (int b = 0; b < n_seqs; ++b) kv->lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
   return GPT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                       const float *rope_sin, const int32_t *tokens, const int32_t *cu_seqlens,
+                       int32_t n_seqs, gpt_kv_cache *kv, int32_t logits_rows, float *logits, float *lse,
+                       float *probs, void *workspace, size_t workspace_bytes, gpt_stream_t stream) {
+  return prefill_impl(c, w, rope_cos, rope_sin, tokens, cu_seqlens, n_seqs, kv, logits_rows, logits, lse, probs,
+                      nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+gpt_status gpt_prefill_loss(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                            const float *rope_sin, const int32_t *tokens, const int32_t *targets,
+                            const int32_t *cu_seqlens, int32_t n_seqs, gpt_kv_cache *kv, float *loss,
+                            float *lse, float *mean, void *workspace, size_t workspace_bytes,
+                            gpt_stream_t stream) {
+  if (!targets) return fail(GPT_ERR_ARG, "NULL required pointer");
+  return prefill_impl(c, w, rope_cos, rope_sin, tokens, cu_seqlens, n_seqs, kv, GPT_ROWS_ALL, nullptr, lse,
+                      nullptr, targets, loss, mean, workspace, workspace_bytes, stream);
 }
 
 gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const float *rope_cos,

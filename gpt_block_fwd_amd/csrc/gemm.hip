@@ -247,7 +247,7 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
   const int nw0 = n0 + wn * WN;
-  if constexpr (EPI == EPI_LOGITS) {
+  if constexpr (EPI == EPI_LOGITS || EPI == EPI_LOSS) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int m = m0 + wm * WM + 32 * j + c32;
@@ -268,6 +268,26 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
         *(float2 *)pp = make_float2(mx, se);
       }
     }
+  }
+  if constexpr (EPI == EPI_LOSS) {
+    // no logits leave the chip: only each row's target logit, read back from
+    // the staged 32-row block by the lane that owns the row
+    static_assert(WN == 64, "one partial block per wave");
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *(f32x4 *)&stg[c32 * kStagePitch + 32 * i + 8 * c + 4 * hi] =
+              (f32x4){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+      const int m = m0 + wm * WM + 32 * j + c32;
+      if (hi == 0 && m < g.M) {
+        const int col = g.targets[m] - nw0;
+        if (col >= 0 && col < WN) g.tgt[m] = stg[c32 * kStagePitch + col];
+      }
+    }
+    return;
   }
   constexpr int EPS = EPI == EPI_LOGITS ? EPI_F32 : EPI;
 #pragma unroll
@@ -608,7 +628,7 @@ void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = 256;
-  static_assert(EPI != EPI_LOGITS || 256 / 4 == kLogitsPartCols, "partial width");
+  static_assert((EPI != EPI_LOGITS && EPI != EPI_LOSS) || 256 / 4 == kLogitsPartCols, "partial width");
   const int tm = (g.M + BM - 1) / BM;
   const int t256 = tm * ((g.N + 255) / 256);
   if constexpr (EPI == EPI_RESID) {
@@ -632,6 +652,7 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
     case EPI_RELU2_BF16: launch_big<EPI_RELU2_BF16>(g, s); break;
     case EPI_RESID: launch_big<EPI_RESID>(g, s); break;
     case EPI_LOGITS: launch_big<EPI_LOGITS>(g, s); break;
+    case EPI_LOSS: launch_big<EPI_LOSS>(g, s); break;
     case EPI_QKV: launch_big<EPI_QKV>(g, s); break;
     default: launch_big<EPI_F32>(g, s); break;
   }

@@ -50,6 +50,17 @@ void launch_softmax_lse(const float *logits, int rows, int V, float *lse, float 
 // lse[r] from the LM-head epilogue's per-block partials; then optional probs.
 void launch_lse_combine(const float *part, int nparts, int rows, float *lse, const float *logits,
                         int V, float *probs, hipStream_t s);
+// Next-token cross-entropy per row, loss[r] = lse[r] - logit of targets[r]
+// (0 for a target outside [0, V)).  From the EPI_LOSS partials and target
+// logits (part, tgt), lse optional:
+void launch_ce_from_parts(const float *part, int nparts, const float *tgt, const int *targets, int V,
+                          int rows, float *loss, float *lse, hipStream_t s);
+// ... or from materialised logits and their lse:
+void launch_ce_from_logits(const float *logits, const float *lse, const int *targets, int V, int rows,
+                           float *loss, hipStream_t s);
+// mean[0] = sum of loss[r] over rows with a target in [0, V) / their number
+// (0 if none), summed in a fixed order by one workgroup.
+void launch_mean_loss(const float *loss, const int *targets, int V, int rows, float *mean, hipStream_t s);
 // scratch: argmax_scratch_floats(rows, V) floats of device memory
 // lens (optional): decode lengths, incremented once the token is chosen
 void launch_argmax(const float *logits, int rows, int V, int *out, float *scratch, int *lens,
@@ -71,7 +82,8 @@ enum Epi {
   EPI_F32 = 3,
   EPI_RELU_F32 = 4,
   EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each kLogitsPartCols columns
-  EPI_QKV = 6      // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
+  EPI_QKV = 6,     // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
+  EPI_LOSS = 7     // EPI_LOGITS' partials and each row's target logit; C is not written
 };
 
 // Extra operands of the EPI_QKV epilogue (column block = one 128-wide head).
@@ -99,7 +111,9 @@ struct GemmArgs {
   void *C;
   long long ldc;
   int epi;
-  float *part;  // EPI_LOGITS: [M][N/kLogitsPartCols][2] partial (max, sum exp)
+  float *part;  // EPI_LOGITS, EPI_LOSS: [M][N/kLogitsPartCols][2] partial (max, sum exp)
+  const int *targets;  // EPI_LOSS: [M] target column of each row (any value)
+  float *tgt;          // EPI_LOSS: [M] C[m][targets[m]], written where targets[m] is in [0, N)
   QkvEpi qkv;   // EPI_QKV
 };
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M

@@ -378,6 +378,90 @@ void launch_lse_combine(const float *part, int nparts, int rows, float *lse, con
   if (probs) probs_kernel<<<rows, 256, 0, s>>>(logits, lse, V, probs);
 }
 
+// ---------------------------------------------------------------- cross-entropy
+// Next-token cross-entropy of row r: lse[r] - logit[r][t], t = targets[r];
+// a target outside [0, V) marks a row with no next token (loss 0).
+
+// From the LM-head loss epilogue: one wave per row merges the row's (max,
+// sum exp) partials as lse_combine_kernel does and subtracts the target
+// logit the epilogue kept.
+__global__ __launch_bounds__(256) void ce_parts_kernel(const float *part, int nparts, const float *tgt,
+                                                       const int *targets, int V, int rows, float *loss,
+                                                       float *lse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const float2 *pp = (const float2 *)part + (long long)r * nparts;
+  float m = -INFINITY, s = 0.f;
+  for (int i = lane; i < nparts; i += 64) {
+    float2 v = pp[i];
+    ms_merge(m, s, v.x, v.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    const float l = m + logf(s);
+    const int t = targets[r];
+    loss[r] = (t >= 0 && t < V) ? l - tgt[r] : 0.f;
+    if (lse) lse[r] = l;
+  }
+}
+
+__global__ __launch_bounds__(256) void ce_logits_kernel(const float *logits, const float *lse,
+                                                        const int *targets, int V, int rows, float *loss) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int t = targets[r];
+  loss[r] = (t >= 0 && t < V) ? lse[r] - logits[(long long)r * V + t] : 0.f;
+}
+
+// One workgroup: thread i sums rows i, i + 1024, ... in fp64, then a fixed
+// tree over the threads, so the mean does not depend on scheduling.
+__global__ __launch_bounds__(1024) void mean_loss_kernel(const float *loss, const int *targets, int V,
+                                                         int rows, float *mean) {
+  __shared__ double ssum[1024];
+  __shared__ int scnt[1024];
+  double acc = 0.0;
+  int cnt = 0;
+  for (int r = threadIdx.x; r < rows; r += 1024) {
+    const int t = targets[r];
+    if (t >= 0 && t < V) {
+      acc += (double)loss[r];
+      ++cnt;
+    }
+  }
+  ssum[threadIdx.x] = acc;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + w];
+      scnt[threadIdx.x] += scnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mean[0] = scnt[0] ? (float)(ssum[0] / scnt[0]) : 0.f;
+}
+
+void launch_ce_from_parts(const float *part, int nparts, const float *tgt, const int *targets, int V,
+                          int rows, float *loss, float *lse, hipStream_t s) {
+  if (rows <= 0) return;
+  ce_parts_kernel<<<(rows + 3) / 4, 256, 0, s>>>(part, nparts, tgt, targets, V, rows, loss, lse);
+}
+
+void launch_ce_from_logits(const float *logits, const float *lse, const int *targets, int V, int rows,
+                           float *loss, hipStream_t s) {
+  if (rows <= 0) return;
+  ce_logits_kernel<<<(rows + 255) / 256, 256, 0, s>>>(logits, lse, targets, V, rows, loss);
+}
+
+void launch_mean_loss(const float *loss, const int *targets, int V, int rows, float *mean, hipStream_t s) {
+  mean_loss_kernel<<<1, 1024, 0, s>>>(loss, targets, V, rows, mean);
+}
+
 // ---------------------------------------------------------------- greedy
 // Argmax per row; among equal maxima the lowest index wins.  Two phases so
 // that a few rows still spread over many CUs: phase 1 reduces chunks of

@@ -189,6 +189,36 @@ gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *r
                        gpt_stream_t stream);
 
 /*
+ * gpt_prefill_loss -- next-token cross-entropy of packed prompts, without
+ * materialising the logits.  [microgpt "Training process", item 2]: the
+ * forward pass predicts each next token and the loss is the cross-entropy
+ * between that prediction and the real token (how surprised the model is).
+ * The forward is gpt_prefill's over every position; then, for row r with
+ * t = targets[r] in [0, vocab):
+ *   loss[r] = log sum_v exp(logits[r][v]) - logits[r][t]
+ * A target outside [0, vocab) (e.g. -1 at a sequence's last position, which
+ * has no next token) gives loss 0, and the row is left out of the mean.
+ *   targets     device int32 [total], packed like tokens
+ *   loss        device fp32 [total] (required)
+ *   lse         device fp32 [total] or NULL
+ *   mean        device fp32 [1] or NULL: the sum of the counted rows' losses
+ *               over their number (0 if no row counts), summed in a fixed
+ *               order so repeated calls agree bit for bit
+ *   kv, tokens, cu_seqlens, rope tables, workspace: as gpt_prefill (the same
+ *               gpt_workspace_bytes covers both calls)
+ * bf16 models with more than 64 rows run the LM head with an epilogue that
+ * keeps, per row, a (max, sum exp) pair for each 64 vocabulary columns and the
+ * target's logit; the fp32 logits never reach device memory.  fp32 models and
+ * prefills of at most 64 rows write the logits into the workspace first.
+ * Errors: as gpt_prefill.
+ */
+gpt_status gpt_prefill_loss(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                            const float *rope_sin, const int32_t *tokens, const int32_t *targets,
+                            const int32_t *cu_seqlens, int32_t n_seqs, gpt_kv_cache *kv,
+                            float *loss, float *lse, float *mean, void *workspace,
+                            size_t workspace_bytes, gpt_stream_t stream);
+
+/*
  * gpt_decode_step -- one KV-cache decode step for every sequence of `kv`
  * ([nanochat-csdn] Engine with KV cache, prefill and decode; [microgpt
  * "Inference"] feed the previous token back).  Sequence s embeds

@@ -62,11 +62,32 @@ def _within_floor(st, fl):
     assert st["disagree_explained"], st
 
 
+def _loss_full(dm, w, targets):
+    t = torch()
+    M = int(w.cu_seqlens[-1])
+    loss = t.empty(M, dtype=t.float32, device="cuda")
+    mean = t.empty(1, dtype=t.float32, device="cuda")
+    dm.prefill_loss(t.from_numpy(w.tokens).cuda(), t.from_numpy(targets).cuda(), w.cu_seqlens, loss,
+                    None, mean)
+    t.cuda.synchronize()
+    return loss, float(mean.cpu().numpy()[0])
+
+
 def test_d12_prefill_full_batch(d12):
-    """8 x 2048 depth-12 prefill, all rows + LSE; sequences 0 and 7 checked."""
+    """8 x 2048 depth-12 prefill, all rows + LSE; sequences 0 and 7 checked.
+    The fused cross-entropy of the same batch matches lse - logit[target] of
+    these logits on every row, and the oracle's losses on the checked ones."""
+    t = torch()
     W, dm = d12
     w = wl.d12_prefill()
     logits, lse = _prefill_full(dm, w)
+    tg = w.next_token_targets()
+    loss, mean = _loss_full(dm, w, tg)
+    ok = t.from_numpy(tg >= 0).cuda()
+    tgd = t.from_numpy(np.maximum(tg, 0).astype(np.int64)).cuda()
+    own = t.where(ok, lse - logits.gather(1, tgd[:, None])[:, 0], t.zeros_like(lse))
+    assert float((loss - own).abs().max()) <= 2e-6
+    assert abs(mean - float(own[ok].double().mean())) <= 1e-5
     cu = w.cu_seqlens
     for b in (0, 7):
         g = logits[cu[b]:cu[b + 1]].cpu().numpy()
@@ -76,6 +97,8 @@ def test_d12_prefill_full_batch(d12):
         print("d12 prefill seq", b, st)
         assert st["max_abs"] <= 3e-2  # literal bar holds at depth 12
         assert st["disagree_explained"]
+        rl = oracle.token_losses(ref[0], tg[cu[b]:cu[b + 1]])
+        assert float(np.max(np.abs(loss[cu[b]:cu[b + 1]].cpu().numpy() - rl))) <= 3e-2
         np.testing.assert_allclose(gl, oracle.logsumexp(g.astype(np.float64)), atol=3e-5)
         if b == 0:
             flo, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[b],

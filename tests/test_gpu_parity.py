@@ -131,6 +131,68 @@ def test_small_bf16_prefill_last_rows_and_cache():
     kv.close()
 
 
+# ---------------------------------------------------------------- next-token cross-entropy
+
+def gpu_loss(dm, tokens, seqlens, targets):
+    t = torch()
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    M = int(cu[-1])
+    loss = t.full((M,), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.empty(M, dtype=t.float32, device="cuda")
+    mean = t.empty(1, dtype=t.float32, device="cuda")
+    dm.prefill_loss(to_dev(np.asarray(tokens, np.int32)), to_dev(np.asarray(targets, np.int32)), cu,
+                    loss, lse, mean)
+    t.cuda.synchronize()
+    return loss.cpu().numpy(), lse.cpu().numpy(), float(mean.cpu().numpy()[0])
+
+
+def test_tiny_loss_fp32():
+    """Per-row losses, lse and the mean of the tiny model against the oracle,
+    with each sequence's last row (no next token) left out."""
+    w = wl.tiny_workload()
+    W, dm = device_model(w.model)
+    tg = w.next_token_targets()
+    loss, lse, mean = gpu_loss(dm, w.tokens, w.seqlens, tg)
+    ref = np.concatenate(oracle.prefill(w.model, W, w.tokens, w.seqlens)[0])
+    rl = oracle.token_losses(ref, tg)
+    assert np.max(np.abs(loss - rl)) <= 1e-4
+    assert (loss[tg < 0] == 0).all()
+    np.testing.assert_allclose(lse, oracle.logsumexp(ref), atol=1e-4)
+    assert abs(mean - oracle.mean_loss(rl, tg, w.model.vocab)) <= 1e-4
+
+
+@pytest.mark.parametrize("n_layer,n_head,lens", [(2, 2, [300, 173, 64, 1]), (1, 1, [40, 9]),
+                                                (2, 6, [513, 70])])
+def test_small_bf16_loss(n_layer, n_head, lens):
+    """bf16: losses within the logit bar of the oracle's, and equal to
+    lse - logit[target] of the same prefill's materialised logits (the fused
+    epilogue keeps the very accumulators the logits path stores).  Rows with
+    a target of -1, -5 or vocab are skipped; 49 rows take the unfused path."""
+    cfg = wl.small_model(n_layer, n_head, vocab=4096)
+    w = wl.ragged_prefill(cfg, lens, seed=n_layer + 3 * n_head)
+    W, dm = device_model(cfg)
+    tg = w.next_token_targets()
+    tg[3] = cfg.vocab
+    tg[5] = -5
+    loss, lse, mean = gpu_loss(dm, w.tokens, w.seqlens, tg)
+    ok = (tg >= 0) & (tg < cfg.vocab)
+    assert (loss[~ok] == 0).all()
+    ref = np.concatenate(oracle.prefill(cfg, W, w.tokens, w.seqlens)[0])
+    rl = oracle.token_losses(ref, tg)
+    d = np.abs(loss - rl)
+    print("loss max |diff|", float(d.max()), "std", float(np.std(loss[ok] - rl[ok])))
+    assert d.max() <= 3e-2
+    logits, lse2 = gpu_prefill(dm, w.tokens, w.seqlens)
+    np.testing.assert_array_equal(lse, lse2)
+    rows = np.nonzero(ok)[0]
+    own = lse2[rows].astype(np.float64) - logits[rows, tg[rows]]
+    np.testing.assert_allclose(loss[rows], own, rtol=0, atol=2e-6)
+    assert abs(mean - float(np.mean(loss[rows].astype(np.float64)))) <= 1e-6
+    # no counted row: the mean is 0
+    _, _, m0 = gpu_loss(dm, w.tokens, w.seqlens, np.full_like(tg, -1))
+    assert m0 == 0.0
+
+
 @pytest.mark.parametrize("temperature", [0.0, 0.7])
 def test_small_bf16_decode_teacher_forced(temperature):
     """Prefill ragged prompts into the paged cache, decode 40 steps crossing
