@@ -18,7 +18,7 @@ __all__ = [
     "READINGS", "rmsnorm", "rope_angles", "rope_tables", "apply_rope",
     "relu", "relu2", "softmax", "logsumexp", "causal_attention", "KVCache",
     "embed", "block", "final_logits", "forward", "prefill", "decode_step",
-    "greedy", "sample", "cross_entropy", "token_losses", "mean_loss", "param_count",
+    "greedy", "sample", "cross_entropy", "token_losses", "mean_loss", "adam_step", "param_count",
     "round_bf16",
     "run_serving",
 ]
@@ -367,6 +367,23 @@ def mean_loss(losses: np.ndarray, targets: np.ndarray, vocab: int) -> float:
     t = np.asarray(targets, np.int64)
     ok = (t >= 0) & (t < vocab)
     return float(np.mean(np.asarray(losses, np.float64)[ok])) if ok.any() else 0.0
+
+
+def adam_step(param: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray, step: int,
+              lr: float, beta1: float, beta2: float, eps: float):
+    """One Adam update (Microgpt, "Training process", item 4): running means
+    of the gradient (momentum) and of its square (a per-parameter step
+    size), each divided by its start-up bias ``1 - beta**step``, in float64.
+
+    Returns ``(param, m, v)`` after the step; the inputs are not modified.
+    """
+    p = np.asarray(param, np.float64)
+    g = np.asarray(grad, np.float64)
+    m1 = beta1 * np.asarray(m, np.float64) + (1.0 - beta1) * g
+    v1 = beta2 * np.asarray(v, np.float64) + (1.0 - beta2) * g * g
+    mhat = m1 / (1.0 - beta1 ** step)
+    vhat = v1 / (1.0 - beta2 ** step)
+    return p - lr * mhat / (np.sqrt(vhat) + eps), m1, v1
 
 
 def param_count(W) -> int:

@@ -149,6 +149,49 @@ def test_init_token_loss_near_3_3():
     assert abs(m - g["value"]) <= g["tol"]
 
 
+# ---------------------------------------------------------------- Adam
+
+def test_adam_first_step_moves_by_lr_times_sign():
+    """From zero moments the bias-corrected means are g and g^2, so the
+    first step is lr * g / (|g| + eps): about lr against the gradient."""
+    rng = np.random.default_rng(21)
+    p = rng.normal(size=50)
+    g = rng.normal(size=50) * 10.0 ** rng.uniform(-3, 3, 50)
+    z = np.zeros(50)
+    lr, eps = 0.01, 1e-8
+    p1, m1, v1 = oracle.adam_step(p, g, z, z, 1, lr, 0.85, 0.99, eps)
+    np.testing.assert_allclose(p1, p - lr * g / (np.abs(g) + eps), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(m1, 0.15 * g, rtol=1e-14)  # 1 - 0.85 is not exactly 0.15 in float64
+    np.testing.assert_allclose(v1, 0.01 * g * g, rtol=1e-14)
+
+
+def test_adam_constant_gradient_has_exact_bias_correction():
+    """With a constant gradient the corrected means stay exactly g and g^2,
+    so every step moves the parameter by the same lr * g / (|g| + eps)."""
+    g = np.array([0.3, -2.0, 1e-4, 7.0])
+    p = np.array([1.0, -1.0, 0.5, 0.0])
+    m = np.zeros(4)
+    v = np.zeros(4)
+    lr, eps = 1e-3, 1e-8
+    for t in range(1, 40):
+        p, m, v = oracle.adam_step(p, g, m, v, t, lr, 0.9, 0.999, eps)
+        np.testing.assert_allclose(m / (1 - 0.9 ** t), g, rtol=1e-12)
+        np.testing.assert_allclose(v / (1 - 0.999 ** t), g * g, rtol=1e-12)
+    np.testing.assert_allclose(p, np.array([1.0, -1.0, 0.5, 0.0]) - 39 * lr * g / (np.abs(g) + eps),
+                               rtol=0, atol=1e-12)
+
+
+def test_adam_is_invariant_to_gradient_scale_and_still_at_zero():
+    rng = np.random.default_rng(22)
+    p, g = rng.normal(size=20), rng.normal(size=20)
+    m, v = rng.normal(size=20) * 0.1, rng.uniform(0.0, 1.0, 20)
+    a = oracle.adam_step(p, g, m, v, 5, 0.02, 0.9, 0.95, 0.0)
+    b = oracle.adam_step(p, 1000.0 * g, 1000.0 * m, 1e6 * v, 5, 0.02, 0.9, 0.95, 0.0)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-13)
+    z = np.zeros(20)
+    np.testing.assert_array_equal(oracle.adam_step(p, z, z, z, 3, 0.1, 0.9, 0.99, 1e-8)[0], p)
+
+
 # ---------------------------------------------------------------- softmax
 
 def test_vocab_softmax_rows_are_distributions():
