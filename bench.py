@@ -86,6 +86,73 @@ def bench_prefill(B, torch, dm, w, steps, warmup, prof_mask=0):
     return dt, dt_prof, logits, lse
 
 
+def bench_prefill_loss(B, torch, dm, w, steps, warmup):
+    """Time `steps` next-token cross-entropy prefills (gpt_prefill_loss: no
+    logits written), then the same again with the LM head timed by events."""
+    n = w.n_seqs
+    cu = w.cu_seqlens
+    M = int(cu[-1])
+    tokens = torch.from_numpy(w.tokens).cuda()
+    targets = torch.from_numpy(w.next_token_targets()).cuda()
+    loss = torch.empty(M, dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = dm.workspace(M, n)
+    B.gpt_profile_enable(0)
+    for _ in range(warmup):
+        dm.prefill_loss(tokens, targets, cu, loss, None, mean, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dm.prefill_loss(tokens, targets, cu, loss, None, mean, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    B.gpt_profile_enable(1 << B.PROF_CLASSES["lmhead"])
+    for _ in range(steps):
+        dm.prefill_loss(tokens, targets, cu, loss, None, mean, workspace=ws)
+    torch.cuda.synchronize()
+    lm = prof_read(B, ["lmhead"])
+    B.gpt_profile_enable(0)
+    return dt, lm, float(mean.cpu().numpy()[0])
+
+
+def bench_adam(B, torch, n, steps, warmup=2):
+    """Adam over n fp32 parameters with the bf16 copy: `steps` updates timed
+    end to end, then again with the kernel timed by events."""
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    p = torch.randn(n, device="cuda", generator=gen)
+    g = torch.randn(n, device="cuda", generator=gen)
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    B.gpt_profile_enable(0)
+    k = 0
+    for _ in range(warmup):
+        k += 1
+        B.gpt_adam_step(p, g, m, v, pb, n, k, 1e-3, 0.9, 0.95, 1e-8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        k += 1
+        B.gpt_adam_step(p, g, m, v, pb, n, k, 1e-3, 0.9, 0.95, 1e-8)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    B.gpt_profile_enable(1 << B.PROF_CLASSES["optim"])
+    for _ in range(steps):
+        k += 1
+        B.gpt_adam_step(p, g, m, v, pb, n, k, 1e-3, 0.9, 0.95, 1e-8)
+    torch.cuda.synchronize()
+    r = prof_read(B, ["optim"])
+    B.gpt_profile_enable(0)
+    del p, g, m, v, pb
+    torch.cuda.empty_cache()
+    kern_gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+    return {"workload": "adam_d12_params", "params": n, "steps": steps,
+            "ms_per_step": round(dt / steps * 1e3, 4),
+            "bytes_per_param": 30,
+            "kernel": {"us_per_launch": round(r["ms"] * 1e3 / max(r["launches"], 1), 1),
+                       "achieved_gbs": round(kern_gbs, 1), "frac": round(kern_gbs / PEAK_HBM_GBS, 4)}}
+
+
 def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     """Prefill the prompts into a fresh cache, pick the first token, then time
     `steps` decode steps (selection included).  A second identical pass with
@@ -338,6 +405,26 @@ def main():
     g0 = logits.cpu().numpy() if not args.skip_cpu else None
     del logits, lse
     torch.cuda.empty_cache()
+
+    # ---------------- depth-12 prefill ending in the next-token loss (no logits written)
+    log("timing depth-12 prefill with the fused cross-entropy")
+    dtl, lml, mean_loss = bench_prefill_loss(B, torch, dm12, w2, args.steps, args.warmup)
+    lml_tfs = lml["flops"] / (lml["ms"] * 1e-3) / 1e12
+    out["d12_prefill_loss"] = {"workload": "d12_prefill_loss", "batch": 8, "seq_len": 2048,
+                               "tokens_per_s": round(args.steps * M / dtl, 1),
+                               "ms_per_step": round(dtl / args.steps * 1e3, 3),
+                               "lm_head_loss_epilogue": {"us_per_launch": round(lml["ms"] * 1e3 / max(lml["launches"], 1), 1),
+                                                         "achieved_tflops": round(lml_tfs, 1),
+                                                         "frac": round(lml_tfs / PEAK_BF16_TFLOPS, 4)},
+                               "mean_loss": round(mean_loss, 4)}
+    log(f"d12 prefill + loss: {out['d12_prefill_loss']['tokens_per_s']:,.0f} tok/s, "
+        f"LM head {lml_tfs:.0f} TFLOP/s, mean loss {mean_loss:.4f}")
+
+    # ---------------- Adam over every depth-12 parameter (fp32 master copy + bf16 copy)
+    n12 = sum(int(np.prod(sh)) for _, sh in wl.weight_shapes(w2.model))
+    log("timing the Adam update over the depth-12 parameters")
+    out["adam"] = bench_adam(B, torch, n12, args.steps)
+    log(f"adam: {out['adam']['kernel']['achieved_gbs']:,.0f} GB/s")
 
     # ---------------- depth-12 decode
     if not args.skip_decode:

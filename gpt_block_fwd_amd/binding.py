@@ -22,13 +22,13 @@ STATUS_NAMES = {0: "GPT_OK", 1: "GPT_ERR_ARG", 2: "GPT_ERR_CAPACITY", 3: "GPT_ER
                 4: "GPT_ERR_HIP"}
 
 PROF_CLASSES = {"gemm": 0, "lmhead": 1, "attn": 2, "decode_attn": 3, "skinny": 4, "norm": 5,
-                "softmax": 6}
+                "softmax": 6, "optim": 7}
 
 #: every entry point declared by include/gpt.h and include/gpt_profile.h
 EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
            "gpt_decode_step",
-           "gpt_select_tokens", "gpt_profile_enable", "gpt_profile_read",
+           "gpt_select_tokens", "gpt_adam_step", "gpt_profile_enable", "gpt_profile_read",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
     L.gpt_decode_step.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, f32, vp, vp,
                                   vp, vp, sz, vp]
     L.gpt_select_tokens.argtypes = [vp, i32, i32, f32, vp, vp, vp]
+    L.gpt_adam_step.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int64, i32, f32, f32, f32, f32, vp]
     L.gpt_profile_enable.argtypes = [ctypes.c_uint32]
     L.gpt_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
@@ -195,6 +196,12 @@ def gpt_select_tokens(logits, rows: int, vocab: int, temperature: float, uniform
                       stream=None):
     _check(lib().gpt_select_tokens(_ptr(logits), rows, vocab, temperature, _ptr(uniforms),
                                    _ptr(tokens_out), _stream(stream)))
+
+
+def gpt_adam_step(param, grad, m, v, param_bf16, n: int, step: int, lr: float, beta1: float,
+                  beta2: float, eps: float, stream=None):
+    _check(lib().gpt_adam_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), _ptr(param_bf16), n, step,
+                               lr, beta1, beta2, eps, _stream(stream)))
 
 
 def gpt_profile_enable(mask: int):

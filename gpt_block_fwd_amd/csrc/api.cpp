@@ -823,6 +823,38 @@ gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, f
   return hip_check("gpt_select_tokens launch");
 }
 
+gpt_status gpt_adam_step(float *param, const float *grad, float *m, float *v, void *param_bf16, int64_t n,
+                         int32_t step, float lr, float beta1, float beta2, float eps, gpt_stream_t stream) {
+  if (!param || !grad || !m || !v) return fail(GPT_ERR_ARG, "NULL required pointer");
+  if (n < 0) return fail(GPT_ERR_ARG, "n must be >= 0");
+  if (step < 1) return fail(GPT_ERR_ARG, "step must be >= 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+    return fail(GPT_ERR_ARG, "betas must lie in [0, 1)");
+  if (!(eps >= 0.f)) return fail(GPT_ERR_ARG, "eps must be >= 0");
+  if (!std::isfinite(lr)) return fail(GPT_ERR_ARG, "lr must be finite");
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
+    return fail(GPT_ERR_ARG, "param, grad, m, v must be 16-byte aligned");
+  if (param_bf16 && (reinterpret_cast<uintptr_t>(param_bf16) & 7))
+    return fail(GPT_ERR_ARG, "param_bf16 must be 8-byte aligned");
+  if (n == 0) return GPT_OK;
+  AdamHyper h;
+  h.lr = lr;
+  h.beta1 = beta1;
+  h.beta2 = beta2;
+  h.one_minus_beta1 = (float)(1.0 - (double)beta1);
+  h.one_minus_beta2 = (float)(1.0 - (double)beta2);
+  h.eps = eps;
+  h.corr1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
+  h.corr2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();
+  {
+    Timed t(GPT_PROF_OPTIM, s, 0, (double)n * (28 + (param_bf16 ? 2 : 0)));
+    launch_adam(param, grad, m, v, (bf16 *)param_bf16, (long long)n, h, s);
+  }
+  return hip_check("gpt_adam_step launch");
+}
+
 gpt_status gpt_debug_gemm(const void *A, const void *W, int32_t M, int32_t N, int32_t K, void *C,
                           int32_t epi, int32_t ksplit, gpt_stream_t stream) {
   if (!A || !W || !C) return fail(GPT_ERR_ARG, "NULL pointer");

@@ -74,6 +74,16 @@ void launch_lens_inc(int *lens, int n, hipStream_t s);
 void launch_gather_rows_bf16(const bf16 *src, bf16 *dst, const int *rows, int n, int d,
                              hipStream_t s);
 
+// ------------------------------------------------------------ Adam
+// m = beta1 m + (1 - beta1) g; v = beta2 v + (1 - beta2) g^2;
+// p -= lr (m corr1) / (sqrt(v corr2) + eps), corr = 1 / (1 - beta^step).
+struct AdamHyper {
+  float lr, beta1, one_minus_beta1, beta2, one_minus_beta2, eps, corr1, corr2;
+};
+// p, g, m, v: fp32 [n], 16-byte aligned; pb (nullable): bf16 [n], 8-byte aligned
+void launch_adam(float *p, const float *g, float *m, float *v, bf16 *pb, long long n, const AdamHyper &h,
+                 hipStream_t s);
+
 // ------------------------------------------------------------ GEMMs
 enum Epi {
   EPI_BF16 = 0,

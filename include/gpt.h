@@ -254,6 +254,32 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
 gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, float temperature,
                              const float *uniforms, int32_t *tokens_out, gpt_stream_t stream);
 
+/*
+ * gpt_adam_step -- one Adam update of n fp32 parameters, in place.
+ * [microgpt "Training process", item 4]: Adam keeps, per parameter, a
+ * running mean of the gradient (momentum) and of its square (which scales
+ * the step size), and moves the parameter by their ratio.  With
+ * t = step >= 1:
+ *   m = beta1 m + (1 - beta1) g
+ *   v = beta2 v + (1 - beta2) g^2
+ *   p = p - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * in fp32 (the bias corrections 1 / (1 - beta^t) are formed in fp64 on the
+ * host and rounded once).  No weight decay.
+ *   param, m, v  device fp32 [n], read and written; m and v start at 0
+ *   grad         device fp32 [n]
+ *   param_bf16   device bf16 [n] or NULL: receives the updated parameters
+ *                rounded to bf16 (nearest even), the dtype the bf16 forward
+ *                reads its weights in
+ * param, grad, m, v must be 16-byte aligned and param_bf16 8-byte aligned;
+ * the arrays must not overlap.  n == 0 enqueues nothing.
+ * Errors: GPT_ERR_ARG for a NULL array, misalignment, n < 0, step < 1,
+ * beta outside [0, 1), a negative or NaN eps, a non-finite lr;
+ * GPT_ERR_HIP if the launch fails.
+ */
+gpt_status gpt_adam_step(float *param, const float *grad, float *m, float *v, void *param_bf16,
+                         int64_t n, int32_t step, float lr, float beta1, float beta2, float eps,
+                         gpt_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ typedef enum {
   GPT_PROF_SKINNY = 4,      /* decode block GEMMs (M = sequences) */
   GPT_PROF_NORM = 5,        /* RMSNorm, RoPE/QK-norm scatter, embedding */
   GPT_PROF_SOFTMAX = 6,     /* vocabulary softmax / LSE and token selection */
-  GPT_PROF_NCLASSES = 7
+  GPT_PROF_OPTIM = 7,       /* optimiser update (Adam) */
+  GPT_PROF_NCLASSES = 8
 } gpt_prof_class;
 
 /* Enable timing for the classes whose bit (1 << class) is set in mask; 0

@@ -110,6 +110,41 @@ def test_prefill_validation_runs_before_device_work():
     _bad(lambda: call(cu=np.array([0, 5000, 5001], np.int32)), B.GPT_ERR_ARG)  # > max_seq
 
 
+def test_prefill_loss_validation():
+    m = wl.small_model(2, 2, vocab=256)
+    cfg = B.make_config(m)
+    w, keep = _weights_struct()
+    cu = np.array([0, 5, 9], np.int32)
+    ws = B.gpt_workspace_bytes(cfg, 9, 2)
+
+    def call(targets=0x5000, loss=0x6000, cu=cu):
+        B.gpt_prefill_loss(cfg, w, 0x4000, 0x4000, 0x3000, targets, cu, 2, None, loss, None, None,
+                           0x100000, ws, 0)
+
+    _bad(lambda: call(targets=None), B.GPT_ERR_ARG)
+    _bad(lambda: call(loss=None), B.GPT_ERR_ARG)
+    _bad(lambda: call(cu=np.array([0, 5, 4], np.int32)), B.GPT_ERR_ARG)
+
+
+def test_adam_validation():
+    def call(p=0x1000, g=0x2000, m=0x3000, v=0x4000, pb=None, n=100, step=1, lr=1e-3, b1=0.9,
+             b2=0.999, eps=1e-8):
+        B.gpt_adam_step(p, g, m, v, pb, n, step, lr, b1, b2, eps, 0)
+
+    _bad(lambda: call(p=None), B.GPT_ERR_ARG)
+    _bad(lambda: call(v=None), B.GPT_ERR_ARG)
+    _bad(lambda: call(g=0x2004), B.GPT_ERR_ARG)
+    _bad(lambda: call(pb=0x5002), B.GPT_ERR_ARG)
+    _bad(lambda: call(n=-1), B.GPT_ERR_ARG)
+    _bad(lambda: call(step=0), B.GPT_ERR_ARG)
+    _bad(lambda: call(b1=1.0), B.GPT_ERR_ARG)
+    _bad(lambda: call(b2=-0.1), B.GPT_ERR_ARG)
+    _bad(lambda: call(eps=-1.0), B.GPT_ERR_ARG)
+    _bad(lambda: call(eps=float("nan")), B.GPT_ERR_ARG)
+    _bad(lambda: call(lr=float("inf")), B.GPT_ERR_ARG)
+    call(n=0)  # nothing to do: no device work, no error
+
+
 def test_misaligned_weights_rejected():
     m = wl.small_model(2, 2, vocab=256)
     cfg = B.make_config(m)

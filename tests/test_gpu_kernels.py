@@ -143,3 +143,34 @@ def test_prefill_attention_matches_oracle(lens, H, qk_norm):
                                       v[s].astype(np.float64), 0)
         # error budget: P rounded to bf16 (2^-9 relative) and the bf16 output
         np.testing.assert_allclose(got[s], ref, atol=1.5e-2, rtol=1e-2)
+
+
+# ---------------------------------------------------------------- Adam
+
+@pytest.mark.parametrize("n,copy", [(1, True), (3, False), (4, True), (1_000_003, True), (4096, False)])
+def test_adam_matches_oracle(n, copy):
+    """Three chained Adam steps against the float64 oracle; the bf16 copy is
+    the nearest-even rounding of the updated fp32 parameters."""
+    t = torch()
+    rng = np.random.default_rng(n)
+    p = rng.normal(size=n).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    dp, dm_, dv = (t.from_numpy(a.copy()).cuda() for a in (p, m, v))
+    pb = t.empty(n, dtype=t.bfloat16, device="cuda") if copy else None
+    lr, b1, b2, eps = 2e-3, 0.85, 0.99, 1e-8
+    rp, rm, rv = p.astype(np.float64), m.astype(np.float64), v.astype(np.float64)
+    sm = np.zeros(n)  # the same running mean over |g|: the scale of m's terms where they cancel
+    for step in (1, 2, 3):
+        g = (rng.normal(size=n) * 10.0 ** rng.uniform(-4, 1, n)).astype(np.float32)
+        B.gpt_adam_step(dp, t.from_numpy(g).cuda(), dm_, dv, pb, n, step, lr, b1, b2, eps)
+        rp, rm, rv = oracle.adam_step(rp, g, rm, rv, step, lr, b1, b2, eps)
+        sm = b1 * sm + (1 - b1) * np.abs(g.astype(np.float64))
+    t.cuda.synchronize()
+    gp, gm, gv = (a.cpu().numpy().astype(np.float64) for a in (dp, dm_, dv))
+    assert np.all(np.abs(gm - rm) <= 2e-6 * sm)
+    np.testing.assert_allclose(gv, rv, rtol=2e-6, atol=1e-30)  # positive terms: no cancellation
+    # fp32 storage of p: a few ulps of p plus a relative error of the step
+    np.testing.assert_allclose(gp, rp, rtol=0, atol=float(np.max(4 * np.spacing(np.abs(rp).astype(np.float32)))) + 1e-5 * lr)
+    if copy:
+        np.testing.assert_array_equal(pb.float().cpu().numpy(), oracle.round_bf16(gp).astype(np.float32))
