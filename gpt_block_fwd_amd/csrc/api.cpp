@@ -37,7 +37,7 @@ gpt_status hip_check(const char *what) {
 }
 
 constexpr int kMaxPrefillSeqs = 512;
-constexpr int kCounters = 4096;  // decode-attention chunk counters (one per sequence)
+constexpr int kCounters = 4096;  // decode-attention chunk counters (one per sequence and K/V head)
 constexpr int kPage = 64;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -111,7 +111,6 @@ gpt_status check_config(const gpt_config *c) {
   if (c->pos_kind == GPT_POS_ROPE && (c->head_dim & 1)) return fail(GPT_ERR_ARG, "RoPE needs an even head_dim");
   if (c->dtype == GPT_DTYPE_BF16) {
     if (c->head_dim != 128) return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs head_dim 128");
-    if (c->n_kv_head != 1) return fail(GPT_ERR_UNSUPPORTED, "bf16 path implements one K/V head (MQA)");
     if (c->n_head > 16) return fail(GPT_ERR_UNSUPPORTED, "bf16 path supports at most 16 query heads");
     if (c->pos_kind != GPT_POS_ROPE) return fail(GPT_ERR_UNSUPPORTED, "bf16 path uses rotary positions");
     if (c->act != GPT_ACT_RELU2) return fail(GPT_ERR_UNSUPPORTED, "bf16 path uses the ReLU^2 MLP");
@@ -535,11 +534,12 @@ gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *
         aa.cu = bf.cu;
         aa.cu_pad = bf.cu_pad;
         aa.H = H;
+        aa.Hkv = Hkv;
         aa.qk_norm = c->qk_norm;
         int max_len = 0;
         for (int b = 0; b < n_seqs; ++b) max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
         aa.n_seqs = n_seqs;
-        aa.max_wg = (max_len * H + kAttnPrefillRows - 1) / kAttnPrefillRows;
+        aa.max_wg = (max_len * (H / Hkv) + kAttnPrefillRows - 1) / kAttnPrefillRows;
         aa.o = (bf16 *)bf.o;
         launch_attn_prefill_bf16(aa, s);
       } else {
@@ -657,7 +657,8 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
       kv->cfg.head_dim != c->head_dim)
     return fail(GPT_ERR_ARG, "kv cache was made for another config");
   const int n = kv->n_seqs;
-  if (n > kCounters) return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences per decode step", kCounters);
+  if ((long long)n * c->n_kv_head > kCounters)
+    return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences x K/V heads per decode step", kCounters);
   for (int b = 0; b < n; ++b)
     if (kv->lens[b] + 1 > kv->capacity)
       return fail(GPT_ERR_CAPACITY, "sequence %d: length %d + 1 exceeds capacity %d", b, kv->lens[b], kv->capacity);
@@ -907,6 +908,7 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
   aa.n_seqs = n_seqs;
   aa.max_wg = (max_len * n_head + kAttnPrefillRows - 1) / kAttnPrefillRows;
   aa.H = n_head;
+  aa.Hkv = 1;
   aa.qk_norm = qk_norm != 0;
   aa.o = (bf16 *)o;
   launch_attn_prefill_bf16(aa, s);

@@ -60,10 +60,13 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
   // blockIdx.y counts row blocks from the last one, so the blocks that see
   // the most keys are dispatched first.
   const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * ROWS;
-  const int H = a.H;
+  // K/V head gk serves the G query heads gk G .. gk G + G - 1; the rows of
+  // this grid plane are (position, head of the group) pairs, r = t G + hg.
+  const int H = a.H, G = a.H / a.Hkv, gk = blockIdx.z;
+  const int kvw = a.Hkv * DH;  // K row width
   const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
   const long long col0 = a.cu_pad[b];
-  const int rows_total = len * H;
+  const int rows_total = len * G;
   if (R0 >= rows_total) return;
   const int Rw = R0 + 32 * RB * wave;
 
@@ -73,15 +76,15 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     int r = min(Rw + 32 * rb + c32, rows_total - 1);
-    prow[rb] = r / H;
-    const bf16 *qp = a.q + ((long long)tok0 * H + r) * DH + 8 * g;
+    prow[rb] = r / G;
+    const bf16 *qp = a.q + ((long long)(tok0 + prow[rb]) * H + gk * G + (r - prow[rb] * G)) * DH + 8 * g;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[rb][s] = *(const bf16x8 *)(qp + 16 * s);
   }
   const int last_row = min(R0 + ROWS - 1, rows_total - 1);
-  const int n_kt = (last_row / H) / KT + 1;
-  const int pw_max = Rw < rows_total ? min(Rw + 32 * RB - 1, rows_total - 1) / H : -1;
-  const int pw_min = Rw / H;
+  const int n_kt = (last_row / G) / KT + 1;
+  const int pw_max = Rw < rows_total ? min(Rw + 32 * RB - 1, rows_total - 1) / G : -1;
+  const int pw_min = Rw / G;
 
   // Direct-to-LDS staging: a tile is 16 KB of K (4 keys x 256 B per wave
   // instruction) and 16 KB of V^T (8 dims x 128 B per instruction); wave w
@@ -96,15 +99,16 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
       const int j = wave + NWV * jj;
       const int key = 4 * j + (lane >> 4), pc = lane & 15;
       const int gkey = min(kt * KT + key, len - 1);
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * DH + ((pc ^ (key & 15)) << 3)),
-                                       LDS_PTR(&sk[j * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          GLOBAL_PTR(a.k + (long long)(tok0 + gkey) * kvw + gk * DH + ((pc ^ (key & 15)) << 3)),
+          LDS_PTR(&sk[j * 512]), 16, 0, 0);
     }
 #pragma unroll
     for (int jj = 0; jj < DJ; ++jj) {
       const int j = wave + NWV * jj;
       const int dim = 8 * j + (lane >> 3), pc = lane & 7;
       __builtin_amdgcn_global_load_lds(
-          GLOBAL_PTR(a.vt + (long long)dim * a.ldvt + col0 + kt * KT + ((pc ^ ((dim >> 1) & 7)) << 3)),
+          GLOBAL_PTR(a.vt + (long long)(gk * DH + dim) * a.ldvt + col0 + kt * KT + ((pc ^ ((dim >> 1) & 7)) << 3)),
           LDS_PTR(&sv[j * 512]), 16, 0, 0);
     }
   };
@@ -273,7 +277,8 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     const int r = Rw + 32 * rb + c32;
     if (r >= rows_total) continue;
     const float inv = 1.0f / lrow[rb];
-    bf16 *op = a.o + ((long long)tok0 * H + r) * DH + 4 * g;
+    const int t = r / G;
+    bf16 *op = a.o + ((long long)(tok0 + t) * H + gk * G + (r - t * G)) * DH + 4 * g;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -303,16 +308,17 @@ DEV int sload(const int *p) {
   return v;
 }
 
-// The query of the new position: every workgroup builds all H heads into
-// LDS (sum of the split-GEMM slabs, RoPE, QK-norm, bf16), head slots spread
+// The query of the new position: every workgroup builds its group's query
+// heads into LDS (sum of the split-GEMM slabs, RoPE, QK-norm, bf16), head slots spread
 // over the half-waves of all its waves.  The chunk holding the new position
 // also builds its k and v, stores them to the cache for later steps, and the
 // wave whose page holds that position patches them into its copy of the page
 // (which it may have read before or after the store).
 //
-// One workgroup per chunk of kDecodePages pages of one sequence; wave w
-// takes page w of the chunk and scores its 64 cached positions for all
-// query heads at once (MQA: one K/V page serves every head).  STAGE: the
+// One workgroup per chunk of kDecodePages pages of one sequence and K/V
+// head (grid z); wave w takes page w of the chunk and scores its 64 cached
+// positions for all query heads that share the K/V head at once (the H / Hkv
+// heads of its group; under MQA every head).  "Heads" below are the group's.  STAGE: the
 // wave first copies its page (K and V^T, 32 KB) into LDS with
 // direct-to-LDS loads that read whole 128-byte lines and takes its MFMA
 // fragments from there; this costs 128 KB of LDS, one workgroup per CU, so
@@ -344,11 +350,14 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   const int b = blockIdx.y, chunk = blockIdx.x;
   const ScatterArgs &in = a.in;
   const PagedKV &kv = in.kv;
+  // K/V head gk and its G query heads hq0 .. hq0 + G - 1
+  const int Hall = in.H, Hkv = in.Hkv, G = Hall / Hkv, gk = blockIdx.z, hq0 = gk * G;
+  const int kvd = Hkv * DH;  // row width of a K page
   const int len = kv.lens[b] + 1;  // positions 0 .. lens[b], the last one new
   const int pn = len - 1;
   const int c0 = chunk * CH;
   if (c0 >= len) return;
-  const int H = in.H;
+  const int H = G;
   const int kpos0 = c0 + wave * 64;
   const int nw = min(NP, (len - c0 + 63) / 64);  // pages of this chunk
   const bool owner = pn < c0 + CH;                // the chunk holds the new position
@@ -360,8 +369,8 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   if (kpos0 < len) {
     const int page = sload(kv.table + b * kv.pages_per_seq + kpos0 / kv.page_size);
     const char *pg = kv.base + (long long)in.layer * kv.layer_stride + (long long)page * kv.page_stride;
-    const bf16 *K = (const bf16 *)pg;
-    const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes);
+    const bf16 *K = (const bf16 *)pg + gk * DH;                      // rows of kvd
+    const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes) + gk * DH * 64;  // [128][64]
     if constexpr (STAGE) {
       // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims
       // x 128 B each; lane i fills slot i of the instruction's kilobyte and
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = 4 * j + (lane >> 4), pc = lane & 15;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * DH + ((pc ^ (key & 15)) << 3)),
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * kvd + ((pc ^ (key & 15)) << 3)),
                                          LDS_PTR(Ks + j * 512), 16, 0, 0);
       }
 #pragma unroll
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * DH + 32 * s + 8 * q4);
+        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * kvd + 32 * s + 8 * q4);
 #pragma unroll
       for (int d = 0; d < 8; ++d)
 #pragma unroll
@@ -395,12 +404,12 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     // lane li of half hw holds dims 4 li .. 4 li + 3 of one slot, so each
     // slab costs one 16-byte load per lane for two slots.  Half-wave
     // hh = 2 wave + hw builds slots hh, hh + 2 NP, ...
-    // Slot j < H: query head j into q_s.  j = H: k, j = H + 1: v of the new
-    // position, into kv_s and the cache.  Query heads and k: half-split
+    // Slot j < H: query head hq0 + j into q_s.  j = H: k, j = H + 1: v of
+    // K/V head gk at the new position, into kv_s and the cache.  Query heads and k: half-split
     // rotation (dim i pairs with i + 64, held by lane li ^ 16), then a
     // weightless RMSNorm over the head.
     const int li = lane & 31, hw = lane >> 5, hh = 2 * wave + hw;
-    const float *u = in.qkv + (long long)b * (H + 2) * DH;
+    const float *u = in.qkv + (long long)b * (Hall + 2 * Hkv) * DH;
     const int st = (int)in.slab;  // slabs of at most 64 rows: far below 2^31 floats
     f32x4 c4 = {}, s4 = {};
     if (in.cos && hh < nslot) {
@@ -411,7 +420,9 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     char *npg = kv.base + (long long)in.layer * kv.layer_stride + (long long)npage * kv.page_stride;
     const int nsl = pn % kv.page_size;
     for (int j = hh; j < nslot; j += 2 * NP) {
-      const float *uj = u + j * DH + 4 * li;
+      // slab column of the slot: query head hq0 + j, K head gk, V head gk
+      const int col = j < H ? hq0 + j : (j == H ? Hall + gk : Hall + Hkv + gk);
+      const float *uj = u + col * DH + 4 * li;
       f32x4 t[kMaxRowSplit];
 #pragma unroll
       for (int k = 0; k < kMaxRowSplit; ++k)
@@ -443,11 +454,11 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
       } else {
         *(bf16x4 *)&kv_s[(j - H) * DH + 4 * li] = y4;
         if (j == H) {
-          *(bf16x4 *)((bf16 *)npg + nsl * DH + 4 * li) = y4;
+          *(bf16x4 *)((bf16 *)npg + nsl * kvd + gk * DH + 4 * li) = y4;
         } else {
           bf16 *vt = (bf16 *)(npg + kv.half_bytes);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vt[(4 * li + e) * kv.page_size + vslot(nsl)] = y4[e];
+          for (int e = 0; e < 4; ++e) vt[(gk * DH + 4 * li + e) * kv.page_size + vslot(nsl)] = y4[e];
         }
       }
     }
@@ -576,7 +587,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   }
   __syncthreads();
   const int S = (len + CH - 1) / CH;   // chunks of this sequence
-  const long long obase = ((long long)b * a.max_splits + chunk) * H * DH;
+  const long long obase = (((long long)b * a.max_splits + chunk) * Hall + hq0) * DH;
   for (int idx = tid; idx < H * DH; idx += NT) {
     const int h = idx >> 7;
     float M = ml_s[0][h][0];
@@ -588,11 +599,11 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
       O += f * ((const float *)wave_area(w))[idx];
     }
     if (S == 1) {
-      a.o[(long long)b * H * DH + idx] = f2bf(O / L);
+      a.o[((long long)b * Hall + hq0) * DH + idx] = f2bf(O / L);
     } else {
       xst(a.o_part + obase + idx, O);
       if ((idx & (DH - 1)) == 0) {
-        float *ml = a.ml_part + (((long long)b * a.max_splits + chunk) * H + h) * 2;
+        float *ml = a.ml_part + (((long long)b * a.max_splits + chunk) * Hall + hq0 + h) * 2;
         xst(ml, M);
         xst(ml + 1, L);
       }
@@ -604,10 +615,10 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   // the next layer.
   stores_done();
   __syncthreads();
-  if (tid == 0) s_prev = arrive(&a.ctr[b]);
+  if (tid == 0) s_prev = arrive(&a.ctr[b * Hkv + gk]);
   __syncthreads();
   if (s_prev != (unsigned)(S - 1)) return;
-  if (tid == 0) a.ctr[b] = 0u;
+  if (tid == 0) a.ctr[b * Hkv + gk] = 0u;
   // Final merge over the S chunks.  (max, sum) of every chunk and head into
   // LDS, then one factor per (chunk, head) with 1/sum folded in, then every
   // output with all of its chunk loads in flight together.
@@ -617,7 +628,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   float *fct = (float *)smem + kMaxDecodeChunks * 32;      // [S][16]
   for (int i = tid; i < S * H; i += NT) {
     const int c = i / H, h = i - c * H;
-    const float *ml = a.ml_part + (((long long)b * a.max_splits + c) * H + h) * 2;
+    const float *ml = a.ml_part + (((long long)b * a.max_splits + c) * Hall + hq0 + h) * 2;
     mlg[(c * 16 + h) * 2] = xld(ml);
     mlg[(c * 16 + h) * 2 + 1] = xld(ml + 1);
   }
@@ -632,7 +643,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   }
   __syncthreads();
   constexpr int OPT = 16 * DH / NT;  // outputs per thread at most
-  const float *ob = a.o_part + (long long)b * a.max_splits * H * DH;
+  const float *ob = a.o_part + ((long long)b * a.max_splits * Hall + hq0) * DH;
   float acc[OPT];
 #pragma unroll
   for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
@@ -643,7 +654,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
       for (int j = 0; j < OPT; ++j) {
         const int idx = tid + NT * j;
-        v[cc][j] = (c0c + cc < S && idx < H * DH) ? xld(ob + (long long)(c0c + cc) * H * DH + idx) : 0.f;
+        v[cc][j] = (c0c + cc < S && idx < H * DH) ? xld(ob + (long long)(c0c + cc) * Hall * DH + idx) : 0.f;
       }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
@@ -656,7 +667,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 #pragma unroll
   for (int j = 0; j < OPT; ++j) {
     const int idx = tid + NT * j;
-    if (idx < H * DH) a.o[(long long)b * H * DH + idx] = f2bf(acc[j]);
+    if (idx < H * DH) a.o[((long long)b * Hall + hq0) * DH + idx] = f2bf(acc[j]);
   }
 }
 
@@ -664,7 +675,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
 
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   if (a.n_seqs <= 0 || a.max_wg <= 0) return;
-  const dim3 grid(a.n_seqs, a.max_wg);
+  const dim3 grid(a.n_seqs, a.max_wg, a.Hkv);
   constexpr int NWV = kAttnPrefillWaves, RB = kAttnPrefillRows / (32 * kAttnPrefillWaves);
   if (a.qk_norm) attn_prefill_kernel<NWV, RB, true><<<grid, 64 * NWV, 0, s>>>(a);
   else attn_prefill_kernel<NWV, RB, false><<<grid, 64 * NWV, 0, s>>>(a);
@@ -676,11 +687,11 @@ void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   // kDecodePages pages) only when the grid is at most one workgroup per CU.
   // Otherwise twice the pages per chunk, so each sequence's final merge has
   // half the chunks; the partial buffers, sized for kDecodeChunk, hold them.
-  if ((long long)a.max_splits * a.n <= 256) {
-    attn_decode_kernel<true, kDecodePages><<<dim3(a.max_splits, a.n), 64 * kDecodePages, 0, s>>>(a);
+  if ((long long)a.max_splits * a.n * a.in.Hkv <= 256) {
+    attn_decode_kernel<true, kDecodePages><<<dim3(a.max_splits, a.n, a.in.Hkv), 64 * kDecodePages, 0, s>>>(a);
   } else {
     AttnDecodeArgs b = a;
     b.max_splits = (a.max_splits + 1) / 2;
-    attn_decode_kernel<false, 2 * kDecodePages><<<dim3(b.max_splits, b.n), 128 * kDecodePages, 0, s>>>(b);
+    attn_decode_kernel<false, 2 * kDecodePages><<<dim3(b.max_splits, b.n, b.in.Hkv), 128 * kDecodePages, 0, s>>>(b);
   }
 }

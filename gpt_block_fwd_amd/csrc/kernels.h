@@ -144,12 +144,14 @@ constexpr int kAttnPrefillWaves = 8;
 constexpr int kAttnPrefillRows = 256;
 struct AttnPrefillArgs {
   const bf16 *q;   // [M][H*128]
-  const bf16 *k;   // [M][128]
-  const bf16 *vt;  // [128][ldvt]
+  const bf16 *k;   // [M][Hkv*128]
+  const bf16 *vt;  // [Hkv*128][ldvt]
   long long ldvt;
   const int *cu, *cu_pad;
-  int n_seqs, max_wg;  // grid: (sequence, kAttnPrefillRows-row block counted from the end)
-  int H;
+  // grid: (sequence, kAttnPrefillRows-row block counted from the end, K/V
+  // head); a K/V head's rows are its H/Hkv query heads at every position
+  int n_seqs, max_wg;
+  int H, Hkv;
   int qk_norm;  // q and k are QK-normalised (RMS <= 1 per head): fixed softmax reference
   bf16 *o;  // [M][H*128]
 };

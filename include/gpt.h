@@ -66,6 +66,9 @@ const char *gpt_last_error(void);
  * connections, a two-layer MLP, an untied output projection.
  * [nanochat-launch tricks]: rotary positions, ReLU^2 MLP, separate Q/K/V.
  * [nanochat-forum]: QK normalisation and multi-query attention.
+ * [microgpt "differences from production models", item 3]: grouped-query
+ * attention.  n_kv_head K/V heads, each shared by n_head / n_kv_head
+ * consecutive query heads: 1 is multi-query, n_head is multi-head.
  *
  *   pos_kind  GPT_POS_LEARNED: x = WTE[id] + WPE[t]  (microgpt layout)
  *             GPT_POS_ROPE:    x = WTE[id]; q, k rotated by half-split RoPE
@@ -73,9 +76,12 @@ const char *gpt_last_error(void);
  *   qk_norm   1: weightless RMSNorm of every q and k head vector after RoPE
  *   max_seq   rows of the RoPE tables / WPE; upper bound on any position
  *
- * Supported: bf16 needs head_dim == 128, pos_kind ROPE, d_model % 128 == 0,
- * d_ff % 128 == 0, n_head % n_kv_head == 0; fp32 needs head_dim <= 64 and
- * d_model <= 1024 (a small-model path).  Anything else is GPT_ERR_UNSUPPORTED.
+ * Supported: bf16 needs head_dim == 128, pos_kind ROPE, act RELU2,
+ * n_head <= 16, d_model == n_head * head_dim, d_ff and vocab multiples of
+ * 128; fp32 needs head_dim <= 64 and d_model % 4 == 0, <= 4096 (a small-model
+ * path).  Both need n_head % n_kv_head == 0.  Anything else is
+ * GPT_ERR_UNSUPPORTED.  A decode step handles at most 4096 sequences x
+ * n_kv_head.
  */
 typedef struct {
   int32_t vocab, n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, max_seq;

@@ -61,10 +61,16 @@ def _bad(fn, status):
 def test_unsupported_configs_are_reported():
     m = wl.depth_model(12)
     import dataclasses
-    for change in ({"head_dim": 64, "d_model": 384}, {"n_kv_head": 2, "n_head": 6},
-                   {"pos_kind": 0}, {"vocab": 1000}):
+    for change in ({"head_dim": 64, "d_model": 384}, {"n_head": 18, "d_model": 18 * 128},
+                   {"pos_kind": 0}, {"vocab": 1000}, {"act": 0}):
         cfg = B.make_config(dataclasses.replace(m, **change))
         _bad(lambda: B.kv_cache_bytes(cfg, 4, 64), B.GPT_ERR_UNSUPPORTED)
+    # grouped-query attention is supported; a K/V head count that does not
+    # divide the query heads is an argument error
+    gqa = B.make_config(dataclasses.replace(m, n_kv_head=2))
+    assert B.kv_cache_bytes(gqa, 4, 64) > B.kv_cache_bytes(B.make_config(m), 4, 64)
+    _bad(lambda: B.kv_cache_bytes(B.make_config(dataclasses.replace(m, n_kv_head=4)), 4, 64),
+         B.GPT_ERR_ARG)
     bad = B.make_config(dataclasses.replace(m, n_head=5))  # 6 % ... n_kv divides, d != H*dh
     _bad(lambda: B.kv_cache_bytes(bad, 4, 64), B.GPT_ERR_UNSUPPORTED)
     neg = B.make_config(dataclasses.replace(m, n_layer=0))

@@ -239,6 +239,64 @@ def test_small_bf16_decode_teacher_forced(temperature):
     kv.close()
 
 
+# ---------------------------------------------------------------- grouped-query attention
+
+@pytest.mark.parametrize("n_head,n_kv,lens", [(6, 2, [300, 173, 64, 1]), (4, 4, [257, 90]),
+                                              (6, 3, [40, 9]), (2, 2, [700])])
+def test_small_bf16_gqa_prefill(n_head, n_kv, lens):
+    """Grouped-query attention (n_kv K/V heads, each shared by n_head / n_kv
+    query heads; n_kv = n_head is multi-head) through the whole prefill;
+    49 rows take the small-M path with its separate RoPE/norm scatter."""
+    cfg = wl.small_model(2, n_head, vocab=4096, n_kv_head=n_kv)
+    w = wl.ragged_prefill(cfg, lens, seed=n_head + 7 * n_kv)
+    W, dm = device_model(cfg)
+    logits, lse = gpu_prefill(dm, w.tokens, w.seqlens)
+    ref = np.concatenate(oracle.prefill(cfg, W, w.tokens, w.seqlens)[0])
+    st = logit_stats(logits, ref)
+    print(st)
+    assert st["max_abs"] <= 3e-2
+    assert st["disagree_explained"]
+    np.testing.assert_allclose(lse, oracle.logsumexp(ref), atol=3e-2)
+
+
+@pytest.mark.parametrize("n_head,n_kv,n_seqs", [(6, 2, 4), (4, 4, 3), (6, 3, 40)])
+def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
+    """Prefill into the paged cache, then 20 greedy decode steps with GQA; the
+    oracle consumes the GPU's tokens.  40 sequences make more than 256
+    decode-attention workgroups (the register-load variant)."""
+    t = torch()
+    cfg = wl.small_model(2, n_head, vocab=4096, n_kv_head=n_kv)
+    rng = np.random.default_rng(n_seqs)
+    lens = [int(x) for x in rng.integers(1, 300, n_seqs)]
+    lens[0] = 255  # the first decode position opens a new page
+    w = wl.ragged_prefill(cfg, lens, seed=n_head * n_kv)
+    W, dm = device_model(cfg)
+    n, steps = n_seqs, 20
+    kv = B.DeviceKV(dm, n, 320)
+    logits0, _ = gpu_prefill(dm, w.tokens, w.seqlens, rows=B.ROWS_LAST, kv=kv.handle)
+    toks = t.empty(n, dtype=t.int32, device="cuda")
+    B.gpt_select_tokens(t.from_numpy(logits0).cuda(), n, cfg.vocab, 0.0, None, toks)
+    ws = dm.workspace(n, n)
+    step_logits = t.empty((n, cfg.vocab), dtype=t.float32, device="cuda")
+    got_tok, got_logits = [toks.cpu().numpy().copy()], [logits0]
+    for s in range(steps):
+        dm.decode_step(kv.handle, toks, toks, logits=step_logits, workspace=ws)
+        got_tok.append(toks.cpu().numpy().copy())
+        got_logits.append(step_logits.cpu().numpy().copy())
+    got_tok = np.stack(got_tok)
+    sample = [0, n - 1]
+    _, ref_logits = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok,
+                                       seqs=sample)
+    st = logit_stats(np.stack(got_logits)[:, sample], ref_logits)
+    print(st)
+    assert st["max_abs"] <= 3e-2
+    assert st["disagree_explained"]
+    for s in range(steps + 1):
+        np.testing.assert_array_equal(got_tok[s], np.argmax(got_logits[s], axis=-1))
+    np.testing.assert_array_equal(kv.lengths(), np.asarray(lens) + steps)
+    kv.close()
+
+
 def test_small_bf16_decode_many_sequences():
     """64 sequences with room for 1100 positions each: more than 256 decode
     attention workgroups, so the register-load variant with 8-page chunks

@@ -91,11 +91,12 @@ def depth_model(depth: int, max_seq: int = 4096, vocab: int = 65536) -> ModelCon
 
 
 def small_model(n_layer: int, n_head: int, vocab: int = 65536,
-                max_seq: int = 4096) -> ModelConfig:
-    """A nanochat-style block with free layer/head counts for quick tests."""
+                max_seq: int = 4096, n_kv_head: int = 1) -> ModelConfig:
+    """A nanochat-style block with free layer/head counts for quick tests
+    (n_kv_head > 1: grouped-query attention)."""
     d = 128 * n_head
     return ModelConfig(vocab=vocab, n_layer=n_layer, d_model=d, n_head=n_head,
-                       n_kv_head=1, head_dim=128, d_ff=4 * d, max_seq=max_seq,
+                       n_kv_head=n_kv_head, head_dim=128, d_ff=4 * d, max_seq=max_seq,
                        rope_base=10000.0, norm_eps=1e-6, pos_kind=POS_ROPE,
                        act=ACT_RELU2, qk_norm=1, dtype=DTYPE_BF16, init_std=0.02)
 
