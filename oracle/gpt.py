@@ -18,7 +18,8 @@ __all__ = [
     "READINGS", "rmsnorm", "rope_angles", "rope_tables", "apply_rope",
     "relu", "relu2", "softmax", "logsumexp", "causal_attention", "KVCache",
     "embed", "block", "final_logits", "forward", "prefill", "decode_step",
-    "greedy", "sample", "cross_entropy", "token_losses", "mean_loss", "adam_step", "param_count",
+    "greedy", "sample", "cross_entropy", "token_losses", "mean_loss", "adam_step",
+    "loss_and_grads", "param_count",
     "round_bf16",
     "run_serving",
 ]
@@ -384,6 +385,139 @@ def adam_step(param: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray,
     mhat = m1 / (1.0 - beta1 ** step)
     vhat = v1 / (1.0 - beta2 ** step)
     return p - lr * mhat / (np.sqrt(vhat) + eps), m1, v1
+
+
+# ------------------------------------------------------------------ backward
+
+def _rms_backward(x: np.ndarray, dy: np.ndarray, eps: float) -> np.ndarray:
+    """Gradient through ``y = x / sqrt(mean(x^2) + eps)`` over the last axis:
+    ``dx = (dy - y * mean(dy * y)) / r``."""
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x / r
+    return (dy - y * np.mean(dy * y, axis=-1, keepdims=True)) / r
+
+
+def _rope_backward(du: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Gradient through ``apply_rope``: the transpose of a rotation turns the
+    pair back by the same angle."""
+    half = du.shape[-1] // 2
+    a, b = du[..., :half], du[..., half:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([a * c + b * s, -a * s + b * c], axis=-1)
+
+
+def loss_and_grads(cfg, W, tokens, seqlens, targets):
+    """Mean next-token cross-entropy of packed sequences and its gradient
+    with respect to every weight, in float64 (Microgpt, "Training process",
+    items 2 and 3: the forward pass and its loss, then the chain rule run
+    backwards from the loss to every parameter).
+
+    The loss is ``mean_loss(token_losses(logits, targets))`` over the rows
+    whose target lies in ``[0, V)``; its gradient with respect to row r's
+    logits is ``(softmax(logits[r]) - onehot(target)) / count``.  The backward
+    retraces ``block``: RMSNorm, the three projections, RoPE, QK-norm,
+    attention with each query head on K/V head ``h * Hkv // H``, the output
+    projection, the MLP and the residual adds, then the final norm and the
+    LM head.  Returns ``(mean_loss, grads)`` with ``grads`` keyed like
+    ``W.flat()`` plus ``"lm_head"``.
+    """
+    f = np.float64
+    eps = cfg.norm_eps
+    n_head, n_kv, dh = cfg.n_head, cfg.n_kv_head, cfg.head_dim
+    tables = rope_tables(cfg.max_seq, dh, cfg.rope_base) if cfg.pos_kind == 1 else None
+    targets = np.asarray(targets, np.int64)
+    V = cfg.vocab
+    count = int(np.sum((targets >= 0) & (targets < V)))
+    g = {"wte": np.zeros(W.wte.shape), "lm_head": np.zeros(W.lm_head.shape)}
+    if W.wpe is not None:
+        g["wpe"] = np.zeros(W.wpe.shape)
+    for i, lw in enumerate(W.layers):
+        for k in ("wq", "wk", "wv", "wo", "w1", "w2"):
+            g[f"layer{i}.{k}"] = np.zeros(lw[k].shape)
+    total = 0.0
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    for b in range(len(seqlens)):
+        tok = np.asarray(tokens[cu[b]:cu[b + 1]], np.int64)
+        tg = targets[cu[b]:cu[b + 1]]
+        t = len(tok)
+        pos = np.arange(t)
+        x = embed(cfg, W, tok, pos, f)
+        saved = []
+        for lw in W.layers:
+            c = {"x": x}
+            h = rmsnorm(x, eps)
+            qr = _linear(h, lw["wq"], f).reshape(t, n_head, dh)
+            kr = _linear(h, lw["wk"], f).reshape(t, n_kv, dh)
+            v = _linear(h, lw["wv"], f).reshape(t, n_kv, dh)
+            if tables is not None:
+                cs, sn = tables[0][pos], tables[1][pos]
+                qr, kr = apply_rope(qr, cs, sn), apply_rope(kr, cs, sn)
+            q = rmsnorm(qr, eps) if cfg.qk_norm else qr
+            k = rmsnorm(kr, eps) if cfg.qk_norm else kr
+            o = causal_attention(q, k, v, 0)
+            c.update(h=h, qr=qr, kr=kr, q=q, k=k, v=v, o=o.reshape(t, n_head * dh))
+            x = x + _linear(c["o"], lw["wo"], f)
+            c["xm"] = x
+            h2 = rmsnorm(x, eps)
+            z = _linear(h2, lw["w1"], f)
+            u = relu2(z) if cfg.act == 1 else relu(z)
+            c.update(h2=h2, z=z, u=u)
+            x = x + _linear(u, lw["w2"], f)
+            saved.append(c)
+        hf = rmsnorm(x, eps)
+        logits = _linear(hf, W.lm_head, f)
+        losses = token_losses(logits, tg)
+        total += float(np.sum(losses))
+        ok = (tg >= 0) & (tg < V)
+        dlog = softmax(logits)
+        dlog[np.nonzero(ok)[0], tg[ok]] -= 1.0
+        dlog[~ok] = 0.0
+        dlog /= max(count, 1)
+        g["lm_head"] += dlog.T @ hf
+        dx = _rms_backward(x, dlog @ W.lm_head.astype(f), eps)
+        scale = 1.0 / math.sqrt(dh)
+        visible = pos[None, :] <= pos[:, None]
+        for i in reversed(range(len(W.layers))):
+            lw, c = W.layers[i], saved[i]
+            # MLP: x += W2 act(W1 rms(xm))
+            g[f"layer{i}.w2"] += dx.T @ c["u"]
+            du = dx @ lw["w2"].astype(f)
+            dz = du * (2.0 * np.maximum(c["z"], 0.0) if cfg.act == 1 else (c["z"] > 0).astype(f))
+            g[f"layer{i}.w1"] += dz.T @ c["h2"]
+            dx = dx + _rms_backward(c["xm"], dz @ lw["w1"].astype(f), eps)
+            # attention: x += Wo o
+            g[f"layer{i}.wo"] += dx.T @ c["o"]
+            do = (dx @ lw["wo"].astype(f)).reshape(t, n_head, dh)
+            q, k, v = c["q"], c["k"], c["v"]
+            dq = np.zeros_like(q)
+            dk = np.zeros_like(k)
+            dv = np.zeros_like(v)
+            for hh in range(n_head):
+                gk = hh * n_kv // n_head
+                sc = np.where(visible, (q[:, hh] @ k[:, gk].T) * scale, -np.inf)
+                p = softmax(sc, axis=-1)
+                dp = do[:, hh] @ v[:, gk].T
+                ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+                dq[:, hh] = ds @ k[:, gk] * scale
+                dk[:, gk] += ds.T @ q[:, hh] * scale
+                dv[:, gk] += p.T @ do[:, hh]
+            if cfg.qk_norm:
+                dq = _rms_backward(c["qr"], dq, eps)
+                dk = _rms_backward(c["kr"], dk, eps)
+            if tables is not None:
+                cs, sn = tables[0][pos], tables[1][pos]
+                dq, dk = _rope_backward(dq, cs, sn), _rope_backward(dk, cs, sn)
+            dq, dk, dv = dq.reshape(t, -1), dk.reshape(t, -1), dv.reshape(t, -1)
+            h = c["h"]
+            g[f"layer{i}.wq"] += dq.T @ h
+            g[f"layer{i}.wk"] += dk.T @ h
+            g[f"layer{i}.wv"] += dv.T @ h
+            dh_ = dq @ lw["wq"].astype(f) + dk @ lw["wk"].astype(f) + dv @ lw["wv"].astype(f)
+            dx = dx + _rms_backward(c["x"], dh_, eps)
+        np.add.at(g["wte"], tok, dx)
+        if W.wpe is not None:
+            np.add.at(g["wpe"], pos, dx)
+    return total / max(count, 1), g
 
 
 def param_count(W) -> int:

@@ -192,6 +192,59 @@ def test_adam_is_invariant_to_gradient_scale_and_still_at_zero():
     np.testing.assert_array_equal(oracle.adam_step(p, z, z, z, 3, 0.1, 0.9, 0.99, 1e-8)[0], p)
 
 
+# ---------------------------------------------------------------- backward
+
+def _f64_weights(W):
+    import dataclasses
+    return dataclasses.replace(
+        W, wte=W.wte.astype(np.float64),
+        wpe=None if W.wpe is None else W.wpe.astype(np.float64),
+        lm_head=W.lm_head.astype(np.float64),
+        layers=[{k: v.astype(np.float64) for k, v in lw.items()} for lw in W.layers])
+
+
+@pytest.mark.parametrize("which", ["tiny", "rope_mqa", "rope_gqa"])
+def test_loss_gradients_match_finite_differences(which):
+    """Every weight tensor's gradient of the mean next-token loss, at sampled
+    entries, against central differences of the oracle's own forward loss
+    (float64 weights, step 1e-5: truncation ~1e-10 relative, roundoff
+    ~2e-16 * loss / step ~ 1e-10 absolute)."""
+    if which == "tiny":
+        w = wl.tiny_workload()
+        cfg = w.model
+    else:
+        import dataclasses
+        cfg = tiny_rope_model()
+        if which == "rope_gqa":
+            cfg = dataclasses.replace(cfg, n_head=4, n_kv_head=2, d_model=16)
+        w = wl.ragged_prefill(cfg, [9, 5, 12], seed=3)
+    W = _f64_weights(wl.make_weights(cfg))
+    tg = w.next_token_targets()
+    tg[2] = -1  # a skipped row in the middle of a sequence
+    loss, g = oracle.loss_and_grads(cfg, W, w.tokens, w.seqlens, tg)
+    lg = np.concatenate(oracle.prefill(cfg, W, w.tokens, w.seqlens)[0])
+    assert loss == pytest.approx(oracle.mean_loss(oracle.token_losses(lg, tg), tg, cfg.vocab), abs=1e-12)
+    rng = np.random.default_rng(len(which))
+    tensors = list(W.flat()) + [("lm_head", W.lm_head)]
+    for name, arr in tensors:
+        assert g[name].shape == arr.shape
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            if name == "wte":
+                idx = (int(w.tokens[rng.integers(0, len(w.tokens))]), idx[1])  # a row that is read
+            old = arr[idx]
+            arr[idx] = old + 1e-5
+            lp = oracle.loss_and_grads(cfg, W, w.tokens, w.seqlens, tg)[0]
+            arr[idx] = old - 1e-5
+            lm = oracle.loss_and_grads(cfg, W, w.tokens, w.seqlens, tg)[0]
+            arr[idx] = old
+            fd = (lp - lm) / 2e-5
+            assert abs(g[name][idx] - fd) <= 1e-6 * (abs(fd) + abs(g[name][idx])) + 1e-9, (name, idx)
+    # rows of the token table that no position reads get no gradient
+    unused = np.setdiff1d(np.arange(cfg.vocab), w.tokens)
+    assert np.all(g["wte"][unused] == 0.0)
+
+
 # ---------------------------------------------------------------- softmax
 
 def test_vocab_softmax_rows_are_distributions():
