@@ -115,6 +115,41 @@ def bench_prefill_loss(B, torch, dm, w, steps, warmup):
     return dt, lm, float(mean.cpu().numpy()[0])
 
 
+def bench_loss_grads(B, torch, dm, w, steps, warmup):
+    """Time `steps` loss-gradient passes (gpt_loss_grads: forward, loss and
+    the gradient of every weight), then the same again with the backward's
+    kernel classes timed by events."""
+    n = w.n_seqs
+    cu = w.cu_seqlens
+    M = int(cu[-1])
+    tokens = torch.from_numpy(w.tokens).cuda()
+    targets = torch.from_numpy(w.next_token_targets()).cuda()
+    loss = torch.empty(M, dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    grads = B.DeviceGrads(dm)
+    ws = dm.train_workspace(M, n)
+    B.gpt_profile_enable(0)
+    for _ in range(warmup):
+        dm.loss_grads(tokens, targets, cu, grads, loss, mean, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dm.loss_grads(tokens, targets, cu, grads, loss, mean, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    names = ["gemm", "lmhead", "attn", "norm", "softmax", "bwd_gemm", "bwd_attn", "bwd_other"]
+    B.gpt_profile_enable(sum(1 << B.PROF_CLASSES[k] for k in names))
+    for _ in range(steps):
+        dm.loss_grads(tokens, targets, cu, grads, loss, mean, workspace=ws)
+    torch.cuda.synchronize()
+    r = {k: prof_read(B, [k]) for k in names}
+    B.gpt_profile_enable(0)
+    m = float(mean.cpu().numpy()[0])
+    del grads, ws, loss, mean
+    torch.cuda.empty_cache()
+    return dt, r, m
+
+
 def bench_adam(B, torch, n, steps, warmup=2):
     """Adam over n fp32 parameters with the bf16 copy: `steps` updates timed
     end to end, then again with the kernel timed by events."""
@@ -339,6 +374,8 @@ def main():
     ap.add_argument("--skip-d26", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-gqa", action="store_true")
+    ap.add_argument("--skip-train", action="store_true")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="one counted depth-12 prefill and a 1 GiB copy, for rocprofv3 --pmc")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
@@ -420,6 +457,30 @@ def main():
     log(f"d12 prefill + loss: {out['d12_prefill_loss']['tokens_per_s']:,.0f} tok/s, "
         f"LM head {lml_tfs:.0f} TFLOP/s, mean loss {mean_loss:.4f}")
 
+    # ---------------- depth-12 loss gradient (forward + backward of every weight)
+    if not args.skip_train:
+        log("timing the depth-12 loss gradient")
+        ts = max(2, args.steps // 3)
+        dtt, tr, tmean = bench_loss_grads(B, torch, dm12, w2, ts, 1)
+        def tf(k):
+            return round(tr[k]["flops"] / (tr[k]["ms"] * 1e-3) / 1e12, 1) if tr[k]["ms"] else 0.0
+        gm = {k: tr[k] for k in ("gemm", "lmhead", "bwd_gemm")}
+        g_fl = sum(v["flops"] for v in gm.values())
+        g_ms = sum(v["ms"] for v in gm.values())
+        out["d12_loss_grads"] = {
+            "workload": "d12_loss_grads", "batch": 8, "seq_len": 2048,
+            "tokens_per_s": round(ts * M / dtt, 1), "ms_per_step": round(dtt / ts * 1e3, 3),
+            "mean_loss": round(tmean, 4),
+            "gemm": {"ms_per_step": round(g_ms / ts, 3),
+                     "achieved_tflops": round(g_fl / (g_ms * 1e-3) / 1e12, 1),
+                     "frac": round(g_fl / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "attention_forward": {"ms_per_step": round(tr["attn"]["ms"] / ts, 3), "achieved_tflops": tf("attn")},
+            "attention_backward": {"ms_per_step": round(tr["bwd_attn"]["ms"] / ts, 3),
+                                   "achieved_tflops": tf("bwd_attn"),
+                                   "frac": round(tf("bwd_attn") / PEAK_BF16_TFLOPS, 4)},
+            "elementwise_ms_per_step": round((tr["bwd_other"]["ms"] + tr["norm"]["ms"] + tr["softmax"]["ms"]) / ts, 3)}
+        log(f"d12 loss grads: {out['d12_loss_grads']}")
+
     # ---------------- Adam over every depth-12 parameter (fp32 master copy + bf16 copy)
     n12 = sum(int(np.prod(sh)) for _, sh in wl.weight_shapes(w2.model))
     log("timing the Adam update over the depth-12 parameters")
@@ -443,6 +504,34 @@ def main():
                          "decode_gemms": {"achieved_gbs": round(sk_gbs, 1),
                                           "frac": round(sk_gbs / PEAK_HBM_GBS, 4)}}
         log(f"d12 decode: {out['decode']['tokens_per_s']:,.0f} tok/s")
+
+    # ---------------- grouped-query attention: the depth-12 shape with 2 K/V heads
+    if not args.skip_gqa:
+        import dataclasses
+        mg = dataclasses.replace(w2.model, n_kv_head=2)
+        wg = dataclasses.replace(w2, model=mg, name="d12_gqa2_prefill")
+        log("timing depth-12 prefill and decode with 2 K/V heads")
+        dmg = B.DeviceModel(mg, wl.make_weights(mg))
+        dtg, _, lgg, _ = bench_prefill(B, torch, dmg, wg, args.steps, args.warmup,
+                                       1 << B.PROF_CLASSES["attn"])
+        del lgg
+        torch.cuda.empty_cache()
+        ag = prof_read(B, ["attn"])
+        ag_tfs = ag["flops"] / (ag["ms"] * 1e-3) / 1e12
+        out["d12_gqa2"] = {"workload": "d12 shape, 6 query heads on 2 K/V heads",
+                           "prefill_tokens_per_s": round(args.steps * M / dtg, 1),
+                           "prefill_attention": {"achieved_tflops": round(ag_tfs, 1),
+                                                 "frac": round(ag_tfs / PEAK_BF16_TFLOPS, 4)}}
+        if not args.skip_decode:
+            w3g = dataclasses.replace(wl.d12_decode(steps=args.decode_steps), model=mg)
+            ddg, attg, _ = bench_decode(B, torch, dmg, w3g, args.decode_steps, 0.0)
+            gbs = attg["bytes"] / (attg["ms"] * 1e-3) / 1e9 if attg["ms"] else 0.0
+            out["d12_gqa2"]["decode_tokens_per_s"] = round(32 * args.decode_steps / ddg, 1)
+            out["d12_gqa2"]["decode_attention"] = {"achieved_gbs": round(gbs, 1),
+                                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del dmg
+        torch.cuda.empty_cache()
+        log(f"d12 gqa2: {out['d12_gqa2']}")
 
     # ---------------- CPU oracle on one sequence
     if not args.skip_cpu:

@@ -22,13 +22,14 @@ STATUS_NAMES = {0: "GPT_OK", 1: "GPT_ERR_ARG", 2: "GPT_ERR_CAPACITY", 3: "GPT_ER
                 4: "GPT_ERR_HIP"}
 
 PROF_CLASSES = {"gemm": 0, "lmhead": 1, "attn": 2, "decode_attn": 3, "skinny": 4, "norm": 5,
-                "softmax": 6, "optim": 7}
+                "softmax": 6, "optim": 7, "bwd_gemm": 8, "bwd_attn": 9, "bwd_other": 10}
 
 #: every entry point declared by include/gpt.h and include/gpt_profile.h
 EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
            "gpt_decode_step",
-           "gpt_select_tokens", "gpt_adam_step", "gpt_profile_enable", "gpt_profile_read",
+           "gpt_select_tokens", "gpt_train_workspace_bytes", "gpt_loss_grads", "gpt_adam_step",
+           "gpt_profile_enable", "gpt_profile_read",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
@@ -52,6 +53,11 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 
 
 class GptWeights(ctypes.Structure):
+    _fields_ = [("wte", ctypes.c_void_p), ("wpe", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("w1", _PP), ("w2", _PP)]
+
+
+class GptGrads(ctypes.Structure):
     _fields_ = [("wte", ctypes.c_void_p), ("wpe", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("w1", _PP), ("w2", _PP)]
 
@@ -84,6 +90,10 @@ def lib() -> ctypes.CDLL:
                                   vp, vp, sz, vp]
     L.gpt_select_tokens.argtypes = [vp, i32, i32, f32, vp, vp, vp]
     L.gpt_adam_step.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int64, i32, f32, f32, f32, f32, vp]
+    L.gpt_train_workspace_bytes.argtypes = [cfgp, i32, i32]
+    L.gpt_train_workspace_bytes.restype = sz
+    L.gpt_loss_grads.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, vp, i32,
+                                 ctypes.POINTER(GptGrads), vp, vp, vp, sz, vp]
     L.gpt_profile_enable.argtypes = [ctypes.c_uint32]
     L.gpt_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
@@ -91,7 +101,7 @@ def lib() -> ctypes.CDLL:
     L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp]
     L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
     for name in EXPORTS:
-        if name not in ("gpt_last_error", "gpt_workspace_bytes"):
+        if name not in ("gpt_last_error", "gpt_workspace_bytes", "gpt_train_workspace_bytes"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -198,6 +208,20 @@ def gpt_select_tokens(logits, rows: int, vocab: int, temperature: float, uniform
                                    _ptr(tokens_out), _stream(stream)))
 
 
+def gpt_train_workspace_bytes(cfg: GptConfig, max_tokens: int, max_seqs: int) -> int:
+    return int(lib().gpt_train_workspace_bytes(ctypes.byref(cfg), max_tokens, max_seqs))
+
+
+def gpt_loss_grads(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, tokens, targets,
+                   cu_seqlens: np.ndarray, n_seqs: int, grads: GptGrads, loss, mean, workspace,
+                   workspace_bytes: int, stream=None):
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    _check(lib().gpt_loss_grads(ctypes.byref(cfg), ctypes.byref(weights), _ptr(rope_cos),
+                                _ptr(rope_sin), _ptr(tokens), _ptr(targets), cu.ctypes.data,
+                                n_seqs, ctypes.byref(grads), _ptr(loss), _ptr(mean),
+                                _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def gpt_adam_step(param, grad, m, v, param_bf16, n: int, step: int, lr: float, beta1: float,
                   beta2: float, eps: float, stream=None):
     _check(lib().gpt_adam_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), _ptr(param_bf16), n, step,
@@ -293,11 +317,54 @@ class DeviceModel:
         gpt_prefill_loss(self.cfg, self.weights, self.rope_cos, self.rope_sin, tokens, targets,
                          cu_seqlens, n, kv, loss, lse, mean, ws, nb, stream)
 
+    def train_workspace(self, max_tokens: int, max_seqs: int):
+        import torch
+        n = gpt_train_workspace_bytes(self.cfg, max_tokens, max_seqs)
+        if n == 0:
+            raise GptError(GPT_ERR_ARG, "gpt_train_workspace_bytes returned 0: " + last_error())
+        return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+
+    def loss_grads(self, tokens, targets, cu_seqlens, grads: "DeviceGrads", loss, mean=None,
+                   workspace=None, stream=None):
+        n = len(cu_seqlens) - 1
+        total = int(cu_seqlens[-1])
+        ws, nb = workspace if workspace is not None else self.train_workspace(total, n)
+        gpt_loss_grads(self.cfg, self.weights, self.rope_cos, self.rope_sin, tokens, targets,
+                       cu_seqlens, n, grads.struct, loss, mean, ws, nb, stream)
+
     def decode_step(self, kv: int, tokens_in, tokens_out, temperature=0.0, uniforms=None,
                     logits=None, workspace=None, stream=None):
         ws, nb = workspace
         gpt_decode_step(self.cfg, self.weights, self.rope_cos, self.rope_sin, kv, tokens_in,
                         temperature, uniforms, tokens_out, logits, ws, nb, stream)
+
+
+class DeviceGrads:
+    """fp32 gradient buffers shaped like a DeviceModel's weights."""
+
+    def __init__(self, dm: "DeviceModel"):
+        import torch
+
+        def like(t):
+            return None if t is None else torch.zeros(t.shape, dtype=torch.float32, device=t.device)
+
+        self.wte, self.wpe, self.lm_head = like(dm.wte), like(dm.wpe), like(dm.lm_head)
+        self.layers = [{k: like(lw[k]) for k in lw} for lw in dm.layers]
+        L = len(self.layers)
+        self._arrs = {k: (ctypes.c_void_p * L)(*[lw[k].data_ptr() for lw in self.layers])
+                      for k in ("wq", "wk", "wv", "wo", "w1", "w2")}
+        self.struct = GptGrads(self.wte.data_ptr(), _ptr(self.wpe), self.lm_head.data_ptr(),
+                               *[ctypes.cast(self._arrs[k], _PP)
+                                 for k in ("wq", "wk", "wv", "wo", "w1", "w2")])
+
+    def flat(self):
+        yield "wte", self.wte
+        if self.wpe is not None:
+            yield "wpe", self.wpe
+        for i, lw in enumerate(self.layers):
+            for k in ("wq", "wk", "wv", "wo", "w1", "w2"):
+                yield f"layer{i}.{k}", lw[k]
+        yield "lm_head", self.lm_head
 
 
 class DeviceKV:

@@ -184,6 +184,62 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   return align256(off);
 }
 
+// Extra buffers of the loss backward, carved after the forward's.
+struct TrainBufs {
+  float *xs;        // [2L + 1][M][d] residual stream at each layer's input and middle, then the last
+  float *logits;    // [M][V]
+  void *dl;         // [M][V] gradient of the logits (model dtype)
+  void *trA, *trB;  // transposed operands of the weight-gradient GEMMs, rows of Mp
+  void *wT;         // a transposed weight
+  float *dx, *dh;   // [M][d] gradient of the residual stream; gradient of a norm's output
+  void *dxb;        // [M][d] dx in the model dtype
+  float *z, *du;    // [M][F]
+  void *u, *dz;     // [M][F] model dtype
+  float *dO, *dq, *dk, *dv, *lse, *dsum;
+  void *dqkv;       // [M][(H + 2Hkv) dh] model dtype
+  int *count;
+  int Mp;
+};
+
+size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base, Bufs *b, TrainBufs *tb) {
+  size_t off = carve(c, M, nseq, base, b);
+  auto take = [&](size_t bytes) -> char * {
+    off = align256(off);
+    char *p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  const long long d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
+  const long long L = c->n_layer, qkv_n = (H + 2 * Hkv) * dh;
+  const size_t es = c->dtype == GPT_DTYPE_BF16 ? 2 : 4;
+  TrainBufs t{};
+  t.Mp = (int)((M + 63) / 64 * 64);
+  const long long Mp = t.Mp;
+  t.xs = (float *)take((2 * L + 1) * M * d * 4);
+  t.logits = (float *)take(M * V * 4);
+  t.dl = take(M * V * es);
+  t.trA = take(std::max({V, F, qkv_n, d, H * dh}) * Mp * es);
+  t.trB = take(std::max({d, F, H * dh}) * Mp * es);
+  t.wT = take(std::max({V * d, F * d, qkv_n * d, H * dh * d}) * es);
+  t.dx = (float *)take(M * d * 4);
+  t.dh = (float *)take(M * d * 4);
+  t.dxb = take(M * d * es);
+  t.z = (float *)take(M * F * 4);
+  t.du = (float *)take(M * F * 4);
+  t.u = take(M * F * es);
+  t.dz = take(M * F * es);
+  t.dO = (float *)take(M * H * dh * 4);
+  t.dq = (float *)take(M * H * dh * 4);
+  t.dk = (float *)take(M * Hkv * dh * 4);
+  t.dv = (float *)take(M * Hkv * dh * 4);
+  t.lse = (float *)take(M * H * 4);
+  t.dsum = (float *)take(M * H * 4);
+  t.dqkv = take(M * qkv_n * es);
+  t.count = (int *)take(4);
+  if (tb) *tb = t;
+  return align256(off);
+}
+
 // ------------------------------------------------------------------ weights
 
 gpt_status check_weights(const gpt_config *c, const gpt_weights *w) {
@@ -398,6 +454,176 @@ size_t gpt_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_
 }  // extern "C"
 
 namespace {
+
+// ------------------------------------------------------------------ forward layers
+// What a prefill forward's layers need: the model, the rotary tables, the
+// carved buffers (the residual stream is bf->x), the cache view and the
+// stream.
+struct Fwd {
+  const gpt_config *c;
+  const gpt_weights *w;
+  const float *cos, *sin;
+  Bufs *bf;
+  PagedKV pv;
+  bool use_cache;
+  int M, n_seqs, max_len;
+  double attn_flops;
+  hipStream_t s;
+};
+
+Fwd make_fwd(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin, Bufs *bf,
+             PagedKV pv, bool use_cache, int M, int n_seqs, const int32_t *cu_seqlens, hipStream_t s) {
+  Fwd f{};
+  f.c = c;
+  f.w = w;
+  f.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
+  f.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
+  f.bf = bf;
+  f.pv = pv;
+  f.use_cache = use_cache;
+  f.M = M;
+  f.n_seqs = n_seqs;
+  for (int b = 0; b < n_seqs; ++b) {
+    const double L = cu_seqlens[b + 1] - cu_seqlens[b];
+    f.max_len = std::max(f.max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
+    f.attn_flops += 4.0 * c->n_head * c->head_dim * L * (L + 1) / 2;
+  }
+  f.s = s;
+  return f;
+}
+
+// h = RMSNorm(x) (bf16 or fp32 per the model dtype)
+void fwd_norm(const Fwd &f, const float *x, void *h) {
+  const gpt_config *c = f.c;
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  Timed t(GPT_PROF_NORM, f.s, 0, (double)f.M * c->d_model * (4 + (bf16p ? 2 : 4)));
+  if (bf16p) launch_rmsnorm_bf16(x, (bf16 *)h, nullptr, f.M, c->d_model, c->norm_eps, f.s);
+  else launch_rmsnorm_f32(x, (float *)h, nullptr, f.M, c->d_model, c->norm_eps, f.s);
+}
+
+// q, k, v of layer l from h = bf->h: q -> bf->q, k -> bf->k, v -> bf->vt
+// (transposed for bf16), after RoPE and QK-norm, and into the cache when
+// there is one.  fused: in the GEMM's epilogue; otherwise the fp32
+// projection goes to bf->qkv first and a scatter kernel finishes.
+void fwd_qkv(const Fwd &f, int l, bool fused) {
+  const gpt_config *c = f.c;
+  Bufs &bf = *f.bf;
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim;
+  const int qkv_n = (H + 2 * Hkv) * dh, M = f.M;
+  GemmArgs g = gemm(bf.h, d, f.w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, fused ? EPI_QKV : EPI_F32);
+  g.W1 = f.w->wk[l];
+  g.W2 = f.w->wv[l];
+  g.n1 = H * dh;
+  g.n2 = (H + Hkv) * dh;
+  if (fused) {
+    QkvEpi &e = g.qkv;
+    e.seq = bf.seq;
+    e.pos = bf.pos;
+    e.vcol = bf.vcol;
+    e.cos = f.cos;
+    e.sin = f.sin;
+    e.eps = c->norm_eps;
+    e.qk_norm = c->qk_norm;
+    e.H = H;
+    e.Hkv = Hkv;
+    e.q_out = (bf16 *)bf.q;
+    e.k_out = (bf16 *)bf.k;
+    e.vt_out = (bf16 *)bf.vt;
+    e.ldvt = bf.ldvt;
+    e.kv = f.pv;
+    e.layer = l;
+    e.use_cache = f.use_cache;
+  }
+  run_gemm(c, g, GPT_PROF_GEMM, f.s);
+  if (fused) return;
+  ScatterArgs sa{};
+  sa.qkv = bf.qkv;
+  sa.M = M;
+  sa.H = H;
+  sa.Hkv = Hkv;
+  sa.seq = bf.seq;
+  sa.pos = bf.pos;
+  sa.vcol = bf.vcol;
+  sa.cos = f.cos;
+  sa.sin = f.sin;
+  sa.qk_norm = c->qk_norm;
+  sa.eps = c->norm_eps;
+  sa.q_out = bf.q;
+  sa.k_out = bf.k;
+  sa.vt_out = bf.vt;
+  sa.ldvt = bf.ldvt;
+  sa.kv = f.pv;
+  sa.layer = l;
+  sa.use_cache = f.use_cache;
+  sa.head_dim = dh;
+  Timed t(GPT_PROF_NORM, f.s, 0, (double)M * qkv_n * 4 + (double)M * qkv_n * (bf16p ? 2 : 4));
+  if (bf16p) launch_rope_norm_scatter_bf16(sa, f.s);
+  else launch_qkv_scatter_f32(sa, f.s);
+}
+
+// o = causal attention of bf->q against bf->k, bf->vt
+void fwd_attention(const Fwd &f) {
+  const gpt_config *c = f.c;
+  Bufs &bf = *f.bf;
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim;
+  Timed t(GPT_PROF_ATTN, f.s, f.attn_flops, (double)f.M * (H + 2 * Hkv + H) * dh * (bf16p ? 2 : 4));
+  if (bf16p) {
+    AttnPrefillArgs aa{};
+    aa.q = (const bf16 *)bf.q;
+    aa.k = (const bf16 *)bf.k;
+    aa.vt = (const bf16 *)bf.vt;
+    aa.ldvt = bf.ldvt;
+    aa.cu = bf.cu;
+    aa.cu_pad = bf.cu_pad;
+    aa.H = H;
+    aa.Hkv = Hkv;
+    aa.qk_norm = c->qk_norm;
+    aa.n_seqs = f.n_seqs;
+    aa.max_wg = (f.max_len * (H / Hkv) + kAttnPrefillRows - 1) / kAttnPrefillRows;
+    aa.o = (bf16 *)bf.o;
+    launch_attn_prefill_bf16(aa, f.s);
+  } else {
+    AttnF32Args aa{};
+    aa.q = (const float *)bf.q;
+    aa.k = (const float *)bf.k;
+    aa.v = (const float *)bf.vt;
+    aa.seq = bf.seq;
+    aa.pos = bf.pos;
+    aa.M = f.M;
+    aa.H = H;
+    aa.Hkv = Hkv;
+    aa.dh = dh;
+    aa.o = (float *)bf.o;
+    launch_attn_prefill_f32(aa, f.s);
+  }
+}
+
+// x += Wo Attn(q, k, v) with q, k, v from RMSNorm(x): the first half of layer l
+void fwd_attn_half(const Fwd &f, int l) {
+  const gpt_config *c = f.c;
+  Bufs &bf = *f.bf;
+  const int d = c->d_model, H = c->n_head, dh = c->head_dim;
+  fwd_norm(f, bf.x, bf.h);
+  fwd_qkv(f, l, c->dtype == GPT_DTYPE_BF16 && f.M > 64);
+  fwd_attention(f);
+  run_gemm(c, gemm(bf.o, H * dh, f.w->wo[l], f.M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, f.s);
+}
+
+// x += W2 act(W1 RMSNorm(x)): the second half of layer l
+void fwd_mlp_half(const Fwd &f, int l) {
+  const gpt_config *c = f.c;
+  Bufs &bf = *f.bf;
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int d = c->d_model, F = c->d_ff, M = f.M;
+  fwd_norm(f, bf.x, bf.h);
+  run_gemm(c, gemm(bf.h, d, f.w->w1[l], M, F, d, bf.u, F,
+                   bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
+           GPT_PROF_GEMM, f.s);
+  run_gemm(c, gemm(bf.u, F, f.w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, f.s);
+}
+
 // Prefill forward.  Logits mode (targets == NULL): logits of `logits_rows`
 // rows, optional lse and probs.  Loss mode: every row's cross-entropy
 // against targets into loss (optional lse, mean); logits is unused.
@@ -461,112 +687,10 @@ gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *
     if (bf16p) launch_embed_bf16(tokens, (const bf16 *)w->wte, bf.x, M, d, s);
     else launch_embed_f32(tokens, (const float *)w->wte, (const float *)w->wpe, bf.pos, bf.x, M, d, s);
   }
-  double attn_flops = 0;
-  for (int b = 0; b < n_seqs; ++b) {
-    const double L = cu_seqlens[b + 1] - cu_seqlens[b];
-    attn_flops += 4.0 * H * dh * L * (L + 1) / 2;
-  }
+  Fwd fw = make_fwd(c, w, rope_cos, rope_sin, &bf, pv, kv != nullptr, M, n_seqs, cu_seqlens, s);
   for (int l = 0; l < c->n_layer; ++l) {
-    {
-      Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
-      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
-      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, M, d, c->norm_eps, s);
-    }
-    const bool fused_qkv = bf16p && M > 64;
-    GemmArgs g = gemm(bf.h, d, w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, fused_qkv ? EPI_QKV : EPI_F32);
-    g.W1 = w->wk[l];
-    g.W2 = w->wv[l];
-    g.n1 = H * dh;
-    g.n2 = (H + Hkv) * dh;
-    if (fused_qkv) {
-      QkvEpi &e = g.qkv;
-      e.seq = bf.seq;
-      e.pos = bf.pos;
-      e.vcol = bf.vcol;
-      e.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
-      e.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
-      e.eps = c->norm_eps;
-      e.qk_norm = c->qk_norm;
-      e.H = H;
-      e.Hkv = Hkv;
-      e.q_out = (bf16 *)bf.q;
-      e.k_out = (bf16 *)bf.k;
-      e.vt_out = (bf16 *)bf.vt;
-      e.ldvt = bf.ldvt;
-      e.kv = pv;
-      e.layer = l;
-      e.use_cache = kv != nullptr;
-    }
-    run_gemm(c, g, GPT_PROF_GEMM, s);
-    if (!fused_qkv) {
-      ScatterArgs sa{};
-      sa.qkv = bf.qkv;
-      sa.M = M;
-      sa.H = H;
-      sa.Hkv = Hkv;
-      sa.seq = bf.seq;
-      sa.pos = bf.pos;
-      sa.vcol = bf.vcol;
-      sa.cos = c->pos_kind == GPT_POS_ROPE ? rope_cos : nullptr;
-      sa.sin = c->pos_kind == GPT_POS_ROPE ? rope_sin : nullptr;
-      sa.qk_norm = c->qk_norm;
-      sa.eps = c->norm_eps;
-      sa.q_out = bf.q;
-      sa.k_out = bf.k;
-      sa.vt_out = bf.vt;
-      sa.ldvt = bf.ldvt;
-      sa.kv = pv;
-      sa.layer = l;
-      sa.use_cache = kv != nullptr;
-      sa.head_dim = dh;
-      Timed t(GPT_PROF_NORM, s, 0, (double)M * qkv_n * 4 + (double)M * qkv_n * (bf16p ? 2 : 4));
-      if (bf16p) launch_rope_norm_scatter_bf16(sa, s);
-      else launch_qkv_scatter_f32(sa, s);
-    }
-    {
-      Timed t(GPT_PROF_ATTN, s, attn_flops, (double)M * (H + 2 * Hkv + H) * dh * (bf16p ? 2 : 4));
-      if (bf16p) {
-        AttnPrefillArgs aa{};
-        aa.q = (const bf16 *)bf.q;
-        aa.k = (const bf16 *)bf.k;
-        aa.vt = (const bf16 *)bf.vt;
-        aa.ldvt = bf.ldvt;
-        aa.cu = bf.cu;
-        aa.cu_pad = bf.cu_pad;
-        aa.H = H;
-        aa.Hkv = Hkv;
-        aa.qk_norm = c->qk_norm;
-        int max_len = 0;
-        for (int b = 0; b < n_seqs; ++b) max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
-        aa.n_seqs = n_seqs;
-        aa.max_wg = (max_len * (H / Hkv) + kAttnPrefillRows - 1) / kAttnPrefillRows;
-        aa.o = (bf16 *)bf.o;
-        launch_attn_prefill_bf16(aa, s);
-      } else {
-        AttnF32Args aa{};
-        aa.q = (const float *)bf.q;
-        aa.k = (const float *)bf.k;
-        aa.v = (const float *)bf.vt;
-        aa.seq = bf.seq;
-        aa.pos = bf.pos;
-        aa.M = M;
-        aa.H = H;
-        aa.Hkv = Hkv;
-        aa.dh = dh;
-        aa.o = (float *)bf.o;
-        launch_attn_prefill_f32(aa, s);
-      }
-    }
-    run_gemm(c, gemm(bf.o, H * dh, w->wo[l], M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
-    {
-      Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + (bf16p ? 2 : 4)));
-      if (bf16p) launch_rmsnorm_bf16(bf.x, (bf16 *)bf.h, nullptr, M, d, c->norm_eps, s);
-      else launch_rmsnorm_f32(bf.x, (float *)bf.h, nullptr, M, d, c->norm_eps, s);
-    }
-    run_gemm(c, gemm(bf.h, d, w->w1[l], M, F, d, bf.u, F,
-                     bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
-             GPT_PROF_GEMM, s);
-    run_gemm(c, gemm(bf.u, F, w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, s);
+    fwd_attn_half(fw, l);
+    fwd_mlp_half(fw, l);
   }
   {
     Timed t(GPT_PROF_NORM, s, 0, (double)rows * d * (4 + (bf16p ? 2 : 4)));
@@ -620,9 +744,280 @@ gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *
     for (int b = 0; b < n_seqs; ++b) kv->lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
   return GPT_OK;
 }
+// dst[c][r] = src[r][c] in the model dtype (src in fp32 or the model dtype)
+void tr_f32(const gpt_config *c, const float *src, long long lds, int R, int C, void *dst, long long ldd, int Rp,
+            hipStream_t s) {
+  if (c->dtype == GPT_DTYPE_BF16) launch_transpose<float, bf16>(src, lds, R, C, (bf16 *)dst, ldd, Rp, s);
+  else launch_transpose<float, float>(src, lds, R, C, (float *)dst, ldd, Rp, s);
+}
+void tr_md(const gpt_config *c, const void *src, long long lds, int R, int C, void *dst, long long ldd, int Rp,
+           hipStream_t s) {
+  if (c->dtype == GPT_DTYPE_BF16)
+    launch_transpose<bf16, bf16>((const bf16 *)src, lds, R, C, (bf16 *)dst, ldd, Rp, s);
+  else launch_transpose<float, float>((const float *)src, lds, R, C, (float *)dst, ldd, Rp, s);
+}
+
+// Mean next-token loss and its gradient for every weight.  Forward: the
+// prefill's layers, keeping the residual stream at each layer's input and
+// middle, then the materialised logits.  Backward: everything else is
+// recomputed per layer from the kept residual stream.  Linear layers
+// y = X W^T take dX = dY W and dW = dY^T X, both on the forward's GEMM
+// kernels with transposed copies of W, dY and X.
+gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin,
+                           const int32_t *tokens, const int32_t *targets, const int32_t *cu_seqlens, int32_t n_seqs,
+                           const gpt_grads *gr, float *loss, float *mean, void *workspace, size_t workspace_bytes,
+                           gpt_stream_t stream) {
+  gpt_status st = check_config(c);
+  if (st) return st;
+  if ((st = check_weights(c, w))) return st;
+  if (!tokens || !targets || !cu_seqlens || !gr || !loss || !workspace) return fail(GPT_ERR_ARG, "NULL required pointer");
+  if (!gr->wte || !gr->lm_head || !gr->wq || !gr->wk || !gr->wv || !gr->wo || !gr->w1 || !gr->w2)
+    return fail(GPT_ERR_ARG, "NULL gradient pointer");
+  if (c->pos_kind == GPT_POS_LEARNED && !gr->wpe) return fail(GPT_ERR_ARG, "wpe gradient required");
+  for (int l = 0; l < c->n_layer; ++l)
+    if (!gr->wq[l] || !gr->wk[l] || !gr->wv[l] || !gr->wo[l] || !gr->w1[l] || !gr->w2[l])
+      return fail(GPT_ERR_ARG, "layer %d gradient pointer is NULL", l);
+  if (n_seqs <= 0) return fail(GPT_ERR_ARG, "n_seqs must be positive");
+  if (n_seqs > kMaxPrefillSeqs) return fail(GPT_ERR_UNSUPPORTED, "at most %d sequences", kMaxPrefillSeqs);
+  if (c->pos_kind == GPT_POS_ROPE && (!rope_cos || !rope_sin)) return fail(GPT_ERR_ARG, "RoPE tables required");
+  if (c->head_dim > 128) return fail(GPT_ERR_UNSUPPORTED, "head_dim above 128");
+  if (cu_seqlens[0] != 0) return fail(GPT_ERR_ARG, "cu_seqlens[0] must be 0");
+  for (int b = 0; b < n_seqs; ++b) {
+    const int len = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (len <= 0) return fail(GPT_ERR_ARG, "sequence %d is empty or cu_seqlens decreases", b);
+    if (len > c->max_seq) return fail(GPT_ERR_ARG, "sequence %d longer than max_seq", b);
+  }
+  const int M = cu_seqlens[n_seqs];
+  {
+    // the GEMM kernels address an operand with 32-bit element offsets
+    const long long Mp = (M + 63) / 64 * 64;
+    const long long widest = std::max({(long long)c->vocab, (long long)c->d_ff,
+                                       (long long)(c->n_head + 2 * c->n_kv_head) * c->head_dim});
+    if (widest * Mp >= (1LL << 31))
+      return fail(GPT_ERR_UNSUPPORTED, "%d rows x %lld columns exceed the backward's 32-bit operand offsets", M,
+                  widest);
+  }
+  const size_t need = carve_train(c, M, n_seqs, nullptr, nullptr, nullptr);
+  if (workspace_bytes < need) return fail(GPT_ERR_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(GPT_ERR_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  hipGetLastError();
+  Bufs bf;
+  TrainBufs tb;
+  carve_train(c, M, n_seqs, (char *)workspace, &bf, &tb);
+  const bool bf16p = c->dtype == GPT_DTYPE_BF16;
+  const int d = c->d_model, H = c->n_head, Hkv = c->n_kv_head, dh = c->head_dim, F = c->d_ff, V = c->vocab;
+  const int L = c->n_layer, qkv_n = (H + 2 * Hkv) * dh, Mp = tb.Mp;
+  const size_t es = bf16p ? 2 : 4;
+  auto xs = [&](int i) { return tb.xs + (long long)i * M * d; };
+  auto copy_x = [&](float *dst) {
+    hipMemcpyAsync(dst, bf.x, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s);
+  };
+  // C[M][N] = A[M][K] B[N][K]^T into fp32
+  auto mm = [&](const void *A, long long lda, const void *B, long long ldb, int m, int n, int k, float *C,
+                long long ldc) {
+    GemmArgs g = gemm(A, lda, B, m, n, k, C, ldc, EPI_F32);
+    g.ldw = ldb;
+    run_gemm(c, g, GPT_PROF_BWD_GEMM, s);
+  };
+  auto to_md = [&](const float *src, void *dst, long long n) {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)n * (4 + es));
+    if (bf16p) launch_cast<float, bf16>(src, (bf16 *)dst, n, s);
+    else launch_cast<float, float>(src, (float *)dst, n, s);
+  };
+  auto rms_bwd = [&](const float *x, const float *dy) {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * 16);
+    launch_rms_bwd(x, dy, tb.dx, M, d, c->norm_eps, s);
+  };
+
+  // ---- forward, keeping the residual stream
+  PrefillMeta meta;
+  meta.n = n_seqs;
+  for (int b = 0; b <= n_seqs; ++b) meta.cu[b] = cu_seqlens[b];
+  {
+    Timed t(GPT_PROF_NORM, s, 0, 0);
+    prefill_meta_kernel<<<1, 256, 0, s>>>(meta, bf.cu, bf.cu_pad, bf.lastrows, bf.ctr, kCounters);
+    launch_rowinfo(bf.cu, bf.cu_pad, n_seqs, M, bf.seq, bf.pos, bf.vcol, s);
+  }
+  {
+    Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + es));
+    if (bf16p) launch_embed_bf16(tokens, (const bf16 *)w->wte, bf.x, M, d, s);
+    else launch_embed_f32(tokens, (const float *)w->wte, (const float *)w->wpe, bf.pos, bf.x, M, d, s);
+  }
+  Fwd fw = make_fwd(c, w, rope_cos, rope_sin, &bf, PagedKV{}, false, M, n_seqs, cu_seqlens, s);
+  for (int l = 0; l < L; ++l) {
+    copy_x(xs(2 * l));
+    fwd_attn_half(fw, l);
+    copy_x(xs(2 * l + 1));
+    fwd_mlp_half(fw, l);
+  }
+  copy_x(xs(2 * L));
+  fwd_norm(fw, bf.x, bf.h);  // hf
+  const bool fused_lse = bf16p && M > 64;
+  {
+    GemmArgs lg = gemm(bf.h, d, w->lm_head, M, V, d, tb.logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
+    lg.part = bf.lpart;
+    run_gemm(c, lg, GPT_PROF_LMHEAD, s);
+    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)M * V * 4);
+    if (fused_lse) launch_lse_combine(bf.lpart, V / kLogitsPartCols, M, bf.lse_tmp, tb.logits, V, nullptr, s);
+    else launch_softmax_lse(tb.logits, M, V, bf.lse_tmp, nullptr, s);
+    launch_ce_from_logits(tb.logits, bf.lse_tmp, targets, V, M, loss, s);
+    if (mean) launch_mean_loss(loss, targets, V, M, mean, s);
+    launch_count_targets(targets, M, V, tb.count, s);
+  }
+
+  // ---- LM head and final norm
+  {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * V * (4 + es));
+    if (bf16p) launch_dlogits<bf16>(tb.logits, bf.lse_tmp, targets, tb.count, M, V, (bf16 *)tb.dl, s);
+    else launch_dlogits<float>(tb.logits, bf.lse_tmp, targets, tb.count, M, V, (float *)tb.dl, s);
+  }
+  {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)(M * (long long)V + (long long)M * d + (long long)V * d) * 2 * es);
+    tr_md(c, tb.dl, V, M, V, tb.trA, Mp, Mp, s);    // dl^T [V][Mp]
+    tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);     // hf^T [d][Mp]
+    tr_md(c, w->lm_head, d, V, d, tb.wT, V, V, s);  // W_lm^T [d][V]
+  }
+  mm(tb.trA, Mp, tb.trB, Mp, V, d, Mp, gr->lm_head, d);  // dW_lm = dl^T hf
+  mm(tb.dl, V, tb.wT, V, M, d, V, tb.dh, d);              // dhf = dl W_lm
+  hipMemsetAsync(tb.dx, 0, (size_t)M * d * 4, s);
+  rms_bwd(xs(2 * L), tb.dh);
+
+  for (int l = L - 1; l >= 0; --l) {
+    const float *xl = xs(2 * l), *xm = xs(2 * l + 1);
+    // ---- MLP: x = xm + W2 act(W1 rms(xm))
+    fwd_norm(fw, xm, bf.h);                                       // h2
+    mm(bf.h, d, w->w1[l], d, M, F, d, tb.z, F);                   // z
+    {
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (4 + es) + (double)M * d * (8 + 2 * es) +
+                                            (double)M * F * 2 * es + (double)d * F * 2 * es);
+      if (bf16p) launch_act_bwd<bf16>(tb.z, nullptr, (bf16 *)tb.u, nullptr, (long long)M * F, c->act, s);
+      else launch_act_bwd<float>(tb.z, nullptr, (float *)tb.u, nullptr, (long long)M * F, c->act, s);
+      tr_f32(c, tb.dx, d, M, d, tb.trA, Mp, Mp, s);              // dx^T [d][Mp]
+      tr_md(c, tb.u, F, M, F, tb.trB, Mp, Mp, s);                // u^T [F][Mp]
+      tr_md(c, w->w2[l], F, d, F, tb.wT, d, d, s);               // W2^T [F][d]
+    }
+    mm(tb.trA, Mp, tb.trB, Mp, d, F, Mp, gr->w2[l], F);           // dW2 = dx^T u
+    const void *dxA = tb.dx;
+    if (bf16p) {
+      to_md(tb.dx, tb.dxb, (long long)M * d);
+      dxA = tb.dxb;
+    }
+    mm(dxA, d, tb.wT, d, M, F, d, tb.du, F);                      // du = dx W2
+    {
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (8 + es) + (double)M * (F + d) * 2 * es +
+                                            (double)d * F * 2 * es);
+      if (bf16p) launch_act_bwd<bf16>(tb.z, tb.du, nullptr, (bf16 *)tb.dz, (long long)M * F, c->act, s);
+      else launch_act_bwd<float>(tb.z, tb.du, nullptr, (float *)tb.dz, (long long)M * F, c->act, s);
+      tr_md(c, tb.dz, F, M, F, tb.trA, Mp, Mp, s);               // dz^T [F][Mp]
+      tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);                // h2^T [d][Mp]
+      tr_md(c, w->w1[l], d, F, d, tb.wT, F, F, s);               // W1^T [d][F]
+    }
+    mm(tb.trA, Mp, tb.trB, Mp, F, d, Mp, gr->w1[l], d);           // dW1 = dz^T h2
+    mm(tb.dz, F, tb.wT, F, M, d, F, tb.dh, d);                    // dh2 = dz W1
+    rms_bwd(xm, tb.dh);
+
+    // ---- attention: xm = xl + Wo Attn(q, k, v)
+    fwd_norm(fw, xl, bf.h);                                       // h
+    fwd_qkv(fw, l, false);                                        // pre -> bf.qkv; q, k, vt
+    fwd_attention(fw);                                            // o
+    {
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * (4 + es) + (double)M * H * dh * 2 * es +
+                                            (double)d * H * dh * 2 * es);
+      tr_f32(c, tb.dx, d, M, d, tb.trA, Mp, Mp, s);              // dx^T
+      tr_md(c, bf.o, H * dh, M, H * dh, tb.trB, Mp, Mp, s);      // o^T [H dh][Mp]
+      tr_md(c, w->wo[l], H * dh, d, H * dh, tb.wT, d, d, s);     // Wo^T [H dh][d]
+    }
+    mm(tb.trA, Mp, tb.trB, Mp, d, H * dh, Mp, gr->wo[l], H * dh); // dWo = dx^T o
+    if (bf16p) {
+      to_md(tb.dx, tb.dxb, (long long)M * d);
+      dxA = tb.dxb;
+    }
+    mm(dxA, d, tb.wT, d, M, H * dh, d, tb.dO, H * dh);            // dO = dx Wo
+    {
+      AttnBwdArgs ab{};
+      ab.q = bf.q;
+      ab.k = bf.k;
+      ab.o = bf.o;
+      ab.v = bf.qkv + (H + Hkv) * dh;
+      ab.ldv = qkv_n;
+      ab.v_bf16 = bf16p;
+      ab.dout = tb.dO;
+      ab.pos = bf.pos;
+      ab.seq = bf.seq;
+      ab.cu = bf.cu;
+      ab.M = M;
+      ab.H = H;
+      ab.Hkv = Hkv;
+      ab.dh = dh;
+      ab.dq = tb.dq;
+      ab.dk = tb.dk;
+      ab.dv = tb.dv;
+      ab.lse = tb.lse;
+      ab.dsum = tb.dsum;
+      Timed t(GPT_PROF_BWD_ATTN, s, 2.5 * fw.attn_flops, (double)M * (3 * H + 4 * Hkv) * dh * 4);
+      if (bf16p) launch_attn_bwd<bf16>(ab, s);
+      else launch_attn_bwd<float>(ab, s);
+    }
+    {
+      QkvBwdArgs qa{};
+      qa.pre = bf.qkv;
+      qa.dq = tb.dq;
+      qa.dk = tb.dk;
+      qa.dv = tb.dv;
+      qa.pos = bf.pos;
+      qa.cos = fw.cos;
+      qa.sin = fw.sin;
+      qa.M = M;
+      qa.H = H;
+      qa.Hkv = Hkv;
+      qa.dh = dh;
+      qa.qk_norm = c->qk_norm;
+      qa.eps = c->norm_eps;
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * qkv_n * (8 + 3 * es) + (double)M * d * 2 * es +
+                                            (double)qkv_n * d * 2 * es);
+      if (bf16p) launch_qkv_bwd<bf16>(qa, (bf16 *)tb.dqkv, s);
+      else launch_qkv_bwd<float>(qa, (float *)tb.dqkv, s);
+      tr_md(c, tb.dqkv, qkv_n, M, qkv_n, tb.trA, Mp, Mp, s);     // dqkv^T [qkv_n][Mp]
+      tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);                // h^T [d][Mp]
+      // [Wq; Wk; Wv]^T [d][qkv_n]
+      tr_md(c, w->wq[l], d, H * dh, d, tb.wT, qkv_n, H * dh, s);
+      tr_md(c, w->wk[l], d, Hkv * dh, d, (char *)tb.wT + (size_t)H * dh * es, qkv_n, Hkv * dh, s);
+      tr_md(c, w->wv[l], d, Hkv * dh, d, (char *)tb.wT + (size_t)(H + Hkv) * dh * es, qkv_n, Hkv * dh, s);
+    }
+    mm(tb.trA, Mp, tb.trB, Mp, H * dh, d, Mp, gr->wq[l], d);
+    mm((char *)tb.trA + (size_t)H * dh * Mp * es, Mp, tb.trB, Mp, Hkv * dh, d, Mp, gr->wk[l], d);
+    mm((char *)tb.trA + (size_t)(H + Hkv) * dh * Mp * es, Mp, tb.trB, Mp, Hkv * dh, d, Mp, gr->wv[l], d);
+    mm(tb.dqkv, qkv_n, tb.wT, qkv_n, M, d, qkv_n, tb.dh, d);       // dh = dqkv [Wq; Wk; Wv]
+    rms_bwd(xl, tb.dh);
+  }
+  // ---- embeddings
+  {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * 12);
+    hipMemsetAsync(gr->wte, 0, (size_t)V * d * 4, s);
+    if (c->pos_kind == GPT_POS_LEARNED) hipMemsetAsync(gr->wpe, 0, (size_t)c->max_seq * d * 4, s);
+    launch_embed_bwd(tokens, bf.pos, tb.dx, gr->wte, c->pos_kind == GPT_POS_LEARNED ? gr->wpe : nullptr, M, d, s);
+  }
+  return hip_check("gpt_loss_grads launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t gpt_train_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_seqs) {
+  if (check_config(c) != GPT_OK || max_tokens <= 0 || max_seqs <= 0) return 0;
+  return carve_train(c, max_tokens, max_seqs, nullptr, nullptr, nullptr);
+}
+
+gpt_status gpt_loss_grads(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin,
+                          const int32_t *tokens, const int32_t *targets, const int32_t *cu_seqlens, int32_t n_seqs,
+                          const gpt_grads *grads, float *loss, float *mean, void *workspace,
+                          size_t workspace_bytes, gpt_stream_t stream) {
+  return loss_grads_impl(c, w, rope_cos, rope_sin, tokens, targets, cu_seqlens, n_seqs, grads, loss, mean,
+                         workspace, workspace_bytes, stream);
+}
 
 gpt_status gpt_prefill(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
                        const float *rope_sin, const int32_t *tokens, const int32_t *cu_seqlens,

@@ -84,6 +84,47 @@ struct AdamHyper {
 void launch_adam(float *p, const float *g, float *m, float *v, bf16 *pb, long long n, const AdamHyper &h,
                  hipStream_t s);
 
+// ------------------------------------------------------------ loss backward
+// dst[c][r] = src[r][c] (r < R, c < C), zero for R <= r < Rp.
+template <typename TI, typename TO>
+void launch_transpose(const TI *src, long long lds, int R, int C, TO *dst, long long ldd, int Rp, hipStream_t s);
+template <typename TI, typename TO>
+void launch_cast(const TI *src, TO *dst, long long n, hipStream_t s);
+// dx[m] += the gradient through y = x / sqrt(mean(x^2) + eps), given dy
+void launch_rms_bwd(const float *x, const float *dy, float *dx, int M, int d, float eps, hipStream_t s);
+// u = act(z) and dz = du act'(z) (either may be NULL)
+template <typename T>
+void launch_act_bwd(const float *z, const float *du, T *u, T *dz, long long n, int relu2, hipStream_t s);
+struct QkvBwdArgs {
+  const float *pre;             // [M][(H + 2Hkv) dh] projection output before RoPE / QK-norm
+  const float *dq, *dk, *dv;    // [M][H dh], [M][Hkv dh] x 2: gradients of the attention inputs
+  const int *pos;
+  const float *cos, *sin;       // [max_seq][dh/2] or NULL (no RoPE)
+  int M, H, Hkv, dh, qk_norm;
+  float eps;
+};
+template <typename T>
+void launch_qkv_bwd(const QkvBwdArgs &a, T *dqkv, hipStream_t s);
+struct AttnBwdArgs {
+  const void *q, *k, *o;  // [M][H dh], [M][Hkv dh], [M][H dh] in the model dtype
+  const float *v;         // rows of ldv floats; v_bf16: rounded to bf16 as the forward used them
+  long long ldv;
+  int v_bf16;
+  const float *dout;      // [M][H dh] gradient of the attention output
+  const int *pos, *seq, *cu;
+  int M, H, Hkv, dh;
+  float *dq, *dk, *dv;    // [M][H dh], [M][Hkv dh] x 2
+  float *lse, *dsum;      // [M][H] scratch
+};
+template <typename T>
+void launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
+template <typename T>
+void launch_dlogits(const float *logits, const float *lse, const int *targets, const int *count, int rows, int V,
+                    T *dl, hipStream_t s);
+void launch_embed_bwd(const int *tokens, const int *pos, const float *dx, float *dwte, float *dwpe, int M, int d,
+                      hipStream_t s);
+void launch_count_targets(const int *targets, int M, int V, int *count, hipStream_t s);
+
 // ------------------------------------------------------------ GEMMs
 enum Epi {
   EPI_BF16 = 0,

@@ -261,6 +261,55 @@ gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, f
                              const float *uniforms, int32_t *tokens_out, gpt_stream_t stream);
 
 /*
+ * Gradients of the mean next-token loss, one fp32 device array per weight,
+ * shaped like it: wte [vocab, d_model]; wpe [max_seq, d_model] (used only
+ * with GPT_POS_LEARNED, else may be NULL); lm_head [vocab, d_model]; per
+ * layer (host arrays of n_layer device pointers) wq, wk, wv, wo, w1, w2.
+ */
+typedef struct {
+  float *wte, *wpe, *lm_head;
+  float *const *wq, *const *wk, *const *wv, *const *wo, *const *w1, *const *w2;
+} gpt_grads;
+
+/* Bytes of device scratch gpt_loss_grads needs for up to max_tokens packed
+ * rows and max_seqs sequences; 0 for an invalid or unsupported config. */
+size_t gpt_train_workspace_bytes(const gpt_config *c, int32_t max_tokens, int32_t max_seqs);
+
+/*
+ * gpt_loss_grads -- the mean next-token cross-entropy of packed sequences
+ * and its gradient with respect to every weight.  [microgpt "Training
+ * process", items 2 and 3]: the forward pass predicts each next token, the
+ * loss is the cross-entropy against the real one, and back-propagation runs
+ * the chain rule from the loss back to every parameter.
+ *   loss = (1/n) sum over rows r with t = targets[r] in [0, vocab) of
+ *          log sum_v exp(logits[r][v]) - logits[r][t],   n = their number
+ * (rows whose target lies outside [0, vocab) count for nothing).  The
+ * forward is gpt_prefill's (no cache).  The gradient of the loss with
+ * respect to row r's logits is (softmax(logits[r]) - onehot(t)) / n; it is
+ * carried back through the LM head, the final RMSNorm, each block (MLP,
+ * RMSNorm, output projection, attention, QK-norm, RoPE, the Q/K/V
+ * projections) and the embeddings.
+ *   tokens, targets  device int32 [total], packed
+ *   cu_seqlens, n_seqs, rope tables: as gpt_prefill
+ *   grads       gradients, overwritten (not accumulated)
+ *   loss        device fp32 [total] per-row losses (0 for skipped rows)
+ *   mean        device fp32 [1] or NULL: the loss above
+ *   workspace   >= gpt_train_workspace_bytes(c, total, n_seqs), 256-byte
+ *               aligned; clobbered
+ * bf16 models run every matrix product as a bf16 GEMM with fp32
+ * accumulation (gradients rounded to bf16 where they are GEMM operands);
+ * everything else is fp32.  The token-table gradient sums rows with fp32
+ * atomics, so its last bits may differ from call to call.
+ * Errors: GPT_ERR_ARG (NULL or inconsistent arguments, small workspace),
+ * GPT_ERR_UNSUPPORTED (config), GPT_ERR_HIP.
+ */
+gpt_status gpt_loss_grads(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                          const float *rope_sin, const int32_t *tokens, const int32_t *targets,
+                          const int32_t *cu_seqlens, int32_t n_seqs, const gpt_grads *grads,
+                          float *loss, float *mean, void *workspace, size_t workspace_bytes,
+                          gpt_stream_t stream);
+
+/*
  * gpt_adam_step -- one Adam update of n fp32 parameters, in place.
  * [microgpt "Training process", item 4]: Adam keeps, per parameter, a
  * running mean of the gradient (momentum) and of its square (which scales

@@ -27,7 +27,10 @@ typedef enum {
   GPT_PROF_NORM = 5,        /* RMSNorm, RoPE/QK-norm scatter, embedding */
   GPT_PROF_SOFTMAX = 6,     /* vocabulary softmax / LSE and token selection */
   GPT_PROF_OPTIM = 7,       /* optimiser update (Adam) */
-  GPT_PROF_NCLASSES = 8
+  GPT_PROF_BWD_GEMM = 8,    /* loss backward: GEMMs (weight and input gradients, recomputed projections) */
+  GPT_PROF_BWD_ATTN = 9,    /* loss backward: attention */
+  GPT_PROF_BWD_OTHER = 10,  /* loss backward: transposes, norms, activations, RoPE, logits, embeddings */
+  GPT_PROF_NCLASSES = 11
 } gpt_prof_class;
 
 /* Enable timing for the classes whose bit (1 << class) is set in mask; 0
