@@ -197,6 +197,8 @@ struct TrainBufs {
   void *u, *dz;     // [M][F] model dtype
   float *dO, *dq, *dk, *dv, *lse, *dsum;
   void *dqkv;       // [M][(H + 2Hkv) dh] model dtype
+  void *vb;         // [M][Hkv dh] bf16 V rows for the attention backward
+  float *ksl;       // k-split slabs of the weight-gradient GEMMs
   int *count;
   int Mp;
 };
@@ -235,6 +237,18 @@ size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base,
   t.lse = (float *)take(M * H * 4);
   t.dsum = (float *)take(M * H * 4);
   t.dqkv = take(M * qkv_n * es);
+  t.vb = take(M * Hkv * dh * 2);
+  {
+    // the weight-gradient GEMMs: [out][in] over K = Mp rows
+    const long long shapes[6][2] = {{V, d}, {d, F}, {F, d}, {d, H * dh}, {H * dh, d}, {Hkv * dh, d}};
+    long long most = 0;
+    if (c->dtype == GPT_DTYPE_BF16)
+      for (auto &sh : shapes) {
+        const int ks = gemm_splitk_ways((int)sh[0], (int)sh[1], (int)Mp);
+        if (ks > 1) most = std::max(most, ks * sh[0] * sh[1]);
+      }
+    t.ksl = (float *)take(most * 4);
+  }
   t.count = (int *)take(4);
   if (tb) *tb = t;
   return align256(off);
@@ -821,6 +835,17 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     g.ldw = ldb;
     run_gemm(c, g, GPT_PROF_BWD_GEMM, s);
   };
+  // weight gradient dW[m][n] = sum over the Mp rows of A^T[m][.] B^T[n][.]: k split where the
+  // [m][n] tiling alone leaves CUs idle
+  auto mmw = [&](const void *A, const void *Bt, int m, int n, float *C) {
+    if (!bf16p) {
+      mm(A, Mp, Bt, Mp, m, n, Mp, C, n);
+      return;
+    }
+    GemmArgs g = gemm(A, Mp, Bt, m, n, Mp, C, n, EPI_F32);
+    Timed t(GPT_PROF_BWD_GEMM, s, 2.0 * m * n * Mp, 2.0 * ((double)m + n) * Mp + 4.0 * m * n);
+    launch_gemm_bf16_splitk(g, gemm_splitk_ways(m, n, Mp), tb.ksl, s);
+  };
   auto to_md = [&](const float *src, void *dst, long long n) {
     Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)n * (4 + es));
     if (bf16p) launch_cast<float, bf16>(src, (bf16 *)dst, n, s);
@@ -879,7 +904,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);     // hf^T [d][Mp]
     tr_md(c, w->lm_head, d, V, d, tb.wT, V, V, s);  // W_lm^T [d][V]
   }
-  mm(tb.trA, Mp, tb.trB, Mp, V, d, Mp, gr->lm_head, d);  // dW_lm = dl^T hf
+  mmw(tb.trA, tb.trB, V, d, gr->lm_head);               // dW_lm = dl^T hf
   mm(tb.dl, V, tb.wT, V, M, d, V, tb.dh, d);              // dhf = dl W_lm
   hipMemsetAsync(tb.dx, 0, (size_t)M * d * 4, s);
   rms_bwd(xs(2 * L), tb.dh);
@@ -898,7 +923,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       tr_md(c, tb.u, F, M, F, tb.trB, Mp, Mp, s);                // u^T [F][Mp]
       tr_md(c, w->w2[l], F, d, F, tb.wT, d, d, s);               // W2^T [F][d]
     }
-    mm(tb.trA, Mp, tb.trB, Mp, d, F, Mp, gr->w2[l], F);           // dW2 = dx^T u
+    mmw(tb.trA, tb.trB, d, F, gr->w2[l]);                         // dW2 = dx^T u
     const void *dxA = tb.dx;
     if (bf16p) {
       to_md(tb.dx, tb.dxb, (long long)M * d);
@@ -914,7 +939,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);                // h2^T [d][Mp]
       tr_md(c, w->w1[l], d, F, d, tb.wT, F, F, s);               // W1^T [d][F]
     }
-    mm(tb.trA, Mp, tb.trB, Mp, F, d, Mp, gr->w1[l], d);           // dW1 = dz^T h2
+    mmw(tb.trA, tb.trB, F, d, gr->w1[l]);                         // dW1 = dz^T h2
     mm(tb.dz, F, tb.wT, F, M, d, F, tb.dh, d);                    // dh2 = dz W1
     rms_bwd(xm, tb.dh);
 
@@ -929,7 +954,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       tr_md(c, bf.o, H * dh, M, H * dh, tb.trB, Mp, Mp, s);      // o^T [H dh][Mp]
       tr_md(c, w->wo[l], H * dh, d, H * dh, tb.wT, d, d, s);     // Wo^T [H dh][d]
     }
-    mm(tb.trA, Mp, tb.trB, Mp, d, H * dh, Mp, gr->wo[l], H * dh); // dWo = dx^T o
+    mmw(tb.trA, tb.trB, d, H * dh, gr->wo[l]);                    // dWo = dx^T o
     if (bf16p) {
       to_md(tb.dx, tb.dxb, (long long)M * d);
       dxA = tb.dxb;
@@ -957,8 +982,14 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       ab.lse = tb.lse;
       ab.dsum = tb.dsum;
       Timed t(GPT_PROF_BWD_ATTN, s, 2.5 * fw.attn_flops, (double)M * (3 * H + 4 * Hkv) * dh * 4);
-      if (bf16p) launch_attn_bwd<bf16>(ab, s);
-      else launch_attn_bwd<float>(ab, s);
+      if (bf16p) {
+        // V as bf16 rows, the values the forward's attention read
+        launch_cast_rows(bf.qkv + (H + Hkv) * dh, qkv_n, M, Hkv * dh, (bf16 *)tb.vb, s);
+        ab.vb = (const bf16 *)tb.vb;
+        launch_attn_bwd<bf16>(ab, s);
+      } else {
+        launch_attn_bwd<float>(ab, s);
+      }
     }
     {
       QkvBwdArgs qa{};
@@ -986,9 +1017,9 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       tr_md(c, w->wk[l], d, Hkv * dh, d, (char *)tb.wT + (size_t)H * dh * es, qkv_n, Hkv * dh, s);
       tr_md(c, w->wv[l], d, Hkv * dh, d, (char *)tb.wT + (size_t)(H + Hkv) * dh * es, qkv_n, Hkv * dh, s);
     }
-    mm(tb.trA, Mp, tb.trB, Mp, H * dh, d, Mp, gr->wq[l], d);
-    mm((char *)tb.trA + (size_t)H * dh * Mp * es, Mp, tb.trB, Mp, Hkv * dh, d, Mp, gr->wk[l], d);
-    mm((char *)tb.trA + (size_t)(H + Hkv) * dh * Mp * es, Mp, tb.trB, Mp, Hkv * dh, d, Mp, gr->wv[l], d);
+    mmw(tb.trA, tb.trB, H * dh, d, gr->wq[l]);
+    mmw((char *)tb.trA + (size_t)H * dh * Mp * es, tb.trB, Hkv * dh, d, gr->wk[l]);
+    mmw((char *)tb.trA + (size_t)(H + Hkv) * dh * Mp * es, tb.trB, Hkv * dh, d, gr->wv[l]);
     mm(tb.dqkv, qkv_n, tb.wT, qkv_n, M, d, qkv_n, tb.dh, d);       // dh = dqkv [Wq; Wk; Wv]
     rms_bwd(xl, tb.dh);
   }

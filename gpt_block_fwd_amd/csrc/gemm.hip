@@ -339,6 +339,16 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
 // group 1 before the barrier that ends its last load phase.
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
+  if constexpr (EPI == EPI_F32) {
+    if (gridDim.y > 1) {  // k split: this grid row's slice of K and its output slab
+      const long long k0 = (long long)blockIdx.y * g.K;
+      g.A = (const bf16 *)g.A + k0;
+      g.W0 = (const bf16 *)g.W0 + k0;
+      g.W1 = (const bf16 *)g.W1 + k0;
+      g.W2 = (const bf16 *)g.W2 + k0;
+      g.C = (float *)g.C + blockIdx.y * g.slab;
+    }
+  }
   // The QKV epilogue needs a whole 128-wide head per wave, and 192-column
   // tiles split into 96-column wave tiles: there the four waves of a group
   // split its 128 rows in two and the columns in two (64x128 or 64x96 wave
@@ -643,7 +653,42 @@ void launch_big(const GemmArgs &g, hipStream_t s) {
   gemm_pp_kernel<BM, 256, EPI><<<t256, 512, 0, s>>>(g);
 }
 
+// C[i] = sum over z of slabs[z][i], z in order
+__global__ __launch_bounds__(256) void slab_sum_kernel(const float *slabs, int ks, long long n, float *C) {
+  const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (4 * i4 >= n) return;
+  f32x4 acc = ((const f32x4 *)slabs)[i4];
+  for (int z = 1; z < ks; ++z) acc += ((const f32x4 *)(slabs + (long long)z * n))[i4];
+  ((f32x4 *)C)[i4] = acc;
+}
+
 }  // namespace
+
+int gemm_splitk_ways(int M, int N, int K) {
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int ks = (256 + tiles - 1) / tiles;
+  ks = std::min(ks, K / (8 * BK));
+  while (ks > 1 && K % (ks * BK)) --ks;
+  return std::max(ks, 1);
+}
+
+void launch_gemm_bf16_splitk(const GemmArgs &g, int ks, float *slabs, hipStream_t s) {
+  if (g.M <= 0) return;
+  if (ks <= 1) {
+    launch_gemm_bf16(g, s);
+    return;
+  }
+  GemmArgs p = g;
+  p.epi = EPI_F32;
+  p.K = g.K / ks;
+  p.C = slabs;
+  p.ldc = g.N;
+  p.slab = (long long)g.M * g.N;
+  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  gemm_pp_kernel<256, 256, EPI_F32><<<dim3(tiles, ks), 512, 0, s>>>(p);
+  const long long n = (long long)g.M * g.N;
+  slab_sum_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(slabs, ks, n, (float *)g.C);
+}
 
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
   if (g.M <= 0) return;

@@ -110,6 +110,7 @@ struct AttnBwdArgs {
   const float *v;         // rows of ldv floats; v_bf16: rounded to bf16 as the forward used them
   long long ldv;
   int v_bf16;
+  const bf16 *vb;         // bf16 path with dh = 128: V as bf16 rows [M][Hkv dh] (else NULL)
   const float *dout;      // [M][H dh] gradient of the attention output
   const int *pos, *seq, *cu;
   int M, H, Hkv, dh;
@@ -118,6 +119,8 @@ struct AttnBwdArgs {
 };
 template <typename T>
 void launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
+// dst[m][c] = bf16(src[m lds + c]) for c < C
+void launch_cast_rows(const float *src, long long lds, int M, int C, bf16 *dst, hipStream_t s);
 template <typename T>
 void launch_dlogits(const float *logits, const float *lse, const int *targets, const int *count, int rows, int V,
                     T *dl, hipStream_t s);
@@ -166,8 +169,18 @@ struct GemmArgs {
   const int *targets;  // EPI_LOSS: [M] target column of each row (any value)
   float *tgt;          // EPI_LOSS: [M] C[m][targets[m]], written where targets[m] is in [0, N)
   QkvEpi qkv;   // EPI_QKV
+  // k split of the large-M kernel (EPI_F32 only): grid row kz multiplies the
+  // kz-th K-long slice of every row of A and W (rows lda / ldw apart) into
+  // C + kz * slab
+  long long slab;
 };
 void launch_gemm_bf16(const GemmArgs &g, hipStream_t s);         // MFMA, large M
+// C (fp32, ldc = N) = A W^T with the k range split ks ways into slabs
+// [ks][M][N] (ks * M * N floats of scratch), then summed in order: for
+// long-K products whose M x N tiling leaves CUs idle.  K % (64 ks) == 0.
+void launch_gemm_bf16_splitk(const GemmArgs &g, int ks, float *slabs, hipStream_t s);
+// ks for launch_gemm_bf16_splitk: about 256 tiles, at least 8 k-tiles per slice
+int gemm_splitk_ways(int M, int N, int K);
 // Decode-row GEMM (M <= 64, N % 64 == 0, K % 64 == 0).  With ks > 1 the k
 // range is split over ks workgroups per column tile and range kz writes its
 // fp32 partial product to C + kz * slab (EPI_F32 only); the consumer sums

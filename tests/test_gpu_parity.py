@@ -413,14 +413,16 @@ def test_tiny_loss_grads_fp32():
         assert err <= 1e-4 * np.max(np.abs(r)) + 1e-7, (k, err, np.max(np.abs(r)))
 
 
-@pytest.mark.parametrize("n_head,n_kv,lens", [(2, 1, [150, 70, 33]), (4, 2, [40, 9]), (2, 2, [130])])
+@pytest.mark.parametrize("n_head,n_kv,lens", [(2, 1, [150, 70, 33]), (4, 2, [40, 9]), (2, 2, [130]),
+                                              (2, 1, [700, 452])])
 def test_small_bf16_loss_grads(n_head, n_kv, lens):
     """bf16 models (MQA, GQA, MHA; 253 rows on the large-M GEMMs, 49 on the
-    decode-row ones): each weight gradient within 5% (relative Frobenius
+    decode-row ones, 1152 rows with the weight-gradient GEMMs split over k):
+    each weight gradient within 5% (relative Frobenius
     norm) of the float64 oracle's, and pointing the same way (cosine >=
     0.998).  The bf16 operands of the forward and of the gradient GEMMs set
     that floor; the loss matches the fused-loss prefill."""
-    cfg = wl.small_model(2, n_head, vocab=2048, max_seq=512, n_kv_head=n_kv)
+    cfg = wl.small_model(2, n_head, vocab=2048, max_seq=1024, n_kv_head=n_kv)
     w = wl.ragged_prefill(cfg, lens, seed=11 + n_head)
     W, dm = device_model(cfg)
     tg = w.next_token_targets()
