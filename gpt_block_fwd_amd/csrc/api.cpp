@@ -139,6 +139,8 @@ struct Bufs {
   int max_splits;
 };
 
+long long b_ldvt(long long M, long long nseq) { return ((M + kPage * nseq) + 63) / 64 * 64; }
+
 size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs *b) {
   size_t off = 0;
   auto take = [&](size_t bytes) -> char * {
@@ -161,7 +163,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.qkv = (float *)take(M * (H + 2 * Hkv) * dh * 4);
   t.q = take(M * H * dh * es);
   t.k = take(M * Hkv * dh * es);
-  t.ldvt = ((M + kPage * nseq) + 63) / 64 * 64;
+  t.ldvt = b_ldvt(M, nseq);
   if (c->dtype == GPT_DTYPE_BF16) t.vt = take(Hkv * dh * t.ldvt * es);
   else t.vt = take(M * Hkv * dh * es);
   t.o = take(M * H * dh * es);
@@ -198,6 +200,9 @@ struct TrainBufs {
   float *dO, *dq, *dk, *dv, *lse, *dsum;
   void *dqkv;       // [M][(H + 2Hkv) dh] model dtype
   void *vb;         // [M][Hkv dh] bf16 V rows for the attention backward
+  void *dob;        // [M][H dh] bf16 dO
+  void *kt, *qt, *dot;  // transposed K, Q, dO (bf16, [dims][ldvt], V^T column order)
+  float *dkp, *dvp; // [H][M][dh] per-query-head partial dK, dV
   float *ksl;       // k-split slabs of the weight-gradient GEMMs
   int *count;
   int Mp;
@@ -238,6 +243,14 @@ size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base,
   t.dsum = (float *)take(M * H * 4);
   t.dqkv = take(M * qkv_n * es);
   t.vb = take(M * Hkv * dh * 2);
+  if (c->dtype == GPT_DTYPE_BF16) {
+    t.dob = take(M * H * dh * 2);
+    t.kt = take(Hkv * dh * b_ldvt(M, nseq) * 2);
+    t.qt = take(H * dh * b_ldvt(M, nseq) * 2);
+    t.dot = take(H * dh * b_ldvt(M, nseq) * 2);
+    t.dkp = (float *)take(H * M * dh * 4);
+    t.dvp = (float *)take(H * M * dh * 4);
+  }
   {
     // the weight-gradient GEMMs: [out][in] over K = Mp rows
     const long long shapes[6][2] = {{V, d}, {d, F}, {F, d}, {d, H * dh}, {H * dh, d}, {Hkv * dh, d}};
@@ -483,6 +496,7 @@ struct Fwd {
   int M, n_seqs, max_len;
   double attn_flops;
   hipStream_t s;
+  float *lse2;  // bf16 attention: each row's base-2 log-sum-exp, or NULL
 };
 
 Fwd make_fwd(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin, Bufs *bf,
@@ -597,6 +611,7 @@ void fwd_attention(const Fwd &f) {
     aa.n_seqs = f.n_seqs;
     aa.max_wg = (f.max_len * (H / Hkv) + kAttnPrefillRows - 1) / kAttnPrefillRows;
     aa.o = (bf16 *)bf.o;
+    aa.lse2 = f.lse2;
     launch_attn_prefill_bf16(aa, f.s);
   } else {
     AttnF32Args aa{};
@@ -908,6 +923,11 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
   mm(tb.dl, V, tb.wT, V, M, d, V, tb.dh, d);              // dhf = dl W_lm
   hipMemsetAsync(tb.dx, 0, (size_t)M * d * 4, s);
   rms_bwd(xs(2 * L), tb.dh);
+  if (bf16p) {  // columns outside the sequences stay zero for every layer
+    hipMemsetAsync(tb.kt, 0, (size_t)Hkv * dh * bf.ldvt * 2, s);
+    hipMemsetAsync(tb.qt, 0, (size_t)H * dh * bf.ldvt * 2, s);
+    hipMemsetAsync(tb.dot, 0, (size_t)H * dh * bf.ldvt * 2, s);
+  }
 
   for (int l = L - 1; l >= 0; --l) {
     const float *xl = xs(2 * l), *xm = xs(2 * l + 1);
@@ -946,7 +966,9 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     // ---- attention: xm = xl + Wo Attn(q, k, v)
     fwd_norm(fw, xl, bf.h);                                       // h
     fwd_qkv(fw, l, false);                                        // pre -> bf.qkv; q, k, vt
-    fwd_attention(fw);                                            // o
+    fw.lse2 = bf16p ? tb.lse : nullptr;
+    fwd_attention(fw);                                            // o (and lse2)
+    fw.lse2 = nullptr;
     {
       Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * (4 + es) + (double)M * H * dh * 2 * es +
                                             (double)d * H * dh * 2 * es);
@@ -983,10 +1005,36 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       ab.dsum = tb.dsum;
       Timed t(GPT_PROF_BWD_ATTN, s, 2.5 * fw.attn_flops, (double)M * (3 * H + 4 * Hkv) * dh * 4);
       if (bf16p) {
-        // V as bf16 rows, the values the forward's attention read
+        // V as bf16 rows (the values the forward's attention read), dO in
+        // bf16, and K, Q, dO transposed in the V^T column order
         launch_cast_rows(bf.qkv + (H + Hkv) * dh, qkv_n, M, Hkv * dh, (bf16 *)tb.vb, s);
-        ab.vb = (const bf16 *)tb.vb;
-        launch_attn_bwd<bf16>(ab, s);
+        launch_cast<float, bf16>(tb.dO, (bf16 *)tb.dob, (long long)M * H * dh, s);
+        launch_transpose_cols<bf16>((const bf16 *)bf.k, Hkv * dh, M, Hkv * dh, bf.vcol, (bf16 *)tb.kt, bf.ldvt, s);
+        launch_transpose_cols<bf16>((const bf16 *)bf.q, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.qt, bf.ldvt, s);
+        launch_transpose_cols<bf16>((const bf16 *)tb.dob, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.dot, bf.ldvt, s);
+        AttnBwdMfmaArgs mb{};
+        mb.q = (const bf16 *)bf.q;
+        mb.k = (const bf16 *)bf.k;
+        mb.vb = (const bf16 *)tb.vb;
+        mb.dob = (const bf16 *)tb.dob;
+        mb.kt = (const bf16 *)tb.kt;
+        mb.qt = (const bf16 *)tb.qt;
+        mb.dot = (const bf16 *)tb.dot;
+        mb.ldt = bf.ldvt;
+        mb.lse2 = tb.lse;
+        mb.dsum = tb.dsum;
+        mb.cu = bf.cu;
+        mb.cu_pad = bf.cu_pad;
+        mb.n_seqs = n_seqs;
+        mb.max_len = fw.max_len;
+        mb.max_wg = (fw.max_len * (H / Hkv) + 127) / 128;
+        mb.M = M;
+        mb.H = H;
+        mb.Hkv = Hkv;
+        mb.dq = tb.dq;
+        mb.dkp = tb.dkp;
+        mb.dvp = tb.dvp;
+        launch_attn_bwd_mfma(mb, tb.dO, (const bf16 *)bf.o, tb.dk, tb.dv, s);
       } else {
         launch_attn_bwd<float>(ab, s);
       }

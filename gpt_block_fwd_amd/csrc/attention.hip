@@ -278,6 +278,8 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
     if (r >= rows_total) continue;
     const float inv = 1.0f / lrow[rb];
     const int t = r / G;
+    if (a.lse2 && g == 0)  // base-2 log-sum-exp of the row's scaled scores
+      a.lse2[(long long)(tok0 + t) * H + gk * G + (r - t * G)] = (FIXREF ? kScoreBound : mrow[rb]) + log2f(lrow[rb]);
     bf16 *op = a.o + ((long long)(tok0 + t) * H + gk * G + (r - t * G)) * DH + 4 * g;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -288,6 +290,275 @@ __global__ __launch_bounds__(64 * NWV) void attn_prefill_kernel(AttnPrefillArgs 
         *(bf16x4 *)(op + 32 * d + 8 * c) = o;
       }
   }
+}
+
+// ------------------------------------------------------------------ backward
+// Attention backward on MFMA (bf16 operands, fp32 accumulation), two passes
+// that recompute the probabilities P = 2^(s sc - lse2) from the forward's
+// base-2 row log-sum-exp:
+//   dq pass, row-parallel like the forward: S^T = K Q^T and dP^T = V dO^T
+//     per 64-key tile, dS = P (dP - D), dQ^T += K^T dS^T;
+//   dk/dv pass, key-parallel with the roles of rows and keys swapped: the
+//     workgroup's keys and their V rows are the fragments, 64-position tiles
+//     of Q, dO, Q^T and dO^T stream through LDS, dV^T += dO^T P,
+//     dK^T += Q^T dS, per query head (a fixed-order sum merges the heads of
+//     a K/V group).
+// D = dO . O per row.  The transposed operands K^T, Q^T, dO^T are stored like
+// the forward's V^T (columns in vperm16 order, zero padding), so P and dS
+// feed the MFMA exactly as P does in the forward.
+
+// 64 rows x 128 bf16 of a row tile into the kidx layout: 16 instructions of 1 KB
+// (4 rows each), row i of the tile read from base + min(i0 + i, last) * stride.
+DEV void dma_rows(bf16 *dst, const bf16 *base, long long stride, int i0, int last, int wave, int nwv, int lane) {
+  for (int j = wave; j < 16; j += nwv) {
+    const int row = 4 * j + (lane >> 4), pc = lane & 15;
+    const int src = min(i0 + row, last);
+    __builtin_amdgcn_global_load_lds(GLOBAL_PTR(base + (long long)src * stride + ((pc ^ (row & 15)) << 3)),
+                                     LDS_PTR(&dst[j * 512]), 16, 0, 0);
+  }
+}
+// 128 dims x 64 stored columns of a transposed operand into the vidx layout.
+DEV void dma_cols(bf16 *dst, const bf16 *base, long long ld, long long col0, int wave, int nwv, int lane) {
+  for (int j = wave; j < 16; j += nwv) {
+    const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+    __builtin_amdgcn_global_load_lds(GLOBAL_PTR(base + (long long)dim * ld + col0 + ((pc ^ ((dim >> 1) & 7)) << 3)),
+                                     LDS_PTR(&dst[j * 512]), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdMfmaArgs a) {
+  constexpr int NWV = 4, ROWS = 32 * NWV;
+  __shared__ bf16 sk[KT * DH], sv[KT * DH], skt[DH * KT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, g = lane >> 5;
+  const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * ROWS;
+  const int H = a.H, G = a.H / a.Hkv, gk = blockIdx.z, kvd = a.Hkv * DH;
+  const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
+  const long long col0 = a.cu_pad[b];
+  const int rows_total = len * G;
+  if (R0 >= rows_total) return;
+  const int Rw = R0 + 32 * wave;
+  const int r = min(Rw + c32, rows_total - 1);
+  const int prow = r / G, hq = gk * G + (r - prow * G);
+  const long long qrow = ((long long)(tok0 + prow) * H + hq) * DH;
+  bf16x8 qf[8], dof[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = *(const bf16x8 *)(a.q + qrow + 16 * s + 8 * g);
+    dof[s] = *(const bf16x8 *)(a.dob + qrow + 16 * s + 8 * g);
+  }
+  const float lse2 = a.lse2[(long long)(tok0 + prow) * H + hq];
+  const float D = a.dsum[(long long)(tok0 + prow) * H + hq];
+  const int last_row = min(R0 + ROWS - 1, rows_total - 1);
+  const int n_kt = (last_row / G) / KT + 1;
+  const int pw_max = Rw < rows_total ? min(Rw + 31, rows_total - 1) / G : -1;
+  const float sc = kLog2e / sqrtf((float)DH);
+  f32x16 dq[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dq[d] = (f32x16){};
+  const bf16 *kbase = a.k + (long long)tok0 * kvd + gk * DH;
+  const bf16 *vbase = a.vb + (long long)tok0 * kvd + gk * DH;
+  const bf16 *ktbase = a.kt + (long long)gk * DH * a.ldt;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    dma_rows(sk, kbase, kvd, kt * KT, len - 1, wave, NWV, lane);
+    dma_rows(sv, vbase, kvd, kt * KT, len - 1, wave, NWV, lane);
+    dma_cols(skt, ktbase, a.ldt, col0 + kt * KT, wave, NWV, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt * KT <= pw_max) {
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = (f32x16){};
+        dpacc[kb] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 kf = *(const bf16x8 *)&sk[kidx(32 * kb + c32, 2 * s + g)];
+          const bf16x8 vf = *(const bf16x8 *)&sv[kidx(32 * kb + c32, 2 * s + g)];
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+          dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc[kb], 0, 0, 0);
+        }
+      }
+      // dS = P (dP - D), P = 2^(s sc - lse2) on visible keys
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * KT + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+          const float p = key > prow ? 0.f : fast_exp2(__builtin_fmaf(sacc[kb][e], sc, -lse2));
+          sacc[kb][e] = p * (dpacc[kb][e] - D);
+        }
+      // dQ^T += K^T dS^T, 16 keys per MFMA (k slot 8g+j <-> key 16h + 8(j/4) + 4g + j%4)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st >> 1, h = st & 1;
+        bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[j] = f2bf(sacc[kb][8 * h + j]);
+        const int col = 32 * kb + 16 * h + 8 * g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 ktf = *(const bf16x8 *)&skt[vidx(32 * d + c32, col)];
+          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf, pf, dq[d], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (Rw + c32 >= rows_total) return;
+  const float scale = 1.0f / sqrtf((float)DH);
+  float *op = a.dq + qrow + 4 * g;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *(f32x4 *)(op + 32 * d + 8 * c) = (f32x4){dq[d][4 * c] * scale, dq[d][4 * c + 1] * scale,
+                                                 dq[d][4 * c + 2] * scale, dq[d][4 * c + 3] * scale};
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
+  constexpr int NWV = 4, KEYS = 32 * NWV;
+  __shared__ bf16 sq[KT * DH], sdo[KT * DH], sqt[DH * KT], sdot[DH * KT];
+  __shared__ float sl[KT], sd[KT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, g = lane >> 5;
+  const int b = blockIdx.x, K0 = blockIdx.y * KEYS, hq = blockIdx.z;
+  const int H = a.H, gk = hq * a.Hkv / a.H, kvd = a.Hkv * DH;
+  const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
+  const long long col0 = a.cu_pad[b];
+  if (K0 >= len) return;
+  const int kw = K0 + 32 * wave;                 // this wave's first key
+  const int key = min(kw + c32, len - 1);
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = *(const bf16x8 *)(a.k + (long long)(tok0 + key) * kvd + gk * DH + 16 * s + 8 * g);
+    vf[s] = *(const bf16x8 *)(a.vb + (long long)(tok0 + key) * kvd + gk * DH + 16 * s + 8 * g);
+  }
+  const float sc = kLog2e / sqrtf((float)DH);
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dk[d] = dv[d] = (f32x16){};
+  const bf16 *qbase = a.q + (long long)tok0 * H * DH + hq * DH;
+  const bf16 *obase = a.dob + (long long)tok0 * H * DH + hq * DH;
+  const bf16 *qtb = a.qt + (long long)hq * DH * a.ldt, *otb = a.dot + (long long)hq * DH * a.ldt;
+  const int t_end = (len - 1) / KT;
+  for (int tt = K0 / KT; tt <= t_end; ++tt) {
+    dma_rows(sq, qbase, (long long)H * DH, tt * KT, len - 1, wave, NWV, lane);
+    dma_rows(sdo, obase, (long long)H * DH, tt * KT, len - 1, wave, NWV, lane);
+    dma_cols(sqt, qtb, a.ldt, col0 + tt * KT, wave, NWV, lane);
+    dma_cols(sdot, otb, a.ldt, col0 + tt * KT, wave, NWV, lane);
+    if (tid < KT) {
+      const int pos = min(tt * KT + tid, len - 1);
+      sl[tid] = a.lse2[(long long)(tok0 + pos) * H + hq];
+      sd[tid] = a.dsum[(long long)(tok0 + pos) * H + hq];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // the tile reaches this wave's keys (positions >= key), and the wave has keys
+    if (tt * KT + KT - 1 >= kw && kw < len) {
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        sacc[pb] = (f32x16){};
+        dpacc[pb] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 qa = *(const bf16x8 *)&sq[kidx(32 * pb + c32, 2 * s + g)];
+          const bf16x8 oa = *(const bf16x8 *)&sdo[kidx(32 * pb + c32, 2 * s + g)];
+          sacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc[pb], 0, 0, 0);
+          dpacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc[pb], 0, 0, 0);
+        }
+      }
+      // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile
+      f32x16 pp[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int pl = 32 * pb + 8 * (e >> 2) + 4 * g + (e & 3), pos = tt * KT + pl;
+          const bool vis = pos >= kw + c32 && pos < len;
+          const float p = vis ? fast_exp2(__builtin_fmaf(sacc[pb][e], sc, -sl[pl])) : 0.f;
+          pp[pb][e] = p;
+          sacc[pb][e] = p * (dpacc[pb][e] - sd[pl]);
+        }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int pb = st >> 1, h = st & 1;
+        bf16x8 pf, sf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pf[j] = f2bf(pp[pb][8 * h + j]);
+          sf[j] = f2bf(sacc[pb][8 * h + j]);
+        }
+        const int col = 32 * pb + 16 * h + 8 * g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 ota = *(const bf16x8 *)&sdot[vidx(32 * d + c32, col)];
+          const bf16x8 qta = *(const bf16x8 *)&sqt[vidx(32 * d + c32, col)];
+          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ota, pf, dv[d], 0, 0, 0);
+          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sf, dk[d], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (kw + c32 >= len) return;
+  const float scale = 1.0f / sqrtf((float)DH);
+  const long long orow = ((long long)hq * a.M + tok0 + kw + c32) * DH + 4 * g;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      *(f32x4 *)(a.dkp + orow + 32 * d + 8 * c) = (f32x4){dk[d][4 * c] * scale, dk[d][4 * c + 1] * scale,
+                                                          dk[d][4 * c + 2] * scale, dk[d][4 * c + 3] * scale};
+      *(f32x4 *)(a.dvp + orow + 32 * d + 8 * c) =
+          (f32x4){dv[d][4 * c], dv[d][4 * c + 1], dv[d][4 * c + 2], dv[d][4 * c + 3]};
+    }
+}
+
+// D[m][h] = dO[m][h] . O[m][h] (fp32 dO, bf16 O); 16 lanes per (row, head)
+__global__ __launch_bounds__(256) void attn_bwd_dsum_kernel(const float *dout, const bf16 *o, int M, int H,
+                                                            float *dsum) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  if (item >= (long long)M * H) return;
+  const float *dp = dout + item * DH + 8 * l16;
+  const bf16x8 ov = *(const bf16x8 *)(o + item * DH + 8 * l16);
+  const f32x4 d0 = *(const f32x4 *)dp, d1 = *(const f32x4 *)(dp + 4);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sum += d0[i] * bf2f(ov[i]) + d1[i] * bf2f(ov[4 + i]);
+  sum += __shfl_xor(sum, 1, 64);
+  sum += __shfl_xor(sum, 2, 64);
+  sum += __shfl_xor(sum, 4, 64);
+  sum += __shfl_xor(sum, 8, 64);
+  if (l16 == 0) dsum[item] = sum;
+}
+
+// dst[c][vcol[m]] = src[m][c] (bf16): the V^T-like layout of a row operand
+template <typename TI>
+__global__ __launch_bounds__(256) void transpose_cols_kernel(const TI *src, long long lds, int M, int C,
+                                                             const int *vcol, bf16 *dst, long long ldt) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)M * C) return;
+  const int m = (int)(i / C), c = (int)(i - (long long)m * C);
+  float v;
+  if constexpr (std::is_same<TI, bf16>::value) v = bf2f(src[(long long)m * lds + c]);
+  else v = src[(long long)m * lds + c];
+  dst[(long long)c * ldt + vcol[m]] = f2bf(v);
+}
+
+// dk[m][g dh + d] = sum over the group's query heads h of dkp[h][m][d] (in order)
+__global__ __launch_bounds__(256) void sum_heads_kernel(const float *part, int M, int H, int Hkv, float *out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long n = (long long)M * Hkv * DH;
+  if (i >= n) return;
+  const int m = (int)(i / (Hkv * DH)), gd = (int)(i - (long long)m * Hkv * DH), gg = gd / DH, d = gd - gg * DH;
+  const int G = H / Hkv;
+  float acc = 0.f;
+  for (int h = gg * G; h < gg * G + G; ++h) acc += part[((long long)h * M + m) * DH + d];
+  out[i] = acc;
 }
 
 // ------------------------------------------------------------------ decode
@@ -680,6 +951,29 @@ void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s) {
   if (a.qk_norm) attn_prefill_kernel<NWV, RB, true><<<grid, 64 * NWV, 0, s>>>(a);
   else attn_prefill_kernel<NWV, RB, false><<<grid, 64 * NWV, 0, s>>>(a);
 }
+
+void launch_attn_bwd_mfma(const AttnBwdMfmaArgs &a, const float *dout, const bf16 *o, float *dk, float *dv,
+                          hipStream_t s) {
+  if (a.n_seqs <= 0 || a.M <= 0) return;
+  const long long items = (long long)a.M * a.H;
+  attn_bwd_dsum_kernel<<<(unsigned)((items + 15) / 16), 256, 0, s>>>(dout, o, a.M, a.H, a.dsum);
+  attn_bwd_dq_kernel<<<dim3(a.n_seqs, a.max_wg, a.Hkv), 256, 0, s>>>(a);
+  attn_bwd_dkv_kernel<<<dim3(a.n_seqs, (a.max_len + 127) / 128, a.H), 256, 0, s>>>(a);
+  const long long n = (long long)a.M * a.Hkv * DH;
+  sum_heads_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.dkp, a.M, a.H, a.Hkv, dk);
+  sum_heads_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.dvp, a.M, a.H, a.Hkv, dv);
+}
+
+template <typename TI>
+void launch_transpose_cols(const TI *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
+                           hipStream_t s) {
+  const long long n = (long long)M * C;
+  if (n > 0) transpose_cols_kernel<TI><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, lds, M, C, vcol, dst, ldt);
+}
+template void launch_transpose_cols<bf16>(const bf16 *, long long, int, int, const int *, bf16 *, long long,
+                                          hipStream_t);
+template void launch_transpose_cols<float>(const float *, long long, int, int, const int *, bf16 *, long long,
+                                           hipStream_t);
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;

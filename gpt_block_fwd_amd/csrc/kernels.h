@@ -208,7 +208,29 @@ struct AttnPrefillArgs {
   int H, Hkv;
   int qk_norm;  // q and k are QK-normalised (RMS <= 1 per head): fixed softmax reference
   bf16 *o;  // [M][H*128]
+  float *lse2;  // [M][H] or NULL: each row's base-2 log-sum-exp of log2(e) q.k / sqrt(128)
 };
+// MFMA attention backward (bf16, head width 128).  The transposed operands
+// kt, qt, dot have the V^T layout: [dims][ldt], a row's column at
+// cu_pad[seq] + vperm16(position), zero elsewhere.
+struct AttnBwdMfmaArgs {
+  const bf16 *q, *k, *vb, *dob;   // [M][H 128], [M][Hkv 128] x 2, [M][H 128] (dO in bf16)
+  const bf16 *kt, *qt, *dot;      // [Hkv 128][ldt], [H 128][ldt] x 2
+  long long ldt;
+  const float *lse2;              // [M][H] from the forward
+  float *dsum;                    // [M][H] D = dO . O (written by the launcher)
+  const int *cu, *cu_pad;
+  int n_seqs, max_wg, max_len;    // max_wg: 128-row blocks of the longest sequence's rows
+  int M, H, Hkv;
+  float *dq;                      // [M][H 128]
+  float *dkp, *dvp;               // [H][M][128] per-query-head partials
+};
+void launch_attn_bwd_mfma(const AttnBwdMfmaArgs &a, const float *dout, const bf16 *o, float *dk, float *dv,
+                          hipStream_t s);
+// dst[c][vcol[m]] = bf16(src[m][c])
+template <typename TI>
+void launch_transpose_cols(const TI *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
+                           hipStream_t s);
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
 
 struct AttnDecodeArgs {
