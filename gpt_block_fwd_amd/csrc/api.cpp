@@ -983,26 +983,6 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     }
     mm(dxA, d, tb.wT, d, M, H * dh, d, tb.dO, H * dh);            // dO = dx Wo
     {
-      AttnBwdArgs ab{};
-      ab.q = bf.q;
-      ab.k = bf.k;
-      ab.o = bf.o;
-      ab.v = bf.qkv + (H + Hkv) * dh;
-      ab.ldv = qkv_n;
-      ab.v_bf16 = bf16p;
-      ab.dout = tb.dO;
-      ab.pos = bf.pos;
-      ab.seq = bf.seq;
-      ab.cu = bf.cu;
-      ab.M = M;
-      ab.H = H;
-      ab.Hkv = Hkv;
-      ab.dh = dh;
-      ab.dq = tb.dq;
-      ab.dk = tb.dk;
-      ab.dv = tb.dv;
-      ab.lse = tb.lse;
-      ab.dsum = tb.dsum;
       Timed t(GPT_PROF_BWD_ATTN, s, 2.5 * fw.attn_flops, (double)M * (3 * H + 4 * Hkv) * dh * 4);
       if (bf16p) {
         // V as bf16 rows (the values the forward's attention read), dO in
@@ -1036,6 +1016,26 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
         mb.dvp = tb.dvp;
         launch_attn_bwd_mfma(mb, tb.dO, (const bf16 *)bf.o, tb.dk, tb.dv, s);
       } else {
+        AttnBwdArgs ab{};
+        ab.q = bf.q;
+        ab.k = bf.k;
+        ab.o = bf.o;
+        ab.v = bf.qkv + (H + Hkv) * dh;
+        ab.ldv = qkv_n;
+        ab.v_bf16 = bf16p;
+        ab.dout = tb.dO;
+        ab.pos = bf.pos;
+        ab.seq = bf.seq;
+        ab.cu = bf.cu;
+        ab.M = M;
+        ab.H = H;
+        ab.Hkv = Hkv;
+        ab.dh = dh;
+        ab.dq = tb.dq;
+        ab.dk = tb.dk;
+        ab.dv = tb.dv;
+        ab.lse = tb.lse;
+        ab.dsum = tb.dsum;
         launch_attn_bwd<float>(ab, s);
       }
     }

@@ -275,156 +275,6 @@ __global__ __launch_bounds__(256) void attn_bwd_keys_kernel(AttnBwdArgs a) {
   }
 }
 
-// bf16 path, dh = 128: lane l16 of an item owns the 8 contiguous dims
-// 8 l16 .. 8 l16 + 7, so q, k and v rows arrive in one 16-byte load per lane
-// and dO in two; V comes from a bf16 row-major copy (a.vb).  The loops over
-// keys (rows) take two at a time for more loads in flight.
-DEV void ld8(const bf16 *p, float (&x)[8]) {
-  const bf16x8 v = *(const bf16x8 *)p;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = bf2f(v[i]);
-}
-DEV void ld8(const float *p, float (&x)[8]) {
-  const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
-DEV float dot8(const float (&a)[8], const float (&b)[8]) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = fmaf(a[i], b[i], s);
-  return s;
-}
-
-__global__ __launch_bounds__(256) void attn_bwd_rows_vec_kernel(AttnBwdArgs a) {
-  constexpr int DH = 128;
-  const int lane = threadIdx.x & 63, c0 = 8 * (lane & 15);
-  const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  if (item >= (long long)a.M * a.H) return;
-  const int m = (int)(item / a.H), h = (int)(item - (long long)m * a.H);
-  const int g = h * a.Hkv / a.H, kvd = a.Hkv * DH;
-  const int p = a.pos[m], r0 = m - p;
-  float qr[8], dor[8], orow[8], dq[8];
-  ld8((const bf16 *)a.q + (long long)m * a.H * DH + h * DH + c0, qr);
-  ld8(a.dout + (long long)m * a.H * DH + h * DH + c0, dor);
-  ld8((const bf16 *)a.o + (long long)m * a.H * DH + h * DH + c0, orow);
-  const float D = sum16(dot8(dor, orow));
-  const float scale = 1.0f / sqrtf((float)DH);
-  const bf16 *kb = (const bf16 *)a.k + (long long)r0 * kvd + g * DH + c0;
-  const bf16 *vb = a.vb + (long long)r0 * kvd + g * DH + c0;
-  float mx = -INFINITY, l = 0.f;
-  int j = 0;
-  for (; j + 1 <= p; j += 2) {
-    float k0[8], k1[8];
-    ld8(kb + (long long)j * kvd, k0);
-    ld8(kb + (long long)(j + 1) * kvd, k1);
-    const float s0 = sum16(dot8(qr, k0)) * scale, s1 = sum16(dot8(qr, k1)) * scale;
-    const float mn = fmaxf(mx, fmaxf(s0, s1));
-    l = l * expf(mx - mn) + expf(s0 - mn) + expf(s1 - mn);
-    mx = mn;
-  }
-  if (j <= p) {
-    float k0[8];
-    ld8(kb + (long long)j * kvd, k0);
-    const float s0 = sum16(dot8(qr, k0)) * scale;
-    const float mn = fmaxf(mx, s0);
-    l = l * expf(mx - mn) + expf(s0 - mn);
-    mx = mn;
-  }
-  const float lse = mx + logf(l);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dq[i] = 0.f;
-  j = 0;
-  for (; j + 1 <= p; j += 2) {
-    float k0[8], k1[8], v0[8], v1[8];
-    ld8(kb + (long long)j * kvd, k0);
-    ld8(kb + (long long)(j + 1) * kvd, k1);
-    ld8(vb + (long long)j * kvd, v0);
-    ld8(vb + (long long)(j + 1) * kvd, v1);
-    const float s0 = sum16(dot8(qr, k0)) * scale, s1 = sum16(dot8(qr, k1)) * scale;
-    const float d0 = sum16(dot8(dor, v0)), d1 = sum16(dot8(dor, v1));
-    const float ds0 = expf(s0 - lse) * (d0 - D) * scale, ds1 = expf(s1 - lse) * (d1 - D) * scale;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dq[i] += ds0 * k0[i] + ds1 * k1[i];
-  }
-  if (j <= p) {
-    float k0[8], v0[8];
-    ld8(kb + (long long)j * kvd, k0);
-    ld8(vb + (long long)j * kvd, v0);
-    const float s0 = sum16(dot8(qr, k0)) * scale, d0 = sum16(dot8(dor, v0));
-    const float ds0 = expf(s0 - lse) * (d0 - D) * scale;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dq[i] += ds0 * k0[i];
-  }
-  float *dqo = a.dq + (long long)m * a.H * DH + h * DH + c0;
-  *(f32x4 *)dqo = (f32x4){dq[0], dq[1], dq[2], dq[3]};
-  *(f32x4 *)(dqo + 4) = (f32x4){dq[4], dq[5], dq[6], dq[7]};
-  if ((lane & 15) == 0) {
-    a.lse[(long long)m * a.H + h] = lse;
-    a.dsum[(long long)m * a.H + h] = D;
-  }
-}
-
-__global__ __launch_bounds__(256) void attn_bwd_keys_vec_kernel(AttnBwdArgs a) {
-  constexpr int DH = 128;
-  const int lane = threadIdx.x & 63, c0 = 8 * (lane & 15);
-  const long long item = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-  if (item >= (long long)a.M * a.Hkv) return;
-  const int j = (int)(item / a.Hkv), g = (int)(item - (long long)j * a.Hkv);
-  const int kvd = a.Hkv * DH, G = a.H / a.Hkv, HD = a.H * DH;
-  const int end = a.cu[a.seq[j] + 1];
-  float kr[8], vr[8], dk[8], dv[8];
-  ld8((const bf16 *)a.k + (long long)j * kvd + g * DH + c0, kr);
-  ld8(a.vb + (long long)j * kvd + g * DH + c0, vr);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dk[i] = dv[i] = 0.f;
-  const float scale = 1.0f / sqrtf((float)DH);
-  for (int hh = g * G; hh < g * G + G; ++hh) {
-    const bf16 *qb = (const bf16 *)a.q + hh * DH + c0;
-    const float *ob = a.dout + hh * DH + c0;
-    int r = j;
-    for (; r + 1 < end; r += 2) {
-      float q0[8], q1[8], o0[8], o1[8];
-      ld8(qb + (long long)r * HD, q0);
-      ld8(qb + (long long)(r + 1) * HD, q1);
-      ld8(ob + (long long)r * HD, o0);
-      ld8(ob + (long long)(r + 1) * HD, o1);
-      const float l0 = a.lse[(long long)r * a.H + hh], l1 = a.lse[(long long)(r + 1) * a.H + hh];
-      const float D0 = a.dsum[(long long)r * a.H + hh], D1 = a.dsum[(long long)(r + 1) * a.H + hh];
-      const float s0 = sum16(dot8(q0, kr)) * scale, s1 = sum16(dot8(q1, kr)) * scale;
-      const float p0 = expf(s0 - l0), p1 = expf(s1 - l1);
-      const float ds0 = p0 * (sum16(dot8(o0, vr)) - D0) * scale;
-      const float ds1 = p1 * (sum16(dot8(o1, vr)) - D1) * scale;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dk[i] += ds0 * q0[i] + ds1 * q1[i];
-        dv[i] += p0 * o0[i] + p1 * o1[i];
-      }
-    }
-    if (r < end) {
-      float q0[8], o0[8];
-      ld8(qb + (long long)r * HD, q0);
-      ld8(ob + (long long)r * HD, o0);
-      const float s0 = sum16(dot8(q0, kr)) * scale;
-      const float p0 = expf(s0 - a.lse[(long long)r * a.H + hh]);
-      const float ds0 = p0 * (sum16(dot8(o0, vr)) - a.dsum[(long long)r * a.H + hh]) * scale;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dk[i] += ds0 * q0[i];
-        dv[i] += p0 * o0[i];
-      }
-    }
-  }
-  float *dko = a.dk + (long long)j * kvd + g * DH + c0, *dvo = a.dv + (long long)j * kvd + g * DH + c0;
-  *(f32x4 *)dko = (f32x4){dk[0], dk[1], dk[2], dk[3]};
-  *(f32x4 *)(dko + 4) = (f32x4){dk[4], dk[5], dk[6], dk[7]};
-  *(f32x4 *)dvo = (f32x4){dv[0], dv[1], dv[2], dv[3]};
-  *(f32x4 *)(dvo + 4) = (f32x4){dv[4], dv[5], dv[6], dv[7]};
-}
-
 // dst[m][c] = bf16(src[m lds + c]), c < C
 __global__ __launch_bounds__(256) void cast_rows_kernel(const float *src, long long lds, int M, int C, bf16 *dst) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -519,11 +369,6 @@ template void launch_qkv_bwd<float>(const QkvBwdArgs &, float *, hipStream_t);
 template <typename T>
 void launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
   const long long rows = (long long)a.M * a.H, keys = (long long)a.M * a.Hkv;
-  if (std::is_same<T, bf16>::value && a.dh == 128 && a.vb) {
-    if (rows > 0) attn_bwd_rows_vec_kernel<<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a);
-    if (keys > 0) attn_bwd_keys_vec_kernel<<<(unsigned)((keys + 15) / 16), 256, 0, s>>>(a);
-    return;
-  }
   if (rows > 0) attn_bwd_rows_kernel<T><<<(unsigned)((rows + 15) / 16), 256, 0, s>>>(a);
   if (keys > 0) attn_bwd_keys_kernel<T><<<(unsigned)((keys + 15) / 16), 256, 0, s>>>(a);
 }
@@ -532,7 +377,6 @@ void launch_cast_rows(const float *src, long long lds, int M, int C, bf16 *dst, 
   const long long n = (long long)M * C;
   if (n > 0) cast_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, lds, M, C, dst);
 }
-template void launch_attn_bwd<bf16>(const AttnBwdArgs &, hipStream_t);
 template void launch_attn_bwd<float>(const AttnBwdArgs &, hipStream_t);
 
 template <typename T>

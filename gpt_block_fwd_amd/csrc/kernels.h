@@ -105,12 +105,13 @@ struct QkvBwdArgs {
 };
 template <typename T>
 void launch_qkv_bwd(const QkvBwdArgs &a, T *dqkv, hipStream_t s);
+// Attention backward on the vector ALUs (any head width up to 128; the
+// fp32 small-model path).
 struct AttnBwdArgs {
   const void *q, *k, *o;  // [M][H dh], [M][Hkv dh], [M][H dh] in the model dtype
   const float *v;         // rows of ldv floats; v_bf16: rounded to bf16 as the forward used them
   long long ldv;
   int v_bf16;
-  const bf16 *vb;         // bf16 path with dh = 128: V as bf16 rows [M][Hkv dh] (else NULL)
   const float *dout;      // [M][H dh] gradient of the attention output
   const int *pos, *seq, *cu;
   int M, H, Hkv, dh;
