@@ -989,9 +989,9 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
         // bf16, and K, Q, dO transposed in the V^T column order
         launch_cast_rows(bf.qkv + (H + Hkv) * dh, qkv_n, M, Hkv * dh, (bf16 *)tb.vb, s);
         launch_cast<float, bf16>(tb.dO, (bf16 *)tb.dob, (long long)M * H * dh, s);
-        launch_transpose_cols<bf16>((const bf16 *)bf.k, Hkv * dh, M, Hkv * dh, bf.vcol, (bf16 *)tb.kt, bf.ldvt, s);
-        launch_transpose_cols<bf16>((const bf16 *)bf.q, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.qt, bf.ldvt, s);
-        launch_transpose_cols<bf16>((const bf16 *)tb.dob, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.dot, bf.ldvt, s);
+        launch_transpose_cols((const bf16 *)bf.k, Hkv * dh, M, Hkv * dh, bf.vcol, (bf16 *)tb.kt, bf.ldvt, s);
+        launch_transpose_cols((const bf16 *)bf.q, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.qt, bf.ldvt, s);
+        launch_transpose_cols((const bf16 *)tb.dob, H * dh, M, H * dh, bf.vcol, (bf16 *)tb.dot, bf.ldvt, s);
         AttnBwdMfmaArgs mb{};
         mb.q = (const bf16 *)bf.q;
         mb.k = (const bf16 *)bf.k;

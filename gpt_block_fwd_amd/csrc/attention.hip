@@ -536,17 +536,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dsum_kernel(const float *dout, c
   if (l16 == 0) dsum[item] = sum;
 }
 
-// dst[c][vcol[m]] = src[m][c] (bf16): the V^T-like layout of a row operand
-template <typename TI>
-__global__ __launch_bounds__(256) void transpose_cols_kernel(const TI *src, long long lds, int M, int C,
-                                                             const int *vcol, bf16 *dst, long long ldt) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)M * C) return;
-  const int m = (int)(i / C), c = (int)(i - (long long)m * C);
-  float v;
-  if constexpr (std::is_same<TI, bf16>::value) v = bf2f(src[(long long)m * lds + c]);
-  else v = src[(long long)m * lds + c];
-  dst[(long long)c * ldt + vcol[m]] = f2bf(v);
+// dst[c][vcol[m]] = src[m][c] (bf16): the V^T-like layout of a row operand.
+// 64 x 64 tiles through LDS: 16-byte reads along rows; the writes of a
+// wave cover 64 consecutive rows, whose columns vcol[m] are consecutive up
+// to the vperm16 order within 16.  C % 64 == 0.
+__global__ __launch_bounds__(256) void transpose_cols_kernel(const bf16 *src, long long lds, int M, const int *vcol,
+                                                             bf16 *dst, long long ldt) {
+  constexpr int P = 66;
+  __shared__ bf16 t[64 * P];
+  const int m0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + 256 * k, row = i >> 3, ch = i & 7, m = m0 + row;
+    if (m < M) {
+      const bf16x8 x = *(const bf16x8 *)(src + (long long)m * lds + c0 + 8 * ch);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = x[e];
+    }
+  }
+  __syncthreads();
+  const int row = tid & 63, m = m0 + row;
+  if (m >= M) return;
+  const long long col = vcol[m];
+  for (int c = tid >> 6; c < 64; c += 4) dst[(long long)(c0 + c) * ldt + col] = t[row * P + c];
 }
 
 // dk[m][g dh + d] = sum over the group's query heads h of dkp[h][m][d] (in order)
@@ -964,16 +976,11 @@ void launch_attn_bwd_mfma(const AttnBwdMfmaArgs &a, const float *dout, const bf1
   sum_heads_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.dvp, a.M, a.H, a.Hkv, dv);
 }
 
-template <typename TI>
-void launch_transpose_cols(const TI *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
+void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
                            hipStream_t s) {
-  const long long n = (long long)M * C;
-  if (n > 0) transpose_cols_kernel<TI><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, lds, M, C, vcol, dst, ldt);
+  if (M <= 0 || C <= 0) return;
+  transpose_cols_kernel<<<dim3(C / 64, (M + 63) / 64), 256, 0, s>>>(src, lds, M, vcol, dst, ldt);
 }
-template void launch_transpose_cols<bf16>(const bf16 *, long long, int, int, const int *, bf16 *, long long,
-                                          hipStream_t);
-template void launch_transpose_cols<float>(const float *, long long, int, int, const int *, bf16 *, long long,
-                                           hipStream_t);
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;

@@ -41,6 +41,53 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI *src, long long
   }
 }
 
+// The same into bf16 with 16-byte accesses both ways (C % 64 == 0, ldd and
+// Rp multiples of 8): a thread reads 8 consecutive columns of a row, and
+// writes 8 consecutive rows of a column from the LDS tile.
+template <typename TI>
+__global__ __launch_bounds__(256) void transpose16_kernel(const TI *src, long long lds, int R, int C, bf16 *dst,
+                                                          long long ldd, int Rp) {
+  constexpr int P = 66;  // row pitch in bf16
+  __shared__ bf16 t[64 * P];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + 256 * k, row = i >> 3, ch = i & 7, r = r0 + row;
+    float v[8];
+    if (r < R) {
+      const TI *p = src + (long long)r * lds + c0 + 8 * ch;
+      if constexpr (std::is_same<TI, bf16>::value) {
+        const bf16x8 x = *(const bf16x8 *)p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf2f(x[e]);
+      } else {
+        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a[e];
+          v[4 + e] = b[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = f2bf(v[e]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int col = tid & 63, rc = (tid >> 6) + 4 * k;  // rows 8 rc .. 8 rc + 7 of the tile
+    const int r = r0 + 8 * rc;
+    if (r >= Rp) continue;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = t[(8 * rc + e) * P + col];
+    *(bf16x8 *)(dst + (long long)(c0 + col) * ldd + r) = o;
+  }
+}
+
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void cast_kernel(const TI *src, TO *dst, long long n) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
@@ -334,6 +381,14 @@ template <typename TI, typename TO>
 void launch_transpose(const TI *src, long long lds, int R, int C, TO *dst, long long ldd, int Rp, hipStream_t s) {
   if (R <= 0 || C <= 0) return;
   const dim3 grid((C + 63) / 64, (std::max(R, Rp) + 63) / 64);
+  if constexpr (std::is_same<TO, bf16>::value) {
+    const int vec = std::is_same<TI, bf16>::value ? 8 : 4;
+    if (C % 64 == 0 && ldd % 8 == 0 && Rp % 8 == 0 && lds % vec == 0 &&
+        (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      transpose16_kernel<TI><<<grid, 256, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
+      return;
+    }
+  }
   transpose_kernel<TI, TO><<<grid, 256, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
 }
 template void launch_transpose<float, bf16>(const float *, long long, int, int, bf16 *, long long, int, hipStream_t);

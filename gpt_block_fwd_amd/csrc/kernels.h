@@ -228,9 +228,8 @@ struct AttnBwdMfmaArgs {
 };
 void launch_attn_bwd_mfma(const AttnBwdMfmaArgs &a, const float *dout, const bf16 *o, float *dk, float *dv,
                           hipStream_t s);
-// dst[c][vcol[m]] = bf16(src[m][c])
-template <typename TI>
-void launch_transpose_cols(const TI *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
+// dst[c][vcol[m]] = src[m][c] (C % 64 == 0, 16-byte aligned rows)
+void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const int *vcol, bf16 *dst, long long ldt,
                            hipStream_t s);
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
 
