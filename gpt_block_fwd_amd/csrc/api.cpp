@@ -334,6 +334,7 @@ GemmArgs gemm(const void *A, long long lda, const void *W, int M, int N, int K, 
 void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
   const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
   double out_b = g.epi == EPI_RESID ? 8.0
+                 : g.epi == EPI_DRELU2 ? 4.0 + es  // reads z, writes dz
                  : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV) ? es : 4.0;
   bool rows = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
   Timed t(rows && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
@@ -935,12 +936,14 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     fwd_norm(fw, xm, bf.h);                                       // h2
     mm(bf.h, d, w->w1[l], d, M, F, d, tb.z, F);                   // z
     {
-      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (4 + es) + (double)M * d * (8 + 2 * es) +
-                                            (double)M * F * 2 * es + (double)d * F * 2 * es);
-      if (bf16p) launch_act_bwd<bf16>(tb.z, nullptr, (bf16 *)tb.u, nullptr, (long long)M * F, c->act, s);
-      else launch_act_bwd<float>(tb.z, nullptr, (float *)tb.u, nullptr, (long long)M * F, c->act, s);
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (4 + es) + (double)M * d * (4 + es) + (double)d * F * 2 * es);
+      if (bf16p) {
+        launch_transpose_relu2(tb.z, F, M, F, (bf16 *)tb.trB, Mp, Mp, s);  // u^T [F][Mp] from z
+      } else {
+        launch_act_bwd<float>(tb.z, nullptr, (float *)tb.u, nullptr, (long long)M * F, c->act, s);
+        tr_md(c, tb.u, F, M, F, tb.trB, Mp, Mp, s);              // u^T [F][Mp]
+      }
       tr_f32(c, tb.dx, d, M, d, tb.trA, Mp, Mp, s);              // dx^T [d][Mp]
-      tr_md(c, tb.u, F, M, F, tb.trB, Mp, Mp, s);                // u^T [F][Mp]
       tr_md(c, w->w2[l], F, d, F, tb.wT, d, d, s);               // W2^T [F][d]
     }
     mmw(tb.trA, tb.trB, d, F, gr->w2[l]);                         // dW2 = dx^T u
@@ -949,12 +952,23 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       to_md(tb.dx, tb.dxb, (long long)M * d);
       dxA = tb.dxb;
     }
-    mm(dxA, d, tb.wT, d, M, F, d, tb.du, F);                      // du = dx W2
+    // the large-M GEMM applies the ReLU^2 backward in its epilogue:
+    // dz = (dx W2) * 2 max(z, 0); otherwise du = dx W2, then a pass
+    const bool fused_dact = bf16p && M > 64;
+    if (fused_dact) {
+      GemmArgs g = gemm(dxA, d, tb.wT, M, F, d, tb.dz, F, EPI_DRELU2);
+      g.aux = tb.z;
+      run_gemm(c, g, GPT_PROF_BWD_GEMM, s);
+    } else {
+      mm(dxA, d, tb.wT, d, M, F, d, tb.du, F);
+    }
     {
-      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (8 + es) + (double)M * (F + d) * 2 * es +
-                                            (double)d * F * 2 * es);
-      if (bf16p) launch_act_bwd<bf16>(tb.z, tb.du, nullptr, (bf16 *)tb.dz, (long long)M * F, c->act, s);
-      else launch_act_bwd<float>(tb.z, tb.du, nullptr, (float *)tb.dz, (long long)M * F, c->act, s);
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * 2 * es + (double)M * d * 2 * es + (double)d * F * 2 * es +
+                                            (fused_dact ? 0.0 : (double)M * F * (8 + es)));
+      if (!fused_dact) {
+        if (bf16p) launch_act_bwd<bf16>(tb.z, tb.du, nullptr, (bf16 *)tb.dz, (long long)M * F, c->act, s);
+        else launch_act_bwd<float>(tb.z, tb.du, nullptr, (float *)tb.dz, (long long)M * F, c->act, s);
+      }
       tr_md(c, tb.dz, F, M, F, tb.trA, Mp, Mp, s);               // dz^T [F][Mp]
       tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);                // h2^T [d][Mp]
       tr_md(c, w->w1[l], d, F, d, tb.wT, F, F, s);               // W1^T [d][F]

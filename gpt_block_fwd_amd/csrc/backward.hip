@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI *src, long long
 // The same into bf16 with 16-byte accesses both ways (C % 64 == 0, ldd and
 // Rp multiples of 8): a thread reads 8 consecutive columns of a row, and
 // writes 8 consecutive rows of a column from the LDS tile.
-template <typename TI>
+template <typename TI, bool RELU2 = false>
 __global__ __launch_bounds__(256) void transpose16_kernel(const TI *src, long long lds, int R, int C, bf16 *dst,
                                                           long long ldd, int Rp) {
   constexpr int P = 66;  // row pitch in bf16
@@ -71,6 +71,13 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const TI *src, long lo
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    if constexpr (RELU2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = fmaxf(v[e], 0.f);
+        v[e] = r * r;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = f2bf(v[e]);
@@ -394,6 +401,13 @@ void launch_transpose(const TI *src, long long lds, int R, int C, TO *dst, long 
 template void launch_transpose<float, bf16>(const float *, long long, int, int, bf16 *, long long, int, hipStream_t);
 template void launch_transpose<bf16, bf16>(const bf16 *, long long, int, int, bf16 *, long long, int, hipStream_t);
 template void launch_transpose<float, float>(const float *, long long, int, int, float *, long long, int, hipStream_t);
+
+void launch_transpose_relu2(const float *z, long long lds, int R, int C, bf16 *dst, long long ldd, int Rp,
+                            hipStream_t s) {
+  if (R <= 0 || C <= 0) return;
+  const dim3 grid((C + 63) / 64, (std::max(R, Rp) + 63) / 64);
+  transpose16_kernel<float, true><<<grid, 256, 0, s>>>(z, lds, R, C, dst, ldd, Rp);
+}
 
 template <typename TI, typename TO>
 void launch_cast(const TI *src, TO *dst, long long n, hipStream_t s) {

@@ -49,6 +49,11 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     }
     bf16x4 o = {f2bf(v0), f2bf(v1), f2bf(v2), f2bf(v3)};
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
+  } else if constexpr (EPI == EPI_DRELU2) {
+    const f32x4 z = *(const f32x4 *)(g.aux + (long long)m * g.ldc + n);
+    bf16x4 o = {f2bf(v0 * 2.f * fmaxf(z[0], 0.f)), f2bf(v1 * 2.f * fmaxf(z[1], 0.f)),
+                f2bf(v2 * 2.f * fmaxf(z[2], 0.f)), f2bf(v3 * 2.f * fmaxf(z[3], 0.f))};
+    *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_RESID) {
     float *p = (float *)g.C + (long long)m * g.ldc + n;
     f32x4 x = *(const f32x4 *)p;
@@ -698,6 +703,7 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
     case EPI_RESID: launch_big<EPI_RESID>(g, s); break;
     case EPI_LOGITS: launch_big<EPI_LOGITS>(g, s); break;
     case EPI_LOSS: launch_big<EPI_LOSS>(g, s); break;
+    case EPI_DRELU2: launch_big<EPI_DRELU2>(g, s); break;
     case EPI_QKV: launch_big<EPI_QKV>(g, s); break;
     default: launch_big<EPI_F32>(g, s); break;
   }

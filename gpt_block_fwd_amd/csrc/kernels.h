@@ -95,6 +95,10 @@ void launch_rms_bwd(const float *x, const float *dy, float *dx, int M, int d, fl
 // u = act(z) and dz = du act'(z) (either may be NULL)
 template <typename T>
 void launch_act_bwd(const float *z, const float *du, T *u, T *dz, long long n, int relu2, hipStream_t s);
+// dst[c][r] = bf16(relu(z[r][c])^2) (r < R, zero for R <= r < Rp): the
+// transposed MLP activation straight from its fp32 pre-activation
+void launch_transpose_relu2(const float *z, long long lds, int R, int C, bf16 *dst, long long ldd, int Rp,
+                            hipStream_t s);
 struct QkvBwdArgs {
   const float *pre;             // [M][(H + 2Hkv) dh] projection output before RoPE / QK-norm
   const float *dq, *dk, *dv;    // [M][H dh], [M][Hkv dh] x 2: gradients of the attention inputs
@@ -138,7 +142,8 @@ enum Epi {
   EPI_RELU_F32 = 4,
   EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each kLogitsPartCols columns
   EPI_QKV = 6,     // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
-  EPI_LOSS = 7     // EPI_LOGITS' partials and each row's target logit; C is not written
+  EPI_LOSS = 7,    // EPI_LOGITS' partials and each row's target logit; C is not written
+  EPI_DRELU2 = 8   // bf16 C = acc * 2 max(z, 0), z = aux[m][n] (fp32, row stride ldc): ReLU^2 backward
 };
 
 // Extra operands of the EPI_QKV epilogue (column block = one 128-wide head).
@@ -167,6 +172,7 @@ struct GemmArgs {
   long long ldc;
   int epi;
   float *part;  // EPI_LOGITS, EPI_LOSS: [M][N/kLogitsPartCols][2] partial (max, sum exp)
+  const float *aux;     // EPI_DRELU2: the pre-activation z
   const int *targets;  // EPI_LOSS: [M] target column of each row (any value)
   float *tgt;          // EPI_LOSS: [M] C[m][targets[m]], written where targets[m] is in [0, N)
   QkvEpi qkv;   // EPI_QKV
