@@ -328,7 +328,10 @@ DEV void dma_cols(bf16 *dst, const bf16 *base, long long ld, long long col0, int
 
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdMfmaArgs a) {
   constexpr int NWV = 4, ROWS = 32 * NWV;
-  __shared__ bf16 sk[KT * DH], sv[KT * DH], skt[DH * KT];
+  // two buffers of (K rows, V rows, K^T), one LDS object each: the next
+  // tile's DMA needs no wait before this tile's reads
+  __shared__ bf16 sk0[KT * DH], sv0[KT * DH], skt0[DH * KT];
+  __shared__ bf16 sk1[KT * DH], sv1[KT * DH], skt1[DH * KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
   const int b = blockIdx.x, R0 = (a.max_wg - 1 - (int)blockIdx.y) * ROWS;
@@ -359,52 +362,69 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdMfmaArgs a) {
   const bf16 *kbase = a.k + (long long)tok0 * kvd + gk * DH;
   const bf16 *vbase = a.vb + (long long)tok0 * kvd + gk * DH;
   const bf16 *ktbase = a.kt + (long long)gk * DH * a.ldt;
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto dma = [&](int kt, bf16 *sk, bf16 *sv, bf16 *skt) {
     dma_rows(sk, kbase, kvd, kt * KT, len - 1, wave, NWV, lane);
     dma_rows(sv, vbase, kvd, kt * KT, len - 1, wave, NWV, lane);
     dma_cols(skt, ktbase, a.ldt, col0 + kt * KT, wave, NWV, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt * KT <= pw_max) {
-      f32x16 sacc[2], dpacc[2];
+  };
+  auto tile = [&](int kt, const bf16 *sk, const bf16 *sv, const bf16 *skt) {
+    if (kt * KT > pw_max) return;
+    f32x16 sacc[2], dpacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = (f32x16){};
-        dpacc[kb] = (f32x16){};
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = (f32x16){};
+      dpacc[kb] = (f32x16){};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kf = *(const bf16x8 *)&sk[kidx(32 * kb + c32, 2 * s + g)];
-          const bf16x8 vf = *(const bf16x8 *)&sv[kidx(32 * kb + c32, 2 * s + g)];
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
-          dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc[kb], 0, 0, 0);
-        }
-      }
-      // dS = P (dP - D), P = 2^(s sc - lse2) on visible keys
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt * KT + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-          const float p = key > prow ? 0.f : fast_exp2(__builtin_fmaf(sacc[kb][e], sc, -lse2));
-          sacc[kb][e] = p * (dpacc[kb][e] - D);
-        }
-      // dQ^T += K^T dS^T, 16 keys per MFMA (k slot 8g+j <-> key 16h + 8(j/4) + 4g + j%4)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st >> 1, h = st & 1;
-        bf16x8 pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = f2bf(sacc[kb][8 * h + j]);
-        const int col = 32 * kb + 16 * h + 8 * g;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const bf16x8 ktf = *(const bf16x8 *)&skt[vidx(32 * d + c32, col)];
-          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf, pf, dq[d], 0, 0, 0);
-        }
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 kf = *(const bf16x8 *)&sk[kidx(32 * kb + c32, 2 * s + g)];
+        const bf16x8 vf = *(const bf16x8 *)&sv[kidx(32 * kb + c32, 2 * s + g)];
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+        dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[s], dpacc[kb], 0, 0, 0);
       }
     }
+    // dS = P (dP - D), P = 2^(s sc - lse2) on visible keys
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * KT + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+        const float p = key > prow ? 0.f : fast_exp2(__builtin_fmaf(sacc[kb][e], sc, -lse2));
+        sacc[kb][e] = p * (dpacc[kb][e] - D);
+      }
+    // dQ^T += K^T dS^T, 16 keys per MFMA (k slot 8g+j <-> key 16h + 8(j/4) + 4g + j%4)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, h = st & 1;
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = f2bf(sacc[kb][8 * h + j]);
+      const int col = 32 * kb + 16 * h + 8 * g;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 ktf = *(const bf16x8 *)&skt[vidx(32 * d + c32, col)];
+        dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf, pf, dq[d], 0, 0, 0);
+      }
+    }
+  };
+  auto land = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  // tile kt computes from one buffer while tile kt + 1 streams into the other
+  auto step = [&](int kt, const bf16 *sk, const bf16 *sv, const bf16 *skt, bf16 *nk, bf16 *nv, bf16 *nkt) {
+    if (kt + 1 < n_kt) dma(kt + 1, nk, nv, nkt);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(kt, sk, sv, skt);
+    land();
+  };
+  dma(0, sk0, sv0, skt0);
+  land();
+  int kt = 0;
+  for (; kt + 1 < n_kt; kt += 2) {
+    step(kt, sk0, sv0, skt0, sk1, sv1, skt1);
+    step(kt + 1, sk1, sv1, skt1, sk0, sv0, skt0);
   }
+  if (kt < n_kt) step(kt, sk0, sv0, skt0, sk1, sv1, skt1);
   if (Rw + c32 >= rows_total) return;
   const float scale = 1.0f / sqrtf((float)DH);
   float *op = a.dq + qrow + 4 * g;
@@ -418,8 +438,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdMfmaArgs a) {
 
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
   constexpr int NWV = 4, KEYS = 32 * NWV;
-  __shared__ bf16 sq[KT * DH], sdo[KT * DH], sqt[DH * KT], sdot[DH * KT];
-  __shared__ float sl[KT], sd[KT];
+  // two buffers of (Q rows, dO rows, Q^T, dO^T, lse2, D), one LDS object each
+  __shared__ bf16 sq0[KT * DH], sdo0[KT * DH], sqt0[DH * KT], sdot0[DH * KT];
+  __shared__ bf16 sq1[KT * DH], sdo1[KT * DH], sqt1[DH * KT], sdot1[DH * KT];
+  __shared__ float sl0[KT], sd0[KT], sl1[KT], sd1[KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
   const int b = blockIdx.x, K0 = blockIdx.y * KEYS, hq = blockIdx.z;
@@ -442,67 +464,103 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
   const bf16 *qbase = a.q + (long long)tok0 * H * DH + hq * DH;
   const bf16 *obase = a.dob + (long long)tok0 * H * DH + hq * DH;
   const bf16 *qtb = a.qt + (long long)hq * DH * a.ldt, *otb = a.dot + (long long)hq * DH * a.ldt;
-  const int t_end = (len - 1) / KT;
-  for (int tt = K0 / KT; tt <= t_end; ++tt) {
+  const int t0 = K0 / KT, t_end = (len - 1) / KT;
+  // per-position lse2 and D of a tile: global loads into registers, stored
+  // to LDS after the previous tile's reads
+  float nl = 0.f, nd = 0.f;
+  auto fetch_ld = [&](int tt) {
+    if (tid < KT) {
+      const int pos = min(tt * KT + tid, len - 1);
+      nl = a.lse2[(long long)(tok0 + pos) * H + hq];
+      nd = a.dsum[(long long)(tok0 + pos) * H + hq];
+    }
+  };
+  auto put_ld = [&](float *sl, float *sd) {
+    if (tid < KT) {
+      sl[tid] = nl;
+      sd[tid] = nd;
+    }
+  };
+  auto dma = [&](int tt, bf16 *sq, bf16 *sdo, bf16 *sqt, bf16 *sdot) {
     dma_rows(sq, qbase, (long long)H * DH, tt * KT, len - 1, wave, NWV, lane);
     dma_rows(sdo, obase, (long long)H * DH, tt * KT, len - 1, wave, NWV, lane);
     dma_cols(sqt, qtb, a.ldt, col0 + tt * KT, wave, NWV, lane);
     dma_cols(sdot, otb, a.ldt, col0 + tt * KT, wave, NWV, lane);
-    if (tid < KT) {
-      const int pos = min(tt * KT + tid, len - 1);
-      sl[tid] = a.lse2[(long long)(tok0 + pos) * H + hq];
-      sd[tid] = a.dsum[(long long)(tok0 + pos) * H + hq];
+  };
+  auto tile = [&](int tt, const bf16 *sq, const bf16 *sdo, const bf16 *sqt, const bf16 *sdot, const float *sl,
+                  const float *sd) {
+    // the tile reaches this wave's keys (positions >= key), and the wave has keys
+    if (!(tt * KT + KT - 1 >= kw && kw < len)) return;
+    f32x16 sacc[2], dpacc[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      sacc[pb] = (f32x16){};
+      dpacc[pb] = (f32x16){};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 qa = *(const bf16x8 *)&sq[kidx(32 * pb + c32, 2 * s + g)];
+        const bf16x8 oa = *(const bf16x8 *)&sdo[kidx(32 * pb + c32, 2 * s + g)];
+        sacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc[pb], 0, 0, 0);
+        dpacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc[pb], 0, 0, 0);
+      }
     }
+    // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile
+    f32x16 pp[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int pl = 32 * pb + 8 * (e >> 2) + 4 * g + (e & 3), pos = tt * KT + pl;
+        const bool vis = pos >= kw + c32 && pos < len;
+        const float p = vis ? fast_exp2(__builtin_fmaf(sacc[pb][e], sc, -sl[pl])) : 0.f;
+        pp[pb][e] = p;
+        sacc[pb][e] = p * (dpacc[pb][e] - sd[pl]);
+      }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int pb = st >> 1, h = st & 1;
+      bf16x8 pf, sf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pf[j] = f2bf(pp[pb][8 * h + j]);
+        sf[j] = f2bf(sacc[pb][8 * h + j]);
+      }
+      const int col = 32 * pb + 16 * h + 8 * g;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 ota = *(const bf16x8 *)&sdot[vidx(32 * d + c32, col)];
+        const bf16x8 qta = *(const bf16x8 *)&sqt[vidx(32 * d + c32, col)];
+        dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ota, pf, dv[d], 0, 0, 0);
+        dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sf, dk[d], 0, 0, 0);
+      }
+    }
+  };
+  auto land = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // the tile reaches this wave's keys (positions >= key), and the wave has keys
-    if (tt * KT + KT - 1 >= kw && kw < len) {
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        sacc[pb] = (f32x16){};
-        dpacc[pb] = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 qa = *(const bf16x8 *)&sq[kidx(32 * pb + c32, 2 * s + g)];
-          const bf16x8 oa = *(const bf16x8 *)&sdo[kidx(32 * pb + c32, 2 * s + g)];
-          sacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc[pb], 0, 0, 0);
-          dpacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc[pb], 0, 0, 0);
-        }
-      }
-      // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile
-      f32x16 pp[2];
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int pl = 32 * pb + 8 * (e >> 2) + 4 * g + (e & 3), pos = tt * KT + pl;
-          const bool vis = pos >= kw + c32 && pos < len;
-          const float p = vis ? fast_exp2(__builtin_fmaf(sacc[pb][e], sc, -sl[pl])) : 0.f;
-          pp[pb][e] = p;
-          sacc[pb][e] = p * (dpacc[pb][e] - sd[pl]);
-        }
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int pb = st >> 1, h = st & 1;
-        bf16x8 pf, sf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pf[j] = f2bf(pp[pb][8 * h + j]);
-          sf[j] = f2bf(sacc[pb][8 * h + j]);
-        }
-        const int col = 32 * pb + 16 * h + 8 * g;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const bf16x8 ota = *(const bf16x8 *)&sdot[vidx(32 * d + c32, col)];
-          const bf16x8 qta = *(const bf16x8 *)&sqt[vidx(32 * d + c32, col)];
-          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ota, pf, dv[d], 0, 0, 0);
-          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sf, dk[d], 0, 0, 0);
-        }
-      }
+  };
+  auto step = [&](int tt, const bf16 *sq, const bf16 *sdo, const bf16 *sqt, const bf16 *sdot, const float *sl,
+                  const float *sd, bf16 *nq, bf16 *ndo, bf16 *nqt, bf16 *ndot, float *nsl, float *nsd) {
+    const bool more = tt + 1 <= t_end;
+    if (more) {
+      dma(tt + 1, nq, ndo, nqt, ndot);
+      fetch_ld(tt + 1);
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    tile(tt, sq, sdo, sqt, sdot, sl, sd);
+    if (more) put_ld(nsl, nsd);
+    land();
+  };
+  dma(t0, sq0, sdo0, sqt0, sdot0);
+  fetch_ld(t0);
+  put_ld(sl0, sd0);
+  land();
+  int tt = t0;
+  for (; tt + 1 <= t_end; tt += 2) {
+    step(tt, sq0, sdo0, sqt0, sdot0, sl0, sd0, sq1, sdo1, sqt1, sdot1, sl1, sd1);
+    step(tt + 1, sq1, sdo1, sqt1, sdot1, sl1, sd1, sq0, sdo0, sqt0, sdot0, sl0, sd0);
   }
+  if (tt <= t_end) step(tt, sq0, sdo0, sqt0, sdot0, sl0, sd0, sq1, sdo1, sqt1, sdot1, sl1, sd1);
   if (kw + c32 >= len) return;
   const float scale = 1.0f / sqrtf((float)DH);
   const long long orow = ((long long)hq * a.M + tok0 + kw + c32) * DH + 4 * g;
