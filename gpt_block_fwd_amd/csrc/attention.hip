@@ -444,7 +444,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
   __shared__ float sl0[KT], sd0[KT], sl1[KT], sd1[KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.x, K0 = blockIdx.y * KEYS, hq = blockIdx.z;
+  // grid (query head, sequence, key block): the key blocks that see the
+  // most rows (the first ones) are dispatched first for every head
+  const int hq = blockIdx.x, b = blockIdx.y, K0 = blockIdx.z * KEYS;
   const int H = a.H, gk = hq * a.Hkv / a.H, kvd = a.Hkv * DH;
   const int tok0 = a.cu[b], len = a.cu[b + 1] - tok0;
   const long long col0 = a.cu_pad[b];
@@ -1028,7 +1030,7 @@ void launch_attn_bwd_mfma(const AttnBwdMfmaArgs &a, const float *dout, const bf1
   const long long items = (long long)a.M * a.H;
   attn_bwd_dsum_kernel<<<(unsigned)((items + 15) / 16), 256, 0, s>>>(dout, o, a.M, a.H, a.dsum);
   attn_bwd_dq_kernel<<<dim3(a.n_seqs, a.max_wg, a.Hkv), 256, 0, s>>>(a);
-  attn_bwd_dkv_kernel<<<dim3(a.n_seqs, (a.max_len + 127) / 128, a.H), 256, 0, s>>>(a);
+  attn_bwd_dkv_kernel<<<dim3(a.H, a.n_seqs, (a.max_len + 127) / 128), 256, 0, s>>>(a);
   const long long n = (long long)a.M * a.Hkv * DH;
   sum_heads_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.dkp, a.M, a.H, a.Hkv, dk);
   sum_heads_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.dvp, a.M, a.H, a.Hkv, dv);

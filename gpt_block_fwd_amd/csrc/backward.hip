@@ -41,9 +41,12 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI *src, long long
   }
 }
 
-// The same into bf16 with 16-byte accesses both ways (C % 64 == 0, ldd and
-// Rp multiples of 8): a thread reads 8 consecutive columns of a row, and
-// writes 8 consecutive rows of a column from the LDS tile.
+// The same into bf16 through a 64 x 64 LDS tile with 16-byte global
+// accesses both ways (C % 64 == 0; lds, ldd, Rp multiples of 8; 16-byte
+// aligned bases).  Reads: 8 lanes cover one source row's 64 columns.
+// Writes: 8 lanes cover one destination row's 64 entries, 8 rows per wave
+// instruction, so every store instruction writes whole 128-byte lines.
+// RELU2: the source is the MLP pre-activation z, the value moved relu(z)^2.
 template <typename TI, bool RELU2 = false>
 __global__ __launch_bounds__(256) void transpose16_kernel(const TI *src, long long lds, int R, int C, bf16 *dst,
                                                           long long ldd, int Rp) {
@@ -68,25 +71,25 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const TI *src, long lo
           v[4 + e] = b[e];
         }
       }
+      if constexpr (RELU2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float q = fmaxf(v[e], 0.f);
+          v[e] = q * q;
+        }
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-    if constexpr (RELU2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float r = fmaxf(v[e], 0.f);
-        v[e] = r * r;
-      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = f2bf(v[e]);
   }
   __syncthreads();
+  const int rc = tid & 7, r = r0 + 8 * rc;  // destination entries r .. r + 7
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int col = tid & 63, rc = (tid >> 6) + 4 * k;  // rows 8 rc .. 8 rc + 7 of the tile
-    const int r = r0 + 8 * rc;
+    const int col = (tid >> 3) + 32 * k;      // destination row c0 + col
     if (r >= Rp) continue;
     bf16x8 o;
 #pragma unroll
@@ -389,8 +392,7 @@ void launch_transpose(const TI *src, long long lds, int R, int C, TO *dst, long 
   if (R <= 0 || C <= 0) return;
   const dim3 grid((C + 63) / 64, (std::max(R, Rp) + 63) / 64);
   if constexpr (std::is_same<TO, bf16>::value) {
-    const int vec = std::is_same<TI, bf16>::value ? 8 : 4;
-    if (C % 64 == 0 && ldd % 8 == 0 && Rp % 8 == 0 && lds % vec == 0 &&
+    if (C % 64 == 0 && ldd % 8 == 0 && Rp % 8 == 0 && lds % 8 == 0 &&
         (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
       transpose16_kernel<TI><<<grid, 256, 0, s>>>(src, lds, R, C, dst, ldd, Rp);
       return;

@@ -97,6 +97,7 @@ template <typename T>
 void launch_act_bwd(const float *z, const float *du, T *u, T *dz, long long n, int relu2, hipStream_t s);
 // dst[c][r] = bf16(relu(z[r][c])^2) (r < R, zero for R <= r < Rp): the
 // transposed MLP activation straight from its fp32 pre-activation
+// (C % 64 == 0; lds, ldd, Rp multiples of 8)
 void launch_transpose_relu2(const float *z, long long lds, int R, int C, bf16 *dst, long long ldd, int Rp,
                             hipStream_t s);
 struct QkvBwdArgs {
