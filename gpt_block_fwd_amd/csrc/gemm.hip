@@ -646,7 +646,7 @@ void launch_big(const GemmArgs &g, hipStream_t s) {
   static_assert((EPI != EPI_LOGITS && EPI != EPI_LOSS) || 256 / 4 == kLogitsPartCols, "partial width");
   const int tm = (g.M + BM - 1) / BM;
   const int t256 = tm * ((g.N + 255) / 256);
-  if constexpr (EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_RESID || EPI == EPI_F32) {
     // 192-column tiles when N splits into them and they take fewer
     // column-rounds over the 256 CUs (d = 768: 256 tiles instead of 192)
     const int t192 = tm * (g.N / 192);
