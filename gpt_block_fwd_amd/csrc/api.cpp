@@ -774,12 +774,7 @@ gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *
     for (int b = 0; b < n_seqs; ++b) kv->lens[b] = cu_seqlens[b + 1] - cu_seqlens[b];
   return GPT_OK;
 }
-// dst[c][r] = src[r][c] in the model dtype (src in fp32 or the model dtype)
-void tr_f32(const gpt_config *c, const float *src, long long lds, int R, int C, void *dst, long long ldd, int Rp,
-            hipStream_t s) {
-  if (c->dtype == GPT_DTYPE_BF16) launch_transpose<float, bf16>(src, lds, R, C, (bf16 *)dst, ldd, Rp, s);
-  else launch_transpose<float, float>(src, lds, R, C, (float *)dst, ldd, Rp, s);
-}
+// dst[c][r] = src[r][c] in the model dtype
 void tr_md(const gpt_config *c, const void *src, long long lds, int R, int C, void *dst, long long ldd, int Rp,
            hipStream_t s) {
   if (c->dtype == GPT_DTYPE_BF16)
@@ -862,14 +857,13 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     Timed t(GPT_PROF_BWD_GEMM, s, 2.0 * m * n * Mp, 2.0 * ((double)m + n) * Mp + 4.0 * m * n);
     launch_gemm_bf16_splitk(g, gemm_splitk_ways(m, n, Mp), tb.ksl, s);
   };
-  auto to_md = [&](const float *src, void *dst, long long n) {
-    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)n * (4 + es));
-    if (bf16p) launch_cast<float, bf16>(src, (bf16 *)dst, n, s);
-    else launch_cast<float, float>(src, (float *)dst, n, s);
-  };
+  // dx in the model dtype: the bf16 copy the RMSNorm backward keeps, or dx itself
+  auto dxA0 = [&]() -> const void * { return bf16p ? tb.dxb : (const void *)tb.dx; };
+  // dx += the RMSNorm backward; bf16 models also get dx in bf16 (tb.dxb),
+  // the A operand of the next input-gradient GEMM
   auto rms_bwd = [&](const float *x, const float *dy) {
-    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * 16);
-    launch_rms_bwd(x, dy, tb.dx, M, d, c->norm_eps, s);
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * (16 + (bf16p ? 2 : 0)));
+    launch_rms_bwd(x, dy, tb.dx, bf16p ? (bf16 *)tb.dxb : nullptr, M, d, c->norm_eps, s);
   };
 
   // ---- forward, keeping the residual stream
@@ -943,15 +937,11 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
         launch_act_bwd<float>(tb.z, nullptr, (float *)tb.u, nullptr, (long long)M * F, c->act, s);
         tr_md(c, tb.u, F, M, F, tb.trB, Mp, Mp, s);              // u^T [F][Mp]
       }
-      tr_f32(c, tb.dx, d, M, d, tb.trA, Mp, Mp, s);              // dx^T [d][Mp]
+      tr_md(c, dxA0(), d, M, d, tb.trA, Mp, Mp, s);              // dx^T [d][Mp]
       tr_md(c, w->w2[l], F, d, F, tb.wT, d, d, s);               // W2^T [F][d]
     }
     mmw(tb.trA, tb.trB, d, F, gr->w2[l]);                         // dW2 = dx^T u
-    const void *dxA = tb.dx;
-    if (bf16p) {
-      to_md(tb.dx, tb.dxb, (long long)M * d);
-      dxA = tb.dxb;
-    }
+    const void *dxA = bf16p ? tb.dxb : (const void *)tb.dx;
     // the large-M GEMM applies the ReLU^2 backward in its epilogue:
     // dz = (dx W2) * 2 max(z, 0); otherwise du = dx W2, then a pass
     const bool fused_dact = bf16p && M > 64;
@@ -986,15 +976,11 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     {
       Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * (4 + es) + (double)M * H * dh * 2 * es +
                                             (double)d * H * dh * 2 * es);
-      tr_f32(c, tb.dx, d, M, d, tb.trA, Mp, Mp, s);              // dx^T
+      tr_md(c, dxA0(), d, M, d, tb.trA, Mp, Mp, s);              // dx^T
       tr_md(c, bf.o, H * dh, M, H * dh, tb.trB, Mp, Mp, s);      // o^T [H dh][Mp]
       tr_md(c, w->wo[l], H * dh, d, H * dh, tb.wT, d, d, s);     // Wo^T [H dh][d]
     }
     mmw(tb.trA, tb.trB, d, H * dh, gr->wo[l]);                    // dWo = dx^T o
-    if (bf16p) {
-      to_md(tb.dx, tb.dxb, (long long)M * d);
-      dxA = tb.dxb;
-    }
     mm(dxA, d, tb.wT, d, M, H * dh, d, tb.dO, H * dh);            // dO = dx Wo
     {
       Timed t(GPT_PROF_BWD_ATTN, s, 2.5 * fw.attn_flops, (double)M * (3 * H + 4 * Hkv) * dh * 4);

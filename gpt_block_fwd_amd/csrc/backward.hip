@@ -107,8 +107,8 @@ __global__ __launch_bounds__(256) void cast_kernel(const TI *src, TO *dst, long 
 // ---------------------------------------------------------------- RMSNorm backward
 // y = x / r, r = sqrt(mean(x^2) + eps): dx += (dy - y mean(dy y)) / r.
 // One wave per row.
-__global__ __launch_bounds__(256) void rms_bwd_kernel(const float *x, const float *dy, float *dx, int M, int d,
-                                                      float eps) {
+__global__ __launch_bounds__(256) void rms_bwd_kernel(const float *x, const float *dy, float *dx, bf16 *dxb, int M,
+                                                      int d, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;
   const float *xr = x + (long long)row * d, *gr = dy + (long long)row * d;
@@ -124,7 +124,12 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const float *x, const floa
   // mean(dy y) = sum(dy x) / (d r)
   const float m = sg * inv / d;
   float *o = dx + (long long)row * d;
-  for (int c = lane; c < d; c += 64) o[c] += (gr[c] - xr[c] * inv * m) * inv;
+  bf16 *ob = dxb ? dxb + (long long)row * d : nullptr;
+  for (int c = lane; c < d; c += 64) {
+    const float v = o[c] + (gr[c] - xr[c] * inv * m) * inv;
+    o[c] = v;
+    if (ob) ob[c] = f2bf(v);
+  }
 }
 
 // ---------------------------------------------------------------- MLP activation
@@ -418,8 +423,8 @@ void launch_cast(const TI *src, TO *dst, long long n, hipStream_t s) {
 template void launch_cast<float, bf16>(const float *, bf16 *, long long, hipStream_t);
 template void launch_cast<float, float>(const float *, float *, long long, hipStream_t);
 
-void launch_rms_bwd(const float *x, const float *dy, float *dx, int M, int d, float eps, hipStream_t s) {
-  if (M > 0) rms_bwd_kernel<<<(M + 3) / 4, 256, 0, s>>>(x, dy, dx, M, d, eps);
+void launch_rms_bwd(const float *x, const float *dy, float *dx, bf16 *dxb, int M, int d, float eps, hipStream_t s) {
+  if (M > 0) rms_bwd_kernel<<<(M + 3) / 4, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps);
 }
 
 template <typename T>

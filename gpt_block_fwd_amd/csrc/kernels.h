@@ -90,8 +90,9 @@ template <typename TI, typename TO>
 void launch_transpose(const TI *src, long long lds, int R, int C, TO *dst, long long ldd, int Rp, hipStream_t s);
 template <typename TI, typename TO>
 void launch_cast(const TI *src, TO *dst, long long n, hipStream_t s);
-// dx[m] += the gradient through y = x / sqrt(mean(x^2) + eps), given dy
-void launch_rms_bwd(const float *x, const float *dy, float *dx, int M, int d, float eps, hipStream_t s);
+// dx[m] += the gradient through y = x / sqrt(mean(x^2) + eps), given dy;
+// dxb (nullable) receives the updated dx in bf16
+void launch_rms_bwd(const float *x, const float *dy, float *dx, bf16 *dxb, int M, int d, float eps, hipStream_t s);
 // u = act(z) and dz = du act'(z) (either may be NULL)
 template <typename T>
 void launch_act_bwd(const float *z, const float *du, T *u, T *dz, long long n, int relu2, hipStream_t s);
