@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
   // two buffers of (Q rows, dO rows, Q^T, dO^T, lse2, D), one LDS object each
   __shared__ bf16 sq0[KT * DH], sdo0[KT * DH], sqt0[DH * KT], sdot0[DH * KT];
   __shared__ bf16 sq1[KT * DH], sdo1[KT * DH], sqt1[DH * KT], sdot1[DH * KT];
-  __shared__ float sl0[KT], sd0[KT], sl1[KT], sd1[KT];
+  __shared__ __attribute__((aligned(16))) float sl0[KT], sd0[KT], sl1[KT], sd1[KT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c32 = lane & 31, g = lane >> 5;
   // grid (query head, sequence, key block): the key blocks that see the
@@ -506,17 +506,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
         dpacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc[pb], 0, 0, 0);
       }
     }
-    // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile
+    // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile; the
+    // four positions of one e/4 are adjacent, so lse2 and D come 16 bytes
+    // at a time
     f32x16 pp[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int pl = 32 * pb + 8 * (e >> 2) + 4 * g + (e & 3), pos = tt * KT + pl;
-        const bool vis = pos >= kw + c32 && pos < len;
-        const float p = vis ? fast_exp2(__builtin_fmaf(sacc[pb][e], sc, -sl[pl])) : 0.f;
-        pp[pb][e] = p;
-        sacc[pb][e] = p * (dpacc[pb][e] - sd[pl]);
+      for (int q = 0; q < 4; ++q) {
+        const int pl0 = 32 * pb + 8 * q + 4 * g;
+        const f32x4 l4 = *(const f32x4 *)&sl[pl0], d4 = *(const f32x4 *)&sd[pl0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * q + i, pos = tt * KT + pl0 + i;
+          const bool vis = pos >= kw + c32 && pos < len;
+          const float p = vis ? fast_exp2(__builtin_fmaf(sacc[pb][e], sc, -l4[i])) : 0.f;
+          pp[pb][e] = p;
+          sacc[pb][e] = p * (dpacc[pb][e] - d4[i]);
+        }
       }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
