@@ -12,11 +12,11 @@
 // exponentiated scores are already laid out as the B operand of
 // O^T = V^T P^T.  Online softmax in the base-2 domain.
 //
-// Decode: one single-wave workgroup per (sequence, 64-position page), so
-// even a small batch spreads over many CUs; K and V^T fragments are loaded
-// straight from the paged cache (every load issued before the first MFMA),
-// v_mfma_f32_16x16x32_bf16 with the (<= 16) query heads as the N side.
-// The last page of a sequence to finish merges the pages (log-sum-exp).
+// Decode: one 4-wave workgroup per chunk of cached pages of a sequence (and
+// K/V head); each wave stages a 64-position page of K and V^T in LDS with
+// whole-line direct-to-LDS loads (in up to 4 rounds per chunk) and scores it
+// with v_mfma_f32_16x16x32_bf16, the (<= 16) query heads as the N side.  The
+// last chunk of a sequence to finish merges the chunks (log-sum-exp).
 #include "kernels.h"
 #include "scatter.h"
 
@@ -665,26 +665,24 @@ DEV int sload(const int *p) {
 // wave whose page holds that position patches them into its copy of the page
 // (which it may have read before or after the store).
 //
-// One workgroup per chunk of kDecodePages pages of one sequence and K/V
-// head (grid z); wave w takes page w of the chunk and scores its 64 cached
-// positions for all query heads that share the K/V head at once (the H / Hkv
-// heads of its group; under MQA every head).  "Heads" below are the group's.  STAGE: the
-// wave first copies its page (K and V^T, 32 KB) into LDS with
-// direct-to-LDS loads that read whole 128-byte lines and takes its MFMA
-// fragments from there; this costs 128 KB of LDS, one workgroup per CU, so
-// it pays only when the grid does not fill the chip.  Otherwise the
-// fragments are loaded from the cache straight into registers.  The pages
-// of a chunk are merged in LDS by log-sum-exp, and the chunk's
-// unnormalised output with its (max, sum) per head goes to the partial
-// buffers.  The last chunk of the sequence to finish merges all chunks and
-// writes o.
-template <bool STAGE, int NP>
+// One workgroup per chunk of NP R pages of one sequence and K/V head (grid
+// z).  Wave w takes pages w, w + NP, ... of the chunk (R rounds) and scores
+// their 64 cached positions for all query heads that share the K/V head at
+// once (the H / Hkv heads of its group; under MQA every head).  "Heads" below
+// are the group's.  Each page (K and V^T, 32 KB) is copied into the wave's
+// LDS area with direct-to-LDS loads that read whole 128-byte lines, and the
+// MFMA fragments are read from there (128 KB of LDS for 4 waves, one
+// workgroup per CU); the next round's page is staged as soon as this round's
+// fragments are in registers.  Online softmax over the rounds.  The pages of
+// a chunk are merged in LDS by log-sum-exp, and the chunk's unnormalised
+// output with its (max, sum) per head goes to the partial buffers.  The last
+// chunk of the sequence to finish merges all chunks and writes o.
+template <int NP, int R>
 __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) {
-  constexpr int NT = 64 * NP, CH = 64 * NP;  // threads; cached positions per chunk
-  // STAGE: per wave a K page and a V^T page; otherwise per wave the fp32
-  // partial output (16 heads x 128).  The partials (and the final merge's
-  // scratch) use the first 8 KB of each wave's area.
-  constexpr int WAVE_BYTES = STAGE ? 2 * 64 * DH * 2 : 16 * DH * 4;
+  constexpr int NT = 64 * NP, CH = 64 * NP * R;  // threads; cached positions per chunk
+  // per wave a K page and a V^T page; the wave's partial output (16 heads x
+  // 128 fp32) later reuses the first 8 KB
+  constexpr int WAVE_BYTES = 2 * 64 * DH * 2;
   constexpr int QS = DH + 8;  // q row pitch: the 16 heads of a fragment read start on different banks
   __shared__ __attribute__((aligned(16))) char smem[NP * WAVE_BYTES];
   __shared__ float ml_s[NP][16][2];  // per-page (max, sum) per head
@@ -708,75 +706,70 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   const int c0 = chunk * CH;
   if (c0 >= len) return;
   const int H = G;
-  const int kpos0 = c0 + wave * 64;
-  const int nw = min(NP, (len - c0 + 63) / 64);  // pages of this chunk
+  const int kpos0 = c0 + wave * 64;               // this wave's first page
+  const int nw = min(NP, (len - c0 + 63) / 64);  // waves with a page
   const bool owner = pn < c0 + CH;                // the chunk holds the new position
-  const bool pw = pn >= kpos0 && pn < kpos0 + 64;  // this wave's page holds it
   const int nslot = H + (owner ? 2 : 0);
-  bf16x8 kf[4][4];
-  bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
+  // Slots are built by half-waves: lane li of half hw holds dims 4 li ..
+  // 4 li + 3 of one slot, so each slab costs one 16-byte load per lane for
+  // two slots.  Half-wave hh = 2 wave + hw builds slots hh, hh + 2 NP, ...
+  // Slot j < H: query head hq0 + j into q_s.  j = H: k, j = H + 1: v of K/V
+  // head gk at the new position, into kv_s and the cache.  The slab loads
+  // follow the page loads: the compiler waits for every load in flight
+  // before the slabs are summed, so issuing them first would only delay the
+  // page loads.
+  const int li = lane & 31, hw = lane >> 5, hh = 2 * wave + hw;
+  const float *u = in.qkv + (long long)b * (Hall + 2 * Hkv) * DH;
+  const int st = (int)in.slab;  // slabs of at most 64 rows: far below 2^31 floats
+  f32x4 t[kMaxRowSplit];
+  auto load_slot = [&](int j) {
+    // slab column of the slot: query head hq0 + j, K head gk, V head gk
+    const int col = j < H ? hq0 + j : (j == H ? Hall + gk : Hall + Hkv + gk);
+    const float *uj = u + col * DH + 4 * li;
+#pragma unroll
+    for (int k = 0; k < kMaxRowSplit; ++k)
+      if (k == 0 || k < in.nslab) t[k] = *(const f32x4 *)(uj + k * st);
+  };
+  f32x4 c4 = {}, s4 = {};
+  if (in.cos && hh < nslot) {
+    c4 = *(const f32x4 *)(in.cos + pn * 64 + 4 * (li & 15));
+    s4 = *(const f32x4 *)(in.sin + pn * 64 + 4 * (li & 15));
+  }
   bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
-  if (kpos0 < len) {
-    const int page = sload(kv.table + b * kv.pages_per_seq + kpos0 / kv.page_size);
-    const char *pg = kv.base + (long long)in.layer * kv.layer_stride + (long long)page * kv.page_stride;
+  // page of cached positions kp .. kp + 63 of this sequence and K/V head
+  auto page_ptr = [&](int kp) {
+    const int page = sload(kv.table + b * kv.pages_per_seq + kp / kv.page_size);
+    return (const char *)kv.base + (long long)in.layer * kv.layer_stride + (long long)page * kv.page_stride;
+  };
+  // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims x
+  // 128 B each; lane i fills slot i of the instruction's kilobyte and so
+  // loads the logical chunk that slot holds.
+  auto stage_page = [&](int kp) {
+    const char *pg = page_ptr(kp);
     const bf16 *K = (const bf16 *)pg + gk * DH;                      // rows of kvd
     const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes) + gk * DH * 64;  // [128][64]
-    if constexpr (STAGE) {
-      // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims
-      // x 128 B each; lane i fills slot i of the instruction's kilobyte and
-      // so loads the logical chunk that slot holds.
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = 4 * j + (lane >> 4), pc = lane & 15;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * kvd + ((pc ^ (key & 15)) << 3)),
-                                         LDS_PTR(Ks + j * 512), 16, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int dim = 8 * j + (lane >> 3), pc = lane & 7;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(Vt + dim * 64 + ((pc ^ ((dim >> 1) & 7)) << 3)),
-                                         LDS_PTR(Vs + j * 512), 16, 0, 0);
-      }
-    } else {
-      // every load of the page is issued before the first MFMA
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)(K + (16 * kb + hl) * kvd + 32 * s + 8 * q4);
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)(Vt + (16 * d + hl) * 64 + 32 * h + 8 * q4);
+    for (int j = 0; j < 16; ++j) {
+      const int key = 4 * j + (lane >> 4), pc = lane & 15;
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * kvd + ((pc ^ (key & 15)) << 3)),
+                                       LDS_PTR(Ks + j * 512), 16, 0, 0);
     }
-  }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(Vt + dim * 64 + ((pc ^ ((dim >> 1) & 7)) << 3)),
+                                       LDS_PTR(Vs + j * 512), 16, 0, 0);
+    }
+  };
+  if (kpos0 < len) stage_page(kpos0);
   {
-    // Slots are built by half-waves while the page loads are in flight:
-    // lane li of half hw holds dims 4 li .. 4 li + 3 of one slot, so each
-    // slab costs one 16-byte load per lane for two slots.  Half-wave
-    // hh = 2 wave + hw builds slots hh, hh + 2 NP, ...
-    // Slot j < H: query head hq0 + j into q_s.  j = H: k, j = H + 1: v of
-    // K/V head gk at the new position, into kv_s and the cache.  Query heads and k: half-split
-    // rotation (dim i pairs with i + 64, held by lane li ^ 16), then a
-    // weightless RMSNorm over the head.
-    const int li = lane & 31, hw = lane >> 5, hh = 2 * wave + hw;
-    const float *u = in.qkv + (long long)b * (Hall + 2 * Hkv) * DH;
-    const int st = (int)in.slab;  // slabs of at most 64 rows: far below 2^31 floats
-    f32x4 c4 = {}, s4 = {};
-    if (in.cos && hh < nslot) {
-      c4 = *(const f32x4 *)(in.cos + pn * 64 + 4 * (li & 15));
-      s4 = *(const f32x4 *)(in.sin + pn * 64 + 4 * (li & 15));
-    }
+    // Query heads and k: half-split rotation (dim i pairs with i + 64, held
+    // by lane li ^ 16), then a weightless RMSNorm over the head.
     const int npage = owner ? sload(kv.table + b * kv.pages_per_seq + pn / kv.page_size) : 0;
     char *npg = kv.base + (long long)in.layer * kv.layer_stride + (long long)npage * kv.page_stride;
     const int nsl = pn % kv.page_size;
     for (int j = hh; j < nslot; j += 2 * NP) {
-      // slab column of the slot: query head hq0 + j, K head gk, V head gk
-      const int col = j < H ? hq0 + j : (j == H ? Hall + gk : Hall + Hkv + gk);
-      const float *uj = u + col * DH + 4 * li;
-      f32x4 t[kMaxRowSplit];
-#pragma unroll
-      for (int k = 0; k < kMaxRowSplit; ++k)
-        if (k == 0 || k < in.nslab) t[k] = *(const f32x4 *)(uj + k * st);
+      load_slot(j);
       f32x4 x = t[0];
 #pragma unroll
       for (int k = 1; k < kMaxRowSplit; ++k)
@@ -822,110 +815,111 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
       if (hl < H) qf[s] = *(const bf16x8 *)&q_s[hl * QS + 32 * s + 8 * q4];
       else qf[s] = (bf16x8){};
     }
-    const int nkey = pn - kpos0;  // the new position's slot in this wave's page, if pw
-    if constexpr (STAGE) {
-      // this wave's page has landed (each wave reads only its own staging area)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (pw) {
-        Ks[kdx(nkey, lane >> 3) + (lane & 7)] = kv_s[lane];
-        Ks[kdx(nkey, (lane + 64) >> 3) + (lane & 7)] = kv_s[lane + 64];
-        const int cc = vslot(nkey);
-        Vs[vdx(lane, cc >> 2) + (cc & 3)] = kv_s[DH + lane];
-        Vs[vdx(lane + 64, cc >> 2) + (cc & 3)] = kv_s[DH + lane + 64];
-      }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)&Ks[kdx(16 * kb + hl, 4 * s + q4)];
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
-    } else if (pw) {
-      bf16x8 kn[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kn[s] = *(const bf16x8 *)&kv_s[32 * s + 8 * q4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        if (16 * kb + hl == nkey) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) kf[kb][s] = kn[s];
-        }
-      const int cc = vslot(nkey), e = cc & 7;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if ((cc >> 3) == 4 * h + q4) {
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const bf16 v = kv_s[DH + 16 * d + hl];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              if (i == e) vf[d][h][i] = v;
-          }
-        }
-    }
-    // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
-    f32x4 sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = (f32x4){};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
-    }
-    const float sc = kLog2e / sqrtf((float)DH);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kpos0 + 16 * kb + 4 * q4 + r;
-        const float v = key < len ? sacc[kb][r] * sc : -INFINITY;
-        sacc[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sacc[kb][r] - mx);
-        sacc[kb][r] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    // positions past the end hold stale data: zero them so 0 * garbage cannot appear
-    if (kpos0 + 64 > len) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (kpos0 + 32 * h + 16 * (j >> 2) + 4 * q4 + (j & 3) >= len) vf[d][h][j] = (bf16)0.f;
-    }
-    // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
+    // Round r: page w + r NP of the chunk.  The next round's page is staged
+    // into the same LDS area once this round's fragments are in registers,
+    // so it lands while this round computes.  Online softmax over the
+    // rounds: running max mx, sum rs and O^T.
+    float mx = -INFINITY, rs = 0.f;
     f32x4 oacc[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
+    for (int r = 0; r < R; ++r) {
+      const int kp = kpos0 + r * NP * 64;
+      if (kp >= len) break;
+      const int nkey = pn - kp;  // the new position's slot in this page, if it holds it
+      const bool pw = nkey >= 0 && nkey < 64;
+      bf16x8 kf[4][4];
+      bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
+      {
+        // this round's page has landed (each wave reads only its own area)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (pw) {
+          Ks[kdx(nkey, lane >> 3) + (lane & 7)] = kv_s[lane];
+          Ks[kdx(nkey, (lane + 64) >> 3) + (lane & 7)] = kv_s[lane + 64];
+          const int cc = vslot(nkey);
+          Vs[vdx(lane, cc >> 2) + (cc & 3)] = kv_s[DH + lane];
+          Vs[vdx(lane + 64, cc >> 2) + (cc & 3)] = kv_s[DH + lane + 64];
+        }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pf;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = f2bf(sacc[2 * h][e]);
-        pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+          for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)&Ks[kdx(16 * kb + hl, 4 * s + q4)];
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
+        if (r + 1 < R && kp + NP * 64 < len) {
+          // the fragment reads (and the patch) have completed: the area is free
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          stage_page(kp + NP * 64);
+        }
       }
+      // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
+      f32x4 sacc[4];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d][h], pf, oacc[d], 0, 0, 0);
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = (f32x4){};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
+      }
+      const float sc = kLog2e / sqrtf((float)DH);
+      float pm = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kp + 16 * kb + 4 * q4 + e;
+          const float v = key < len ? sacc[kb][e] * sc : -INFINITY;
+          sacc[kb][e] = v;
+          pm = fmaxf(pm, v);
+        }
+      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+      const float mn = fmaxf(mx, pm);
+      const float scale = fast_exp2(mx - mn);  // 0 in the first round (mx = -inf)
+      mx = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = fast_exp2(sacc[kb][e] - mn);
+          sacc[kb][e] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      rs = rs * scale + ps;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) oacc[d] *= scale;
+      // positions past the end hold stale data: zero them so 0 * garbage cannot appear
+      if (kp + 64 > len) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (kp + 32 * h + 16 * (j >> 2) + 4 * q4 + (j & 3) >= len) vf[d][h][j] = (bf16)0.f;
+      }
+      // O^T += V^T P^T; k slot 8 q4 + j <-> key 32 h + 16 (j/4) + 4 q4 + j%4
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[e] = f2bf(sacc[2 * h][e]);
+          pf[4 + e] = f2bf(sacc[2 * h + 1][e]);
+        }
+#pragma unroll
+        for (int d = 0; d < 8; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d][h], pf, oacc[d], 0, 0, 0);
+      }
     }
     if (hl < H) {
-      // lane holds head hl, dims 16 d + 4 q4 + r; with STAGE the partial
-      // overwrites this wave's K staging area, whose reads the MFMAs above
-      // have consumed
+      // lane holds head hl, dims 16 d + 4 q4 + r; the partial overwrites
+      // this wave's K staging area, whose reads the MFMAs above have
+      // consumed
       float *o_w = (float *)wave_area(wave);
 #pragma unroll
       for (int d = 0; d < 8; ++d) *(f32x4 *)&o_w[hl * DH + 16 * d + 4 * q4] = oacc[d];
@@ -938,20 +932,23 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   __syncthreads();
   const int S = (len + CH - 1) / CH;   // chunks of this sequence
   const long long obase = (((long long)b * a.max_splits + chunk) * Hall + hq0) * DH;
-  for (int idx = tid; idx < H * DH; idx += NT) {
-    const int h = idx >> 7;
+  // Merge the pages: each thread takes 4 consecutive dims of one head.
+  for (int i4 = tid; i4 < H * DH / 4; i4 += NT) {
+    const int idx = 4 * i4, h = idx >> 7;
     float M = ml_s[0][h][0];
     for (int w = 1; w < nw; ++w) M = fmaxf(M, ml_s[w][h][0]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f32x4 O = {};
     for (int w = 0; w < nw; ++w) {
       const float f = fast_exp2(ml_s[w][h][0] - M);
       L += f * ml_s[w][h][1];
-      O += f * ((const float *)wave_area(w))[idx];
+      O += f * *(const f32x4 *)((const float *)wave_area(w) + idx);
     }
     if (S == 1) {
-      a.o[((long long)b * Hall + hq0) * DH + idx] = f2bf(O / L);
+      *(bf16x4 *)&a.o[((long long)b * Hall + hq0) * DH + idx] =
+          (bf16x4){f2bf(O[0] / L), f2bf(O[1] / L), f2bf(O[2] / L), f2bf(O[3] / L)};
     } else {
-      xst(a.o_part + obase + idx, O);
+      xst4(a.o_part + obase + idx, O);
       if ((idx & (DH - 1)) == 0) {
         float *ml = a.ml_part + (((long long)b * a.max_splits + chunk) * Hall + hq0 + h) * 2;
         xst(ml, M);
@@ -969,55 +966,44 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   __syncthreads();
   if (s_prev != (unsigned)(S - 1)) return;
   if (tid == 0) a.ctr[b * Hkv + gk] = 0u;
-  // Final merge over the S chunks.  (max, sum) of every chunk and head into
-  // LDS, then one factor per (chunk, head) with 1/sum folded in, then every
-  // output with all of its chunk loads in flight together.
-  // the per-wave areas are free by now
-  static_assert(kMaxDecodeChunks * 48 * 4 <= NP * WAVE_BYTES, "merge scratch exceeds LDS");
-  float *mlg = (float *)smem;                              // [S][16][2]
-  float *fct = (float *)smem + kMaxDecodeChunks * 32;      // [S][16]
-  for (int i = tid; i < S * H; i += NT) {
-    const int c = i / H, h = i - c * H;
-    const float *ml = a.ml_part + (((long long)b * a.max_splits + c) * Hall + hq0 + h) * 2;
-    mlg[(c * 16 + h) * 2] = xld(ml);
-    mlg[(c * 16 + h) * 2 + 1] = xld(ml + 1);
-  }
-  __syncthreads();
-  if (tid < H) {
-    float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, mlg[(c * 16 + tid) * 2]);
-    float L = 0.f;
-    for (int c = 0; c < S; ++c) L += fast_exp2(mlg[(c * 16 + tid) * 2] - M) * mlg[(c * 16 + tid) * 2 + 1];
-    const float inv = 1.0f / L;
-    for (int c = 0; c < S; ++c) fct[c * 16 + tid] = fast_exp2(mlg[(c * 16 + tid) * 2] - M) * inv;
-  }
-  __syncthreads();
-  constexpr int OPT = 16 * DH / NT;  // outputs per thread at most
+  // Final merge over the S chunks, 4 dims of one head per thread: the
+  // (max, sum) and partial output of up to 8 chunks are loaded at once, then
+  // folded into a running (max, sum, output).
   const float *ob = a.o_part + ((long long)b * a.max_splits * Hall + hq0) * DH;
-  float acc[OPT];
+  const float *mb = a.ml_part + ((long long)b * a.max_splits * Hall + hq0) * 2;
+  for (int i4 = tid; i4 < H * DH / 4; i4 += NT) {
+    const int idx = 4 * i4, h = idx >> 7;
+    float M = -INFINITY, L = 0.f;
+    f32x4 O = {};
+    for (int cg = 0; cg < S; cg += 8) {
+      float m[8], l[8];
+      f32x4 v[8];
 #pragma unroll
-  for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
-  for (int c0c = 0; c0c < S; c0c += 4) {
-    float v[4][OPT];
+      for (int cc = 0; cc < 8; ++cc)
+        if (cg + cc < S) {
+          const long long c = cg + cc;
+          m[cc] = xld(mb + (c * Hall + h) * 2);
+          l[cc] = xld(mb + (c * Hall + h) * 2 + 1);
+          v[cc] = xld4(ob + c * Hall * DH + idx);
+        }
+      float Mg = M;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+      for (int cc = 0; cc < 8; ++cc)
+        if (cg + cc < S) Mg = fmaxf(Mg, m[cc]);
+      const float r = fast_exp2(M - Mg);  // 0 on the first group (M = -inf)
+      L *= r;
+      O *= r;
 #pragma unroll
-      for (int j = 0; j < OPT; ++j) {
-        const int idx = tid + NT * j;
-        v[cc][j] = (c0c + cc < S && idx < H * DH) ? xld(ob + (long long)(c0c + cc) * Hall * DH + idx) : 0.f;
-      }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int j = 0; j < OPT; ++j) {
-        const int idx = tid + NT * j;
-        if (c0c + cc < S && idx < H * DH) acc[j] += fct[(c0c + cc) * 16 + (idx >> 7)] * v[cc][j];
-      }
-  }
-#pragma unroll
-  for (int j = 0; j < OPT; ++j) {
-    const int idx = tid + NT * j;
-    if (idx < H * DH) a.o[((long long)b * Hall + hq0) * DH + idx] = f2bf(acc[j]);
+      for (int cc = 0; cc < 8; ++cc)
+        if (cg + cc < S) {
+          const float f = fast_exp2(m[cc] - Mg);
+          L += f * l[cc];
+          O += f * v[cc];
+        }
+      M = Mg;
+    }
+    *(bf16x4 *)&a.o[((long long)b * Hall + hq0) * DH + idx] =
+        (bf16x4){f2bf(O[0] / L), f2bf(O[1] / L), f2bf(O[2] / L), f2bf(O[3] / L)};
   }
 }
 
@@ -1051,15 +1037,20 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
 
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  // Staging through LDS holds one workgroup per CU: use it (chunks of
-  // kDecodePages pages) only when the grid is at most one workgroup per CU.
-  // Otherwise twice the pages per chunk, so each sequence's final merge has
-  // half the chunks; the partial buffers, sized for kDecodeChunk, hold them.
-  if ((long long)a.max_splits * a.n * a.in.Hkv <= 256) {
-    attn_decode_kernel<true, kDecodePages><<<dim3(a.max_splits, a.n, a.in.Hkv), 64 * kDecodePages, 0, s>>>(a);
-  } else {
-    AttnDecodeArgs b = a;
-    b.max_splits = (a.max_splits + 1) / 2;
-    attn_decode_kernel<false, 2 * kDecodePages><<<dim3(b.max_splits, b.n, b.in.Hkv), 128 * kDecodePages, 0, s>>>(b);
+  // One workgroup per CU (128 KB of LDS each): R, the pages each wave takes
+  // in turn, is the smallest of 1 .. 4 that keeps the grid (chunks of
+  // kDecodePages R pages) within 256 workgroups.  a.max_splits counts chunks
+  // of kDecodePages pages, for which the partial buffers are sized.
+  const long long per = (long long)a.n * a.in.Hkv;
+  int R = 1;
+  while (R < 4 && (long long)((a.max_splits + R - 1) / R) * per > 256) ++R;
+  AttnDecodeArgs b = a;
+  b.max_splits = (a.max_splits + R - 1) / R;
+  const dim3 grid(b.max_splits, b.n, b.in.Hkv);
+  switch (R) {
+    case 1: attn_decode_kernel<kDecodePages, 1><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    case 2: attn_decode_kernel<kDecodePages, 2><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    case 3: attn_decode_kernel<kDecodePages, 3><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    default: attn_decode_kernel<kDecodePages, 4><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
   }
 }

@@ -527,15 +527,16 @@ DEV void wait_ahead(int ahead) {
 // block w % 2 and substep w / 2, and the two substep halves are added
 // through LDS at the end.  v_mfma_f32_16x16x32_bf16: lane l holds weight row
 // l%16 / activation row 16 mb + l%16, k elements 8 (l/16) .. +8 of the step.
-template <int EPI, int MB, bool DEEP, int BNR>
+template <int EPI, int MB, int BNR>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long long slab) {
   constexpr int MBE = (MB + 1) & ~1;      // activation 16-row blocks loaded
   constexpr int ROWS = BNR + 16 * MBE;    // LDS tile rows: weights, then activations
   static_assert((ROWS / 8) % 4 == 0, "DMA instructions must split evenly over the waves");
   constexpr int NI = (ROWS / 8) / 4;      // DMA instructions per wave per chunk
-  // Stages: a 72 KB ring (two workgroups per CU), or 144 KB (one workgroup
-  // per CU) when the grid is too small to fill the chip.
-  constexpr int S = (DEEP ? 147456 : 73728) / (ROWS * BK * 2);
+  // Stages: a 72 KB ring, so two workgroups fit on a CU.  A 144 KB ring
+  // (one workgroup per CU) was slower on every decode shape, also for grids
+  // of fewer workgroups than CUs.
+  constexpr int S = 73728 / (ROWS * BK * 2);
   static_assert(S >= 3 && (S - 2) * NI < 64, "ring depth");
   __shared__ bf16 lds[S][ROWS * BK];
 
@@ -614,30 +615,23 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(GemmArgs g, int ks, long
   }
 }
 
-template <int EPI, bool DEEP, int BNR>
+template <int EPI, int BNR>
 void launch_rows_d(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
   const dim3 grid(g.N / BNR, ks);
   switch ((g.M + 15) / 16) {
-    case 1: gemm_rows_kernel<EPI, 1, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    case 2: gemm_rows_kernel<EPI, 2, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    case 3: gemm_rows_kernel<EPI, 3, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
-    default: gemm_rows_kernel<EPI, 4, DEEP, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 1: gemm_rows_kernel<EPI, 1, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 2: gemm_rows_kernel<EPI, 2, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    case 3: gemm_rows_kernel<EPI, 3, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
+    default: gemm_rows_kernel<EPI, 4, BNR><<<grid, 256, 0, s>>>(g, ks, slab); break;
   }
 }
 
 template <int EPI>
 void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
-  // 256 CUs.  At most 128 tiles of 64 columns: halve the tiles.  A grid
-  // that leaves CUs without a second workgroup gets the deep ring.
+  // 256 CUs.  Fewer than 128 tiles of 64 columns: halve the tiles.
   const long long t64 = (long long)(g.N / 64) * ks;
-  if (t64 <= 128) {
-    if (2 * t64 <= 256) launch_rows_d<EPI, true, 32>(g, ks, slab, s);
-    else launch_rows_d<EPI, false, 32>(g, ks, slab, s);
-  } else if (t64 <= 256) {
-    launch_rows_d<EPI, true, 64>(g, ks, slab, s);
-  } else {
-    launch_rows_d<EPI, false, 64>(g, ks, slab, s);
-  }
+  if (t64 < 128) launch_rows_d<EPI, 32>(g, ks, slab, s);
+  else launch_rows_d<EPI, 64>(g, ks, slab, s);
 }
 
 template <int EPI>
@@ -719,11 +713,14 @@ void launch_gemm_bf16_rows(const GemmArgs &g, int ks, long long slab, hipStream_
   }
 }
 
-// About 320 workgroups (the chip holds two per CU), at least two 64-deep
-// chunks per k range, at most kMaxRowSplit ranges.
+// About 224 workgroups of 64 columns (timed on the decode shapes: 200 to
+// 250 beat both one per CU and the 320 to 400 of two per CU, since each
+// range re-reads the activation rows and adds a slab for the consumer to
+// sum), at least two 64-deep chunks per k range, at most kMaxRowSplit
+// ranges.
 int gemm_rows_ksplit(int N, int K) {
   const int tiles = N / 64, chunks = K / BK;
-  int ks = (320 + tiles / 2) / tiles;
+  int ks = (224 + tiles / 2) / tiles;
   ks = std::min(ks, chunks / 2);
   ks = std::min(ks, kMaxRowSplit);
   return std::max(ks, 1);

@@ -262,8 +262,8 @@ def test_small_bf16_gqa_prefill(n_head, n_kv, lens):
 @pytest.mark.parametrize("n_head,n_kv,n_seqs", [(6, 2, 4), (4, 4, 3), (6, 3, 40)])
 def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
     """Prefill into the paged cache, then 20 greedy decode steps with GQA; the
-    oracle consumes the GPU's tokens.  40 sequences make more than 256
-    decode-attention workgroups (the register-load variant)."""
+    oracle consumes the GPU's tokens.  (6, 3, 40): 240 decode-attention
+    workgroups of one page per wave."""
     t = torch()
     cfg = wl.small_model(2, n_head, vocab=4096, n_kv_head=n_kv)
     rng = np.random.default_rng(n_seqs)
@@ -297,20 +297,23 @@ def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
     kv.close()
 
 
-def test_small_bf16_decode_many_sequences():
-    """64 sequences with room for 1100 positions each: more than 256 decode
-    attention workgroups, so the register-load variant with 8-page chunks
-    runs; 3 greedy steps, the longest and the shortest sequence
+@pytest.mark.parametrize("n_head,cap", [(2, 1100), (7, 2100)])
+def test_small_bf16_decode_many_sequences(n_head, cap):
+    """64 sequences with room for `cap` positions each: 4-page chunks would
+    make more than 256 decode-attention workgroups, so each wave takes 2
+    (cap 1100) or 3 (cap 2100) pages in turn, with the online softmax across
+    them.  7 heads: the 9 q/k/v slots of the owning chunk take two passes of
+    its 8 half-waves.  3 greedy steps, the longest and the shortest sequence
     teacher-forced through the oracle."""
     t = torch()
-    cfg = wl.small_model(2, 2, vocab=4096)
+    cfg = wl.small_model(2, n_head, vocab=4096)
     rng = np.random.default_rng(21)
-    lens = rng.integers(1, 1090, size=64)
-    lens[0], lens[1] = 1089, 1
+    lens = rng.integers(1, cap - 10, size=64)
+    lens[0], lens[1] = cap - 11, 1
     w = wl.ragged_prefill(cfg, lens, seed=21)
     W, dm = device_model(cfg)
     n, steps = len(lens), 3
-    kv = B.DeviceKV(dm, n, 1100)
+    kv = B.DeviceKV(dm, n, cap)
     logits0, _ = gpu_prefill(dm, w.tokens, w.seqlens, rows=B.ROWS_LAST, kv=kv.handle)
     toks = t.empty(n, dtype=t.int32, device="cuda")
     B.gpt_select_tokens(t.from_numpy(logits0).cuda(), n, cfg.vocab, 0.0, None, toks)
