@@ -335,7 +335,9 @@ void run_gemm(const gpt_config *c, const GemmArgs &g, int cls, hipStream_t s) {
   const double es = c->dtype == GPT_DTYPE_BF16 ? 2.0 : 4.0;
   double out_b = g.epi == EPI_RESID ? 8.0
                  : g.epi == EPI_DRELU2 ? 4.0 + es  // reads z, writes dz
-                 : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV) ? es : 4.0;
+                 : (g.epi == EPI_BF16 || g.epi == EPI_RELU2_BF16 || g.epi == EPI_QKV || g.epi == EPI_LOGITS_BF16)
+                     ? es
+                     : 4.0;
   bool rows = c->dtype == GPT_DTYPE_BF16 && g.M <= 64;
   Timed t(rows && cls == GPT_PROF_GEMM ? GPT_PROF_SKINNY : cls, s, 2.0 * g.M * g.N * g.K,
           es * ((double)g.M * g.K + (double)g.N * g.K) + out_b * g.M * g.N);
@@ -889,28 +891,42 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
   }
   copy_x(xs(2 * L));
   fwd_norm(fw, bf.x, bf.h);  // hf
+  // Large M in bf16: the LM head stores the logits in bf16 (the precision
+  // the softmax gradient is rounded to anyway) with the softmax partials and
+  // each row's fp32 target logit, from which the loss comes; the gradient
+  // kernel then writes dl and its transpose in one pass.
   const bool fused_lse = bf16p && M > 64;
   {
-    GemmArgs lg = gemm(bf.h, d, w->lm_head, M, V, d, tb.logits, V, fused_lse ? EPI_LOGITS : EPI_F32);
+    GemmArgs lg = gemm(bf.h, d, w->lm_head, M, V, d, tb.logits, V, fused_lse ? EPI_LOGITS_BF16 : EPI_F32);
     lg.part = bf.lpart;
+    lg.targets = targets;
+    lg.tgt = bf.tgt;
     run_gemm(c, lg, GPT_PROF_LMHEAD, s);
-    Timed t(GPT_PROF_SOFTMAX, s, 0, (double)M * V * 4);
-    if (fused_lse) launch_lse_combine(bf.lpart, V / kLogitsPartCols, M, bf.lse_tmp, tb.logits, V, nullptr, s);
-    else launch_softmax_lse(tb.logits, M, V, bf.lse_tmp, nullptr, s);
-    launch_ce_from_logits(tb.logits, bf.lse_tmp, targets, V, M, loss, s);
+    if (fused_lse) {
+      Timed t(GPT_PROF_SOFTMAX, s, 0, (double)M * (V / kLogitsPartCols) * 8 + (double)M * 12);
+      launch_ce_from_parts(bf.lpart, V / kLogitsPartCols, bf.tgt, targets, V, M, loss, bf.lse_tmp, s);
+    } else {
+      Timed t(GPT_PROF_SOFTMAX, s, 0, (double)M * V * 4);
+      launch_softmax_lse(tb.logits, M, V, bf.lse_tmp, nullptr, s);
+      launch_ce_from_logits(tb.logits, bf.lse_tmp, targets, V, M, loss, s);
+    }
     if (mean) launch_mean_loss(loss, targets, V, M, mean, s);
     launch_count_targets(targets, M, V, tb.count, s);
   }
 
   // ---- LM head and final norm
-  {
+  if (fused_lse) {
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * V * 2 * es + (double)V * Mp * es);
+    launch_dlogits_t((const bf16 *)tb.logits, bf.lse_tmp, targets, tb.count, M, V, (bf16 *)tb.dl,
+                     (bf16 *)tb.trA, Mp, Mp, s);  // dl and dl^T [V][Mp]
+  } else {
     Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * V * (4 + es));
     if (bf16p) launch_dlogits<bf16>(tb.logits, bf.lse_tmp, targets, tb.count, M, V, (bf16 *)tb.dl, s);
     else launch_dlogits<float>(tb.logits, bf.lse_tmp, targets, tb.count, M, V, (float *)tb.dl, s);
   }
   {
-    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)(M * (long long)V + (long long)M * d + (long long)V * d) * 2 * es);
-    tr_md(c, tb.dl, V, M, V, tb.trA, Mp, Mp, s);    // dl^T [V][Mp]
+    Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)((fused_lse ? 0 : M * (long long)V) + (long long)M * d + (long long)V * d) * 2 * es);
+    if (!fused_lse) tr_md(c, tb.dl, V, M, V, tb.trA, Mp, Mp, s);  // dl^T [V][Mp]
     tr_md(c, bf.h, d, M, d, tb.trB, Mp, Mp, s);     // hf^T [d][Mp]
     tr_md(c, w->lm_head, d, V, d, tb.wT, V, V, s);  // W_lm^T [d][V]
   }

@@ -252,7 +252,7 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
   const int nw0 = n0 + wn * WN;
-  if constexpr (EPI == EPI_LOGITS || EPI == EPI_LOSS) {
+  if constexpr (EPI == EPI_LOGITS || EPI == EPI_LOSS || EPI == EPI_LOGITS_BF16) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int m = m0 + wm * WM + 32 * j + c32;
@@ -295,8 +295,15 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
     return;
   }
   constexpr int EPS = EPI == EPI_LOGITS ? EPI_F32 : EPI;
+  static_assert(EPI != EPI_LOGITS_BF16 || WN == 64, "one partial block per wave");
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    // EPI_LOGITS_BF16: the lane that owns row mrow keeps its target logit
+    // (fp32, from the staged block) when the target falls in this wave tile
+    const int mrow = m0 + wm * WM + 32 * j + c32;
+    int tcol = -1;
+    if constexpr (EPI == EPI_LOGITS_BF16)
+      if (hi == 0 && mrow < g.M) tcol = g.targets[mrow] - nw0;
     // columns 0-63 of the wave tile, then (96-wide tiles) columns 64-95
 #pragma unroll
     for (int i0 = 0; i0 < TN; i0 += 2) {
@@ -310,6 +317,8 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
           *(f32x4 *)&stg[c32 * kStagePitch + 32 * i + 8 * c + 4 * hi] =
               (f32x4){acc[i0 + i][j][4 * c], acc[i0 + i][j][4 * c + 1], acc[i0 + i][j][4 * c + 2],
                       acc[i0 + i][j][4 * c + 3]};
+      if constexpr (EPI == EPI_LOGITS_BF16)
+        if (tcol >= 32 * i0 && tcol < 32 * (i0 + ni)) g.tgt[mrow] = stg[c32 * kStagePitch + tcol - 32 * i0];
 #pragma unroll
       for (int q = 0; q < 4 * ni; ++q) {
         const int r = (64 / lpr) * q + rr;
@@ -321,6 +330,9 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
           // nothing in this pass reads the logits again: non-temporal stores
           // keep them from displacing the operands in L2 (10% on the LM head)
           __builtin_nontemporal_store(v, (f32x4 *)((float *)g.C + (long long)m * g.ldc + n));
+        } else if constexpr (EPI == EPI_LOGITS_BF16) {
+          const bf16x4 o = {f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+          __builtin_nontemporal_store(o, (bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n));
         } else {
           epi_store4<EPS>(g, m, n, v[0], v[1], v[2], v[3]);
         }
@@ -637,7 +649,8 @@ void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = 256;
-  static_assert((EPI != EPI_LOGITS && EPI != EPI_LOSS) || 256 / 4 == kLogitsPartCols, "partial width");
+  static_assert((EPI != EPI_LOGITS && EPI != EPI_LOSS && EPI != EPI_LOGITS_BF16) || 256 / 4 == kLogitsPartCols,
+                "partial width");
   const int tm = (g.M + BM - 1) / BM;
   const int t256 = tm * ((g.N + 255) / 256);
   if constexpr (EPI == EPI_RESID || EPI == EPI_F32) {
@@ -697,6 +710,7 @@ void launch_gemm_bf16(const GemmArgs &g, hipStream_t s) {
     case EPI_RESID: launch_big<EPI_RESID>(g, s); break;
     case EPI_LOGITS: launch_big<EPI_LOGITS>(g, s); break;
     case EPI_LOSS: launch_big<EPI_LOSS>(g, s); break;
+    case EPI_LOGITS_BF16: launch_big<EPI_LOGITS_BF16>(g, s); break;
     case EPI_DRELU2: launch_big<EPI_DRELU2>(g, s); break;
     case EPI_QKV: launch_big<EPI_QKV>(g, s); break;
     default: launch_big<EPI_F32>(g, s); break;

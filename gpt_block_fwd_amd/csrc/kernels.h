@@ -128,6 +128,10 @@ template <typename T>
 void launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
 // dst[m][c] = bf16(src[m lds + c]) for c < C
 void launch_cast_rows(const float *src, long long lds, int M, int C, bf16 *dst, hipStream_t s);
+// From bf16 logits [rows][V]: dl [rows][V] and its transpose dlt [V][ldt]
+// (columns rows .. Rp - 1 zero); V % 64 == 0, Rp % 64 == 0, ldt % 8 == 0.
+void launch_dlogits_t(const bf16 *logits, const float *lse, const int *targets, const int *count, int rows, int V,
+                      bf16 *dl, bf16 *dlt, long long ldt, int Rp, hipStream_t s);
 template <typename T>
 void launch_dlogits(const float *logits, const float *lse, const int *targets, const int *count, int rows, int V,
                     T *dl, hipStream_t s);
@@ -145,7 +149,8 @@ enum Epi {
   EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each kLogitsPartCols columns
   EPI_QKV = 6,     // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
   EPI_LOSS = 7,    // EPI_LOGITS' partials and each row's target logit; C is not written
-  EPI_DRELU2 = 8   // bf16 C = acc * 2 max(z, 0), z = aux[m][n] (fp32, row stride ldc): ReLU^2 backward
+  EPI_DRELU2 = 8,  // bf16 C = acc * 2 max(z, 0), z = aux[m][n] (fp32, row stride ldc): ReLU^2 backward
+  EPI_LOGITS_BF16 = 9  // EPI_LOSS' partials and target logit, and C = the logits in bf16
 };
 
 // Extra operands of the EPI_QKV epilogue (column block = one 128-wide head).
