@@ -206,6 +206,12 @@ struct TrainBufs {
   float *ksl;       // k-split slabs of the weight-gradient GEMMs
   int *count;
   int Mp;
+  // bf16: each layer's forward activations, kept for the backward: the
+  // normed inputs h and h2, q, k, V^T, the attention output o and its
+  // per-row base-2 log-sum-exp, and u = act(W1 h2).  Layer l's copy of a
+  // buffer starts l times its size in.
+  void *hl, *h2l, *ql, *kl, *vtl, *ol, *ul;
+  float *lsel;
 };
 
 size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base, Bufs *b, TrainBufs *tb) {
@@ -263,6 +269,16 @@ size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base,
     t.ksl = (float *)take(most * 4);
   }
   t.count = (int *)take(4);
+  if (c->dtype == GPT_DTYPE_BF16) {
+    t.hl = take(L * M * d * 2);
+    t.h2l = take(L * M * d * 2);
+    t.ql = take(L * M * H * dh * 2);
+    t.kl = take(L * M * Hkv * dh * 2);
+    t.vtl = take(L * Hkv * dh * b_ldvt(M, nseq) * 2);
+    t.ol = take(L * M * H * dh * 2);
+    t.ul = take(L * M * F * 2);
+    t.lsel = (float *)take(L * M * H * 4);
+  }
   if (tb) *tb = t;
   return align256(off);
 }
@@ -883,12 +899,42 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     else launch_embed_f32(tokens, (const float *)w->wte, (const float *)w->wpe, bf.pos, bf.x, M, d, s);
   }
   Fwd fw = make_fwd(c, w, rope_cos, rope_sin, &bf, PagedKV{}, false, M, n_seqs, cu_seqlens, s);
+  // bf16 prefills on the large-M kernels keep every layer's activations
+  // (tb.hl ...) and the backward recomputes only the QKV projection; the
+  // others keep the residual stream alone and recompute each layer.
+  const bool keep = bf16p && M > 64;
+  const Bufs bf0 = bf;
+  auto layer_ptr = [&](void *base, long long elems, size_t esz, int l) -> void * {
+    return (char *)base + (size_t)l * elems * esz;
+  };
+  auto h_l = [&](int l) { return layer_ptr(tb.hl, (long long)M * d, 2, l); };
+  auto h2_l = [&](int l) { return layer_ptr(tb.h2l, (long long)M * d, 2, l); };
+  auto q_l = [&](int l) { return layer_ptr(tb.ql, (long long)M * H * dh, 2, l); };
+  auto k_l = [&](int l) { return layer_ptr(tb.kl, (long long)M * Hkv * dh, 2, l); };
+  auto vt_l = [&](int l) { return layer_ptr(tb.vtl, (long long)Hkv * dh * bf.ldvt, 2, l); };
+  auto o_l = [&](int l) { return layer_ptr(tb.ol, (long long)M * H * dh, 2, l); };
+  auto u_l = [&](int l) { return layer_ptr(tb.ul, (long long)M * F, 2, l); };
+  auto lse_l = [&](int l) { return (float *)layer_ptr(tb.lsel, (long long)M * H, 4, l); };
   for (int l = 0; l < L; ++l) {
+    if (keep) {
+      bf.h = h_l(l);
+      bf.q = q_l(l);
+      bf.k = k_l(l);
+      bf.vt = vt_l(l);
+      bf.o = o_l(l);
+      fw.lse2 = lse_l(l);
+    }
     copy_x(xs(2 * l));
     fwd_attn_half(fw, l);
+    if (keep) {
+      bf.h = h2_l(l);
+      bf.u = u_l(l);
+    }
     copy_x(xs(2 * l + 1));
     fwd_mlp_half(fw, l);
   }
+  bf = bf0;
+  fw.lse2 = nullptr;
   copy_x(xs(2 * L));
   fwd_norm(fw, bf.x, bf.h);  // hf
   // Large M in bf16: the LM head stores the logits in bf16 (the precision
@@ -943,11 +989,18 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
   for (int l = L - 1; l >= 0; --l) {
     const float *xl = xs(2 * l), *xm = xs(2 * l + 1);
     // ---- MLP: x = xm + W2 act(W1 rms(xm))
-    fwd_norm(fw, xm, bf.h);                                       // h2
-    mm(bf.h, d, w->w1[l], d, M, F, d, tb.z, F);                   // z
+    if (keep) {
+      bf.h = h2_l(l);                                             // h2 kept
+    } else {
+      fwd_norm(fw, xm, bf.h);                                     // h2
+      mm(bf.h, d, w->w1[l], d, M, F, d, tb.z, F);                 // z
+    }
     {
-      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * (4 + es) + (double)M * d * (4 + es) + (double)d * F * 2 * es);
-      if (bf16p) {
+      Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * F * ((keep ? 2 : 4) + es) + (double)M * d * (4 + es) +
+                                            (double)d * F * 2 * es);
+      if (keep) {
+        tr_md(c, u_l(l), F, M, F, tb.trB, Mp, Mp, s);           // u^T [F][Mp]
+      } else if (bf16p) {
         launch_transpose_relu2(tb.z, F, M, F, (bf16 *)tb.trB, Mp, Mp, s);  // u^T [F][Mp] from z
       } else {
         launch_act_bwd<float>(tb.z, nullptr, (float *)tb.u, nullptr, (long long)M * F, c->act, s);
@@ -959,11 +1012,12 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     mmw(tb.trA, tb.trB, d, F, gr->w2[l]);                         // dW2 = dx^T u
     const void *dxA = bf16p ? tb.dxb : (const void *)tb.dx;
     // the large-M GEMM applies the ReLU^2 backward in its epilogue:
-    // dz = (dx W2) * 2 max(z, 0); otherwise du = dx W2, then a pass
-    const bool fused_dact = bf16p && M > 64;
+    // dz = (dx W2) * 2 sqrt(u) with the kept u; otherwise du = dx W2, then a
+    // pass over the recomputed z
+    const bool fused_dact = keep;
     if (fused_dact) {
       GemmArgs g = gemm(dxA, d, tb.wT, M, F, d, tb.dz, F, EPI_DRELU2);
-      g.aux = tb.z;
+      g.aux = (const bf16 *)u_l(l);
       run_gemm(c, g, GPT_PROF_BWD_GEMM, s);
     } else {
       mm(dxA, d, tb.wT, d, M, F, d, tb.du, F);
@@ -984,11 +1038,28 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     rms_bwd(xm, tb.dh);
 
     // ---- attention: xm = xl + Wo Attn(q, k, v)
-    fwd_norm(fw, xl, bf.h);                                       // h
-    fwd_qkv(fw, l, false);                                        // pre -> bf.qkv; q, k, vt
-    fw.lse2 = bf16p ? tb.lse : nullptr;
-    fwd_attention(fw);                                            // o (and lse2)
-    fw.lse2 = nullptr;
+    float *lse_cur = tb.lse;
+    if (keep) {
+      // h, q, k, V^T, o and lse2 kept; the fp32 projection (pre) recomputed
+      bf.h = h_l(l);
+      bf.q = q_l(l);
+      bf.k = k_l(l);
+      bf.vt = vt_l(l);
+      bf.o = o_l(l);
+      lse_cur = lse_l(l);
+      GemmArgs g = gemm(bf.h, d, w->wq[l], M, qkv_n, d, bf.qkv, qkv_n, EPI_F32);
+      g.W1 = w->wk[l];
+      g.W2 = w->wv[l];
+      g.n1 = H * dh;
+      g.n2 = (H + Hkv) * dh;
+      run_gemm(c, g, GPT_PROF_BWD_GEMM, s);                       // pre -> bf.qkv
+    } else {
+      fwd_norm(fw, xl, bf.h);                                     // h
+      fwd_qkv(fw, l, false);                                      // pre -> bf.qkv; q, k, vt
+      fw.lse2 = bf16p ? tb.lse : nullptr;
+      fwd_attention(fw);                                          // o (and lse2)
+      fw.lse2 = nullptr;
+    }
     {
       Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * (4 + es) + (double)M * H * dh * 2 * es +
                                             (double)d * H * dh * 2 * es);
@@ -1017,7 +1088,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
         mb.qt = (const bf16 *)tb.qt;
         mb.dot = (const bf16 *)tb.dot;
         mb.ldt = bf.ldvt;
-        mb.lse2 = tb.lse;
+        mb.lse2 = lse_cur;
         mb.dsum = tb.dsum;
         mb.cu = bf.cu;
         mb.cu_pad = bf.cu_pad;
@@ -1087,6 +1158,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     mm(tb.dqkv, qkv_n, tb.wT, qkv_n, M, d, qkv_n, tb.dh, d);       // dh = dqkv [Wq; Wk; Wv]
     rms_bwd(xl, tb.dh);
   }
+  bf = bf0;
   // ---- embeddings
   {
     Timed t(GPT_PROF_BWD_OTHER, s, 0, (double)M * d * 12);

@@ -50,9 +50,10 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     bf16x4 o = {f2bf(v0), f2bf(v1), f2bf(v2), f2bf(v3)};
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_DRELU2) {
-    const f32x4 z = *(const f32x4 *)(g.aux + (long long)m * g.ldc + n);
-    bf16x4 o = {f2bf(v0 * 2.f * fmaxf(z[0], 0.f)), f2bf(v1 * 2.f * fmaxf(z[1], 0.f)),
-                f2bf(v2 * 2.f * fmaxf(z[2], 0.f)), f2bf(v3 * 2.f * fmaxf(z[3], 0.f))};
+    // d/dz max(z, 0)^2 = 2 max(z, 0) = 2 sqrt(u)
+    const bf16x4 u = *(const bf16x4 *)(g.aux + (long long)m * g.ldc + n);
+    bf16x4 o = {f2bf(v0 * 2.f * sqrtf(bf2f(u[0]))), f2bf(v1 * 2.f * sqrtf(bf2f(u[1]))),
+                f2bf(v2 * 2.f * sqrtf(bf2f(u[2]))), f2bf(v3 * 2.f * sqrtf(bf2f(u[3])))};
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_RESID) {
     float *p = (float *)g.C + (long long)m * g.ldc + n;

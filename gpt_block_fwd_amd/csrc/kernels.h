@@ -149,7 +149,7 @@ enum Epi {
   EPI_LOGITS = 5,  // fp32 store + per-row (max, sum exp) over each kLogitsPartCols columns
   EPI_QKV = 6,     // RoPE + QK-norm + bf16 scatter of q / k / v^T (+ paged cache)
   EPI_LOSS = 7,    // EPI_LOGITS' partials and each row's target logit; C is not written
-  EPI_DRELU2 = 8,  // bf16 C = acc * 2 max(z, 0), z = aux[m][n] (fp32, row stride ldc): ReLU^2 backward
+  EPI_DRELU2 = 8,  // bf16 C = acc * 2 sqrt(u), u = aux[m][n] = max(z, 0)^2 (bf16, row stride ldc): ReLU^2 backward
   EPI_LOGITS_BF16 = 9  // EPI_LOSS' partials and target logit, and C = the logits in bf16
 };
 
@@ -178,10 +178,10 @@ struct GemmArgs {
   void *C;
   long long ldc;
   int epi;
-  float *part;  // EPI_LOGITS, EPI_LOSS: [M][N/kLogitsPartCols][2] partial (max, sum exp)
-  const float *aux;     // EPI_DRELU2: the pre-activation z
-  const int *targets;  // EPI_LOSS: [M] target column of each row (any value)
-  float *tgt;          // EPI_LOSS: [M] C[m][targets[m]], written where targets[m] is in [0, N)
+  float *part;  // EPI_LOGITS, EPI_LOSS, EPI_LOGITS_BF16: [M][N/kLogitsPartCols][2] partial (max, sum exp)
+  const bf16 *aux;     // EPI_DRELU2: the activation u = max(z, 0)^2
+  const int *targets;  // EPI_LOSS, EPI_LOGITS_BF16: [M] target column of each row (any value)
+  float *tgt;          // EPI_LOSS, EPI_LOGITS_BF16: [M] C[m][targets[m]] (fp32), where targets[m] is in [0, N)
   QkvEpi qkv;   // EPI_QKV
   // k split of the large-M kernel (EPI_F32 only): grid row kz multiplies the
   // kz-th K-long slice of every row of A and W (rows lda / ldw apart) into
