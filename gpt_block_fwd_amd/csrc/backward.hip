@@ -132,6 +132,49 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const float *x, const floa
   }
 }
 
+// The same with 16-byte accesses, the row held in registers between the two
+// passes: lane l takes floats 256 c + 4 l .. +3 of each 256-float chunk c
+// (NC chunks, d <= 256 NC, d % 4 == 0).
+template <int NC>
+__global__ __launch_bounds__(256) void rms_bwd4_kernel(const float *x, const float *dy, float *dx, bf16 *dxb,
+                                                       int M, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const long long base = (long long)row * d;
+  f32x4 xv[NC], gv[NC];
+  float ss = 0.f, sg = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = 256 * c + 4 * lane;
+    if (i < d) {
+      xv[c] = *(const f32x4 *)(x + base + i);
+      gv[c] = *(const f32x4 *)(dy + base + i);
+    } else {
+      xv[c] = (f32x4){};
+      gv[c] = (f32x4){};
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss += xv[c][e] * xv[c][e];
+      sg += gv[c][e] * xv[c][e];
+    }
+  }
+  ss = wave_sum(ss);
+  sg = wave_sum(sg);
+  const float r = sqrtf(ss / d + eps), inv = 1.0f / r;
+  const float m = sg * inv / d;  // mean(dy y)
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = 256 * c + 4 * lane;
+    if (i >= d) continue;
+    f32x4 v = *(const f32x4 *)(dx + base + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += (gv[c][e] - xv[c][e] * inv * m) * inv;
+    *(f32x4 *)(dx + base + i) = v;
+    if (dxb) *(bf16x4 *)(dxb + base + i) = (bf16x4){f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+  }
+}
+
 // ---------------------------------------------------------------- MLP activation
 // u = act(z) and dz = du act'(z): ReLU^2 (2 max(z, 0)) or ReLU ([z > 0]).
 template <typename T>
@@ -474,7 +517,21 @@ template void launch_cast<float, bf16>(const float *, bf16 *, long long, hipStre
 template void launch_cast<float, float>(const float *, float *, long long, hipStream_t);
 
 void launch_rms_bwd(const float *x, const float *dy, float *dx, bf16 *dxb, int M, int d, float eps, hipStream_t s) {
-  if (M > 0) rms_bwd_kernel<<<(M + 3) / 4, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps);
+  if (M <= 0) return;
+  const unsigned grid = (unsigned)((M + 3) / 4);
+  if (d % 4 == 0 && d <= 2048) {
+    switch ((d + 255) / 256) {
+      case 1: rms_bwd4_kernel<1><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 2: rms_bwd4_kernel<2><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 3: rms_bwd4_kernel<3><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 4: rms_bwd4_kernel<4><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 5: rms_bwd4_kernel<5><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 6: rms_bwd4_kernel<6><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      case 7: rms_bwd4_kernel<7><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+      default: rms_bwd4_kernel<8><<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps); return;
+    }
+  }
+  rms_bwd_kernel<<<grid, 256, 0, s>>>(x, dy, dx, dxb, M, d, eps);
 }
 
 template <typename T>
