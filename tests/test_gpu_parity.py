@@ -297,12 +297,12 @@ def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
     kv.close()
 
 
-@pytest.mark.parametrize("n_head,cap", [(2, 1100), (7, 2100)])
+@pytest.mark.parametrize("n_head,cap", [(2, 1100), (7, 2100), (2, 3600)])
 def test_small_bf16_decode_many_sequences(n_head, cap):
     """64 sequences with room for `cap` positions each: 4-page chunks would
     make more than 256 decode-attention workgroups, so each wave takes 2
-    (cap 1100) or 3 (cap 2100) pages in turn, with the online softmax across
-    them.  7 heads: the 9 q/k/v slots of the owning chunk take two passes of
+    (cap 1100), 3 (cap 2100) or 4 (cap 3600) pages in turn, with the online
+    softmax across them.  7 heads: the 9 q/k/v slots of the owning chunk take two passes of
     its 8 half-waves.  3 greedy steps, the longest and the shortest sequence
     teacher-forced through the oracle."""
     t = torch()
