@@ -19,14 +19,15 @@ GEMM_SHAPES = [
     (513, 1920, 1664),
     # residual add on 192-column tiles (N = 768, 1152, 384), ragged M
     (700, 768, 3072),
-    # decode-row kernel (M <= 64): 1, 2, 3 and 4 row blocks, ragged M, 64-column tiles
+    # decode-row kernel (M <= 64): 1, 2, 3 and 4 row blocks, ragged M; 32-column
+    # tiles where 64-column ones would number fewer than 128
     (1, 128, 64),
     (33, 768, 768),
     (64, 1024, 3072),
     (64, 1920, 1664),
     (17, 6656, 1664),
     (40, 384, 1152),
-    # 64-column tiles: deep ring (129-256 tiles) and two workgroups per CU (> 256)
+    # 64-column tiles: 160 and 512 of them
     (48, 10240, 768),
     (8, 32768, 256),
 ]
