@@ -702,6 +702,12 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   const int Hall = in.H, Hkv = in.Hkv, G = Hall / Hkv, gk = blockIdx.z, hq0 = gk * G;
   const int kvd = Hkv * DH;  // row width of a K page
   const int len = kv.lens[b] + 1;  // positions 0 .. lens[b], the last one new
+  // This wave's first page-table entry does not depend on len: it is read
+  // together with it (the scalar load's wait covers both), so the page copy
+  // starts one round trip earlier.  The index is clamped to the table's row;
+  // an entry past the sequence is not used.
+  const int page0 = sload(kv.table + b * kv.pages_per_seq +
+                          min((chunk * CH + wave * 64) / kv.page_size, kv.pages_per_seq - 1));
   const int pn = len - 1;
   const int c0 = chunk * CH;
   if (c0 >= len) return;
@@ -736,16 +742,15 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     s4 = *(const f32x4 *)(in.sin + pn * 64 + 4 * (li & 15));
   }
   bf16 *Ks = (bf16 *)wave_area(wave), *Vs = Ks + 64 * DH;
-  // page of cached positions kp .. kp + 63 of this sequence and K/V head
-  auto page_ptr = [&](int kp) {
-    const int page = sload(kv.table + b * kv.pages_per_seq + kp / kv.page_size);
+  // cache page `page` of this layer
+  auto page_ptr = [&](int page) {
     return (const char *)kv.base + (long long)in.layer * kv.layer_stride + (long long)page * kv.page_stride;
   };
   // 32 wave instructions of 1 KB: K as 4 keys x 256 B each, V^T as 8 dims x
   // 128 B each; lane i fills slot i of the instruction's kilobyte and so
   // loads the logical chunk that slot holds.
-  auto stage_page = [&](int kp) {
-    const char *pg = page_ptr(kp);
+  auto stage_page = [&](int page) {
+    const char *pg = page_ptr(page);
     const bf16 *K = (const bf16 *)pg + gk * DH;                      // rows of kvd
     const bf16 *Vt = (const bf16 *)(pg + kv.half_bytes) + gk * DH * 64;  // [128][64]
 #pragma unroll
@@ -761,7 +766,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
                                        LDS_PTR(Vs + j * 512), 16, 0, 0);
     }
   };
-  if (kpos0 < len) stage_page(kpos0);
+  if (kpos0 < len) stage_page(page0);
   {
     // Query heads and k: half-split rotation (dim i pairs with i + 64, held
     // by lane li ^ 16), then a weightless RMSNorm over the head.
@@ -851,7 +856,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
         if (r + 1 < R && kp + NP * 64 < len) {
           // the fragment reads (and the patch) have completed: the area is free
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          stage_page(kp + NP * 64);
+          stage_page(sload(kv.table + b * kv.pages_per_seq + (kp + NP * 64) / kv.page_size));
         }
       }
       // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
