@@ -189,7 +189,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
 // Extra buffers of the loss backward, carved after the forward's.
 struct TrainBufs {
   float *xs;        // [2L + 1][M][d] residual stream at each layer's input and middle, then the last
-  float *logits;    // [M][V]
+  float *logits;    // [M][V] fp32, or bf16 where the LM head fuses the softmax partials
   void *dl;         // [M][V] gradient of the logits (model dtype)
   void *trA, *trB;  // transposed operands of the weight-gradient GEMMs, rows of Mp
   void *wT;         // a transposed weight
@@ -229,7 +229,8 @@ size_t carve_train(const gpt_config *c, long long M, long long nseq, char *base,
   t.Mp = (int)((M + 63) / 64 * 64);
   const long long Mp = t.Mp;
   t.xs = (float *)take((2 * L + 1) * M * d * 4);
-  t.logits = (float *)take(M * V * 4);
+  // bf16 steps of more than 64 rows store bf16 logits; smaller ones fp32
+  t.logits = (float *)take(c->dtype == GPT_DTYPE_BF16 ? std::max(M * V * 2, std::min(M, 64LL) * V * 4) : M * V * 4);
   t.dl = take(M * V * es);
   t.trA = take(std::max({V, F, qkv_n, d, H * dh}) * Mp * es);
   t.trB = take(std::max({d, F, H * dh}) * Mp * es);
