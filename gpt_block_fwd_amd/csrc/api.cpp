@@ -517,6 +517,7 @@ struct Fwd {
   double attn_flops;
   hipStream_t s;
   float *lse2;  // bf16 attention: each row's base-2 log-sum-exp, or NULL
+  float *x_out; // residual GEMMs write bf->x + f(bf->x) here instead of in place, or NULL
 };
 
 Fwd make_fwd(const gpt_config *c, const gpt_weights *w, const float *rope_cos, const float *rope_sin, Bufs *bf,
@@ -657,7 +658,9 @@ void fwd_attn_half(const Fwd &f, int l) {
   fwd_norm(f, bf.x, bf.h);
   fwd_qkv(f, l, c->dtype == GPT_DTYPE_BF16 && f.M > 64);
   fwd_attention(f);
-  run_gemm(c, gemm(bf.o, H * dh, f.w->wo[l], f.M, d, H * dh, bf.x, d, EPI_RESID), GPT_PROF_GEMM, f.s);
+  GemmArgs g = gemm(bf.o, H * dh, f.w->wo[l], f.M, d, H * dh, f.x_out ? f.x_out : bf.x, d, EPI_RESID);
+  if (f.x_out) g.rin = bf.x;
+  run_gemm(c, g, GPT_PROF_GEMM, f.s);
 }
 
 // x += W2 act(W1 RMSNorm(x)): the second half of layer l
@@ -670,7 +673,9 @@ void fwd_mlp_half(const Fwd &f, int l) {
   run_gemm(c, gemm(bf.h, d, f.w->w1[l], M, F, d, bf.u, F,
                    bf16p ? EPI_RELU2_BF16 : (c->act == GPT_ACT_RELU ? EPI_RELU_F32 : EPI_RELU2_BF16)),
            GPT_PROF_GEMM, f.s);
-  run_gemm(c, gemm(bf.u, F, f.w->w2[l], M, d, F, bf.x, d, EPI_RESID), GPT_PROF_GEMM, f.s);
+  GemmArgs g = gemm(bf.u, F, f.w->w2[l], M, d, F, f.x_out ? f.x_out : bf.x, d, EPI_RESID);
+  if (f.x_out) g.rin = bf.x;
+  run_gemm(c, g, GPT_PROF_GEMM, f.s);
 }
 
 // Prefill forward.  Logits mode (targets == NULL): logits of `logits_rows`
@@ -855,9 +860,6 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
   const int L = c->n_layer, qkv_n = (H + 2 * Hkv) * dh, Mp = tb.Mp;
   const size_t es = bf16p ? 2 : 4;
   auto xs = [&](int i) { return tb.xs + (long long)i * M * d; };
-  auto copy_x = [&](float *dst) {
-    hipMemcpyAsync(dst, bf.x, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s);
-  };
   // C[M][N] = A[M][K] B[N][K]^T into fp32
   auto mm = [&](const void *A, long long lda, const void *B, long long ldb, int m, int n, int k, float *C,
                 long long ldc) {
@@ -894,6 +896,9 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
     prefill_meta_kernel<<<1, 256, 0, s>>>(meta, bf.cu, bf.cu_pad, bf.lastrows, bf.ctr, kCounters);
     launch_rowinfo(bf.cu, bf.cu_pad, n_seqs, M, bf.seq, bf.pos, bf.vcol, s);
   }
+  // The residual stream lives in the kept buffers: the embedding writes
+  // xs(0), and each half-layer's residual GEMM writes xs(i + 1) = xs(i) + f.
+  bf.x = xs(0);
   {
     Timed t(GPT_PROF_NORM, s, 0, (double)M * d * (4 + es));
     if (bf16p) launch_embed_bf16(tokens, (const bf16 *)w->wte, bf.x, M, d, s);
@@ -925,19 +930,21 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
       bf.o = o_l(l);
       fw.lse2 = lse_l(l);
     }
-    copy_x(xs(2 * l));
+    fw.x_out = xs(2 * l + 1);
     fwd_attn_half(fw, l);
+    bf.x = xs(2 * l + 1);
     if (keep) {
       bf.h = h2_l(l);
       bf.u = u_l(l);
     }
-    copy_x(xs(2 * l + 1));
+    fw.x_out = xs(2 * l + 2);
     fwd_mlp_half(fw, l);
+    bf.x = xs(2 * l + 2);
   }
   bf = bf0;
   fw.lse2 = nullptr;
-  copy_x(xs(2 * L));
-  fwd_norm(fw, bf.x, bf.h);  // hf
+  fw.x_out = nullptr;
+  fwd_norm(fw, xs(2 * L), bf.h);  // hf
   // Large M in bf16: the LM head stores the logits in bf16 (the precision
   // the softmax gradient is rounded to anyway) with the softmax partials and
   // each row's fp32 target logit, from which the loss comes; the gradient

@@ -57,7 +57,7 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_RESID) {
     float *p = (float *)g.C + (long long)m * g.ldc + n;
-    f32x4 x = *(const f32x4 *)p;
+    f32x4 x = *(const f32x4 *)(g.rin ? g.rin + (long long)m * g.ldc + n : p);
     x[0] += v0; x[1] += v1; x[2] += v2; x[3] += v3;
     *(f32x4 *)p = x;
   } else {

@@ -180,6 +180,7 @@ struct GemmArgs {
   int epi;
   float *part;  // EPI_LOGITS, EPI_LOSS, EPI_LOGITS_BF16: [M][N/kLogitsPartCols][2] partial (max, sum exp)
   const bf16 *aux;     // EPI_DRELU2: the activation u = max(z, 0)^2
+  const float *rin;    // EPI_RESID: C = rin + A W^T (same layout as C); NULL: C += A W^T
   const int *targets;  // EPI_LOSS, EPI_LOGITS_BF16: [M] target column of each row (any value)
   float *tgt;          // EPI_LOSS, EPI_LOGITS_BF16: [M] C[m][targets[m]] (fp32), where targets[m] is in [0, N)
   QkvEpi qkv;   // EPI_QKV

@@ -738,7 +738,7 @@ __global__ void gemm_f32_kernel(GemmArgs g) {
   float acc = 0.f;
   for (int k = 0; k < g.K; ++k) acc = fmaf(a[k], w[k], acc);
   float *c = (float *)g.C + (long long)m * g.ldc + n;
-  if (g.epi == EPI_RESID) *c += acc;
+  if (g.epi == EPI_RESID) *c = (g.rin ? g.rin[(long long)m * g.ldc + n] : *c) + acc;
   else if (g.epi == EPI_RELU_F32) *c = fmaxf(acc, 0.f);
   else if (g.epi == EPI_RELU2_BF16) { float r = fmaxf(acc, 0.f); *c = r * r; }  // fp32 output here
   else *c = acc;
