@@ -388,7 +388,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder-block path has no multi-GPU "
-              "sharding in this build (run with --gpus 1)", file=sys.stderr)
+              "sharding (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

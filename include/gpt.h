@@ -48,7 +48,7 @@ typedef enum {
   GPT_OK = 0,
   GPT_ERR_ARG = 1,         /* a pointer, size or layout argument is invalid */
   GPT_ERR_CAPACITY = 2,    /* a sequence would outgrow its KV-cache capacity */
-  GPT_ERR_UNSUPPORTED = 3, /* a valid configuration this build has no kernels for */
+  GPT_ERR_UNSUPPORTED = 3, /* a valid configuration the library has no kernels for */
   GPT_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
 } gpt_status;
 
