@@ -409,50 +409,66 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float *logits, const
 // Softmax gradient of the LM head from bf16 logits, in both layouts the
 // backward's GEMMs take: dl[m][v] = (exp(z[m][v] - lse[m]) - [v == t_m]) /
 // count (zero for rows without a target) row-major [M][V], and transposed
-// [V][ldt] with columns M .. Rp - 1 zero.  64 x 64 tiles: a thread reads 8
-// consecutive logits of one row (8 lanes per 128-byte line) and writes its
-// 8 gradients straight back; the tile passes through LDS for the transposed
-// copy, whose stores also cover whole lines (8 lanes per destination row).
+// [V][ldt] with columns M .. Rp - 1 zero.  A workgroup takes 64 rows and
+// kDlCols columns in 64 x 64 tiles: a thread reads 8 consecutive logits of
+// one row (8 lanes per 128-byte line) and writes its 8 gradients straight
+// back; each tile passes through LDS for the transposed copy, whose stores
+// also cover whole lines (8 lanes per destination row).  The rows' lse,
+// target and validity are loaded once per workgroup.
+constexpr int kDlCols = 256;
 __global__ __launch_bounds__(256) void dlogits_t_kernel(const bf16 *z, const float *lse, const int *targets,
                                                         const int *count, int M, int V, bf16 *dl, bf16 *dlt,
                                                         long long ldt, int Rp) {
   constexpr int P = 66;  // row pitch in bf16
   __shared__ bf16 t[64 * P];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int r0 = blockIdx.y * 64, tid = threadIdx.x;
   const float inv = 1.0f / (float)max(*count, 1);
+  // this thread's two source rows
+  int tg[2];
+  float l2[2];  // lse in the base-2 domain
+  bool ok[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int i = tid + 256 * k, row = i >> 3, ch = i & 7, r = r0 + row;
-    bf16x8 o;
-    if (r < M) {
-      const int tg = targets[r];
-      const bool ok = tg >= 0 && tg < V;
-      const float l = lse[r];
-      const long long off = (long long)r * V + c0 + 8 * ch;
-      const bf16x8 x = *(const bf16x8 *)(z + off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = c0 + 8 * ch + e;
-        o[e] = f2bf(ok ? (expf(bf2f(x[e]) - l) - (v == tg ? 1.f : 0.f)) * inv : 0.f);
-      }
-      *(bf16x8 *)(dl + off) = o;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (bf16)0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = o[e];
+    const int r = r0 + ((tid + 256 * k) >> 3);
+    tg[k] = r < M ? targets[r] : -1;
+    ok[k] = r < M && tg[k] >= 0 && tg[k] < V;
+    l2[k] = r < M ? lse[r] * kLog2e : 0.f;
   }
-  __syncthreads();
-  const int rc = tid & 7, r = r0 + 8 * rc;  // destination entries r .. r + 7
-  if (r >= Rp) return;
+  const int rc = tid & 7, rd = r0 + 8 * rc;  // destination entries rd .. rd + 7
+  for (int c0 = blockIdx.x * kDlCols; c0 < min(V, (int)(blockIdx.x + 1) * kDlCols); c0 += 64) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int col = (tid >> 3) + 32 * k;  // destination row c0 + col
-    bf16x8 w;
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 256 * k, row = i >> 3, ch = i & 7, r = r0 + row;
+      bf16x8 o;
+      if (r < M) {
+        const long long off = (long long)r * V + c0 + 8 * ch;
+        const bf16x8 x = *(const bf16x8 *)(z + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = t[(8 * rc + e) * P + col];
-    *(bf16x8 *)(dlt + (long long)(c0 + col) * ldt + r) = w;
+        for (int e = 0; e < 8; ++e) {
+          const int v = c0 + 8 * ch + e;
+          // exp(z - lse) = 2^(z log2 e - lse log2 e)
+          o[e] = f2bf(ok[k] ? (fast_exp2(bf2f(x[e]) * kLog2e - l2[k]) - (v == tg[k] ? 1.f : 0.f)) * inv : 0.f);
+        }
+        *(bf16x8 *)(dl + off) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (bf16)0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[row * P + 8 * ch + e] = o[e];
+    }
+    __syncthreads();
+    if (rd < Rp) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int col = (tid >> 3) + 32 * k;  // destination row c0 + col
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = t[(8 * rc + e) * P + col];
+        *(bf16x8 *)(dlt + (long long)(c0 + col) * ldt + rd) = w;
+      }
+    }
+    __syncthreads();  // the tile is read before the next one overwrites it
   }
 }
 
@@ -575,7 +591,8 @@ template void launch_dlogits<float>(const float *, const float *, const int *, c
 void launch_dlogits_t(const bf16 *logits, const float *lse, const int *targets, const int *count, int rows, int V,
                       bf16 *dl, bf16 *dlt, long long ldt, int Rp, hipStream_t s) {
   if (rows <= 0) return;
-  dlogits_t_kernel<<<dim3(V / 64, Rp / 64), 256, 0, s>>>(logits, lse, targets, count, rows, V, dl, dlt, ldt, Rp);
+  dlogits_t_kernel<<<dim3((V + kDlCols - 1) / kDlCols, Rp / 64), 256, 0, s>>>(logits, lse, targets, count, rows, V,
+                                                                              dl, dlt, ldt, Rp);
 }
 
 void launch_embed_bwd(const int *tokens, const int *pos, const float *dx, float *dwte, float *dwpe, int M, int d,
