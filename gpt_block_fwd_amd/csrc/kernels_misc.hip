@@ -691,10 +691,132 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(const float *logit
   }
 }
 
+// The same choice with the row read once: for V <= NS super-tiles the
+// thread keeps its NS x 8 entries in registers.  The weights of every
+// super-tile are summed per wave and then over the waves in order; the
+// total is the sum of those super-tile totals in order, the super-tile
+// holding the crossing is the first whose running total passes the target,
+// and a scan of the threads' sums inside it finds the thread and the entry.
+// The last entry of positive weight stands in where rounding leaves no
+// crossing.
+template <int NS>
+__global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *logits, int V, float inv_t,
+                                                                  const float *uniforms, int *out, int *lens) {
+  constexpr int NW = kSampThreads / 64;
+  __shared__ float red[NW][NS];
+  __shared__ float wsum[NW];
+  __shared__ int s_pick, s_last;
+  const float *row = logits + (long long)blockIdx.x * V;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float x[NS][kSampPer];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) samp_load(row, V, st * kSampTile, t, x[st]);
+  float m = -INFINITY;
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) m = fmaxf(m, x[st][j]);
+  m = wave_max(m);
+  if (lane == 0) red[w][0] = m;
+  if (t == 0) {
+    s_pick = -1;
+    s_last = -1;
+  }
+  __syncthreads();
+  m = red[0][0];
+  for (int k = 1; k < NW; ++k) m = fmaxf(m, red[k][0]);
+  __syncthreads();  // red is reused below
+  const float sc = inv_t * kLog2e;
+  float ts[NS];
+  int last = -1;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    ts[st] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      x[st][j] = fast_exp2((x[st][j] - m) * sc);
+      ts[st] += x[st][j];
+      if (x[st][j] > 0.f) last = st * kSampTile + kSampPer * t + j;
+    }
+    const float v = wave_sum(ts[st]);
+    if (lane == 0) red[w][st] = v;
+  }
+  __syncthreads();
+  float T[NS], total = 0.f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    T[st] = 0.f;
+    for (int k = 0; k < NW; ++k) T[st] += red[k][st];
+    total += T[st];
+  }
+  const float target = uniforms[blockIdx.x] * total;
+  // the super-tile holding the crossing (the same for every thread)
+  int sx = -1;
+  float run = 0.f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (sx < 0) {
+      if (run + T[st] > target) sx = st;
+      else run += T[st];
+    }
+  if (sx >= 0) {
+    float e[kSampPer], mine = 0.f, before = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      if (st == sx) {
+#pragma unroll
+        for (int j = 0; j < kSampPer; ++j) e[j] = x[st][j];
+        mine = ts[st];
+      }
+    for (int k = 0; k < w; ++k) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        if (st == sx) before += red[k][st];
+    }
+    // inclusive scan of the threads' sums of the super-tile in thread order
+    float incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    (void)wsum;
+    const float excl = run + before + incl - mine;
+    if (excl <= target && target < excl + mine) {
+      float cum = excl;
+      int pick = -1;
+#pragma unroll
+      for (int j = 0; j < kSampPer; ++j) {
+        cum += e[j];
+        if (pick < 0 && cum > target) pick = sx * kSampTile + kSampPer * t + j;
+      }
+      if (pick < 0) pick = last;  // rounding inside the thread's entries
+      atomicMax(&s_pick, pick);
+    }
+  }
+  if (last >= 0) atomicMax(&s_last, last);
+  __syncthreads();
+  if (t == 0) {
+    out[blockIdx.x] = s_pick >= 0 ? s_pick : (s_last >= 0 ? s_last : 0);
+    if (lens) lens[blockIdx.x] += 1;  // decode: the step's position is now cached
+  }
+}
+
 void launch_sample(const float *logits, int rows, int V, float temperature, const float *u,
                    int *out, int *lens, hipStream_t s) {
   if (rows <= 0) return;
-  sample_kernel<<<rows, kSampThreads, 0, s>>>(logits, V, 1.0f / temperature, u, out, lens);
+  const float it = 1.0f / temperature;
+  switch ((V + kSampTile - 1) / kSampTile) {
+    case 1: sample_reg_kernel<1><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 2: sample_reg_kernel<2><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 3: sample_reg_kernel<3><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 4: sample_reg_kernel<4><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 5: sample_reg_kernel<5><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 6: sample_reg_kernel<6><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 7: sample_reg_kernel<7><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    case 8: sample_reg_kernel<8><<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+    default: sample_kernel<<<rows, kSampThreads, 0, s>>>(logits, V, it, u, out, lens); return;
+  }
 }
 
 // ---------------------------------------------------------------- KV lengths
