@@ -116,6 +116,9 @@ gpt_status check_config(const gpt_config *c) {
     if (c->act != GPT_ACT_RELU2) return fail(GPT_ERR_UNSUPPORTED, "bf16 path uses the ReLU^2 MLP");
     if (c->d_model % 128 || c->d_ff % 128 || c->vocab % 128)
       return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs d_model, d_ff, vocab multiples of 128");
+    // weight rows are addressed with 32-bit element offsets
+    if ((long long)c->vocab * c->d_model >= (1LL << 31) || (long long)c->d_ff * c->d_model >= (1LL << 31))
+      return fail(GPT_ERR_UNSUPPORTED, "bf16 path needs vocab x d_model and d_ff x d_model below 2^31");
   } else {
     if (c->head_dim > 64) return fail(GPT_ERR_UNSUPPORTED, "fp32 path needs head_dim <= 64");
     if (c->d_model % 4 || c->d_model > 4096) return fail(GPT_ERR_UNSUPPORTED, "fp32 path needs d_model % 4 == 0, <= 4096");
@@ -702,6 +705,14 @@ gpt_status prefill_impl(const gpt_config *c, const gpt_weights *w, const float *
     if (len > c->max_seq) return fail(GPT_ERR_ARG, "sequence %d longer than max_seq", b);
   }
   const int M = cu_seqlens[n_seqs];
+  {
+    // the tiled GEMM and the row kernels address an activation operand with
+    // 32-bit element offsets (row x width)
+    const long long widest = std::max({(long long)c->d_model, (long long)c->d_ff,
+                                       (long long)c->n_head * c->head_dim});
+    if (widest * M >= (1LL << 31))
+      return fail(GPT_ERR_UNSUPPORTED, "%d rows x %lld columns exceed the 32-bit operand offsets", M, widest);
+  }
   if (kv) {
     if (kv->n_seqs != n_seqs) return fail(GPT_ERR_ARG, "n_seqs %d != kv cache's %d", n_seqs, kv->n_seqs);
     if (kv->cfg.n_layer != c->n_layer || kv->cfg.dtype != c->dtype || kv->cfg.n_kv_head != c->n_kv_head ||

@@ -574,11 +574,12 @@ void launch_argmax(const float *logits, int rows, int V, int *out, float *scratc
 // weights e_i = 2^((x_i - max) log2(e) / T); the token is the first i whose
 // cumulative weight exceeds u * total.  The row is walked in super-tiles of
 // 8192 entries; thread t owns entries 8t .. 8t + 8 of each (32 contiguous
-// bytes, so a wave's loads are contiguous).  Pass 1: the row max.  Pass 2:
-// the total.  Pass 3: super-tile by super-tile, an inclusive scan of the
-// threads' sums finds the super-tile, then the thread, then the entry where
-// the running sum passes the target.  If rounding leaves the target at or
-// above the last running sum, the last entry of positive weight is taken.
+// bytes, so a wave's loads are contiguous).  The row max, then each
+// super-tile's total (per-wave sums added in wave order); the total weight
+// is the sum of the super-tile totals in order.  The first super-tile whose
+// running total passes the target holds the crossing, and samp_claim finds
+// the thread and the entry inside it.  If rounding leaves the target at or
+// above the total, the last entry of positive weight is taken.
 
 constexpr int kSampThreads = 1024, kSampPer = 8, kSampTile = kSampThreads * kSampPer;
 
@@ -594,22 +595,74 @@ DEV void samp_load(const float *row, int V, int base, int t, float (&x)[kSampPer
   }
 }
 
-// Block-wide sum (fixed tree: per-wave reduction, then the 16 wave sums in order).
-DEV float samp_block_sum(float v, float *red) {
-  v = wave_sum(v);
-  const int t = threadIdx.x;
+// The crossing inside the super-tile that holds it.  Called by every thread
+// of the workgroup (it has a barrier) with the same `run` (weight of the
+// super-tiles before this one) and `target`; `wtot` holds the super-tile's
+// 16 wave totals, and the super-tile's total is their sum in wave order from
+// zero -- the same sum that chose this super-tile.  Thread t claims the half-open
+// range [lo_t, lo_{t+1}) of the running weight, where lo_t is its wave's
+// start (run plus the earlier waves' totals, summed in wave order) plus the
+// exclusive scan of the wave's thread sums, and the last thread's range ends
+// at run plus the super-tile total.  Each boundary is one value computed once
+// and handed to both neighbours, so the ranges tile [run, run + total)
+// exactly: a target inside it is claimed by at least one thread, whatever the
+// rounding.  The claiming thread walks its 8 entries from lo_t to the first
+// whose running weight passes the target; if rounding leaves none, it takes
+// the last entry of positive weight at or before its own entries in this
+// super-tile.  Where rounding makes ranges overlap, the lowest index wins.
+DEV void samp_claim(const float (&e)[kSampPer], float mine, const float *wtot, float run, float target,
+                    int idx0, int *s_pick, int *s_wlast) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float before = 0.f;
+  for (int k = 0; k < w; ++k) before += wtot[k];
+  const float base_w = run + before, base_n = run + (before + wtot[w]);
+  float incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+  const float lo = base_w + excl;
+  float hi = __shfl_down(lo, 1, 64);
+  if (lane == 63) hi = base_n;
+  // last positive entry at or before this thread's, within the super-tile
+  int lastp = -1;
+#pragma unroll
+  for (int j = 0; j < kSampPer; ++j)
+    if (e[j] > 0.f) lastp = idx0 + j;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(lastp, o, 64);
+    if (lane >= o) lastp = max(lastp, v);
+  }
+  if (lane == 63) s_wlast[w] = lastp;
   __syncthreads();
-  if ((t & 63) == 0) red[t >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int k = 0; k < kSampThreads / 64; ++k) s += red[k];
-  return s;
+  for (int k = 0; k < w; ++k) lastp = max(lastp, s_wlast[k]);
+  if (lo <= target && target < hi) {
+    float cum = lo;
+    int pick = -1;
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j) {
+      cum += e[j];
+      if (pick < 0 && cum > target) pick = idx0 + j;
+    }
+    if (pick < 0) pick = lastp;
+    if (pick >= 0) atomicMin(s_pick, pick);
+  }
 }
 
+constexpr int kNoPick = 0x7fffffff;
+
+// Rows longer than the register-resident kernel takes: three passes over
+// the row (max; per-super-tile totals; the super-tile holding the crossing),
+// the per-super-tile totals formed identically in the last two.
 __global__ __launch_bounds__(kSampThreads) void sample_kernel(const float *logits, int V, float inv_t,
                                                               const float *uniforms, int *out, int *lens) {
-  __shared__ float red[kSampThreads / 64];
-  __shared__ float wsum[kSampThreads / 64];
+  constexpr int NW = kSampThreads / 64;
+  __shared__ float red[NW];
+  __shared__ int s_wlast[NW];
   __shared__ int s_pick, s_last;
   const float *row = logits + (long long)blockIdx.x * V;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -624,87 +677,76 @@ __global__ __launch_bounds__(kSampThreads) void sample_kernel(const float *logit
   m = wave_max(m);
   if (lane == 0) red[w] = m;
   if (t == 0) {
-    s_pick = -1;
+    s_pick = kNoPick;
     s_last = -1;
   }
   __syncthreads();
   m = red[0];
-  for (int k = 1; k < kSampThreads / 64; ++k) m = fmaxf(m, red[k]);
+  for (int k = 1; k < NW; ++k) m = fmaxf(m, red[k]);
   const float sc = inv_t * kLog2e;
-  // pass 2: total weight
-  float local = 0.f;
-  for (int base = 0; base < V; base += kSampTile) {
+  // weights of this thread's entries of super-tile `base`, their sum, and
+  // the super-tile's wave totals in red (ends with a barrier)
+  auto tile = [&](int base, float (&e)[kSampPer], float &mine) {
     samp_load(row, V, base, t, x);
-#pragma unroll
-    for (int j = 0; j < kSampPer; ++j) local += fast_exp2((x[j] - m) * sc);
-  }
-  const float total = samp_block_sum(local, red);
-  const float target = uniforms[blockIdx.x] * total;
-  // pass 3: find the crossing
-  float run = 0.f;  // weight of the super-tiles before this one
-  int last = -1;
-  for (int base = 0; base < V; base += kSampTile) {
-    samp_load(row, V, base, t, x);
-    float e[kSampPer], mine = 0.f;
+    mine = 0.f;
 #pragma unroll
     for (int j = 0; j < kSampPer; ++j) {
       e[j] = fast_exp2((x[j] - m) * sc);
       mine += e[j];
+    }
+    const float v = wave_sum(mine);
+    __syncthreads();  // every thread is done reading red
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+  };
+  // pass 2: the total, as the sum of the super-tile totals in order
+  float total = 0.f;
+  int last = -1;
+  for (int base = 0; base < V; base += kSampTile) {
+    float e[kSampPer], mine;
+    tile(base, e, mine);
+#pragma unroll
+    for (int j = 0; j < kSampPer; ++j)
       if (e[j] > 0.f) last = base + kSampPer * t + j;
+    float T = 0.f;
+    for (int k = 0; k < NW; ++k) T += red[k];
+    total += T;
+  }
+  const float target = uniforms[blockIdx.x] * total;
+  // pass 3: the first super-tile whose running total passes the target
+  float run = 0.f;
+  for (int base = 0; base < V; base += kSampTile) {
+    float e[kSampPer], mine;
+    tile(base, e, mine);
+    float T = 0.f;
+    for (int k = 0; k < NW; ++k) T += red[k];
+    if (run + T > target) {  // the same in every thread
+      samp_claim(e, mine, red, run, target, base + kSampPer * t, &s_pick, s_wlast);
+      break;
     }
-    // inclusive scan of the threads' sums in thread order
-    float incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    float before = 0.f, tile_total = 0.f;
-    for (int k = 0; k < kSampThreads / 64; ++k) {
-      if (k < w) before += wsum[k];
-      tile_total += wsum[k];
-    }
-    const float excl = run + before + incl - mine;
-    if (excl <= target && target < excl + mine) {
-      float cum = excl;
-      int pick = -1;
-#pragma unroll
-      for (int j = 0; j < kSampPer; ++j) {
-        cum += e[j];
-        if (pick < 0 && cum > target) pick = base + kSampPer * t + j;
-      }
-      if (pick < 0) pick = last;  // rounding inside the thread's entries
-      atomicMax(&s_pick, pick);
-    }
-    __syncthreads();
-    if (s_pick >= 0) break;  // uniform: every thread reads the same value
-    run += tile_total;
+    run += T;
   }
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
   if (t == 0) {
-    out[blockIdx.x] = s_pick >= 0 ? s_pick : (s_last >= 0 ? s_last : 0);
+    out[blockIdx.x] = s_pick != kNoPick ? s_pick : (s_last >= 0 ? s_last : 0);
     if (lens) lens[blockIdx.x] += 1;  // decode: the step's position is now cached
   }
 }
 
 // The same choice with the row read once: for V <= NS super-tiles the
 // thread keeps its NS x 8 entries in registers.  The weights of every
-// super-tile are summed per wave and then over the waves in order; the
-// total is the sum of those super-tile totals in order, the super-tile
-// holding the crossing is the first whose running total passes the target,
-// and a scan of the threads' sums inside it finds the thread and the entry.
-// The last entry of positive weight stands in where rounding leaves no
-// crossing.
+// super-tile are summed per wave; the total is the sum of the super-tile
+// totals in order, and the super-tile holding the crossing is the first
+// whose running total passes the target.  The last entry of positive weight
+// stands in where rounding leaves no crossing.
 template <int NS>
 __global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *logits, int V, float inv_t,
                                                                   const float *uniforms, int *out, int *lens) {
   constexpr int NW = kSampThreads / 64;
-  __shared__ float red[NW][NS];
-  __shared__ float wsum[NW];
+  __shared__ float red[NS][NW];
+  __shared__ float red_m[NW];
+  __shared__ int s_wlast[NW];
   __shared__ int s_pick, s_last;
   const float *row = logits + (long long)blockIdx.x * V;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -717,15 +759,14 @@ __global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *l
 #pragma unroll
     for (int j = 0; j < kSampPer; ++j) m = fmaxf(m, x[st][j]);
   m = wave_max(m);
-  if (lane == 0) red[w][0] = m;
+  if (lane == 0) red_m[w] = m;
   if (t == 0) {
-    s_pick = -1;
+    s_pick = kNoPick;
     s_last = -1;
   }
   __syncthreads();
-  m = red[0][0];
-  for (int k = 1; k < NW; ++k) m = fmaxf(m, red[k][0]);
-  __syncthreads();  // red is reused below
+  m = red_m[0];
+  for (int k = 1; k < NW; ++k) m = fmaxf(m, red_m[k]);
   const float sc = inv_t * kLog2e;
   float ts[NS];
   int last = -1;
@@ -739,14 +780,14 @@ __global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *l
       if (x[st][j] > 0.f) last = st * kSampTile + kSampPer * t + j;
     }
     const float v = wave_sum(ts[st]);
-    if (lane == 0) red[w][st] = v;
+    if (lane == 0) red[st][w] = v;
   }
   __syncthreads();
   float T[NS], total = 0.f;
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     T[st] = 0.f;
-    for (int k = 0; k < NW; ++k) T[st] += red[k][st];
+    for (int k = 0; k < NW; ++k) T[st] += red[st][k];
     total += T[st];
   }
   const float target = uniforms[blockIdx.x] * total;
@@ -760,7 +801,7 @@ __global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *l
       else run += T[st];
     }
   if (sx >= 0) {
-    float e[kSampPer], mine = 0.f, before = 0.f;
+    float e[kSampPer], mine = 0.f;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
       if (st == sx) {
@@ -768,36 +809,12 @@ __global__ __launch_bounds__(kSampThreads) void sample_reg_kernel(const float *l
         for (int j = 0; j < kSampPer; ++j) e[j] = x[st][j];
         mine = ts[st];
       }
-    for (int k = 0; k < w; ++k) {
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-        if (st == sx) before += red[k][st];
-    }
-    // inclusive scan of the threads' sums of the super-tile in thread order
-    float incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    (void)wsum;
-    const float excl = run + before + incl - mine;
-    if (excl <= target && target < excl + mine) {
-      float cum = excl;
-      int pick = -1;
-#pragma unroll
-      for (int j = 0; j < kSampPer; ++j) {
-        cum += e[j];
-        if (pick < 0 && cum > target) pick = sx * kSampTile + kSampPer * t + j;
-      }
-      if (pick < 0) pick = last;  // rounding inside the thread's entries
-      atomicMax(&s_pick, pick);
-    }
+    samp_claim(e, mine, red[sx], run, target, sx * kSampTile + kSampPer * t, &s_pick, s_wlast);
   }
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
   if (t == 0) {
-    out[blockIdx.x] = s_pick >= 0 ? s_pick : (s_last >= 0 ? s_last : 0);
+    out[blockIdx.x] = s_pick != kNoPick ? s_pick : (s_last >= 0 ? s_last : 0);
     if (lens) lens[blockIdx.x] += 1;  // decode: the step's position is now cached
   }
 }

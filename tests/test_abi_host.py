@@ -116,6 +116,41 @@ def test_prefill_validation_runs_before_device_work():
     _bad(lambda: call(cu=np.array([0, 5000, 5001], np.int32)), B.GPT_ERR_ARG)  # > max_seq
 
 
+def test_prefill_rows_beyond_32bit_offsets_rejected():
+    """The GEMMs address activation rows with 32-bit element offsets: a
+    depth-26 prefill whose rows x widest activation (d_ff = 6656) reaches
+    2^31 is refused before any launch, for logits and for the loss, while
+    one row fewer than the limit passes that check (and then fails only on
+    the deliberately short workspace)."""
+    m = wl.depth_model(26, max_seq=4096)
+    cfg = B.make_config(m)
+    w, keep = _weights_struct(m.n_layer)
+    limit = (1 << 31) // m.d_ff          # first row count that overflows is limit + 1
+    n = (limit + 1 + 4095) // 4096
+    lens = np.full(n, 4096, np.int64)
+    lens[-1] -= n * 4096 - (limit + 1)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert int(cu[-1]) * m.d_ff >= 1 << 31 and (int(cu[-1]) - 1) * m.d_ff < 1 << 31
+    msg = _bad(lambda: B.gpt_prefill(cfg, w, 0x4000, 0x4000, 0x3000, cu, n, None, B.ROWS_LAST,
+                                     0x2000, None, None, 0x100000, 1 << 40, 0), B.GPT_ERR_UNSUPPORTED)
+    assert "32-bit" in msg
+    _bad(lambda: B.gpt_prefill_loss(cfg, w, 0x4000, 0x4000, 0x3000, 0x5000, cu, n, None, 0x6000,
+                                    None, None, 0x100000, 1 << 40, 0), B.GPT_ERR_UNSUPPORTED)
+    cu2 = cu.copy()
+    cu2[-1] -= 1
+    msg = _bad(lambda: B.gpt_prefill(cfg, w, 0x4000, 0x4000, 0x3000, cu2, n, None, B.ROWS_LAST,
+                                     0x2000, None, None, 0x100000, 256, 0), B.GPT_ERR_ARG)
+    assert "workspace" in msg
+
+
+def test_weights_beyond_32bit_offsets_rejected():
+    """An LM head of 2^20 x 2048 entries is refused by every entry point."""
+    cfg = B.make_config(wl.small_model(1, 16, vocab=1 << 20))
+    assert B.gpt_workspace_bytes(cfg, 1, 1) == 0
+    assert "2^31" in B.last_error()
+    assert "2^31" in _bad(lambda: B.kv_cache_bytes(cfg, 1, 64), B.GPT_ERR_UNSUPPORTED)
+
+
 def test_prefill_loss_validation():
     m = wl.small_model(2, 2, vocab=256)
     cfg = B.make_config(m)

@@ -384,6 +384,44 @@ def test_sampling_inverse_cdf(V):
         assert lo - 1e-5 <= U[j] <= c[k] + 1e-5, (j, k, lo, c[k], U[j])
 
 
+def _boundary_rows(rng, rows, V, spread):
+    """Rows of logits and uniforms aimed at the cumulative weight just before
+    or after an entry index that starts a thread's 8 entries, a wave's 512 or
+    a super-tile's 8192 (where the kernel's partial sums meet), plus plain
+    draws; with a large spread most weights underflow to zero."""
+    lg = (rng.standard_normal((rows, V)) * spread).astype(np.float32)
+    U = np.empty(rows, np.float32)
+    cdfs = []
+    for j in range(rows):
+        c = np.cumsum(oracle.softmax(lg[j].astype(np.float64) / 0.7))
+        cdfs.append(c)
+        b = [8, 512, 8192][j % 3]
+        k = int(rng.integers(1, V // b)) * b
+        eps = (1 if j % 2 else -1) * 10.0 ** rng.uniform(-9, -6)
+        U[j] = np.float32(min(max(c[k - 1] + eps, 0.0), 1 - 2 ** -24)) if j % 4 else rng.random()
+    return lg, U, cdfs
+
+
+@pytest.mark.parametrize("V,spread", [(65536, 0.8), (65536, 40.0), (100000, 0.8)])
+def test_sampling_at_range_boundaries(V, spread):
+    """512 rows with uniforms aimed at the boundaries between the kernel's
+    per-thread, per-wave and per-super-tile partial sums, for the
+    register-resident kernel (V = 65536) and the three-pass one (V = 100000):
+    every pick lies at the float64 inverse-CDF crossing within 1e-5
+    (Microgpt, "Inference")."""
+    t = torch()
+    rng = np.random.default_rng(int(V + spread))
+    rows = 512
+    lg, U, cdfs = _boundary_rows(rng, rows, V, spread)
+    out = t.empty(rows, dtype=t.int32, device="cuda")
+    B.gpt_select_tokens(t.from_numpy(lg).cuda(), rows, V, 0.7, t.from_numpy(U).cuda(), out)
+    got = out.cpu().numpy()
+    for j in range(rows):
+        c, k = cdfs[j], got[j]
+        lo = c[k - 1] if k > 0 else 0.0
+        assert lo - 1e-5 <= U[j] <= c[k] + 1e-5, (j, k, lo, c[k], U[j])
+
+
 # ---------------------------------------------------------------- loss backward
 
 def gpu_loss_grads(cfg, dm, w, targets):
