@@ -188,10 +188,14 @@ def bench_adam(B, torch, n, steps, warmup=2):
                        "achieved_gbs": round(kern_gbs, 1), "frac": round(kern_gbs / PEAK_HBM_GBS, 4)}}
 
 
+PROF_STRIDE = 8
+
+
 def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     """Prefill the prompts into a fresh cache, pick the first token, then time
     `steps` decode steps (selection included).  A second identical pass with
-    HIP-event timing gives the per-kernel-class figures."""
+    HIP-event timing on every PROF_STRIDE-th step gives the per-kernel-class
+    figures."""
     n = w.n_seqs
     cu = w.cu_seqlens
     cap = int(w.seqlens.max()) + steps
@@ -208,8 +212,10 @@ def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
         B.gpt_select_tokens(logits, n, dm.model.vocab, temperature,
                             U[0] if U is not None else None, toks)
 
-    def run(k):
+    def run(k, mask=0):
         for s in range(k):
+            if mask:  # time every PROF_STRIDE-th step: bounded event count, all lengths covered
+                B.gpt_profile_mask(mask if s % PROF_STRIDE == 0 else 0)
             dm.decode_step(kv.handle, toks, toks, temperature=temperature,
                            uniforms=U[s + 1] if U is not None else None, workspace=dws)
 
@@ -224,9 +230,9 @@ def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     dt = time.perf_counter() - t0
     start()
     torch.cuda.synchronize()
-    B.gpt_profile_enable(1 << B.PROF_CLASSES["decode_attn"] | 1 << B.PROF_CLASSES["skinny"]
-                         | 1 << B.PROF_CLASSES["lmhead"])
-    run(steps)
+    mask = 1 << B.PROF_CLASSES["decode_attn"] | 1 << B.PROF_CLASSES["skinny"] | 1 << B.PROF_CLASSES["lmhead"]
+    B.gpt_profile_enable(mask)
+    run(steps, mask)
     torch.cuda.synchronize()
     att = prof_read(B, ["decode_attn"])
     sk = prof_read(B, ["skinny", "lmhead"])
@@ -337,32 +343,187 @@ def measured_traffic():
     return round(float(t["bytes_per_launch"]), 0)
 
 
+# ---------------------------------------------------------------- the oracle legs
+# Everything below that imports the oracle runs on the host cores after the
+# GPU timings: the oracle's own timing (cpu_baseline) and the parity samples
+# that compare the GPU's logits with it.
+
+LITERAL_MAX_ABS, LITERAL_TOP1 = 3e-2, 0.999
+
+
+def host_cores():
+    """Cores this process may run on, and BLAS limited to that many threads."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(cores)
+    except Exception:  # pragma: no cover
+        pass
+    return cores
+
+
+def parity_stats(gpu, ref, chosen=None):
+    """max |diff|, std, top-1 agreement of the GPU's choice (or its argmax)
+    with the oracle's argmax, and the literal-bar flags.  `gpu` and `ref` may
+    be lists of row blocks (kept apart to bound host memory)."""
+    if not isinstance(gpu, list):
+        gpu, ref = [gpu], [ref]
+        chosen = None if chosen is None else [chosen]
+    n = s1 = s2 = agree = 0
+    maxd = 0.0
+    for i, (g, r) in enumerate(zip(gpu, ref)):
+        V = np.shape(g)[-1]
+        g = np.asarray(g, np.float64).reshape(-1, V)
+        r = np.asarray(r, np.float64).reshape(-1, V)
+        d = g - r
+        maxd = max(maxd, float(np.max(np.abs(d))))
+        n += d.size
+        s1 += float(np.sum(d))
+        s2 += float(np.sum(d * d))
+        g1 = np.argmax(g, -1) if chosen is None else np.asarray(chosen[i]).reshape(-1)
+        agree += int(np.sum(g1 == np.argmax(r, -1)))
+        rows = len(g1) if i == 0 else rows + len(g1)
+    top1 = agree / rows
+    std = float(np.sqrt(max(s2 / n - (s1 / n) ** 2, 0.0)))
+    return {"rows": int(rows), "max_abs": round(maxd, 5), "std": round(std, 6),
+            "top1": round(top1, 5), "literal_max_met": maxd <= LITERAL_MAX_ABS,
+            "literal_top1_met": top1 >= LITERAL_TOP1}
+
+
+def parity_entry(stats, floor, what):
+    """One parity record: the GPU against the oracle, and the bf16 storage
+    floor (the oracle rounding at the bf16 storage points) against it."""
+    return {"what": what, "gpu_vs_oracle": stats,
+            "bf16_floor_vs_oracle": {k: floor[k] for k in ("max_abs", "std", "top1")},
+            "literal_bars": {"max_abs<=3e-2": stats["literal_max_met"],
+                             "top1>=0.999": stats["literal_top1_met"]}}
+
+
 def cpu_baseline(w, W, gpu_logits):
     """Time the oracle (fp32 BLAS) over every sequence of the workload on the
-    host cores, and compare its logits with the GPU's (parity sample)."""
+    host cores, and compare its logits with the GPU's; the bf16 storage floor
+    on sequence 0."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    cores = host_cores()
     cu = w.cu_seqlens
-    total, maxd, agree, rows = 0.0, 0.0, 0, 0
+    total, g_all, r_all = 0.0, [], []
     for b in range(w.n_seqs):
         t0 = time.perf_counter()
         ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[b])
         total += time.perf_counter() - t0
-        g = gpu_logits[cu[b]:cu[b + 1]]
-        maxd = max(maxd, float(np.max(np.abs(g.astype(np.float64) - ref[0]))))
-        agree += int(np.sum(np.argmax(g, -1) == np.argmax(ref[0], -1)))
-        rows += len(g)
+        g_all.append(gpu_logits[cu[b]:cu[b + 1]])
+        r_all.append(ref[0])
         del ref
-    out = {"value": round(rows / total, 2), "unit": "tokens/s", "cores": int(threads),
+    rows = int(cu[-1])
+    out = {"value": round(rows / total, 2), "unit": "tokens/s", "cores": cores,
            "kind": "oracle",
-           "sample": f"all {w.n_seqs} depth-12 sequences ({rows} tokens), numpy fp32 BLAS, "
-                     f"{total:.1f} s"}
-    parity = {"rows": rows, "max_abs": maxd, "top1": agree / rows}
-    return out, parity
+           "sample": f"all {w.n_seqs} depth-12 sequences ({rows} tokens), numpy fp32 BLAS "
+                     f"on {cores} threads, {total:.1f} s"}
+    st = parity_stats(g_all, r_all)
+    flo, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[0], bf16_points=True)
+    fl = parity_stats(flo[0], r_all[0])
+    return out, parity_entry(st, fl, f"all {rows} rows of the {w.n_seqs} sequences; floor on sequence 0")
+
+
+def prefill_parity(w, W, g, seq):
+    """GPU logits of one sequence of a prefill against the oracle and the floor."""
+    import oracle
+    ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[seq])
+    flo, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[seq],
+                            bf16_points=True)
+    return parity_entry(parity_stats(g, ref[0]), parity_stats(flo[0], ref[0]),
+                        f"sequence {seq} ({len(g)} rows)")
+
+
+def decode_parity(w, W, got_tok, got_lg, sample, steps, greedy):
+    """Teacher-forced oracle decode of the sampled sequences over the GPU's
+    tokens, against the GPU's per-step logits, and the floor."""
+    import oracle
+    _, ref = oracle.run_serving(w.model, W, w.tokens, w.seqlens, steps, forced=got_tok,
+                                dtype=np.float32, seqs=sample)
+    _, flo = oracle.run_serving(w.model, W, w.tokens, w.seqlens, steps, forced=got_tok,
+                                dtype=np.float32, seqs=sample, bf16_points=True)
+    chosen = got_tok[:, sample] if greedy else None
+    return parity_entry(parity_stats(got_lg, ref, chosen), parity_stats(flo, ref),
+                        f"sequences {sample}, the first {steps} decode steps and the prompt's "
+                        f"last row, teacher-forced")
+
+
+def decode_capture(B, torch, dm, w, steps, temperature, sample):
+    """Prefill, then `steps` decode steps keeping every step's tokens and the
+    sampled sequences' logits (for the parity legs; not timed)."""
+    n = w.n_seqs
+    kv = B.DeviceKV(dm, n, int(w.seqlens.max()) + steps)
+    logits = torch.empty((n, dm.model.vocab), dtype=torch.float32, device="cuda")
+    dm.prefill(torch.from_numpy(w.tokens).cuda(), w.cu_seqlens, logits, kv=kv.handle,
+               logits_rows=B.ROWS_LAST)
+    U = torch.from_numpy(w.uniforms).cuda() if w.uniforms is not None else None
+    toks = torch.empty(n, dtype=torch.int32, device="cuda")
+    B.gpt_select_tokens(logits, n, dm.model.vocab, temperature, U[0] if U is not None else None, toks)
+    ws = dm.workspace(n, n)
+    got_tok, got_lg = [toks.cpu().numpy().copy()], [logits[sample].cpu().numpy()]
+    for s_ in range(steps):
+        dm.decode_step(kv.handle, toks, toks, temperature=temperature,
+                       uniforms=U[s_ + 1] if U is not None else None, logits=logits, workspace=ws)
+        got_tok.append(toks.cpu().numpy().copy())
+        got_lg.append(logits[sample].cpu().numpy())
+    kv.close()
+    del logits, ws
+    torch.cuda.empty_cache()
+    return np.stack(got_tok), np.stack(got_lg)
+
+
+# ---------------------------------------------------------------- decode-attention sweep
+
+SWEEP = [(8, 512), (8, 2560), (8, 8192), (32, 512), (32, 2560), (32, 8192), (64, 512), (64, 1024),
+         (64, 2560), (64, 4096), (128, 1024), (128, 2048)]
+
+
+def decode_sweep(B, torch, steps=8):
+    """Decode attention of the depth-26 shape (13 query heads on one K/V
+    head) over B sequences of L cached positions: a one-layer model keeps the
+    cache fill cheap; the kernel's launches are timed by HIP events."""
+    import dataclasses
+    cfg = dataclasses.replace(wl.depth_model(26), n_layer=1, max_seq=8192 + steps)
+    dm = B.DeviceModel(cfg, wl.make_weights(cfg))
+    rows = []
+    for nb, L in SWEEP:
+        w = wl.uniform_prefill(cfg, nb, L, seed=nb + L)
+        kv = B.DeviceKV(dm, nb, L + steps)
+        lg = torch.empty((nb, cfg.vocab), dtype=torch.float32, device="cuda")
+        dm.prefill(torch.from_numpy(w.tokens).cuda(), w.cu_seqlens, lg, kv=kv.handle, logits_rows=B.ROWS_LAST)
+        toks = torch.zeros(nb, dtype=torch.int32, device="cuda")
+        ws = dm.workspace(nb, nb)
+        dm.decode_step(kv.handle, toks, toks, workspace=ws)  # warm-up
+        torch.cuda.synchronize()
+        B.gpt_profile_enable(1 << B.PROF_CLASSES["decode_attn"])
+        for _ in range(steps):
+            dm.decode_step(kv.handle, toks, toks, workspace=ws)
+        torch.cuda.synchronize()
+        r = prof_read(B, ["decode_attn"])
+        B.gpt_profile_enable(0)
+        gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        rows.append({"B": nb, "L": L, "us_per_launch": round(r["ms"] * 1e3 / max(r["launches"], 1), 2),
+                     "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+        log(f"sweep B={nb} L={L}: {rows[-1]['us_per_launch']} us, {gbs:,.0f} GB/s")
+        kv.close()
+        del lg, ws
+        torch.cuda.empty_cache()
+    del dm
+    torch.cuda.empty_cache()
+    return {"model": "depth-26 shape, 1 layer (13 query heads, 1 K/V head, head 128)",
+            "bytes": "(L + 1) x 512 B per sequence (K and V, bf16) + q and o", "steps": steps,
+            "points": rows}
+
+
+def step_bytes(model, n, mean_len, vocab):
+    """Algorithmic HBM bytes of one decode step: every bf16 weight once, the
+    cached K/V read (mean length + 1 positions), the new K/V written, and
+    the fp32 logits written and read back by the selection."""
+    wbytes = 2 * sum(int(np.prod(sh)) for _, sh in wl.weight_shapes(model))
+    kv = model.n_layer * n * (mean_len + 1) * 2 * model.n_kv_head * model.head_dim * 2
+    kvw = model.n_layer * n * 2 * model.n_kv_head * model.head_dim * 2
+    return wbytes + kv + kvw + 2 * n * vocab * 4
 
 
 def main():
@@ -370,7 +531,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps of both decode legs (default: 256 at depth 12, 512 at depth 26)")
+    ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-d26", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
@@ -427,6 +590,9 @@ def main():
         "norm_rope_embed_ms_per_step": round(norm["ms"] / args.steps, 3),
         "softmax_ms_per_step": round(smx["ms"] / args.steps, 3),
         "ms_per_step_with_event_timing": round(dt_prof / args.steps * 1e3, 3),
+        "whole_prefill": {"tflop_per_step": round((g["flops"] + attn["flops"]) / args.steps / 1e12, 4),
+                          "achieved_tflops": round((g["flops"] + attn["flops"]) / dt / 1e12, 1),
+                          "frac": round((g["flops"] + attn["flops"]) / dt / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     log(f"d12 prefill: {value:,.0f} tok/s, gemm {gemm_tfs:.0f} TFLOP/s, attn {attn_tfs:.0f} TFLOP/s")
 
@@ -489,15 +655,19 @@ def main():
 
     # ---------------- depth-12 decode
     if not args.skip_decode:
-        w3 = wl.d12_decode(steps=args.decode_steps)
+        dsteps = args.decode_steps or 256
+        w3 = wl.d12_decode(steps=dsteps)
         log("timing depth-12 decode")
-        ddt, att, sk = bench_decode(B, torch, dm12, w3, args.decode_steps, 0.0)
+        ddt, att, sk = bench_decode(B, torch, dm12, w3, dsteps, 0.0)
+        sb = step_bytes(w3.model, 32, 512 + (dsteps - 1) / 2, w3.model.vocab)
         att_gbs = att["bytes"] / (att["ms"] * 1e-3) / 1e9 if att["ms"] else 0.0
         sk_gbs = sk["bytes"] / (sk["ms"] * 1e-3) / 1e9 if sk["ms"] else 0.0
         out["decode"] = {"workload": "d12_decode", "batch": 32, "prompt": 512,
-                         "steps": args.decode_steps,
-                         "tokens_per_s": round(32 * args.decode_steps / ddt, 1),
-                         "ms_per_step": round(ddt / args.decode_steps * 1e3, 4),
+                         "steps": dsteps,
+                         "tokens_per_s": round(32 * dsteps / ddt, 1),
+                         "ms_per_step": round(ddt / dsteps * 1e3, 4),
+                         "whole_step": {"algorithmic_bytes": round(sb), "achieved_gbs": round(sb / (ddt / dsteps) / 1e9, 1),
+                                        "frac": round(sb / (ddt / dsteps) / 1e9 / PEAK_HBM_GBS, 4)},
                          "decode_attention": {"achieved_gbs": round(att_gbs, 1),
                                               "frac": round(att_gbs / PEAK_HBM_GBS, 4),
                                               "us_per_launch": round(att["ms"] * 1e3 / max(att["launches"], 1), 2)},
@@ -523,22 +693,30 @@ def main():
                            "prefill_attention": {"achieved_tflops": round(ag_tfs, 1),
                                                  "frac": round(ag_tfs / PEAK_BF16_TFLOPS, 4)}}
         if not args.skip_decode:
-            w3g = dataclasses.replace(wl.d12_decode(steps=args.decode_steps), model=mg)
-            ddg, attg, _ = bench_decode(B, torch, dmg, w3g, args.decode_steps, 0.0)
+            w3g = dataclasses.replace(wl.d12_decode(steps=args.decode_steps or 256), model=mg)
+            ddg, attg, _ = bench_decode(B, torch, dmg, w3g, args.decode_steps or 256, 0.0)
             gbs = attg["bytes"] / (attg["ms"] * 1e-3) / 1e9 if attg["ms"] else 0.0
-            out["d12_gqa2"]["decode_tokens_per_s"] = round(32 * args.decode_steps / ddg, 1)
+            out["d12_gqa2"]["decode_tokens_per_s"] = round(32 * (args.decode_steps or 256) / ddg, 1)
             out["d12_gqa2"]["decode_attention"] = {"achieved_gbs": round(gbs, 1),
                                                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
         del dmg
         torch.cuda.empty_cache()
         log(f"d12 gqa2: {out['d12_gqa2']}")
 
-    # ---------------- CPU oracle on one sequence
+    # ---------------- the oracle on the host cores: its timing and the parity samples
+    parity = {}
     if not args.skip_cpu:
         log("timing the oracle on the host")
-        cb, parity = cpu_baseline(w2, W12, g0)
+        cb, parity["d12_prefill"] = cpu_baseline(w2, W12, g0)
         out["cpu_baseline"] = cb
-        out["parity_sample"] = parity
+        del g0
+        if not args.skip_decode:
+            ps = min(args.decode_steps or 256, 64)
+            wp = wl.d12_decode(steps=ps)
+            log("depth-12 decode parity sample")
+            tk, lg = decode_capture(B, torch, dm12, wp, ps, 0.0, [0, 31])
+            parity["d12_decode"] = decode_parity(wp, W12, tk, lg, [0, 31], ps, greedy=True)
+        out["parity"] = parity
     del dm12
     torch.cuda.empty_cache()
 
@@ -548,12 +726,14 @@ def main():
         log("generating depth-26 weights")
         W26 = wl.make_weights(w4.model)
         dm26 = B.DeviceModel(w4.model, W26)
-        del W26
+        if args.skip_cpu:
+            del W26
         log("timing depth-26 prefill")
         s26 = max(2, args.steps // 3)
         dt4, _, lg4, _ = bench_prefill(B, torch, dm26, w4, s26, 1,
                                     1 << B.PROF_CLASSES["gemm"] | 1 << B.PROF_CLASSES["lmhead"]
                                     | 1 << B.PROF_CLASSES["attn"])
+        g26 = lg4[:int(w4.cu_seqlens[1])].cpu().numpy() if not args.skip_cpu else None
         del lg4
         torch.cuda.empty_cache()
         g4 = prof_read(B, ["gemm", "lmhead"])
@@ -563,20 +743,46 @@ def main():
                               "tokens_per_s": round(s26 * M4 / dt4, 1),
                               "ms_per_step": round(dt4 / s26 * 1e3, 3),
                               "gemm_tflops": round(g4["flops"] / (g4["ms"] * 1e-3) / 1e12, 1),
-                              "attn_tflops": round(a4["flops"] / (a4["ms"] * 1e-3) / 1e12, 1)}
+                              "attn_tflops": round(a4["flops"] / (a4["ms"] * 1e-3) / 1e12, 1),
+                              "gemm_frac": round(g4["flops"] / (g4["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "attn_frac": round(a4["flops"] / (a4["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "whole_prefill": {"tflop_per_step": round((g4["flops"] + a4["flops"]) / s26 / 1e12, 3),
+                                                "frac": round((g4["flops"] + a4["flops"]) / dt4 / 1e12 / PEAK_BF16_TFLOPS, 4)}}
         log(f"d26 prefill: {out['d26_prefill']['tokens_per_s']:,.0f} tok/s")
         if not args.skip_decode:
-            w5 = wl.d26_serving(steps=512)
+            s5 = args.decode_steps or 512
+            w5 = wl.d26_serving(steps=s5)
             log("timing depth-26 serving decode")
-            ddt5, att5, sk5 = bench_decode(B, torch, dm26, w5, 512, 0.7)
+            ddt5, att5, sk5 = bench_decode(B, torch, dm26, w5, s5, 0.7)
             att_gbs = att5["bytes"] / (att5["ms"] * 1e-3) / 1e9 if att5["ms"] else 0.0
+            sb5 = step_bytes(w5.model, 64, float(np.mean(w5.seqlens)) + (s5 - 1) / 2, w5.model.vocab)
             out["d26_serving"] = {"workload": "d26_serving", "batch": 64,
-                                  "prompt": "U[64,2048]", "steps": 512, "temperature": 0.7,
-                                  "tokens_per_s": round(64 * 512 / ddt5, 1),
-                                  "ms_per_step": round(ddt5 / 512 * 1e3, 4),
+                                  "prompt": "U[64,2048]", "steps": s5, "temperature": 0.7,
+                                  "tokens_per_s": round(64 * s5 / ddt5, 1),
+                                  "ms_per_step": round(ddt5 / s5 * 1e3, 4),
+                                  "whole_step": {"algorithmic_bytes": round(sb5),
+                                                 "achieved_gbs": round(sb5 / (ddt5 / s5) / 1e9, 1),
+                                                 "frac": round(sb5 / (ddt5 / s5) / 1e9 / PEAK_HBM_GBS, 4)},
                                   "decode_attention": {"achieved_gbs": round(att_gbs, 1),
-                                                       "frac": round(att_gbs / PEAK_HBM_GBS, 4)}}
+                                                       "frac": round(att_gbs / PEAK_HBM_GBS, 4),
+                                                       "us_per_launch": round(att5["ms"] * 1e3 / max(att5["launches"], 1), 2)}}
             log(f"d26 serving: {out['d26_serving']['tokens_per_s']:,.0f} tok/s")
+            if not args.skip_cpu:
+                ps5 = min(s5, 64)
+                w5p = wl.d26_serving(steps=ps5)
+                b5 = int(np.argmax(w5p.seqlens))
+                log("depth-26 serving parity sample")
+                tk5, lg5 = decode_capture(B, torch, dm26, w5p, ps5, 0.7, [b5])
+                out["parity"]["d26_serving"] = decode_parity(w5p, W26, tk5, lg5, [b5], ps5, greedy=False)
+        if not args.skip_cpu:
+            log("depth-26 prefill parity sample")
+            out["parity"]["d26_prefill"] = prefill_parity(w4, W26, g26, 0)
+            del W26, g26
+        del dm26
+        torch.cuda.empty_cache()
+    if not args.skip_decode and not args.skip_sweep:
+        log("decode-attention sweep over batch and cached length")
+        out["decode_attention_sweep"] = decode_sweep(B, torch)
     print(json.dumps(out), flush=True)
 
 

@@ -29,7 +29,7 @@ EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
            "gpt_decode_step",
            "gpt_select_tokens", "gpt_train_workspace_bytes", "gpt_loss_grads", "gpt_adam_step",
-           "gpt_profile_enable", "gpt_profile_read",
+           "gpt_profile_enable", "gpt_profile_mask", "gpt_profile_read",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.gpt_loss_grads.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, vp, i32,
                                  ctypes.POINTER(GptGrads), vp, vp, vp, sz, vp]
     L.gpt_profile_enable.argtypes = [ctypes.c_uint32]
+    L.gpt_profile_mask.argtypes = [ctypes.c_uint32]
     L.gpt_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double)]
@@ -230,6 +231,10 @@ def gpt_adam_step(param, grad, m, v, param_bf16, n: int, step: int, lr: float, b
 
 def gpt_profile_enable(mask: int):
     _check(lib().gpt_profile_enable(mask))
+
+
+def gpt_profile_mask(mask: int):
+    _check(lib().gpt_profile_mask(mask))
 
 
 def gpt_profile_read(cls: int):

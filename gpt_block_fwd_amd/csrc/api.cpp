@@ -1502,6 +1502,11 @@ gpt_status gpt_profile_enable(uint32_t mask) {
   return GPT_OK;
 }
 
+gpt_status gpt_profile_mask(uint32_t mask) {
+  g_prof.mask = mask;
+  return GPT_OK;
+}
+
 gpt_status gpt_profile_read(int32_t cls, double *ms, int64_t *launches, double *flops, double *bytes) {
   if (cls < 0 || cls >= GPT_PROF_NCLASSES) return fail(GPT_ERR_ARG, "bad class");
   double tot = 0, fl = 0, by = 0;

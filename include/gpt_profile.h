@@ -37,6 +37,11 @@ typedef enum {
  * disables.  Clears every accumulated record. */
 gpt_status gpt_profile_enable(uint32_t mask);
 
+/* Change which classes are timed without clearing the records, so that a
+ * long run can be sampled (for instance every eighth decode step) and the
+ * number of HIP events stays bounded. */
+gpt_status gpt_profile_mask(uint32_t mask);
+
 /* Totals since the last enable for one class: summed kernel time in
  * milliseconds, number of launches, algorithmic flops and bytes. */
 gpt_status gpt_profile_read(int32_t cls, double *ms, int64_t *launches, double *flops,

@@ -2,14 +2,16 @@
 times, on sampled sequences the oracle computes one by one.
 
 bf16 bar.  Literal: max |logit diff| <= 3e-2 (asserted at depth 12) and top-1
->= 99.9% (reported).  Random N(0, 0.02) weights give near-flat logits, and
-rounding operands to bf16 at the storage points of any bf16-MFMA path moves
-logits by about 3.5e-3 (depth 12) / 7e-3 (depth 26) std, so the literal
-top-1 bar (both depths) and the 3e-2 max bar (depth 26) are out of reach of
-every bf16-operand implementation.  Asserted instead, on the same sequence:
-the GPU's error is within 1.25x of the bf16 storage floor (the oracle with
-bf16 rounding at those points, against the exact oracle), and every top-1
-disagreement has an oracle top-2 margin below twice the largest error.
+>= 99.9% (reported, with the literal flags, in each test's output).  Random
+N(0, 0.02) weights give near-flat logits, and rounding operands to bf16 at
+the storage points of any bf16-MFMA path moves logits by about 3.5e-3
+(depth 12) / 7e-3 (depth 26) std, so the literal top-1 bar (both depths) and
+the 3e-2 max bar (depth 26) are out of reach of every bf16-operand
+implementation.  Asserted instead: the GPU's error is within 1.25x of the
+bf16 storage floor (the oracle with bf16 rounding at those points, itself
+pinned by scalar loops, against the exact oracle) on the same sequence, and
+every row where the GPU's choice differs from the oracle's argmax is
+explained by that row's own logit errors.
 """
 import numpy as np
 import pytest
@@ -59,7 +61,7 @@ def _prefill_full(dm, w):
 def _within_floor(st, fl):
     assert st["std"] <= FLOOR_FACTOR * fl["std"], (st, fl)
     assert st["max_abs"] <= FLOOR_FACTOR * fl["max_abs"], (st, fl)
-    assert st["disagree_explained"], st
+    assert st["rows_explained"], st
 
 
 def _loss_full(dm, w, targets):
@@ -74,7 +76,7 @@ def _loss_full(dm, w, targets):
 
 
 def test_d12_prefill_full_batch(d12):
-    """8 x 2048 depth-12 prefill, all rows + LSE; sequences 0 and 7 checked.
+    """8 x 2048 depth-12 prefill, all rows + LSE; every sequence checked.
     The fused cross-entropy of the same batch matches lse - logit[target] of
     these logits on every row, and the oracle's losses on the checked ones."""
     t = torch()
@@ -89,14 +91,14 @@ def test_d12_prefill_full_batch(d12):
     assert float((loss - own).abs().max()) <= 2e-6
     assert abs(mean - float(own[ok].double().mean())) <= 1e-5
     cu = w.cu_seqlens
-    for b in (0, 7):
+    for b in range(w.n_seqs):
         g = logits[cu[b]:cu[b + 1]].cpu().numpy()
         gl = lse[cu[b]:cu[b + 1]].cpu().numpy()
         ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[b])
         st = logit_stats(g, ref[0])
         print("d12 prefill seq", b, st)
         assert st["max_abs"] <= 3e-2  # literal bar holds at depth 12
-        assert st["disagree_explained"]
+        assert st["rows_explained"], st
         rl = oracle.token_losses(ref[0], tg[cu[b]:cu[b + 1]])
         assert float(np.max(np.abs(loss[cu[b]:cu[b + 1]].cpu().numpy() - rl))) <= 3e-2
         np.testing.assert_allclose(gl, oracle.logsumexp(g.astype(np.float64)), atol=3e-5)
@@ -109,8 +111,9 @@ def test_d12_prefill_full_batch(d12):
 
 
 def test_d12_decode_full(d12):
-    """32 prompts of 512, 256 greedy steps (cache grows to 768); sequences 0
-    and 31 teacher-forced through the oracle at every step."""
+    """32 prompts of 512, 256 greedy steps (cache grows to 768); sequences 0,
+    10, 21 and 31 teacher-forced through the oracle at every step, judged on
+    the tokens the GPU chose."""
     t = torch()
     W, dm = d12
     w = wl.d12_decode()
@@ -122,7 +125,7 @@ def test_d12_decode_full(d12):
     toks = t.empty(n, dtype=t.int32, device="cuda")
     B.gpt_select_tokens(logits, n, dm.model.vocab, 0.0, None, toks)
     ws = dm.workspace(n, n)
-    sample = [0, 31]
+    sample = [0, 10, 21, 31]
     got_tok = [toks.cpu().numpy().copy()]
     got_lg = [logits[sample].cpu().numpy()]
     for _ in range(steps):
@@ -138,36 +141,39 @@ def test_d12_decode_full(d12):
     got_tok = np.stack(got_tok)
     _, ref = oracle.run_serving(w.model, W, w.tokens, w.seqlens, steps, forced=got_tok,
                                 dtype=np.float32, seqs=sample)
-    st = logit_stats(np.stack(got_lg), ref)
+    st = logit_stats(np.stack(got_lg), ref, chosen=got_tok[:, sample])
     print("d12 decode", st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
 
 
 def test_d26_prefill_full_batch(d26):
-    """16 x 2048 depth-26 prefill, all rows + LSE; sequence 0 checked against
-    the oracle and the bf16 storage floor."""
+    """16 x 2048 depth-26 prefill, all rows + LSE; sequences 0 and 15 checked
+    against the oracle and the bf16 storage floor."""
     W, dm = d26
     w = wl.d26_prefill()
     logits, lse = _prefill_full(dm, w)
     cu = w.cu_seqlens
-    g = logits[cu[0]:cu[1]].cpu().numpy()
-    gl = lse[cu[0]:cu[1]].cpu().numpy()
+    seqs = [0, 15]
+    g = [logits[cu[b]:cu[b + 1]].cpu().numpy() for b in seqs]
+    gl = [lse[cu[b]:cu[b + 1]].cpu().numpy() for b in seqs]
     del logits, lse
     torch().cuda.empty_cache()
-    ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[0])
-    flo, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=[0],
+    ref, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=seqs)
+    flo, _ = oracle.prefill(w.model, W, w.tokens, w.seqlens, dtype=np.float32, seqs=seqs,
                             bf16_points=True)
-    st, fl = logit_stats(g, ref[0]), logit_stats(flo[0], ref[0])
-    print("d26 prefill", st, "floor", fl, "literal 3e-2 bar met:", st["max_abs"] <= 3e-2)
-    _within_floor(st, fl)
-    np.testing.assert_allclose(gl, oracle.logsumexp(g.astype(np.float64)), atol=3e-5)
+    for i, b in enumerate(seqs):
+        st, fl = logit_stats(g[i], ref[i]), logit_stats(flo[i], ref[i])
+        print("d26 prefill seq", b, st, "floor", fl)
+        _within_floor(st, fl)
+        np.testing.assert_allclose(gl[i], oracle.logsumexp(g[i].astype(np.float64)), atol=3e-5)
 
 
 def test_d26_serving_full(d26):
     """64 prompts with lengths U[64, 2048], 512 temperature-0.7 sampled steps
-    (cache up to 2560).  The longest sequence is teacher-forced through the
-    oracle and the bf16 floor at every step; every 64th step, every sequence's
+    (cache up to 2560).  The longest, the shortest and a middle-length
+    sequence are teacher-forced through the oracle and the bf16 floor at
+    every step; every 64th step, every sequence's
     sampled token is checked against the inverse CDF of its own logits."""
     t = torch()
     W, dm = d26
@@ -181,9 +187,10 @@ def test_d26_serving_full(d26):
     toks = t.empty(n, dtype=t.int32, device="cuda")
     B.gpt_select_tokens(logits, n, dm.model.vocab, 0.7, U[0], toks)
     ws = dm.workspace(n, n)
-    b = int(np.argmax(w.seqlens))
+    order = np.argsort(w.seqlens, kind="stable")
+    sample = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
     got_tok = [toks.cpu().numpy().copy()]
-    got_lg = [logits[b].cpu().numpy()]
+    got_lg = [logits[sample].cpu().numpy()]
 
     def check_all(s, lg, tk):
         for j in range(n):
@@ -198,16 +205,18 @@ def test_d26_serving_full(d26):
                        workspace=ws)
         tk = toks.cpu().numpy().copy()
         got_tok.append(tk)
-        got_lg.append(logits[b].cpu().numpy())
+        got_lg.append(logits[sample].cpu().numpy())
         if (s + 1) % 64 == 0:
             check_all(s + 1, logits.cpu().numpy(), tk)
     np.testing.assert_array_equal(kv.lengths(), w.seqlens + steps)
     kv.close()
     got_tok = np.stack(got_tok)
     _, ref = oracle.run_serving(w.model, W, w.tokens, w.seqlens, steps, forced=got_tok,
-                                dtype=np.float32, seqs=[b])
+                                dtype=np.float32, seqs=sample)
     _, flo = oracle.run_serving(w.model, W, w.tokens, w.seqlens, steps, forced=got_tok,
-                                dtype=np.float32, seqs=[b], bf16_points=True)
-    st, fl = logit_stats(np.stack(got_lg)[:, None], ref), logit_stats(flo, ref)
-    print("d26 serving seq", b, st, "floor", fl)
-    _within_floor(st, fl)
+                                dtype=np.float32, seqs=sample, bf16_points=True)
+    got_lg = np.stack(got_lg)
+    for j, b in enumerate(sample):
+        st, fl = logit_stats(got_lg[:, j:j + 1], ref[:, j:j + 1]), logit_stats(flo[:, j:j + 1], ref[:, j:j + 1])
+        print("d26 serving seq", b, "length", int(w.seqlens[b]), st, "floor", fl)
+        _within_floor(st, fl)

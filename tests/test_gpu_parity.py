@@ -1,10 +1,11 @@
 """End-to-end parity of the HIP path (through the C ABI) against the oracle.
 
 fp32 tiny model: max |logit diff| <= 1e-4 and greedy ids bit-exact.
-bf16 models: max |logit diff| <= 3e-2; top-1 agreement is reported and every
-disagreement must sit on an oracle top-2 margin below twice the largest
-logit error (the bf16 storage noise floor on near-flat random-weight logits
-makes a literal 99.9% top-1 bar unreachable for any bf16-operand path).
+bf16 models: max |logit diff| <= 3e-2; top-1 agreement is reported, and
+every row where the GPU's choice differs from the oracle's argmax must be
+explained by that row's own logit errors (the bf16 storage noise floor on
+near-flat random-weight logits makes a literal 99.9% top-1 bar unreachable
+for any bf16-operand path; tests/test_gpu_fullsize.py measures that floor).
 """
 import numpy as np
 import pytest
@@ -106,7 +107,7 @@ def test_small_bf16_prefill(n_layer, n_head, lens):
     st = logit_stats(logits, ref)
     print(st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
     np.testing.assert_allclose(lse, oracle.logsumexp(ref), atol=3e-2)
     # the softmax outputs are distributions consistent with the GPU's own logits
     lg = logits.astype(np.float64)
@@ -220,10 +221,10 @@ def test_small_bf16_decode_teacher_forced(temperature):
         got_logits.append(step_logits.cpu().numpy().copy())
     got_tok = np.stack(got_tok)
     _, ref_logits = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok)
-    st = logit_stats(np.stack(got_logits), ref_logits)
+    st = logit_stats(np.stack(got_logits), ref_logits, chosen=got_tok if temperature <= 0 else None)
     print(st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
     # every chosen token is a valid choice for the GPU's own logits
     for s in range(steps + 1):
         for j in range(n):
@@ -255,7 +256,7 @@ def test_small_bf16_gqa_prefill(n_head, n_kv, lens):
     st = logit_stats(logits, ref)
     print(st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
     np.testing.assert_allclose(lse, oracle.logsumexp(ref), atol=3e-2)
 
 
@@ -287,10 +288,10 @@ def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
     sample = [0, n - 1]
     _, ref_logits = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok,
                                        seqs=sample)
-    st = logit_stats(np.stack(got_logits)[:, sample], ref_logits)
+    st = logit_stats(np.stack(got_logits)[:, sample], ref_logits, chosen=got_tok[:, sample])
     print(st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
     for s in range(steps + 1):
         np.testing.assert_array_equal(got_tok[s], np.argmax(got_logits[s], axis=-1))
     np.testing.assert_array_equal(kv.lengths(), np.asarray(lens) + steps)
@@ -329,11 +330,50 @@ def test_small_bf16_decode_many_sequences(n_head, cap):
     got_tok = np.stack(got_tok)
     sample = [0, 1]
     _, ref = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok, seqs=sample)
-    st = logit_stats(np.stack(got_logits)[:, sample], ref)
+    st = logit_stats(np.stack(got_logits)[:, sample], ref, chosen=got_tok[:, sample])
     print(st)
     assert st["max_abs"] <= 3e-2
-    assert st["disagree_explained"]
+    assert st["rows_explained"], st
     for s_ in range(1, steps + 1):  # greedy: every sequence's token is its own argmax
+        np.testing.assert_array_equal(got_tok[s_], np.argmax(got_logits[s_], axis=-1))
+
+
+@pytest.mark.parametrize("n_seqs", [65, 130])
+def test_small_bf16_decode_beyond_64_sequences(n_seqs):
+    """More than 64 sequences per step take the large-tile GEMMs (residual
+    adds in the GEMM epilogue, RMSNorm on its own, the large-M LM head) and
+    feed decode attention an unsplit QKV projection.  6 greedy steps; the
+    first, the 65th and the last sequence are teacher-forced through the
+    oracle."""
+    t = torch()
+    cfg = wl.small_model(2, 2, vocab=4096)
+    rng = np.random.default_rng(n_seqs)
+    lens = rng.integers(1, 600, size=n_seqs)
+    lens[0], lens[64] = 599, 1
+    w = wl.ragged_prefill(cfg, lens, seed=n_seqs)
+    W, dm = device_model(cfg)
+    n, steps = n_seqs, 6
+    kv = B.DeviceKV(dm, n, 640)
+    logits0, _ = gpu_prefill(dm, w.tokens, w.seqlens, rows=B.ROWS_LAST, kv=kv.handle)
+    toks = t.empty(n, dtype=t.int32, device="cuda")
+    B.gpt_select_tokens(t.from_numpy(logits0).cuda(), n, cfg.vocab, 0.0, None, toks)
+    ws = dm.workspace(n, n)
+    step_logits = t.empty((n, cfg.vocab), dtype=t.float32, device="cuda")
+    got_tok, got_logits = [toks.cpu().numpy().copy()], [logits0]
+    for _ in range(steps):
+        dm.decode_step(kv.handle, toks, toks, logits=step_logits, workspace=ws)
+        got_tok.append(toks.cpu().numpy().copy())
+        got_logits.append(step_logits.cpu().numpy().copy())
+    np.testing.assert_array_equal(kv.lengths(), w.seqlens + steps)
+    kv.close()
+    got_tok = np.stack(got_tok)
+    sample = [0, 64, n - 1]
+    _, ref = oracle.run_serving(cfg, W, w.tokens, w.seqlens, steps, forced=got_tok, seqs=sample)
+    st = logit_stats(np.stack(got_logits)[:, sample], ref, chosen=got_tok[:, sample])
+    print(st)
+    assert st["max_abs"] <= 3e-2
+    assert st["rows_explained"], st
+    for s_ in range(1, steps + 1):
         np.testing.assert_array_equal(got_tok[s_], np.argmax(got_logits[s_], axis=-1))
 
 
@@ -454,14 +494,24 @@ def test_tiny_loss_grads_fp32():
         assert err <= 1e-4 * np.max(np.abs(r)) + 1e-7, (k, err, np.max(np.abs(r)))
 
 
+# Per-entry bound on bf16-model weight gradients, relative to the tensor's
+# RMS gradient.  Every GEMM of the backward takes bf16 operands: each
+# rounding leaves a relative error of at most 2^-9, so one product's entry
+# errs by about 2^-8 of the RMS of its terms, and the chain through the
+# layers compounds that to the 1.2-1.5% relative Frobenius error measured on
+# these models.  An entry that errs by ten times that typical error, 0.15 of
+# the RMS, is outside any plausible tail of the rounding noise.
+GRAD_ELEM_TOL = 0.15
+
+
 @pytest.mark.parametrize("n_head,n_kv,lens", [(2, 1, [150, 70, 33]), (4, 2, [40, 9]), (2, 2, [130]),
                                               (2, 1, [700, 452])])
 def test_small_bf16_loss_grads(n_head, n_kv, lens):
     """bf16 models (MQA, GQA, MHA; 253 rows on the large-M GEMMs, 49 on the
     decode-row ones, 1152 rows with the weight-gradient GEMMs split over k):
     each weight gradient within 5% (relative Frobenius
-    norm) of the float64 oracle's, and pointing the same way (cosine >=
-    0.998).  The bf16 operands of the forward and of the gradient GEMMs set
+    norm) of the float64 oracle's, pointing the same way (cosine >=
+    0.998), and every entry within GRAD_ELEM_TOL of the tensor's RMS.  The bf16 operands of the forward and of the gradient GEMMs set
     that floor; the loss matches the fused-loss prefill."""
     cfg = wl.small_model(2, n_head, vocab=2048, max_seq=1024, n_kv_head=n_kv)
     w = wl.ragged_prefill(cfg, lens, seed=11 + n_head)
@@ -472,7 +522,7 @@ def test_small_bf16_loss_grads(n_head, n_kv, lens):
     assert abs(mean - ref_mean) <= 1e-3
     l2, _, m2 = gpu_loss(dm, w.tokens, w.seqlens, tg)
     assert abs(mean - m2) <= 1e-5
-    worst = 0.0
+    worst, worst_el = 0.0, 0.0
     for k, r in ref.items():
         nr = np.linalg.norm(r)
         if nr == 0:
@@ -482,4 +532,14 @@ def test_small_bf16_loss_grads(n_head, n_kv, lens):
         cos = float(np.sum(g[k] * r) / (np.linalg.norm(g[k]) * nr))
         worst = max(worst, rel)
         assert rel <= 5e-2 and cos >= 0.998, (k, rel, cos)
-    print("worst relative gradient error", worst)
+        # element by element: every entry within GRAD_ELEM_TOL of the
+        # tensor's RMS gradient (rows of the token table that no token reads
+        # stay exactly zero)
+        rms = nr / np.sqrt(r.size)
+        el = float(np.max(np.abs(g[k] - r))) / rms
+        worst_el = max(worst_el, el)
+        assert el <= GRAD_ELEM_TOL, (k, el)
+        if k == "wte":
+            unread = np.all(r == 0, axis=1)
+            assert np.all(g[k][unread] == 0), k
+    print("worst relative gradient error", worst, "worst entry / tensor RMS", worst_el)

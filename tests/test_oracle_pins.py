@@ -9,6 +9,7 @@ import cmath
 import json
 import math
 import os
+import struct
 
 import numpy as np
 import pytest
@@ -416,11 +417,30 @@ def test_mqa_equals_mha_with_replicated_kv():
 
 # ---------------------------------------------------------------- whole model
 
-def scalar_forward(cfg, W, tokens):
+def bf16_scalar(x):
+    """Round a Python float to float32 (ties to even, through the C cast of
+    struct) and then to the nearest bfloat16 value (8 significant bits, ties
+    to even via Python's round): the value a float32 GPU register holds after
+    conversion to bf16.  Written independently of oracle.round_bf16."""
+    x32 = struct.unpack("f", struct.pack("f", x))[0]
+    if x32 == 0.0 or not math.isfinite(x32):
+        return x32
+    m, e = math.frexp(x32)
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def scalar_forward(cfg, W, tokens, bf16=False):
     """Pure-Python scalar loops over one sequence, written independently of
-    the vectorised oracle (pre-norm blocks, learned or rotary positions)."""
+    the vectorised oracle (pre-norm blocks, learned or rotary positions).
+
+    ``bf16`` rounds to bf16 where a bf16-operand GPU path stores its GEMM
+    operands: each normed input (h, h2 and the final hf), q, k and v after
+    RoPE and QK-norm, the unnormalised attention weights exp(s - max) that
+    multiply V (the sum that divides stays unrounded), the attention output o
+    and the MLP activation u."""
     d, H, Hkv, dh = cfg.d_model, cfg.n_head, cfg.n_kv_head, cfg.head_dim
     T = len(tokens)
+    rb = (lambda vec: [bf16_scalar(a) for a in vec]) if bf16 else (lambda vec: vec)
 
     def rms(vec):
         ms = sum(a * a for a in vec) / len(vec)
@@ -449,7 +469,7 @@ def scalar_forward(cfg, W, tokens):
     for lw in W.layers:
         Ks, Vs, Qs = [], [], []
         for t in range(T):
-            h = rms(xs[t])
+            h = rb(rms(xs[t]))
             q, k, v = matvec(lw["wq"], h), matvec(lw["wk"], h), matvec(lw["wv"], h)
             qh = [q[i * dh:(i + 1) * dh] for i in range(H)]
             kh = [k[i * dh:(i + 1) * dh] for i in range(Hkv)]
@@ -460,7 +480,7 @@ def scalar_forward(cfg, W, tokens):
             if cfg.qk_norm:
                 qh = [rms(a) for a in qh]
                 kh = [rms(a) for a in kh]
-            Qs.append(qh), Ks.append(kh), Vs.append(vh)
+            Qs.append([rb(a) for a in qh]), Ks.append([rb(a) for a in kh]), Vs.append([rb(a) for a in vh])
         new = []
         for t in range(T):
             o = []
@@ -471,15 +491,16 @@ def scalar_forward(cfg, W, tokens):
                 m = max(s)
                 e = [math.exp(a - m) for a in s]
                 z = sum(e)
-                o += [sum(e[j] * Vs[j][g][c] for j in range(t + 1)) / z for c in range(dh)]
-            a = matvec(lw["wo"], o)
+                ew = rb(e)
+                o += [sum(ew[j] * Vs[j][g][c] for j in range(t + 1)) / z for c in range(dh)]
+            a = matvec(lw["wo"], rb(o))
             x = [xs[t][c] + a[c] for c in range(d)]
-            zz = matvec(lw["w1"], rms(x))
-            act = [max(a, 0.0) ** 2 if cfg.act == 1 else max(a, 0.0) for a in zz]
+            zz = matvec(lw["w1"], rb(rms(x)))
+            act = rb([max(a, 0.0) ** 2 if cfg.act == 1 else max(a, 0.0) for a in zz])
             m2 = matvec(lw["w2"], act)
             new.append([x[c] + m2[c] for c in range(d)])
         xs = new
-    return np.array([matvec(W.lm_head, rms(x)) for x in xs])
+    return np.array([matvec(W.lm_head, rb(rms(x))) for x in xs])
 
 
 def test_tiny_forward_matches_scalar_loops():
@@ -496,6 +517,99 @@ def test_rope_model_forward_matches_scalar_loops():
     toks = np.array([1, 5, 5, 0, 10, 2, 7], np.int64)
     np.testing.assert_allclose(oracle.forward(cfg, W, toks), scalar_forward(cfg, W, toks),
                                atol=1e-12)
+
+
+def test_bf16_scalar_rounding_known_values():
+    assert bf16_scalar(1.0) == 1.0
+    assert bf16_scalar(1.0 + 2 ** -8) == 1.0                 # tie to even (down)
+    assert bf16_scalar(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6   # tie to even (up)
+    assert bf16_scalar(1.0 + 2 ** -8 + 2 ** -20) == 1.0 + 2 ** -7
+    assert bf16_scalar(-3.0) == -3.0
+    assert bf16_scalar(0.1) == 0.10009765625
+
+
+@pytest.mark.parametrize("which", ["tiny", "rope"])
+def test_bf16_storage_mode_matches_scalar_loops(which):
+    """The oracle's bf16-storage mode (used only to measure the bf16 noise
+    floor) rounds at exactly the points the scalar loop rounds, on the
+    microgpt layout and on a RoPE + QK-norm + MQA + ReLU^2 model: agreement
+    to 1e-12, far below one bf16 step, so a rounding point added, dropped or
+    moved anywhere would fail.  It also differs from the exact mode."""
+    if which == "tiny":
+        cfg, W = wl.tiny_model(), wl.make_weights(wl.tiny_model())
+        toks = wl.tiny_workload().seq_tokens(2)[:9]
+    else:
+        cfg = tiny_rope_model()
+        W = wl.make_weights(cfg, seed=4)
+        toks = np.array([3, 9, 9, 1, 0, 7, 2, 10], np.int64)
+    got = oracle.forward(cfg, W, toks, bf16_points=True)
+    np.testing.assert_allclose(got, scalar_forward(cfg, W, toks, bf16=True), atol=1e-12, rtol=0)
+    assert np.max(np.abs(got - oracle.forward(cfg, W, toks))) > 1e-4
+
+
+def test_bf16_storage_mode_decode_equals_recompute():
+    """In bf16-storage mode the cache holds the rounded k and v, so decoding
+    position by position reproduces the full forward (1e-12)."""
+    cfg = tiny_rope_model()
+    W = wl.make_weights(cfg, seed=4)
+    toks = np.array([3, 9, 9, 1, 0, 7, 2, 10, 4], np.int64)
+    full = oracle.forward(cfg, W, toks, bf16_points=True)
+    cache = oracle.KVCache(cfg.n_layer)
+    part = [oracle.forward(cfg, W, toks[:4], cache, bf16_points=True)]
+    for t in range(4, len(toks)):
+        part.append(oracle.forward(cfg, W, toks[t:t + 1], cache, bf16_points=True))
+    np.testing.assert_allclose(np.concatenate(part), full, atol=1e-12, rtol=0)
+
+
+def test_prefill_packing_matches_per_sequence_forward():
+    """oracle.prefill slices packed tokens by the cumulative lengths: each
+    sequence's logits (all rows, or the last row) equal a forward of that
+    sequence alone, also for a subset of sequences in any order."""
+    cfg = tiny_rope_model()
+    W = wl.make_weights(cfg, seed=6)
+    lens = np.array([5, 1, 9, 3])
+    rng = np.random.default_rng(13)
+    toks = rng.integers(0, cfg.vocab, size=int(lens.sum()))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    outs, _ = oracle.prefill(cfg, W, toks, lens)
+    last, _ = oracle.prefill(cfg, W, toks, lens, rows="last", seqs=[3, 0, 2])
+    for b in range(len(lens)):
+        ref = oracle.forward(cfg, W, toks[cu[b]:cu[b + 1]])
+        np.testing.assert_array_equal(outs[b], ref)
+    for j, b in enumerate([3, 0, 2]):
+        np.testing.assert_allclose(last[j], oracle.forward(cfg, W, toks[cu[b]:cu[b + 1]])[-1:],
+                                   atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "forced", "sampled"])
+def test_run_serving_matches_forward_on_the_whole_sequence(mode):
+    """Serving (prefill a prompt into the cache, choose a token from the last
+    logits, feed it back at the next position) equals one forward over the
+    prompt followed by the fed tokens: the logits of every step are the rows
+    of that forward from the prompt's last position on (1e-12), each choice
+    is the selection rule applied to its row (with the uniform of its step
+    and sequence), and teacher forcing feeds the given tokens instead."""
+    cfg = tiny_rope_model()
+    W = wl.make_weights(cfg, seed=7)
+    lens = np.array([3, 6, 1])
+    rng = np.random.default_rng(14)
+    toks = rng.integers(0, cfg.vocab, size=int(lens.sum()))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    steps, seqs = 5, [2, 0]
+    U = rng.random((steps + 1, len(lens)))
+    forced = rng.integers(0, cfg.vocab, size=(steps + 1, len(lens)))
+    T = 0.7 if mode == "sampled" else 0.0
+    chosen, logits = oracle.run_serving(cfg, W, toks, lens, steps, temperature=T,
+                                        uniforms=U if T else None,
+                                        forced=forced if mode == "forced" else None, seqs=seqs)
+    for j, b in enumerate(seqs):
+        fed = (forced[:steps, b] if mode == "forced" else chosen[:steps, j])
+        seq = np.concatenate([toks[cu[b]:cu[b + 1]], fed])
+        ref = oracle.forward(cfg, W, seq)[lens[b] - 1:]
+        np.testing.assert_allclose(logits[:, j], ref, atol=1e-12, rtol=0)
+        for s_ in range(steps + 1):
+            want = oracle.sample(ref[s_], T, U[s_, b]) if T else int(np.argmax(ref[s_]))
+            assert chosen[s_, j] == want
 
 
 @pytest.mark.parametrize("cfg_fn", [wl.tiny_model, tiny_rope_model])
