@@ -484,12 +484,12 @@ def decode_sweep(B, torch, steps=8):
     head) over B sequences of L cached positions: a one-layer model keeps the
     cache fill cheap; the kernel's launches are timed by HIP events."""
     import dataclasses
-    cfg = dataclasses.replace(wl.depth_model(26), n_layer=1, max_seq=8192 + steps)
+    cfg = dataclasses.replace(wl.depth_model(26), n_layer=1, max_seq=8192 + steps + 1)
     dm = B.DeviceModel(cfg, wl.make_weights(cfg))
     rows = []
     for nb, L in SWEEP:
         w = wl.uniform_prefill(cfg, nb, L, seed=nb + L)
-        kv = B.DeviceKV(dm, nb, L + steps)
+        kv = B.DeviceKV(dm, nb, L + steps + 1)  # the warm-up step, then `steps`
         lg = torch.empty((nb, cfg.vocab), dtype=torch.float32, device="cuda")
         dm.prefill(torch.from_numpy(w.tokens).cuda(), w.cu_seqlens, lg, kv=kv.handle, logits_rows=B.ROWS_LAST)
         toks = torch.zeros(nb, dtype=torch.int32, device="cuda")

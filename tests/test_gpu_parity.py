@@ -494,14 +494,23 @@ def test_tiny_loss_grads_fp32():
         assert err <= 1e-4 * np.max(np.abs(r)) + 1e-7, (k, err, np.max(np.abs(r)))
 
 
-# Per-entry bound on bf16-model weight gradients, relative to the tensor's
-# RMS gradient.  Every GEMM of the backward takes bf16 operands: each
-# rounding leaves a relative error of at most 2^-9, so one product's entry
-# errs by about 2^-8 of the RMS of its terms, and the chain through the
-# layers compounds that to the 1.2-1.5% relative Frobenius error measured on
-# these models.  An entry that errs by ten times that typical error, 0.15 of
-# the RMS, is outside any plausible tail of the rounding noise.
-GRAD_ELEM_TOL = 0.15
+# Per-entry bound on bf16-model weight gradients:
+#   |g - r| <= GRAD_REL |r| + GRAD_ABS max(rms(row of r), rms(r)).
+# Every GEMM of the backward takes bf16 operands, each rounded with a
+# relative error of at most 2^-9, so a product's entry errs by at most 2^-8
+# of the sum of its terms' magnitudes; the chain through the layers
+# compounds the operand errors to the 1.2-1.5% relative Frobenius error
+# measured on these models.  An entry dominated by one term errs by about
+# that fraction of itself, hence 3% of the entry.  An entry that sums many
+# terms of both signs can err by much more than its own size, but not by
+# more than a few times that 1.5% of the typical entry around it: 0.1 of an
+# RMS.  The row's RMS is the scale where a row shares one large upstream
+# factor (the LM head's rows of target tokens are about V times its other
+# rows); the tensor's where a row is small only because its upstream factor
+# nearly vanishes (an MLP feature whose ReLU^2 derivative 2 max(z, 0) is
+# near zero for every token, and is itself moved by the forward's rounding
+# of z at the scale of the other features).
+GRAD_REL, GRAD_ABS = 0.03, 0.1
 
 
 @pytest.mark.parametrize("n_head,n_kv,lens", [(2, 1, [150, 70, 33]), (4, 2, [40, 9]), (2, 2, [130]),
@@ -511,7 +520,7 @@ def test_small_bf16_loss_grads(n_head, n_kv, lens):
     decode-row ones, 1152 rows with the weight-gradient GEMMs split over k):
     each weight gradient within 5% (relative Frobenius
     norm) of the float64 oracle's, pointing the same way (cosine >=
-    0.998), and every entry within GRAD_ELEM_TOL of the tensor's RMS.  The bf16 operands of the forward and of the gradient GEMMs set
+    0.998), and every entry within GRAD_REL of itself plus GRAD_ABS of the larger of its row's and its tensor's RMS.  The bf16 operands of the forward and of the gradient GEMMs set
     that floor; the loss matches the fused-loss prefill."""
     cfg = wl.small_model(2, n_head, vocab=2048, max_seq=1024, n_kv_head=n_kv)
     w = wl.ragged_prefill(cfg, lens, seed=11 + n_head)
@@ -532,14 +541,12 @@ def test_small_bf16_loss_grads(n_head, n_kv, lens):
         cos = float(np.sum(g[k] * r) / (np.linalg.norm(g[k]) * nr))
         worst = max(worst, rel)
         assert rel <= 5e-2 and cos >= 0.998, (k, rel, cos)
-        # element by element: every entry within GRAD_ELEM_TOL of the
-        # tensor's RMS gradient (rows of the token table that no token reads
+        # element by element (the token table's rows that no token reads
         # stay exactly zero)
-        rms = nr / np.sqrt(r.size)
-        el = float(np.max(np.abs(g[k] - r))) / rms
+        live = np.any(r != 0, axis=1)
+        assert np.all(g[k][~live] == 0), k
+        rms = np.maximum(np.sqrt(np.mean(r[live] ** 2, axis=1, keepdims=True)), np.sqrt(np.mean(r[live] ** 2)))
+        el = float(np.max(np.abs(g[k][live] - r[live]) / (GRAD_REL * np.abs(r[live]) + GRAD_ABS * rms)))
         worst_el = max(worst_el, el)
-        assert el <= GRAD_ELEM_TOL, (k, el)
-        if k == "wte":
-            unread = np.all(r == 0, axis=1)
-            assert np.all(g[k][unread] == 0), k
-    print("worst relative gradient error", worst, "worst entry / tensor RMS", worst_el)
+        assert el <= 1.0, (k, el)
+    print("worst relative gradient error", worst, "worst entry error / its bound", worst_el)
