@@ -27,7 +27,7 @@ PROF_CLASSES = {"gemm": 0, "lmhead": 1, "attn": 2, "decode_attn": 3, "skinny": 4
 #: every entry point declared by include/gpt.h and include/gpt_profile.h
 EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
-           "gpt_decode_step",
+           "gpt_decode_step", "gpt_decode_step_noalloc",
            "gpt_select_tokens", "gpt_train_workspace_bytes", "gpt_loss_grads", "gpt_adam_step",
            "gpt_profile_enable", "gpt_profile_mask", "gpt_profile_read",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, vp, sz, vp]
     L.gpt_decode_step.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, f32, vp, vp,
                                   vp, vp, sz, vp]
+    L.gpt_decode_step_noalloc.argtypes = [cfgp, ctypes.POINTER(GptWeights), vp, vp, vp, vp, f32, vp,
+                                          vp, vp, vp]
     L.gpt_select_tokens.argtypes = [vp, i32, i32, f32, vp, vp, vp]
     L.gpt_adam_step.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int64, i32, f32, f32, f32, f32, vp]
     L.gpt_train_workspace_bytes.argtypes = [cfgp, i32, i32]
@@ -201,6 +203,14 @@ def gpt_decode_step(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, kv:
                                  _ptr(rope_sin), kv, _ptr(tokens_in), temperature, _ptr(uniforms),
                                  _ptr(tokens_out), _ptr(logits), _ptr(workspace), workspace_bytes,
                                  _stream(stream)))
+
+
+def gpt_decode_step_noalloc(cfg: GptConfig, weights: GptWeights, rope_cos, rope_sin, kv: int,
+                            tokens_in, temperature: float, uniforms, tokens_out, logits, stream=None):
+    _check(lib().gpt_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), _ptr(rope_cos),
+                                         _ptr(rope_sin), kv, _ptr(tokens_in), temperature,
+                                         _ptr(uniforms), _ptr(tokens_out), _ptr(logits),
+                                         _stream(stream)))
 
 
 def gpt_select_tokens(logits, rows: int, vocab: int, temperature: float, uniforms, tokens_out,

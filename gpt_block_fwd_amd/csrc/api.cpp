@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1387,6 +1388,59 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
   if ((st = hip_check("gpt_decode_step launch"))) return st;
   for (int b = 0; b < n; ++b) kv->lens[b] += 1;
   return GPT_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation decode
+// The scratch of gpt_decode_step_noalloc.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the per-device address from
+// hipGetSymbolAddress is ever handed to kernels or copies.
+static __device__ __align__(256) char scratch[GPT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // per device id, looked up once
+
+gpt_status scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(GPT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GPT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gpt_status gpt_decode_step_noalloc(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                                   const float *rope_sin, gpt_kv_cache *kv, const int32_t *tokens_in,
+                                   float temperature, const float *uniforms, int32_t *tokens_out,
+                                   float *logits, gpt_stream_t stream) {
+  gpt_status st = check_config(c);
+  if (st) return st;
+  if (!kv) return fail(GPT_ERR_ARG, "NULL required pointer");
+  const size_t need = carve(c, kv->n_seqs, kv->n_seqs, nullptr, nullptr);
+  if (need > GPT_NOALLOC_SCRATCH_BYTES)
+    return fail(GPT_ERR_CAPACITY, "a decode step of %d sequences needs %zu bytes of scratch, more than the %zu "
+                "the no-allocation entry point holds", kv->n_seqs, need, (size_t)GPT_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((st = scratch_on_current_device(&ws))) return st;
+  const uint32_t mask = g_prof.mask;  // timing events would be created on demand: none here
+  g_prof.mask = 0;
+  st = gpt_decode_step(c, w, rope_cos, rope_sin, kv, tokens_in, temperature, uniforms, tokens_out, logits, ws,
+                       GPT_NOALLOC_SCRATCH_BYTES, stream);
+  g_prof.mask = mask;
+  return st;
 }
 
 gpt_status gpt_select_tokens(const float *logits, int32_t rows, int32_t vocab, float temperature,

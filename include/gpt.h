@@ -251,6 +251,28 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
                            gpt_stream_t stream);
 
 /*
+ * gpt_decode_step_noalloc -- gpt_decode_step without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * kernels run on a file-scope device scratch array of
+ * GPT_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * until the process ends; its address on the current device is looked up
+ * once, on the first call on that device.  The call allocates nothing and
+ * records no profiling events.  Arguments, results and errors are those of
+ * gpt_decode_step, plus GPT_ERR_CAPACITY (nothing enqueued) when the step
+ * needs more scratch than that, i.e. gpt_workspace_bytes(c, n_seqs, n_seqs)
+ * > GPT_NOALLOC_SCRATCH_BYTES.  Every call on a GPU shares its scratch:
+ * calls that overlap on one GPU (other streams or threads) race; calls in
+ * one stream are ordered and safe.  The scratch keeps the last call's
+ * contents; what a step needs zeroed, its own kernels clear.
+ */
+#define GPT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gpt_status gpt_decode_step_noalloc(const gpt_config *c, const gpt_weights *w, const float *rope_cos,
+                                   const float *rope_sin, gpt_kv_cache *kv, const int32_t *tokens_in,
+                                   float temperature, const float *uniforms, int32_t *tokens_out,
+                                   float *logits, gpt_stream_t stream);
+
+/*
  * gpt_select_tokens -- token choice on rows of given logits, with the same
  * rule as gpt_decode_step (greedy or inverse-CDF temperature sampling).
  * Used for the first token after a prefill.  logits device fp32 [rows, vocab];
