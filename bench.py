@@ -262,13 +262,16 @@ def gemm_source_hash():
     return h.hexdigest()
 
 
-def traffic_pass():
-    """One warm-up and one counted depth-12 prefill, then a 1 GiB copy."""
+def traffic_pass(decode=True):
+    """For rocprofv3 counter passes: one warm-up and one counted depth-12
+    prefill, then (decode) the depth-12 decode and depth-26 serving shapes
+    for a few steps each, then copies of known size."""
     import torch
     from gpt_block_fwd_amd import binding as B
     B.lib()
     w = wl.d12_prefill()
-    dm = B.DeviceModel(w.model, wl.make_weights(w.model))
+    W12 = wl.make_weights(w.model)
+    dm = B.DeviceModel(w.model, W12)
     M = int(w.cu_seqlens[-1])
     logits = torch.empty((M, dm.model.vocab), dtype=torch.float32, device="cuda")
     lse = torch.empty(M, dtype=torch.float32, device="cuda")
@@ -277,8 +280,20 @@ def traffic_pass():
     for _ in range(2):
         dm.prefill(tokens, w.cu_seqlens, logits, lse, workspace=ws)
         torch.cuda.synchronize()
-    del logits
+    del logits, ws
     torch.cuda.empty_cache()
+    log("counted prefill done")
+    if decode:
+        for wd, dmod, temp in ((wl.d12_decode(steps=4), dm, 0.0), (wl.d26_serving(steps=4), None, 0.7)):
+            if dmod is None:
+                del dm
+                torch.cuda.empty_cache()
+                dmod = B.DeviceModel(wd.model, wl.make_weights(wd.model))
+            decode_capture(B, torch, dmod, wd, 4, temp, [0])
+            torch.cuda.synchronize()
+            log(f"counted decode {wd.name} done")
+        del dmod
+        torch.cuda.empty_cache()
     # calibration: a plain elementwise copy (fp16 -> fp32: reads COPY_BYTES / 2,
     # writes COPY_BYTES), then the runtime's blit copy (COPY_BYTES each way)
     xh = torch.ones(COPY_BYTES // 4, dtype=torch.float16, device="cuda")
@@ -316,8 +331,11 @@ def summarize_traffic(fetch_csv, write_csv, out_path):
         blit = [r for r in rows if "copyBuffer" in r[1]][-1]
         known = COPY_BYTES / 2 if name == "fetch" else COPY_BYTES
         factor = known / 1024.0 / elem[2]
-        gemm = [r for r in rows if "gemm_pp_kernel" in r[1]]
-        counted = gemm[len(gemm) // 2:]
+        # the first two depth-12 prefills (QKV, O, W1, W2 per layer, then the
+        # LM head: 49 GEMM launches each); the second is the counted one
+        per = 4 * 12 + 1
+        gemm = [r for r in rows if "gemm_pp_kernel" in r[1]][:2 * per]
+        counted = gemm[per:]
         res[name] = {"copy_kernel": elem[1][:80], "copy_kib": elem[2], "copy_known_kib": known / 1024.0,
                      "factor": factor, "blit_kib": blit[2], "blit_known_kib": COPY_BYTES / 1024.0,
                      "launches": len(counted), "kib_per_launch": sum(r[2] for r in counted) / len(counted)}
@@ -329,6 +347,45 @@ def summarize_traffic(fetch_csv, write_csv, out_path):
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+
+
+def summarize_counters(paths, out_md, title):
+    """Per-kernel means of every counter in rocprofv3 counter_collection CSVs
+    (one or more passes), grouped by kernel and grid size, as a markdown
+    table; FETCH_SIZE and WRITE_SIZE are also given in MB per dispatch with
+    the copy-calibrated factors (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0, see
+    summarize_traffic)."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                name = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0][:48]
+                grid = r.get("Grid_Size", r.get("Grid_Size_X", ""))
+                wg = r.get("Workgroup_Size", r.get("Workgroup_Size_X", ""))
+                vals[(name, grid, wg)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    counters = sorted({c for v in vals.values() for c in v})
+    scale = {"FETCH_SIZE": 2.0 * 1024 / 1e6, "WRITE_SIZE": 1024 / 1e6}
+    lines = [f"# {title}", "", "| kernel | grid | wg | dispatches | " +
+             " | ".join(c + (" (MB)" if c in scale else "") for c in counters) + " |",
+             "|---|---|---|---|" + "---|" * len(counters)]
+    for (name, grid, wg), cv in sorted(vals.items(), key=lambda kv: kv[0]):
+        n = max(len(v) for v in cv.values())
+        cells = []
+        for c in counters:
+            v = cv.get(c)
+            if not v:
+                cells.append("")
+                continue
+            m = sum(v) / len(v)
+            cells.append(f"{m * scale[c]:.2f}" if c in scale else f"{m:.4g}")
+        lines.append(f"| `{name}` | {grid} | {wg} | {n} | " + " | ".join(cells) + " |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as fh:
+        fh.write(text)
+    print(text)
 
 
 def measured_traffic():
@@ -542,9 +599,16 @@ def main():
     ap.add_argument("--traffic-pass", action="store_true",
                     help="one counted depth-12 prefill and a 1 GiB copy, for rocprofv3 --pmc")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="per-kernel counter means of rocprofv3 counter CSVs into --counters-out")
+    ap.add_argument("--counters-out", default="counters.md")
+    ap.add_argument("--counters-title", default="rocprofv3 counters per kernel")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.counters_out, args.counters_title)
         return
     if args.traffic_pass:
         traffic_pass()
