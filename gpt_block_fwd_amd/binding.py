@@ -30,7 +30,7 @@ EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "gpt_decode_step", "gpt_decode_step_noalloc",
            "gpt_select_tokens", "gpt_train_workspace_bytes", "gpt_loss_grads", "gpt_adam_step",
            "gpt_profile_enable", "gpt_profile_mask", "gpt_profile_read",
-           "gpt_debug_gemm", "gpt_debug_attn_prefill", "gpt_debug_decode_policy")
+           "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
 class GptError(RuntimeError):
@@ -102,7 +102,6 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double)]
     L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp]
-    L.gpt_debug_decode_policy.argtypes = [i32, i32]
     L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
     for name in EXPORTS:
         if name not in ("gpt_last_error", "gpt_workspace_bytes", "gpt_train_workspace_bytes"):
@@ -258,10 +257,6 @@ def gpt_profile_read(cls: int):
 
 def gpt_debug_gemm(A, W, M: int, N: int, K: int, C, epi: int, ksplit: int = 1, stream=None):
     _check(lib().gpt_debug_gemm(_ptr(A), _ptr(W), M, N, K, _ptr(C), epi, ksplit, _stream(stream)))
-
-
-def gpt_debug_decode_policy(waves: int, rounds: int):
-    _check(lib().gpt_debug_decode_policy(waves, rounds))
 
 
 def gpt_debug_attn_prefill(q, k, vt, ldvt: int, cu_seqlens, n_seqs: int, n_head: int, cu_dev, o,

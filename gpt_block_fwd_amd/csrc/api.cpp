@@ -38,7 +38,6 @@ gpt_status hip_check(const char *what) {
 }
 
 constexpr int kMaxPrefillSeqs = 512;
-int g_decode_policy = 0;  // decode-attention variant forced by gpt_debug_decode_policy (0: chosen per step)
 constexpr int kCounters = 4096;  // decode-attention chunk counters (one per sequence and K/V head)
 constexpr int kPage = 64;
 
@@ -174,7 +173,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.o = take(M * H * dh * es);
   t.u = take(M * (long long)c->d_ff * es);
   t.lse_tmp = (float *)take(M * 4);
-  t.max_splits = (c->max_seq + kDecodeMinChunk - 1) / kDecodeMinChunk;
+  t.max_splits = (c->max_seq + kDecodeChunk - 1) / kDecodeChunk;
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
@@ -443,9 +442,9 @@ gpt_status kv_cache_alloc(const gpt_config *c, int32_t n_seqs, int32_t capacity_
   if (!bytes_inout) return fail(GPT_ERR_ARG, "bytes_inout is NULL");
   if (n_seqs <= 0 || capacity_per_seq <= 0) return fail(GPT_ERR_ARG, "n_seqs and capacity must be positive");
   if (capacity_per_seq > c->max_seq) return fail(GPT_ERR_ARG, "capacity exceeds max_seq");
-  if (c->dtype == GPT_DTYPE_BF16 && capacity_per_seq > kDecodeMaxPositions)
+  if (c->dtype == GPT_DTYPE_BF16 && capacity_per_seq > kMaxDecodeChunks * kDecodeChunk)
     return fail(GPT_ERR_UNSUPPORTED, "bf16 decode supports at most %d cached positions per sequence",
-                kDecodeMaxPositions);
+                kMaxDecodeChunks * kDecodeChunk);
   if (page_size != kPage) return fail(GPT_ERR_UNSUPPORTED, "page_size must be 64");
   const long long pps = (capacity_per_seq + page_size - 1) / page_size;
   const long long n_pages = pps * n_seqs;
@@ -1331,12 +1330,12 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         AttnDecodeArgs aa{};
         aa.in = sl;
         aa.n = n;
-        aa.max_splits = (kv->capacity + kDecodeMinChunk - 1) / kDecodeMinChunk;
+        aa.max_splits = (kv->capacity + kDecodeChunk - 1) / kDecodeChunk;
         aa.o_part = bf.opart;
         aa.ml_part = bf.mlpart;
         aa.o = (bf16 *)bf.o;
         aa.ctr = bf.ctr;
-        launch_attn_decode_bf16(aa, kv->lens.data(), g_decode_policy, s);
+        launch_attn_decode_bf16(aa, s);
       }
       proj_resid_norm(bf.o, H * dh, w->wo[l]);
       run_gemm(c, gemm(bf.h, d, w->w1[l], n, F, d, bf.u, F, EPI_RELU2_BF16), GPT_PROF_GEMM, s);
@@ -1549,13 +1548,6 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
   aa.o = (bf16 *)o;
   launch_attn_prefill_bf16(aa, s);
   return hip_check("gpt_debug_attn_prefill");
-}
-
-gpt_status gpt_debug_decode_policy(int32_t waves, int32_t rounds) {
-  if (!((waves == 0 && rounds == 0) || ((waves == 2 || waves == 4) && rounds >= 1 && rounds <= 4)))
-    return fail(GPT_ERR_ARG, "waves must be 2 or 4 and rounds 1 .. 4, or both 0");
-  g_decode_policy = waves * 16 + rounds;
-  return GPT_OK;
 }
 
 gpt_status gpt_profile_enable(uint32_t mask) {

@@ -695,12 +695,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   // memory counter
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane & 15, q4 = lane >> 4;
-  int b = blockIdx.y, chunk = blockIdx.x;
-  if (a.nmap) {  // the host's work map: this workgroup's sequence and chunk
-    const unsigned e = a.map[blockIdx.x];
-    b = (int)(e >> 16);
-    chunk = (int)(e & 0xffffu);
-  }
+  const int b = blockIdx.y, chunk = blockIdx.x;
   const ScatterArgs &in = a.in;
   const PagedKV &kv = in.kv;
   // K/V head gk and its G query heads hq0 .. hq0 + G - 1
@@ -1045,73 +1040,22 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
   transpose_cols_kernel<<<dim3(C / 64, (M + 63) / 64), 256, 0, s>>>(src, lds, M, vcol, dst, ldt);
 }
 
-static_assert(sizeof(AttnDecodeArgs) <= 4096, "decode-attention arguments must fit the kernel-argument limit");
-
-template <int NP>
-void launch_decode_np(const AttnDecodeArgs &b, int R, const dim3 &grid, hipStream_t s) {
-  switch (R) {
-    case 1: attn_decode_kernel<NP, 1><<<grid, 64 * NP, 0, s>>>(b); break;
-    case 2: attn_decode_kernel<NP, 2><<<grid, 64 * NP, 0, s>>>(b); break;
-    case 3: attn_decode_kernel<NP, 3><<<grid, 64 * NP, 0, s>>>(b); break;
-    default: attn_decode_kernel<NP, 4><<<grid, 64 * NP, 0, s>>>(b); break;
-  }
-}
-
-void launch_attn_decode_bf16(const AttnDecodeArgs &a, const int *host_lens, int policy, hipStream_t s) {
+void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0) return;
-  // Chunks of NP R pages: NP waves per workgroup (32 KB of LDS each), each
-  // taking R pages in turn.  The host knows every cached length, so it lists
-  // exactly the chunks that have positions, in the first of these variants
-  // whose chunks fit one workgroup per CU.  Each workgroup pays a fixed
-  // latency chain (its query from the projection slabs, the first page, and
-  // for a split sequence the publish and the last chunk's merge) that
-  // outweighs a second round of pages: at the depth-12 decode and depth-26
-  // serving shapes, 4 waves x 1 round, then x 2 rounds, beat smaller chunks
-  // (2 waves, or more workgroups than CUs) by 15-40%.
-  struct Variant { int np, r, slots; };
-  static const Variant variants[] = {{4, 1, 256}, {4, 2, 256}, {4, 3, 256}, {4, 4, 256}};
-  const int Hkv = a.in.Hkv;
-  auto chunks = [&](int pages) {
-    long long t = 0;
-    for (int i = 0; i < a.n; ++i) t += (host_lens[i] + 1 + 64 * pages - 1) / (64 * pages);
-    return t * Hkv;
-  };
-  int np = 0, R = 0;
-  if (policy) {
-    np = policy / 16;
-    R = policy % 16;
-  } else {
-    for (const Variant &v : variants)
-      if (chunks(v.np * v.r) <= std::min(v.slots, kDecodeMapMax)) {
-        np = v.np;
-        R = v.r;
-        break;
-      }
-  }
+  // One workgroup per CU (128 KB of LDS each): R, the pages each wave takes
+  // in turn, is the smallest of 1 .. 4 that keeps the grid (chunks of
+  // kDecodePages R pages) within 256 workgroups.  a.max_splits counts chunks
+  // of kDecodePages pages, for which the partial buffers are sized.
+  const long long per = (long long)a.n * a.in.Hkv;
+  int R = 1;
+  while (R < 4 && (long long)((a.max_splits + R - 1) / R) * per > 256) ++R;
   AttnDecodeArgs b = a;
-  b.nmap = 0;
-  const int CH = 64 * (np ? np : 4) * (R ? R : 1);
-  if (np && chunks(np * R) <= kDecodeMapMax && CH >= kDecodeMinChunk) {
-    int x = 0;
-    for (int i = 0; i < a.n; ++i) {
-      const int c = (host_lens[i] + 1 + CH - 1) / CH;
-      for (int j = 0; j < c; ++j) b.map[x++] = (unsigned)i << 16 | (unsigned)j;
-    }
-    b.nmap = x;  // grid z runs over the K/V heads
-    b.max_splits = (a.max_splits * kDecodeMinChunk + CH - 1) / CH;
-    const dim3 grid(b.nmap, 1, Hkv);
-    if (np == 2) launch_decode_np<2>(b, R, grid, s);
-    else launch_decode_np<4>(b, R, grid, s);
-    return;
+  b.max_splits = (a.max_splits + R - 1) / R;
+  const dim3 grid(b.max_splits, b.n, b.in.Hkv);
+  switch (R) {
+    case 1: attn_decode_kernel<kDecodePages, 1><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    case 2: attn_decode_kernel<kDecodePages, 2><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    case 3: attn_decode_kernel<kDecodePages, 3><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    default: attn_decode_kernel<kDecodePages, 4><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
   }
-  // Too many chunks for a map: one workgroup per (chunk of the capacity,
-  // sequence); R, the pages each of 4 waves takes in turn, is the smallest
-  // of 1 .. 4 that keeps the grid within 256 workgroups.
-  const long long per = (long long)a.n * Hkv;
-  const int cap_chunks4 = (a.max_splits * kDecodeMinChunk + 255) / 256;  // chunks of 4 pages
-  R = 1;
-  while (R < 4 && (long long)((cap_chunks4 + R - 1) / R) * per > 256) ++R;
-  b.max_splits = (cap_chunks4 + R - 1) / R;
-  const dim3 grid(b.max_splits, b.n, Hkv);
-  launch_decode_np<4>(b, R, grid, s);
 }

@@ -247,7 +247,6 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
                            hipStream_t s);
 void launch_attn_prefill_bf16(const AttnPrefillArgs &a, hipStream_t s);
 
-constexpr int kDecodeMapMax = 640;  // workgroups a decode-attention work map can list
 struct AttnDecodeArgs {
   // The new position of each sequence b: its q|k|v projection row b (fp32,
   // in.nslab partial slabs, H + 2 slots of 128), the RoPE tables and QK-norm
@@ -255,22 +254,12 @@ struct AttnDecodeArgs {
   // k and v at position lens[b] and attends over positions 0 .. lens[b].
   ScatterArgs in;
   int n, max_splits;
-  float *o_part;  // [n][max_splits][H][128], one split per chunk of cached positions
+  float *o_part;  // [n][max_splits][H][128], one split per kDecodeChunk positions
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
   unsigned *ctr;  // [n] chunk-completion counters, zero before first use
-  // Work map, built on the host from the cached lengths (set by the
-  // launcher): workgroup x of the grid takes chunk map[x] & 0xffff of
-  // sequence map[x] >> 16, so the grid holds exactly the chunks that have
-  // positions.  nmap == 0: the grid is (max_splits, n) and chunks past a
-  // sequence's end exit at once.
-  int nmap;
-  unsigned map[kDecodeMapMax];
 };
-// host_lens: the cached lengths before this step (the host mirror), from
-// which the launcher sizes the chunks and builds the work map.  policy 0
-// chooses; otherwise waves * 16 + rounds forces that variant (measurement).
-void launch_attn_decode_bf16(const AttnDecodeArgs &a, const int *host_lens, int policy, hipStream_t s);
+void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
 
 struct AttnF32Args {
   const float *q, *k, *v;  // prefill: [M][H*dh], [M][Hkv*dh]
@@ -283,6 +272,7 @@ struct AttnF32Args {
 void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
 void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
 
-constexpr int kDecodeMaxPositions = 16384;  // cached positions per sequence the bf16 decode takes
-constexpr int kDecodeMinChunk = 128;       // smallest chunk of cached positions per decode-attention workgroup
+constexpr int kDecodePages = 4;                      // pages per decode-attention workgroup
+constexpr int kDecodeChunk = 64 * kDecodePages;      // cached positions per decode-attention workgroup
+constexpr int kMaxDecodeChunks = 64;                 // chunks per sequence the final merge holds in LDS
 constexpr int kLogitsPartCols = 64;  // columns per LM-head softmax partial (one wave's width)

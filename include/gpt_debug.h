@@ -51,17 +51,6 @@ gpt_status gpt_debug_attn_prefill(const void *q, const void *k, const void *vt, 
                                   const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_head, int32_t qk_norm,
                                   int32_t *cu_dev, void *o, gpt_stream_t stream);
 
-/*
- * Decode attention splits each sequence's cached positions into chunks of
- * waves x rounds pages (64 positions each), one workgroup of `waves` waves
- * per chunk, each wave taking `rounds` pages in turn; by default the library
- * picks the variant per step from the cached lengths.  This forces one
- * variant for every later decode step of the process, for measurement:
- * waves 2 or 4, rounds 1 .. 4; (0, 0) restores the default.
- * Errors: GPT_ERR_ARG for other values.
- */
-gpt_status gpt_debug_decode_policy(int32_t waves, int32_t rounds);
-
 #ifdef __cplusplus
 }
 #endif
