@@ -38,6 +38,30 @@ gpt_status hip_check(const char *what) {
 }
 
 constexpr int kMaxPrefillSeqs = 512;
+
+// Decode-attention chunking for one step, from the host mirror of the cached
+// lengths: a sequence of P pages (its positions and the new one) splits into
+// ceil(P / chunk) chunks of `chunk` pages, one workgroup each (one per CU,
+// for the LDS).  The smallest chunk that keeps the busy workgroups within
+// the 256 CUs spreads the pages most evenly; a chunk of more than 4 pages
+// takes its waves more than one round.  Chunks of at least
+// ceil(longest / partial-buffer splits) pages fit the partial buffers, and
+// at most 4 kDecodePages pages keep a wave within 4 rounds.
+void decode_chunking(const int *lens, int n, int n_kv_head, int splits_alloc, int *chunk_pages, int *splits,
+                     int *work) {
+  int pmax = 1;
+  for (int b = 0; b < n; ++b) pmax = std::max(pmax, (lens[b] + 1 + 63) / 64);
+  int chunk = std::max(1, (pmax + splits_alloc - 1) / splits_alloc);
+  long long wgs = 0;
+  for (;; ++chunk) {
+    wgs = 0;
+    for (int b = 0; b < n; ++b) wgs += ((lens[b] + 1 + 63) / 64 + chunk - 1) / chunk;
+    if (wgs * n_kv_head <= 256 || chunk == 4 * kDecodePages) break;
+  }
+  *chunk_pages = chunk;
+  *splits = (pmax + chunk - 1) / chunk;
+  *work = (int)wgs;
+}
 constexpr int kCounters = 4096;  // decode-attention chunk counters (one per sequence and K/V head)
 constexpr int kPage = 64;
 
@@ -138,6 +162,7 @@ struct Bufs {
   float *llogits;  // logits for the cross-entropy where the LM head cannot fuse it
   float *slabs;   // partial products of split decode-row GEMMs
   unsigned *ctr;  // completion counters of decode attention
+  int *dmap;      // decode-attention work list: [nseq * max_splits][8]
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
   int max_splits;
@@ -173,9 +198,10 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.o = take(M * H * dh * es);
   t.u = take(M * (long long)c->d_ff * es);
   t.lse_tmp = (float *)take(M * 4);
-  t.max_splits = (c->max_seq + kDecodeChunk - 1) / kDecodeChunk;
+  t.max_splits = (c->max_seq + 64 * kDecodeMinChunkPages - 1) / (64 * kDecodeMinChunkPages);
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
+  t.dmap = (int *)take(nseq * t.max_splits * 8 * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
   t.ctr = (unsigned *)take((size_t)kCounters * 4);
   t.slabs = (float *)take((size_t)kMaxRowSplit * std::min(M, 64LL) * std::max(d, (H + 2 * Hkv) * dh) * 4);
@@ -442,9 +468,9 @@ gpt_status kv_cache_alloc(const gpt_config *c, int32_t n_seqs, int32_t capacity_
   if (!bytes_inout) return fail(GPT_ERR_ARG, "bytes_inout is NULL");
   if (n_seqs <= 0 || capacity_per_seq <= 0) return fail(GPT_ERR_ARG, "n_seqs and capacity must be positive");
   if (capacity_per_seq > c->max_seq) return fail(GPT_ERR_ARG, "capacity exceeds max_seq");
-  if (c->dtype == GPT_DTYPE_BF16 && capacity_per_seq > kMaxDecodeChunks * kDecodeChunk)
+  if (c->dtype == GPT_DTYPE_BF16 && capacity_per_seq > kDecodeMaxPositions)
     return fail(GPT_ERR_UNSUPPORTED, "bf16 decode supports at most %d cached positions per sequence",
-                kMaxDecodeChunks * kDecodeChunk);
+                kDecodeMaxPositions);
   if (page_size != kPage) return fail(GPT_ERR_UNSUPPORTED, "page_size must be 64");
   const long long pps = (capacity_per_seq + page_size - 1) / page_size;
   const long long n_pages = pps * n_seqs;
@@ -1285,6 +1311,11 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
     // (slabs) -> residual + RMSNorm.
     // Above 64 rows the large-M GEMMs write x and the norms run on their own.
     const bool rows = n <= 64;
+    // decode-attention chunks of this step (the lengths are the same for
+    // every layer): chosen on the host, listed on the device once
+    int chunk_pages = 0, splits = 0, work = 0;
+    decode_chunking(kv->lens.data(), n, Hkv, bf.max_splits, &chunk_pages, &splits, &work);
+    launch_decode_map(pv, n, chunk_pages, bf.dmap, s);
     {
       Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 8);
       launch_embed_norm_bf16(tokens_in, (const bf16 *)w->wte, bf.x, (bf16 *)bf.h, n, d, c->norm_eps,
@@ -1330,7 +1361,10 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
         AttnDecodeArgs aa{};
         aa.in = sl;
         aa.n = n;
-        aa.max_splits = (kv->capacity + kDecodeChunk - 1) / kDecodeChunk;
+        aa.chunk_pages = chunk_pages;
+        aa.max_splits = splits;
+        aa.work = work;
+        aa.map = bf.dmap;
         aa.o_part = bf.opart;
         aa.ml_part = bf.mlpart;
         aa.o = (bf16 *)bf.o;

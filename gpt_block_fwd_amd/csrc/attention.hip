@@ -665,8 +665,9 @@ DEV int sload(const int *p) {
 // wave whose page holds that position patches them into its copy of the page
 // (which it may have read before or after the store).
 //
-// One workgroup per chunk of NP R pages of one sequence and K/V head (grid
-// z).  Wave w takes pages w, w + NP, ... of the chunk (R rounds) and scores
+// One workgroup per chunk of a.chunk_pages pages of one sequence and K/V
+// head (grid z).  Wave w takes pages w, w + NP, ... of the chunk (at most R
+// rounds) and scores
 // their 64 cached positions for all query heads that share the K/V head at
 // once (the H / Hkv heads of its group; under MQA every head).  "Heads" below
 // are the group's.  Each page (K and V^T, 32 KB) is copied into the wave's
@@ -679,7 +680,8 @@ DEV int sload(const int *p) {
 // chunk of the sequence to finish merges all chunks and writes o.
 template <int NP, int R>
 __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) {
-  constexpr int NT = 64 * NP, CH = 64 * NP * R;  // threads; cached positions per chunk
+  constexpr int NT = 64 * NP;
+  const int CH = 64 * a.chunk_pages;  // cached positions per chunk (at most 64 NP R)
   // per wave a K page and a V^T page; the wave's partial output (16 heads x
   // 128 fp32) later reuses the first 8 KB
   constexpr int WAVE_BYTES = 2 * 64 * DH * 2;
@@ -695,25 +697,26 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   // memory counter
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane & 15, q4 = lane >> 4;
-  const int b = blockIdx.y, chunk = blockIdx.x;
+  // this workgroup's chunk from the step's work list (consecutive workgroups
+  // go to different XCDs, so the chunks spread evenly over them)
+  const int *wk = a.map + 8 * blockIdx.x;
+  const int b = wk[0], chunk = wk[1];
   const ScatterArgs &in = a.in;
   const PagedKV &kv = in.kv;
   // K/V head gk and its G query heads hq0 .. hq0 + G - 1
   const int Hall = in.H, Hkv = in.Hkv, G = Hall / Hkv, gk = blockIdx.z, hq0 = gk * G;
   const int kvd = Hkv * DH;  // row width of a K page
-  const int len = kv.lens[b] + 1;  // positions 0 .. lens[b], the last one new
-  // This wave's first page-table entry does not depend on len: it is read
-  // together with it (the scalar load's wait covers both), so the page copy
-  // starts one round trip earlier.  The index is clamped to the table's row;
-  // an entry past the sequence is not used.
-  const int page0 = sload(kv.table + b * kv.pages_per_seq +
-                          min((chunk * CH + wave * 64) / kv.page_size, kv.pages_per_seq - 1));
+  const int len = wk[2];  // positions 0 .. lens[b], the last one new
+  // The work list also holds this wave's first page (the block-table entry
+  // clamped to the table's row; one past the chunk is not used), so the page
+  // copy starts after one round trip.
+  const int page0 = wk[4 + wave];
   const int pn = len - 1;
   const int c0 = chunk * CH;
-  if (c0 >= len) return;
+  const int cend = min(c0 + CH, len);             // end of this chunk's positions
   const int H = G;
   const int kpos0 = c0 + wave * 64;               // this wave's first page
-  const int nw = min(NP, (len - c0 + 63) / 64);  // waves with a page
+  const int nw = min(NP, (cend - c0 + 63) / 64);  // waves with a page
   const bool owner = pn < c0 + CH;                // the chunk holds the new position
   const int nslot = H + (owner ? 2 : 0);
   // Slots are built by half-waves: lane li of half hw holds dims 4 li ..
@@ -766,7 +769,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
                                        LDS_PTR(Vs + j * 512), 16, 0, 0);
     }
   };
-  if (kpos0 < len) stage_page(page0);
+  if (kpos0 < cend) stage_page(page0);
   {
     // Query heads and k: half-split rotation (dim i pairs with i + 64, held
     // by lane li ^ 16), then a weightless RMSNorm over the head.
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   }
   // q_s and kv_s complete (a bare barrier: the page loads stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (kpos0 < len) {
+  if (kpos0 < cend) {
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -830,7 +833,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
     for (int r = 0; r < R; ++r) {
       const int kp = kpos0 + r * NP * 64;
-      if (kp >= len) break;
+      if (kp >= cend) break;
       const int nkey = pn - kp;  // the new position's slot in this page, if it holds it
       const bool pw = nkey >= 0 && nkey < 64;
       bf16x8 kf[4][4];
@@ -853,7 +856,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
         for (int d = 0; d < 8; ++d)
 #pragma unroll
           for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
-        if (r + 1 < R && kp + NP * 64 < len) {
+        if (r + 1 < R && kp + NP * 64 < cend) {
           // the fragment reads (and the patch) have completed: the area is free
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           stage_page(sload(kv.table + b * kv.pages_per_seq + (kp + NP * 64) / kv.page_size));
@@ -1040,22 +1043,57 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
   transpose_cols_kernel<<<dim3(C / 64, (M + 63) / 64), 256, 0, s>>>(src, lds, M, vcol, dst, ldt);
 }
 
+// One workgroup: each thread takes sequences t, t + 256, ...; a block-wide
+// exclusive scan of their chunk counts gives each sequence's first entry.
+__global__ __launch_bounds__(256) void decode_map_kernel(PagedKV kv, int n, int chunk_pages, int *map) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int run = 0;  // entries of the sequences before this pass
+  for (int base = 0; base < n; base += 256) {
+    const int b = base + tid;
+    const int len = b < n ? kv.lens[b] + 1 : 0;
+    const int pages = (len + 63) / 64;
+    const int nc = (pages + chunk_pages - 1) / chunk_pages;
+    int inc = nc;  // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int first = before + inc - nc;
+    for (int c = 0; c < nc; ++c) {
+      int *e = map + 8 * (first + c);
+      e[0] = b;
+      e[1] = c;
+      e[2] = len;
+      e[3] = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        e[4 + w] = kv.table[(long long)b * kv.pages_per_seq + min(c * chunk_pages + w, kv.pages_per_seq - 1)];
+    }
+    run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();  // wsum is rewritten by the next pass
+  }
+}
+
+void launch_decode_map(const PagedKV &kv, int n, int chunk_pages, int *map, hipStream_t s) {
+  if (n <= 0) return;
+  decode_map_kernel<<<1, 256, 0, s>>>(kv, n, chunk_pages, map);
+}
+
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
-  if (a.n <= 0) return;
-  // One workgroup per CU (128 KB of LDS each): R, the pages each wave takes
-  // in turn, is the smallest of 1 .. 4 that keeps the grid (chunks of
-  // kDecodePages R pages) within 256 workgroups.  a.max_splits counts chunks
-  // of kDecodePages pages, for which the partial buffers are sized.
-  const long long per = (long long)a.n * a.in.Hkv;
-  int R = 1;
-  while (R < 4 && (long long)((a.max_splits + R - 1) / R) * per > 256) ++R;
-  AttnDecodeArgs b = a;
-  b.max_splits = (a.max_splits + R - 1) / R;
-  const dim3 grid(b.max_splits, b.n, b.in.Hkv);
+  if (a.n <= 0 || a.work <= 0) return;
+  // a.chunk_pages pages per workgroup, R = the rounds its waves take
+  const int R = (a.chunk_pages + kDecodePages - 1) / kDecodePages;
+  const dim3 grid(a.work, 1, a.in.Hkv);
   switch (R) {
-    case 1: attn_decode_kernel<kDecodePages, 1><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
-    case 2: attn_decode_kernel<kDecodePages, 2><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
-    case 3: attn_decode_kernel<kDecodePages, 3><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
-    default: attn_decode_kernel<kDecodePages, 4><<<grid, 64 * kDecodePages, 0, s>>>(b); break;
+    case 1: attn_decode_kernel<kDecodePages, 1><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
+    case 2: attn_decode_kernel<kDecodePages, 2><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
+    case 3: attn_decode_kernel<kDecodePages, 3><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
+    default: attn_decode_kernel<kDecodePages, 4><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
   }
 }

@@ -253,13 +253,22 @@ struct AttnDecodeArgs {
   // setting, the paged cache, the layer and H.  The kernel builds q, appends
   // k and v at position lens[b] and attends over positions 0 .. lens[b].
   ScatterArgs in;
-  int n, max_splits;
-  float *o_part;  // [n][max_splits][H][128], one split per kDecodeChunk positions
+  int n;
+  int max_splits;   // chunks per sequence in the partial buffers' layout
+  int chunk_pages;  // cached pages per chunk: 1 .. 4 kDecodePages
+  int work;         // chunks that hold positions: the grid's x extent
+  const int *map;   // [work][8] from launch_decode_map: sequence, chunk, positions, the chunk's first 4 pages
+  float *o_part;  // [n][max_splits][H][128], one split per chunk
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
   unsigned *ctr;  // [n] chunk-completion counters, zero before first use
 };
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
+// The chunks of one decode step that hold positions, in order of sequence
+// then chunk: map[i] = {sequence, chunk, lens[sequence] + 1, 0, the block-table
+// entries of the chunk's pages 0 .. 3 (clamped to the table's row)}; `work`
+// entries, where work = sum over sequences of ceil(pages / chunk_pages).
+void launch_decode_map(const PagedKV &kv, int n, int chunk_pages, int *map, hipStream_t s);
 
 struct AttnF32Args {
   const float *q, *k, *v;  // prefill: [M][H*dh], [M][Hkv*dh]
@@ -272,7 +281,7 @@ struct AttnF32Args {
 void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
 void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
 
-constexpr int kDecodePages = 4;                      // pages per decode-attention workgroup
-constexpr int kDecodeChunk = 64 * kDecodePages;      // cached positions per decode-attention workgroup
-constexpr int kMaxDecodeChunks = 64;                 // chunks per sequence the final merge holds in LDS
+constexpr int kDecodePages = 4;                      // waves (one staged page each) per decode-attention workgroup
+constexpr int kDecodeMinChunkPages = 2;              // smallest chunk the partial buffers are sized for
+constexpr int kDecodeMaxPositions = 16384;           // longest cached sequence the bf16 decode accepts
 constexpr int kLogitsPartCols = 64;  // columns per LM-head softmax partial (one wave's width)
