@@ -1140,7 +1140,7 @@ gpt_status loss_grads_impl(const gpt_config *c, const gpt_weights *w, const floa
         mb.cu_pad = bf.cu_pad;
         mb.n_seqs = n_seqs;
         mb.max_len = fw.max_len;
-        mb.max_wg = (fw.max_len * (H / Hkv) + 127) / 128;
+        mb.max_wg = (fw.max_len * (H / Hkv) + 255) / 256;  // 256-row blocks of the dq pass
         mb.M = M;
         mb.H = H;
         mb.Hkv = Hkv;

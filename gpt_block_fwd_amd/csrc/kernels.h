@@ -235,7 +235,7 @@ struct AttnBwdMfmaArgs {
   const float *lse2;              // [M][H] from the forward
   float *dsum;                    // [M][H] D = dO . O (written by the launcher)
   const int *cu, *cu_pad;
-  int n_seqs, max_wg, max_len;    // max_wg: 128-row blocks of the longest sequence's rows
+  int n_seqs, max_wg, max_len;    // max_wg: 256-row blocks (dq pass) of the longest sequence's rows
   int M, H, Hkv;
   float *dq;                      // [M][H 128]
   float *dkp, *dvp;               // [H][M][128] per-query-head partials
