@@ -305,12 +305,33 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
     int tcol = -1;
     if constexpr (EPI == EPI_LOGITS_BF16)
       if (hi == 0 && mrow < g.M) tcol = g.targets[mrow] - nw0;
+    // EPI_RESID: every residual value this row block adds is loaded first,
+    // in one batch.  Loaded one store at a time, each load's wait also
+    // covers the stores before it (one counter), and a wave's 24 to 32
+    // load-add-store steps became as many memory round trips.
+    constexpr int NQ = TN == 3 ? 12 : 4 * TN;  // stores per lane per row block
+    f32x4 res[EPI == EPI_RESID ? NQ : 1];
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int i0 = 0, qb = 0; i0 < TN; i0 += 2) {
+        const int ni = TN - i0 >= 2 ? 2 : 1;
+        const int lpr = 8 * ni;
+        const int rr = lane / lpr, cc = 4 * (lane % lpr);
+#pragma unroll
+        for (int q = 0; q < 4 * ni; ++q, ++qb) {
+          const int m = min(m0 + wm * WM + 32 * j + (64 / lpr) * q + rr, g.M - 1);
+          const long long off = (long long)m * g.ldc + nw0 + 32 * i0 + cc;
+          res[qb] = *(const f32x4 *)(g.rin ? g.rin + off : (const float *)g.C + off);
+        }
+      }
+    }
     // columns 0-63 of the wave tile, then (96-wide tiles) columns 64-95
 #pragma unroll
     for (int i0 = 0; i0 < TN; i0 += 2) {
       const int ni = TN - i0 >= 2 ? 2 : 1;   // 32-column blocks in this pass
       const int lpr = 8 * ni;                // lanes per 32 ni-column row
       const int rr = lane / lpr, cc = 4 * (lane % lpr);
+      const int qb0 = 4 * i0;                // this pass's first residual
 #pragma unroll
       for (int i = 0; i < ni; ++i)
 #pragma unroll
@@ -334,6 +355,8 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
         } else if constexpr (EPI == EPI_LOGITS_BF16) {
           const bf16x4 o = {f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
           __builtin_nontemporal_store(o, (bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n));
+        } else if constexpr (EPI == EPI_RESID) {
+          *(f32x4 *)((float *)g.C + (long long)m * g.ldc + n) = res[qb0 + q] + v;
         } else {
           epi_store4<EPS>(g, m, n, v[0], v[1], v[2], v[3]);
         }
