@@ -49,12 +49,6 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
     }
     bf16x4 o = {f2bf(v0), f2bf(v1), f2bf(v2), f2bf(v3)};
     *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
-  } else if constexpr (EPI == EPI_DRELU2) {
-    // d/dz max(z, 0)^2 = 2 max(z, 0) = 2 sqrt(u)
-    const bf16x4 u = *(const bf16x4 *)(g.aux + (long long)m * g.ldc + n);
-    bf16x4 o = {f2bf(v0 * 2.f * sqrtf(bf2f(u[0]))), f2bf(v1 * 2.f * sqrtf(bf2f(u[1]))),
-                f2bf(v2 * 2.f * sqrtf(bf2f(u[2]))), f2bf(v3 * 2.f * sqrtf(bf2f(u[3])))};
-    *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
   } else if constexpr (EPI == EPI_RESID) {
     float *p = (float *)g.C + (long long)m * g.ldc + n;
     f32x4 x = *(const f32x4 *)(g.rin ? g.rin + (long long)m * g.ldc + n : p);
@@ -305,13 +299,15 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
     int tcol = -1;
     if constexpr (EPI == EPI_LOGITS_BF16)
       if (hi == 0 && mrow < g.M) tcol = g.targets[mrow] - nw0;
-    // EPI_RESID: every residual value this row block adds is loaded first,
-    // in one batch.  Loaded one store at a time, each load's wait also
-    // covers the stores before it (one counter), and a wave's 24 to 32
-    // load-add-store steps became as many memory round trips.
+    // EPI_RESID and EPI_DRELU2: every value this row block reads (the
+    // residual it adds to, or u) is loaded first, in one batch.  Loaded one
+    // store at a time, each load's wait also covers the stores before it
+    // (one counter), and a wave's 24 to 32 load-store steps became as many
+    // memory round trips.
     constexpr int NQ = TN == 3 ? 12 : 4 * TN;  // stores per lane per row block
     f32x4 res[EPI == EPI_RESID ? NQ : 1];
-    if constexpr (EPI == EPI_RESID) {
+    bf16x4 au[EPI == EPI_DRELU2 ? NQ : 1];
+    if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
 #pragma unroll
       for (int i0 = 0, qb = 0; i0 < TN; i0 += 2) {
         const int ni = TN - i0 >= 2 ? 2 : 1;
@@ -321,7 +317,8 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
         for (int q = 0; q < 4 * ni; ++q, ++qb) {
           const int m = min(m0 + wm * WM + 32 * j + (64 / lpr) * q + rr, g.M - 1);
           const long long off = (long long)m * g.ldc + nw0 + 32 * i0 + cc;
-          res[qb] = *(const f32x4 *)(g.rin ? g.rin + off : (const float *)g.C + off);
+          if constexpr (EPI == EPI_RESID) res[qb] = *(const f32x4 *)(g.rin ? g.rin + off : (const float *)g.C + off);
+          else au[qb] = *(const bf16x4 *)(g.aux + off);
         }
       }
     }
@@ -357,6 +354,12 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
           __builtin_nontemporal_store(o, (bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n));
         } else if constexpr (EPI == EPI_RESID) {
           *(f32x4 *)((float *)g.C + (long long)m * g.ldc + n) = res[qb0 + q] + v;
+        } else if constexpr (EPI == EPI_DRELU2) {
+          // d/dz max(z, 0)^2 = 2 max(z, 0) = 2 sqrt(u)
+          const bf16x4 u = au[qb0 + q];
+          const bf16x4 o = {f2bf(v[0] * 2.f * sqrtf(bf2f(u[0]))), f2bf(v[1] * 2.f * sqrtf(bf2f(u[1]))),
+                            f2bf(v[2] * 2.f * sqrtf(bf2f(u[2]))), f2bf(v[3] * 2.f * sqrtf(bf2f(u[3])))};
+          *(bf16x4 *)((bf16 *)g.C + (long long)m * g.ldc + n) = o;
         } else {
           epi_store4<EPS>(g, m, n, v[0], v[1], v[2], v[3]);
         }
