@@ -298,19 +298,35 @@ def test_small_bf16_gqa_decode_teacher_forced(n_head, n_kv, n_seqs):
     kv.close()
 
 
-@pytest.mark.parametrize("n_head,cap", [(2, 1100), (7, 2100), (2, 3600)])
-def test_small_bf16_decode_many_sequences(n_head, cap):
-    """64 sequences with room for `cap` positions each: 4-page chunks would
-    make more than 256 decode-attention workgroups, so each wave takes 2
-    (cap 1100), 3 (cap 2100) or 4 (cap 3600) pages in turn, with the online
-    softmax across them.  7 heads: the 9 q/k/v slots of the owning chunk take two passes of
-    its 8 half-waves.  3 greedy steps, the longest and the shortest sequence
-    teacher-forced through the oracle."""
+def decode_chunk_pages(lens, n_kv_head=1):
+    """The decode step's chunk size for these cached lengths, as the library
+    picks it: the fewest pages per chunk (1 .. 16) for which the chunks that
+    hold positions (the new one included) number at most 256.  (The library
+    also keeps at least ceil(longest / partial-buffer splits) pages, at most
+    2 with max_seq >= the longest sequence, which these cases never reach.)"""
+    pages = [(int(n) + 1 + 63) // 64 for n in lens]
+    chunk = 1
+    while chunk < 16 and sum(-(-p // chunk) for p in pages) * n_kv_head > 256:
+        chunk += 1
+    return chunk
+
+
+@pytest.mark.parametrize("n_head,cap,rounds", [(2, 1100, 1), (7, 2100, 2), (2, 3600, 3), (2, 6400, 4)])
+def test_small_bf16_decode_many_sequences(n_head, cap, rounds):
+    """64 sequences of up to `cap` positions: the decode-attention chunks
+    grow with the total length, so each wave takes 1 (cap 1100) to 4 (cap
+    6400) pages in turn, with the online softmax across them.  7 heads: the
+    9 q/k/v slots of the owning chunk take two passes of its 8 half-waves.  3
+    greedy steps, the longest and the shortest sequence teacher-forced
+    through the oracle."""
     t = torch()
-    cfg = wl.small_model(2, n_head, vocab=4096)
+    cfg = wl.small_model(2, n_head, vocab=4096, max_seq=max(cap, 4096))
     rng = np.random.default_rng(21)
     lens = rng.integers(1, cap - 10, size=64)
     lens[0], lens[1] = cap - 11, 1
+    # the rounds this case is meant to reach, on every step
+    for s_ in range(3):
+        assert -(-decode_chunk_pages(lens + s_) // 4) == rounds
     w = wl.ragged_prefill(cfg, lens, seed=21)
     W, dm = device_model(cfg)
     n, steps = len(lens), 3
