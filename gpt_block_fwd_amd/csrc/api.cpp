@@ -1315,11 +1315,11 @@ gpt_status gpt_decode_step(const gpt_config *c, const gpt_weights *w, const floa
     // every layer): chosen on the host, listed on the device once
     int chunk_pages = 0, splits = 0, work = 0;
     decode_chunking(kv->lens.data(), n, Hkv, bf.max_splits, &chunk_pages, &splits, &work);
-    launch_decode_map(pv, n, chunk_pages, bf.dmap, s);
     {
+      DecodeMapArgs dm{pv, n, chunk_pages, bf.max_splits, bf.dmap};
       Timed t(GPT_PROF_NORM, s, 0, (double)n * d * 8);
       launch_embed_norm_bf16(tokens_in, (const bf16 *)w->wte, bf.x, (bf16 *)bf.h, n, d, c->norm_eps,
-                             bf.ctr, kCounters, s);
+                             bf.ctr, kCounters, dm, s);
     }
     // x += A W^T, then h = RMSNorm(x)
     auto proj_resid_norm = [&](const void *A, int K, const void *Wt) {

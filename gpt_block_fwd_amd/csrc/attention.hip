@@ -704,6 +704,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   // go to different XCDs, so the chunks spread evenly over them)
   const int *wk = a.map + 8 * blockIdx.x;
   const int b = wk[0], chunk = wk[1];
+  if (b >= a.n) return;  // only a list out of step with the lengths holds one
   const ScatterArgs &in = a.in;
   const PagedKV &kv = in.kv;
   // K/V head gk and its G query heads hq0 .. hq0 + G - 1
@@ -1048,46 +1049,6 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
 
 // One workgroup: each thread takes sequences t, t + 256, ...; a block-wide
 // exclusive scan of their chunk counts gives each sequence's first entry.
-__global__ __launch_bounds__(256) void decode_map_kernel(PagedKV kv, int n, int chunk_pages, int *map) {
-  __shared__ int wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int run = 0;  // entries of the sequences before this pass
-  for (int base = 0; base < n; base += 256) {
-    const int b = base + tid;
-    const int len = b < n ? kv.lens[b] + 1 : 0;
-    const int pages = (len + 63) / 64;
-    const int nc = (pages + chunk_pages - 1) / chunk_pages;
-    int inc = nc;  // inclusive scan over the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    int before = run;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int first = before + inc - nc;
-    for (int c = 0; c < nc; ++c) {
-      int *e = map + 8 * (first + c);
-      e[0] = b;
-      e[1] = c;
-      e[2] = len;
-      e[3] = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        e[4 + w] = kv.table[(long long)b * kv.pages_per_seq + min(c * chunk_pages + w, kv.pages_per_seq - 1)];
-    }
-    run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();  // wsum is rewritten by the next pass
-  }
-}
-
-void launch_decode_map(const PagedKV &kv, int n, int chunk_pages, int *map, hipStream_t s) {
-  if (n <= 0) return;
-  decode_map_kernel<<<1, 256, 0, s>>>(kv, n, chunk_pages, map);
-}
-
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0 || a.work <= 0) return;
   // a.chunk_pages pages per workgroup, R = the rounds its waves take

@@ -8,8 +8,21 @@
 void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *seq, int *pos,
                     int *vcol, hipStream_t s);
 void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s);
+// The chunks of one decode step that hold positions, in order of sequence
+// then chunk: map[i] = {sequence, chunk, lens[sequence] + 1, 0, the block-table
+// entries of the chunk's pages 0 .. 3 (clamped to the table's row)}; the list
+// has sum over sequences of min(ceil(pages / chunk_pages), max_chunks)
+// entries, and map holds room for n max_chunks of them.
+struct DecodeMapArgs {
+  PagedKV kv;
+  int n, chunk_pages, max_chunks;
+  int *map;  // null: no list
+};
+// Decode rows: x = WTE[tok], h = RMSNorm(x) (bf16), the completion counters
+// cleared, and (dm.map set) the step's decode-attention work list written by
+// one more workgroup.
 void launch_embed_norm_bf16(const int *tok, const bf16 *wte, float *x, bf16 *h, int M, int d,
-                            float eps, unsigned *ctr, int nctr, hipStream_t s);
+                            float eps, unsigned *ctr, int nctr, const DecodeMapArgs &dm, hipStream_t s);
 void launch_embed_f32(const int *tok, const float *wte, const float *wpe, const int *pos, float *x,
                       int M, int d, hipStream_t s);
 void launch_rmsnorm_bf16(const float *x, bf16 *y, const int *rows, int M, int d, float eps,
@@ -257,18 +270,13 @@ struct AttnDecodeArgs {
   int max_splits;   // chunks per sequence in the partial buffers' layout
   int chunk_pages;  // cached pages per chunk: 1 .. 4 kDecodePages
   int work;         // chunks that hold positions: the grid's x extent
-  const int *map;   // [work][8] from launch_decode_map: sequence, chunk, positions, the chunk's first 4 pages
+  const int *map;   // [work][8], the step's work list (DecodeMapArgs)
   float *o_part;  // [n][max_splits][H][128], one split per chunk
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
   unsigned *ctr;  // [n] chunk-completion counters, zero before first use
 };
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s);
-// The chunks of one decode step that hold positions, in order of sequence
-// then chunk: map[i] = {sequence, chunk, lens[sequence] + 1, 0, the block-table
-// entries of the chunk's pages 0 .. 3 (clamped to the table's row)}; `work`
-// entries, where work = sum over sequences of ceil(pages / chunk_pages).
-void launch_decode_map(const PagedKV &kv, int n, int chunk_pages, int *map, hipStream_t s);
 
 struct AttnF32Args {
   const float *q, *k, *v;  // prefill: [M][H*dh], [M][Hkv*dh]

@@ -44,12 +44,61 @@ __global__ void embed_bf16_kernel(const int *tok, const bf16 *wte, float *x, int
   dst[1] = b;
 }
 
+// The step's decode-attention work list (one workgroup): the chunks that
+// hold positions, in order of sequence then chunk.  A wave-wide inclusive
+// scan of the chunk counts, plus the waves before it, gives each sequence its
+// first entry.
+DEV void decode_map_block(const DecodeMapArgs &a) {
+  __shared__ int wsum[4];
+  const PagedKV &kv = a.kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int run = 0;  // entries of the sequences before this pass
+  for (int base = 0; base < a.n; base += 256) {
+    const int b = base + tid;
+    const int len = b < a.n ? kv.lens[b] + 1 : 0;
+    const int pages = (len + 63) / 64;
+    // at most max_chunks per sequence, the list's room per sequence (the
+    // host picks chunk_pages so that none has more, from its copy of the
+    // lengths; the bound keeps the list in its buffer should the copies
+    // ever disagree)
+    const int nc = min((pages + a.chunk_pages - 1) / a.chunk_pages, a.max_chunks);
+    int inc = nc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int first = before + inc - nc;
+    for (int c = 0; c < nc; ++c) {
+      int *e = a.map + 8 * (first + c);
+      e[0] = b;
+      e[1] = c;
+      e[2] = len;
+      e[3] = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        e[4 + w] = kv.table[(long long)b * kv.pages_per_seq + min(c * a.chunk_pages + w, kv.pages_per_seq - 1)];
+    }
+    run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();  // wsum is rewritten by the next pass
+  }
+}
+
 // Decode rows: x = WTE[token] (fp32), h = rms(x) (bf16), one wave per row.
 // Block 0 also clears the completion counters the fused kernels of the step
-// use (they reset what they use, so this only matters for a fresh workspace).
+// use (they reset what they use, so this only matters for a fresh workspace),
+// and one more workgroup after the rows' writes the step's work list.
 __global__ __launch_bounds__(256) void embed_norm_bf16_kernel(const int *tok, const bf16 *wte, float *x,
                                                               bf16 *h, int M, int d, float eps,
-                                                              unsigned *ctr, int nctr) {
+                                                              unsigned *ctr, int nctr, DecodeMapArgs dm) {
+  if (blockIdx.x == gridDim.x - 1 && dm.map) {
+    decode_map_block(dm);
+    return;
+  }
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctr; i += blockDim.x) ctr[i] = 0u;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -66,8 +115,9 @@ __global__ __launch_bounds__(256) void embed_norm_bf16_kernel(const int *tok, co
 }
 
 void launch_embed_norm_bf16(const int *tok, const bf16 *wte, float *x, bf16 *h, int M, int d,
-                            float eps, unsigned *ctr, int nctr, hipStream_t s) {
-  embed_norm_bf16_kernel<<<(M + 3) / 4, 256, 0, s>>>(tok, wte, x, h, M, d, eps, ctr, nctr);
+                            float eps, unsigned *ctr, int nctr, const DecodeMapArgs &dm, hipStream_t s) {
+  const int blocks = (M + 3) / 4 + (dm.map && dm.n > 0 ? 1 : 0);
+  embed_norm_bf16_kernel<<<blocks, 256, 0, s>>>(tok, wte, x, h, M, d, eps, ctr, nctr, dm);
 }
 
 // One workgroup per row; d <= 2048, so a thread holds at most two
