@@ -43,10 +43,10 @@ constexpr int kMaxPrefillSeqs = 512;
 // lengths: a sequence of P pages (its positions and the new one) splits into
 // ceil(P / chunk) chunks of `chunk` pages, one workgroup each (one per CU,
 // for the LDS).  The smallest chunk that keeps the busy workgroups within
-// the 256 CUs spreads the pages most evenly; a chunk of more than 4 pages
-// takes its waves more than one round.  Chunks of at least
-// ceil(longest / partial-buffer splits) pages fit the partial buffers, and
-// at most 4 kDecodePages pages keep a wave within 4 rounds.
+// the 256 CUs spreads the pages most evenly.  Chunks of up to 4 pages run on
+// four waves, 5 to 8 on eight waves in one round, 9 to 16 on eight waves in
+// two.  Chunks of at least ceil(longest / partial-buffer splits) pages fit
+// the partial buffers.
 void decode_chunking(const int *lens, int n, int n_kv_head, int splits_alloc, int *chunk_pages, int *splits,
                      int *work) {
   int pmax = 1;
@@ -56,7 +56,7 @@ void decode_chunking(const int *lens, int n, int n_kv_head, int splits_alloc, in
   for (;; ++chunk) {
     wgs = 0;
     for (int b = 0; b < n; ++b) wgs += ((lens[b] + 1 + 63) / 64 + chunk - 1) / chunk;
-    if (wgs * n_kv_head <= 256 || chunk == 4 * kDecodePages) break;
+    if (wgs * n_kv_head <= 256 || chunk == 16) break;
   }
   *chunk_pages = chunk;
   *splits = (pmax + chunk - 1) / chunk;
@@ -162,7 +162,7 @@ struct Bufs {
   float *llogits;  // logits for the cross-entropy where the LM head cannot fuse it
   float *slabs;   // partial products of split decode-row GEMMs
   unsigned *ctr;  // completion counters of decode attention
-  int *dmap;      // decode-attention work list: [nseq * max_splits][8]
+  int *dmap;      // decode-attention work list: [nseq * max_splits][kDecodeMapStride]
   void *h, *q, *k, *vt, *o, *u;
   long long ldvt;
   int max_splits;
@@ -201,7 +201,7 @@ size_t carve(const gpt_config *c, long long M, long long nseq, char *base, Bufs 
   t.max_splits = (c->max_seq + 64 * kDecodeMinChunkPages - 1) / (64 * kDecodeMinChunkPages);
   t.opart = (float *)take(nseq * t.max_splits * H * dh * 4);
   t.mlpart = (float *)take(nseq * t.max_splits * H * 2 * 4);
-  t.dmap = (int *)take(nseq * t.max_splits * 8 * 4);
+  t.dmap = (int *)take(nseq * t.max_splits * kDecodeMapStride * 4);
   t.dlogits = (float *)take(nseq * (long long)c->vocab * 4);
   t.ctr = (unsigned *)take((size_t)kCounters * 4);
   t.slabs = (float *)take((size_t)kMaxRowSplit * std::min(M, 64LL) * std::max(d, (H + 2 * Hkv) * dh) * 4);

@@ -684,10 +684,16 @@ DEV int sload(const int *p) {
 template <int NP, int R>
 __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) {
   constexpr int NT = 64 * NP;
+  // VREG: eight waves, each staging only its K page in LDS and loading its
+  // V^T fragments straight into registers (128 KB of LDS holds eight K pages
+  // but only four K + V^T pairs), so a chunk of up to 8 pages lands in one
+  // round.
+  constexpr bool VREG = NP == 8;
+  static_assert(NP == 4 || NP == 8, "four waves (K and V^T staged) or eight (K staged)");
   const int CH = 64 * a.chunk_pages;  // cached positions per chunk (at most 64 NP R)
-  // per wave a K page and a V^T page; the wave's partial output (16 heads x
-  // 128 fp32) later reuses the first 8 KB
-  constexpr int WAVE_BYTES = 2 * 64 * DH * 2;
+  // per wave a K page (and, four waves, a V^T page); the wave's partial
+  // output (16 heads x 128 fp32) later reuses the first 8 KB
+  constexpr int WAVE_BYTES = (VREG ? 1 : 2) * 64 * DH * 2;
   constexpr int QS = DH + 8;  // q row pitch: the 16 heads of a fragment read start on different banks
   __shared__ __attribute__((aligned(16))) char smem[NP * WAVE_BYTES];
   __shared__ float ml_s[NP][16][2];  // per-page (max, sum) per head
@@ -702,7 +708,7 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
   const int hl = lane & 15, q4 = lane >> 4;
   // this workgroup's chunk from the step's work list (consecutive workgroups
   // go to different XCDs, so the chunks spread evenly over them)
-  const int *wk = a.map + 8 * blockIdx.x;
+  const int *wk = a.map + kDecodeMapStride * blockIdx.x;
   const int b = wk[0], chunk = wk[1];
   if (b >= a.n) return;  // only a list out of step with the lengths holds one
   const ScatterArgs &in = a.in;
@@ -766,14 +772,29 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
       __builtin_amdgcn_global_load_lds(GLOBAL_PTR(K + key * kvd + ((pc ^ (key & 15)) << 3)),
                                        LDS_PTR(Ks + j * 512), 16, 0, 0);
     }
+    if constexpr (!VREG)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int dim = 8 * j + (lane >> 3), pc = lane & 7;
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(Vt + dim * 64 + ((pc ^ ((dim >> 1) & 7)) << 3)),
-                                       LDS_PTR(Vs + j * 512), 16, 0, 0);
-    }
+      for (int j = 0; j < 16; ++j) {
+        const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(Vt + dim * 64 + ((pc ^ ((dim >> 1) & 7)) << 3)),
+                                         LDS_PTR(Vs + j * 512), 16, 0, 0);
+      }
   };
-  if (kpos0 < cend) stage_page(page0);
+  // VREG: the V^T fragments of a page straight from the cache, in the layout
+  // the four-wave kernel reads them from LDS: dims 16 d + hl, the eight
+  // stored key columns 8 (4 h + q4) .. +8 (two sets for two rounds)
+  bf16x8 vreg[VREG && R > 1 ? 2 : 1][8][2];
+  auto load_v = [&](int page, bf16x8 (&vr)[8][2]) __attribute__((always_inline)) {
+    const bf16 *Vt = (const bf16 *)(page_ptr(page) + kv.half_bytes) + gk * DH * 64;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vr[d][h] = *(const bf16x8 *)(Vt + (16 * d + hl) * 64 + 8 * (4 * h + q4));
+  };
+  if (kpos0 < cend) {
+    stage_page(page0);
+    if constexpr (VREG) load_v(page0, vreg[0]);
+  }
   {
     // Query heads and k: half-split rotation (dim i pairs with i + 64, held
     // by lane li ^ 16), then a weightless RMSNorm over the head.
@@ -835,13 +856,16 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
     f32x4 oacc[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){};
+#pragma unroll
     for (int r = 0; r < R; ++r) {
       const int kp = kpos0 + r * NP * 64;
       if (kp >= cend) break;
       const int nkey = pn - kp;  // the new position's slot in this page, if it holds it
       const bool pw = nkey >= 0 && nkey < 64;
       bf16x8 kf[4][4];
-      bf16x8 vf[8][2];  // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
+      // V^T: dims 16 d + hl, the eight keys of k slots 8 q4 .. of half h
+      // (four waves: read from LDS below)
+      bf16x8 (&vf)[8][2] = vreg[VREG && R > 1 ? (r & 1) : 0];
       {
         // this round's page has landed (each wave reads only its own area)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -849,21 +873,41 @@ __global__ __launch_bounds__(64 * NP) void attn_decode_kernel(AttnDecodeArgs a) 
           Ks[kdx(nkey, lane >> 3) + (lane & 7)] = kv_s[lane];
           Ks[kdx(nkey, (lane + 64) >> 3) + (lane & 7)] = kv_s[lane + 64];
           const int cc = vslot(nkey);
-          Vs[vdx(lane, cc >> 2) + (cc & 3)] = kv_s[DH + lane];
-          Vs[vdx(lane + 64, cc >> 2) + (cc & 3)] = kv_s[DH + lane + 64];
+          if constexpr (VREG) {
+            // the stored column cc is element cc % 8 of vf[.][cc / 32] in the
+            // lanes of q4 = (cc / 8) % 4
+            if (q4 == ((cc >> 3) & 3)) {
+              const int hn = cc >> 5, jn = cc & 7;
+#pragma unroll
+              for (int d = 0; d < 8; ++d) {
+                const bf16 v = kv_s[DH + 16 * d + hl];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                  for (int j = 0; j < 8; ++j)
+                    if (h == hn && j == jn) vf[d][h][j] = v;
+              }
+            }
+          } else {
+            Vs[vdx(lane, cc >> 2) + (cc & 3)] = kv_s[DH + lane];
+            Vs[vdx(lane + 64, cc >> 2) + (cc & 3)] = kv_s[DH + lane + 64];
+          }
         }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8 *)&Ks[kdx(16 * kb + hl, 4 * s + q4)];
+        if constexpr (!VREG)
 #pragma unroll
-        for (int d = 0; d < 8; ++d)
+          for (int d = 0; d < 8; ++d)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
+            for (int h = 0; h < 2; ++h) vf[d][h] = *(const bf16x8 *)&Vs[vdx(16 * d + hl, 2 * (4 * h + q4))];
         if (r + 1 < R && kp + NP * 64 < cend) {
           // the fragment reads (and the patch) have completed: the area is free
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          stage_page(sload(kv.table + b * kv.pages_per_seq + (kp + NP * 64) / kv.page_size));
+          const int npg = sload(kv.table + b * kv.pages_per_seq + (kp + NP * 64) / kv.page_size);
+          stage_page(npg);
+          if constexpr (VREG) load_v(npg, vreg[(r + 1) & 1]);
         }
       }
       // S^T[key][head] = K Q^T: lane holds head hl, keys 16 kb + 4 q4 + r
@@ -1051,13 +1095,10 @@ void launch_transpose_cols(const bf16 *src, long long lds, int M, int C, const i
 // exclusive scan of their chunk counts gives each sequence's first entry.
 void launch_attn_decode_bf16(const AttnDecodeArgs &a, hipStream_t s) {
   if (a.n <= 0 || a.work <= 0) return;
-  // a.chunk_pages pages per workgroup, R = the rounds its waves take
-  const int R = (a.chunk_pages + kDecodePages - 1) / kDecodePages;
+  // a.chunk_pages pages per workgroup: up to 4 on four waves, 5 to 8 on
+  // eight (one round), 9 to 16 on eight in two rounds
   const dim3 grid(a.work, 1, a.in.Hkv);
-  switch (R) {
-    case 1: attn_decode_kernel<kDecodePages, 1><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
-    case 2: attn_decode_kernel<kDecodePages, 2><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
-    case 3: attn_decode_kernel<kDecodePages, 3><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
-    default: attn_decode_kernel<kDecodePages, 4><<<grid, 64 * kDecodePages, 0, s>>>(a); break;
-  }
+  if (a.chunk_pages <= 4) attn_decode_kernel<4, 1><<<grid, 256, 0, s>>>(a);
+  else if (a.chunk_pages <= 8) attn_decode_kernel<8, 1><<<grid, 512, 0, s>>>(a);
+  else attn_decode_kernel<8, 2><<<grid, 512, 0, s>>>(a);
 }

@@ -9,8 +9,9 @@ void launch_rowinfo(const int *cu, const int *cu_pad, int n_seqs, int M, int *se
                     int *vcol, hipStream_t s);
 void launch_embed_bf16(const int *tok, const bf16 *wte, float *x, int M, int d, hipStream_t s);
 // The chunks of one decode step that hold positions, in order of sequence
-// then chunk: map[i] = {sequence, chunk, lens[sequence] + 1, 0, the block-table
-// entries of the chunk's pages 0 .. 3 (clamped to the table's row)}; the list
+// then chunk: map[kDecodeMapStride i ..] = {sequence, chunk, lens[sequence] + 1,
+// 0, the block-table entries of the chunk's pages 0 .. 7 (clamped to the
+// table's row)}; the list
 // has sum over sequences of min(ceil(pages / chunk_pages), max_chunks)
 // entries, and map holds room for n max_chunks of them.
 struct DecodeMapArgs {
@@ -268,9 +269,9 @@ struct AttnDecodeArgs {
   ScatterArgs in;
   int n;
   int max_splits;   // chunks per sequence in the partial buffers' layout
-  int chunk_pages;  // cached pages per chunk: 1 .. 4 kDecodePages
+  int chunk_pages;  // cached pages per chunk: 1 .. 16
   int work;         // chunks that hold positions: the grid's x extent
-  const int *map;   // [work][8], the step's work list (DecodeMapArgs)
+  const int *map;   // [work][kDecodeMapStride], the step's work list (DecodeMapArgs)
   float *o_part;  // [n][max_splits][H][128], one split per chunk
   float *ml_part; // [n][max_splits][H][2]
   bf16 *o;        // [n][H*128]
@@ -289,7 +290,7 @@ struct AttnF32Args {
 void launch_attn_prefill_f32(const AttnF32Args &a, hipStream_t s);
 void launch_attn_decode_f32(const AttnF32Args &a, hipStream_t s);
 
-constexpr int kDecodePages = 4;                      // waves (one staged page each) per decode-attention workgroup
+constexpr int kDecodeMapStride = 16;                 // ints per decode work-list entry (8 pages)
 constexpr int kDecodeMinChunkPages = 2;              // smallest chunk the partial buffers are sized for
 constexpr int kDecodeMaxPositions = 16384;           // longest cached sequence the bf16 decode accepts
 constexpr int kLogitsPartCols = 64;  // columns per LM-head softmax partial (one wave's width)

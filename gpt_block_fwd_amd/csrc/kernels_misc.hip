@@ -74,13 +74,13 @@ DEV void decode_map_block(const DecodeMapArgs &a) {
     for (int w = 0; w < wave; ++w) before += wsum[w];
     const int first = before + inc - nc;
     for (int c = 0; c < nc; ++c) {
-      int *e = a.map + 8 * (first + c);
+      int *e = a.map + kDecodeMapStride * (first + c);
       e[0] = b;
       e[1] = c;
       e[2] = len;
       e[3] = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < 8; ++w)
         e[4 + w] = kv.table[(long long)b * kv.pages_per_seq + min(c * a.chunk_pages + w, kv.pages_per_seq - 1)];
     }
     run += wsum[0] + wsum[1] + wsum[2] + wsum[3];

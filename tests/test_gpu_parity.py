@@ -311,12 +311,17 @@ def decode_chunk_pages(lens, n_kv_head=1):
     return chunk
 
 
-@pytest.mark.parametrize("n_head,cap,rounds", [(2, 1100, 1), (7, 2100, 2), (2, 3600, 3), (2, 6400, 4)])
-def test_small_bf16_decode_many_sequences(n_head, cap, rounds):
+@pytest.mark.parametrize("n_head,cap,chunk", [(7, 1250, 4), (2, 2100, 6), (2, 2900, 8), (2, 3600, 9),
+                                              (2, 6400, 16)])
+def test_small_bf16_decode_many_sequences(n_head, cap, chunk):
     """64 sequences of up to `cap` positions: the decode-attention chunks
-    grow with the total length, so each wave takes 1 (cap 1100) to 4 (cap
-    6400) pages in turn, with the online softmax across them.  7 heads: the
-    9 q/k/v slots of the owning chunk take two passes of its 8 half-waves.  3
+    grow with the total length.  Chunks of up to 4 pages run on four waves
+    that stage K and V^T in LDS (cap 1250: every wave busy); 5 to 8 pages on
+    eight waves that stage K and hold V^T in registers (cap 2100: two waves
+    idle; cap 2900: all busy), and 9 to 16 pages on those eight waves in two
+    rounds with the online softmax across them (cap 3600: one wave takes a
+    second page; cap 6400: all do).  7 heads (cap 1250): the 9 q/k/v slots of
+    the owning chunk take two passes of the four waves' 8 half-waves.  3
     greedy steps, the longest and the shortest sequence teacher-forced
     through the oracle."""
     t = torch()
@@ -324,9 +329,9 @@ def test_small_bf16_decode_many_sequences(n_head, cap, rounds):
     rng = np.random.default_rng(21)
     lens = rng.integers(1, cap - 10, size=64)
     lens[0], lens[1] = cap - 11, 1
-    # the rounds this case is meant to reach, on every step
+    # the chunk size this case is meant to reach, on every step
     for s_ in range(3):
-        assert -(-decode_chunk_pages(lens + s_) // 4) == rounds
+        assert decode_chunk_pages(lens + s_) == chunk
     w = wl.ragged_prefill(cfg, lens, seed=21)
     W, dm = device_model(cfg)
     n, steps = len(lens), 3
