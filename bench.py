@@ -228,6 +228,17 @@ def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     run(steps)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # host cost of issuing a step: two steps enqueued onto an idle GPU, timed
+    # on the host alone (median of up to 5), against the step's GPU time
+    start()
+    host = []
+    for _ in range(min(5, steps // 2)):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        run(2)
+        host.append((time.perf_counter() - h0) / 2)
+    torch.cuda.synchronize()
+    host_us = sorted(host)[len(host) // 2] * 1e6 if host else None
     start()
     torch.cuda.synchronize()
     mask = 1 << B.PROF_CLASSES["decode_attn"] | 1 << B.PROF_CLASSES["skinny"] | 1 << B.PROF_CLASSES["lmhead"]
@@ -238,7 +249,7 @@ def bench_decode(B, torch, dm, w, steps, temperature, warm_steps=3):
     sk = prof_read(B, ["skinny", "lmhead"])
     B.gpt_profile_enable(0)
     kv.close()
-    return dt, att, sk
+    return dt, att, sk, host_us
 
 
 # ---------------------------------------------------------------- HBM traffic of the GEMM kernel
@@ -722,7 +733,7 @@ def main():
         dsteps = args.decode_steps or 256
         w3 = wl.d12_decode(steps=dsteps)
         log("timing depth-12 decode")
-        ddt, att, sk = bench_decode(B, torch, dm12, w3, dsteps, 0.0)
+        ddt, att, sk, host_us = bench_decode(B, torch, dm12, w3, dsteps, 0.0)
         sb = step_bytes(w3.model, 32, 512 + (dsteps - 1) / 2, w3.model.vocab)
         att_gbs = att["bytes"] / (att["ms"] * 1e-3) / 1e9 if att["ms"] else 0.0
         sk_gbs = sk["bytes"] / (sk["ms"] * 1e-3) / 1e9 if sk["ms"] else 0.0
@@ -736,7 +747,8 @@ def main():
                                               "frac": round(att_gbs / PEAK_HBM_GBS, 4),
                                               "us_per_launch": round(att["ms"] * 1e3 / max(att["launches"], 1), 2)},
                          "decode_gemms": {"achieved_gbs": round(sk_gbs, 1),
-                                          "frac": round(sk_gbs / PEAK_HBM_GBS, 4)}}
+                                          "frac": round(sk_gbs / PEAK_HBM_GBS, 4)},
+                         "host_enqueue_us_per_step": round(host_us, 1) if host_us else None}
         log(f"d12 decode: {out['decode']['tokens_per_s']:,.0f} tok/s")
 
     # ---------------- grouped-query attention: the depth-12 shape with 2 K/V heads
@@ -758,7 +770,7 @@ def main():
                                                  "frac": round(ag_tfs / PEAK_BF16_TFLOPS, 4)}}
         if not args.skip_decode:
             w3g = dataclasses.replace(wl.d12_decode(steps=args.decode_steps or 256), model=mg)
-            ddg, attg, _ = bench_decode(B, torch, dmg, w3g, args.decode_steps or 256, 0.0)
+            ddg, attg, _, _ = bench_decode(B, torch, dmg, w3g, args.decode_steps or 256, 0.0)
             gbs = attg["bytes"] / (attg["ms"] * 1e-3) / 1e9 if attg["ms"] else 0.0
             out["d12_gqa2"]["decode_tokens_per_s"] = round(32 * (args.decode_steps or 256) / ddg, 1)
             out["d12_gqa2"]["decode_attention"] = {"achieved_gbs": round(gbs, 1),
@@ -817,7 +829,7 @@ def main():
             s5 = args.decode_steps or 512
             w5 = wl.d26_serving(steps=s5)
             log("timing depth-26 serving decode")
-            ddt5, att5, sk5 = bench_decode(B, torch, dm26, w5, s5, 0.7)
+            ddt5, att5, sk5, host5 = bench_decode(B, torch, dm26, w5, s5, 0.7)
             att_gbs = att5["bytes"] / (att5["ms"] * 1e-3) / 1e9 if att5["ms"] else 0.0
             sb5 = step_bytes(w5.model, 64, float(np.mean(w5.seqlens)) + (s5 - 1) / 2, w5.model.vocab)
             out["d26_serving"] = {"workload": "d26_serving", "batch": 64,
@@ -829,7 +841,8 @@ def main():
                                                  "frac": round(sb5 / (ddt5 / s5) / 1e9 / PEAK_HBM_GBS, 4)},
                                   "decode_attention": {"achieved_gbs": round(att_gbs, 1),
                                                        "frac": round(att_gbs / PEAK_HBM_GBS, 4),
-                                                       "us_per_launch": round(att5["ms"] * 1e3 / max(att5["launches"], 1), 2)}}
+                                                       "us_per_launch": round(att5["ms"] * 1e3 / max(att5["launches"], 1), 2)},
+                                  "host_enqueue_us_per_step": round(host5, 1) if host5 else None}
             log(f"d26 serving: {out['d26_serving']['tokens_per_s']:,.0f} tok/s")
             if not args.skip_cpu:
                 ps5 = min(s5, 64)
