@@ -585,10 +585,12 @@ def decode_sweep(B, torch, steps=8):
 
 
 def step_bytes(model, n, mean_len, vocab):
-    """Algorithmic HBM bytes of one decode step: every bf16 weight once, the
+    """Algorithmic HBM bytes of one decode step: every bf16 weight once,
+    except the token embedding, of which the step reads only its n rows; the
     cached K/V read (mean length + 1 positions), the new K/V written, and
     the fp32 logits written and read back by the selection."""
-    wbytes = 2 * sum(int(np.prod(sh)) for _, sh in wl.weight_shapes(model))
+    wbytes = 2 * sum(int(np.prod(sh)) for name, sh in wl.weight_shapes(model) if name != "wte")
+    wbytes += 2 * n * model.d_model
     kv = model.n_layer * n * (mean_len + 1) * 2 * model.n_kv_head * model.head_dim * 2
     kvw = model.n_layer * n * 2 * model.n_kv_head * model.head_dim * 2
     return wbytes + kv + kvw + 2 * n * vocab * 4
