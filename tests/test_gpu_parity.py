@@ -311,9 +311,10 @@ def decode_chunk_pages(lens, n_kv_head=1):
     return chunk
 
 
-@pytest.mark.parametrize("n_head,cap,chunk", [(7, 1250, 4), (2, 2100, 6), (2, 2900, 8), (2, 3600, 9),
-                                              (2, 6400, 16)])
-def test_small_bf16_decode_many_sequences(n_head, cap, chunk):
+@pytest.mark.parametrize("n_head,n_kv,cap,chunk", [(7, 1, 1250, 4), (2, 1, 2100, 6), (2, 1, 2900, 8),
+                                                   (2, 1, 3600, 9), (2, 1, 6400, 16), (4, 2, 1100, 7),
+                                                   (4, 2, 1650, 10)])
+def test_small_bf16_decode_many_sequences(n_head, n_kv, cap, chunk):
     """64 sequences of up to `cap` positions: the decode-attention chunks
     grow with the total length.  Chunks of up to 4 pages run on four waves
     that stage K and V^T in LDS (cap 1250: every wave busy); 5 to 8 pages on
@@ -321,17 +322,19 @@ def test_small_bf16_decode_many_sequences(n_head, cap, chunk):
     idle; cap 2900: all busy), and 9 to 16 pages on those eight waves in two
     rounds with the online softmax across them (cap 3600: one wave takes a
     second page; cap 6400: all do).  7 heads (cap 1250): the 9 q/k/v slots of
-    the owning chunk take two passes of the four waves' 8 half-waves.  3
-    greedy steps, the longest and the shortest sequence teacher-forced
-    through the oracle."""
+    the owning chunk take two passes of the four waves' 8 half-waves.  Two
+    K/V heads (4 query heads): a workgroup per chunk and K/V head, so the
+    chunks double in count and the eight-wave shapes are reached at shorter
+    lengths, one and two rounds.  3 greedy steps, the longest and the
+    shortest sequence teacher-forced through the oracle."""
     t = torch()
-    cfg = wl.small_model(2, n_head, vocab=4096, max_seq=max(cap, 4096))
+    cfg = wl.small_model(2, n_head, vocab=4096, max_seq=max(cap, 4096), n_kv_head=n_kv)
     rng = np.random.default_rng(21)
     lens = rng.integers(1, cap - 10, size=64)
     lens[0], lens[1] = cap - 11, 1
     # the chunk size this case is meant to reach, on every step
     for s_ in range(3):
-        assert decode_chunk_pages(lens + s_) == chunk
+        assert decode_chunk_pages(lens + s_, n_kv) == chunk
     w = wl.ragged_prefill(cfg, lens, seed=21)
     W, dm = device_model(cfg)
     n, steps = len(lens), 3
