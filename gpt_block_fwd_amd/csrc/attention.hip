@@ -3,20 +3,23 @@
 //
 // Prefill: the H query heads of a sequence are flattened into rows
 // r = position * H + head, which is exactly the memory order of q.  Row r
-// sees keys 0 .. r / H.  A workgroup owns 64 * kAttnPrefillWaves
-// consecutive rows (64 per wave); every 64-key K tile and transposed V tile
-// is staged once in LDS and serves all of them, so the single K/V head is
-// read once per workgroup rather than once per query head.  Scores are formed transposed,
+// sees keys 0 .. r / H.  A workgroup owns kAttnPrefillRows consecutive rows
+// (32 per wave); every 64-key K tile and transposed V tile is staged once in
+// LDS and serves all of them, so the single K/V head is read once per
+// workgroup rather than once per query head.  Scores are formed transposed,
 // S^T = K Q^T, so each lane's accumulators hold one row and its softmax
 // statistics stay lane-local (one cross-lane exchange per 32 keys); the
 // exponentiated scores are already laid out as the B operand of
-// O^T = V^T P^T.  Online softmax in the base-2 domain.
+// O^T = V^T P^T.  Softmax in the base-2 domain, against a fixed reference
+// when q and k are QK-normalised, else online.
 //
-// Decode: one 4-wave workgroup per chunk of cached pages of a sequence (and
-// K/V head); each wave stages a 64-position page of K and V^T in LDS with
-// whole-line direct-to-LDS loads (in up to 4 rounds per chunk) and scores it
-// with v_mfma_f32_16x16x32_bf16, the (<= 16) query heads as the N side.  The
-// last chunk of a sequence to finish merges the chunks (log-sum-exp).
+// Decode: one workgroup per chunk of cached pages of a sequence (and K/V
+// head).  Chunks of up to 4 pages: 4 waves, each staging a 64-position page
+// of K and V^T in LDS with whole-line direct-to-LDS loads; 5 to 16 pages: 8
+// waves, each staging its page's K in LDS and loading its V^T fragments into
+// registers, in one or two rounds.  Pages are scored with
+// v_mfma_f32_16x16x32_bf16, the (<= 16) query heads as the N side.  The last
+// chunk of a sequence to finish merges the chunks (log-sum-exp).
 #include "kernels.h"
 #include "scatter.h"
 
