@@ -2,10 +2,11 @@
 // K-contiguous), fp32 accumulation, fused epilogues (bf16 store, ReLU^2 ->
 // bf16, fp32 residual add, fp32 store).
 //
-// Large-M kernel: 256x256x64 tiles staged through double-buffered LDS by
-// direct-to-LDS loads with a 16-byte XOR swizzle, one
-// v_mfma_f32_32x32x16_bf16 per 32x32 block and 16-deep k substep; eight waves
-// in two groups that alternate load and compute phases.  The MFMA
+// Large-M kernel: 256x256x64 tiles staged through double-buffered LDS (each
+// buffer split into its two 32-deep k halves) by direct-to-LDS loads with a
+// 16-byte XOR swizzle, one v_mfma_f32_32x32x16_bf16 per 32x32 block and
+// 16-deep k substep; eight waves in two groups that alternate load and
+// compute phases.  The MFMA
 // A operand is the weight tile and the B operand the activation tile, so a
 // lane's accumulator holds one activation row and runs of 4 consecutive
 // output columns (vector stores in the epilogue).  Workgroup ids are remapped
@@ -30,6 +31,12 @@ constexpr int BK = 64;
 // 0-15 of a fragment read) land in 16 distinct 16-byte bank groups.
 DEV int swz_key(int row) { return (row >> 1) & 7; }
 DEV int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 3); }
+
+// LDS half tile [rows][32 bf16] (one 32-deep k half of a 64-deep k-tile):
+// chunk c (0..3) of row r is stored in slot c ^ ((r / 4) % 4), so the 16
+// rows of one ds_read_b128 phase land in 16 distinct 16-byte bank groups.
+constexpr int HK = BK / 2;
+DEV int hswz(int row, int chunk) { return row * HK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
 DEV const bf16 *wrow(const GemmArgs &g, int n) {
   if (n < g.n1) return (const bf16 *)g.W0 + (long long)n * g.ldw;
@@ -156,6 +163,29 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
 
 #define GLOBAL_PTR(p) ((const void __attribute__((address_space(1))) *)(p))
 #define LDS_PTR(p) ((void __attribute__((address_space(3))) *)(p))
+
+// global_load_lds_dwordx4 issued from inline asm: 16 bytes per lane from the
+// lane's address p into LDS at lds + 16 lane (lds wave-uniform; the LDS
+// address goes in M0, which the asm saves and restores).  The compiler does
+// not see this load, so it adds no wait for it: the caller orders every LDS
+// read of the target after an explicit vmcnt wait (and a barrier, for the
+// other waves' loads).  It writes no register, so nothing the compiler
+// reuses can be overwritten while it is in flight.
+DEV void dma16(const void *p, const void *lds) {
+  const unsigned l = (unsigned)(unsigned long)LDS_PTR(lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(p), "s"(l)
+      : "memory");
+}
+
+template <int N>
+DEV void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Tile origin of this workgroup.  XCD-aware remap: the hardware hands
 // workgroup ids to the 8 XCDs round robin; give each XCD a contiguous range
@@ -372,15 +402,14 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
 // rows 128 q .. 128 q + 127 of the 256x256 tile, wave w of a group columns
 // 64 w .. 64 w + 63 (for QKV: rows 64 (w / 2) .. and columns 128 (w % 2) ..
 // of the group's half).  The groups alternate between a load phase (the LDS ->
-// register reads of two 16-deep substeps) and a compute phase (their 16
-// MFMAs), group 1 one phase behind group 0, so each SIMD's matrix core runs
-// one group's compute phase while the other group loads.  Every phase ends
-// at a workgroup barrier, and a load phase's reads have completed before it.
-// Each group streams half of every k-tile into LDS by DMA.  Both issue their
-// half of k-tile t+1 in their first load phase of k-tile t, after its reads
-// (the target buffer was last read two phases earlier), and both wait for it
-// three phases later: group 0 after its last compute phase of k-tile t,
-// group 1 before the barrier that ends its last load phase.
+// register reads of the two 16-deep substeps of a 32-deep k half) and a
+// compute phase (their MFMAs), group 1 one phase behind group 0, so each
+// SIMD's matrix core runs one group's compute phase while the other group
+// loads.  Every phase ends at a workgroup barrier, and a load phase's reads
+// have completed before it.  Each k-tile's buffer is two LDS objects, one per
+// k half, so a half can be refilled as soon as both groups have read it; the
+// direct-to-LDS loads that refill them are issued between the MFMAs of the
+// compute phases (the schedule is spelled out in the kernel).
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   if constexpr (EPI == EPI_F32) {
@@ -400,11 +429,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   constexpr bool WIDE = EPI == EPI_QKV || BN == 192;
   constexpr int NW = 8, WM = WIDE ? BM / 4 : BM / 2, WN = WIDE ? BN / 2 : BN / 4;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int PA = BM / 8 / NW, PB = BN / 8 / NW;  // 1 KB direct-to-LDS loads per wave per k-tile
-  // One LDS object per buffer, so the compiler can tell a DMA into one
-  // buffer from reads of the other and adds no wait for it.
-  __shared__ bf16 sa0[BM * BK], sa1[BM * BK];
-  __shared__ bf16 sb0[BN * BK], sb1[BN * BK];
+  // Each of the two buffers is two LDS objects, one per 32-deep k half
+  // (A rows 0 .. BM-1, then B rows, 64 bytes a row).  The loads that fill
+  // them are issued from inline asm (dma16), which the compiler does not
+  // track: it adds no wait for them, and the schedule below places every
+  // wait itself.
+  constexpr int HR = BM + BN;
+  __shared__ bf16 h00[HR * HK], h01[HR * HK], h10[HR * HK], h11[HR * HK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
@@ -416,47 +447,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   constexpr bool LOGITS = EPI == EPI_LOGITS || EPI == EPI_LOSS || EPI == EPI_LOGITS_BF16;
   tile_origin<BM, BN, LOGITS ? 2 : 4>(g, m0, n0);
 
-  // Direct global->LDS loads (global_load_lds_dwordx4): one instruction of a
-  // wave fills 1 KB of LDS = 8 rows of 64 bf16, lane i landing at row i/8,
-  // 16-byte slot i%8.  The slot holds logical k-chunk (i%8) ^ swz_key(row),
-  // so the lane loads that chunk: the XOR swizzle costs nothing.
-  // Instruction p of wave w fills rows (8 p + w) * 8 .. +8 of the tile;
-  // 8-row groups never straddle a weight segment (segment boundaries are
-  // multiples of 128), so the row base is wave-uniform and a lane keeps a
-  // 32-bit offset.
-  const int lr = lane >> 3;
-  int aoff[PA], boff[PB];
-  const bf16 *bbase[PB];
-#pragma unroll
-  for (int p = 0; p < PA; ++p) {
-    const int lrow = (NW * p + wave) * 8 + lr;
-    const int r = min(m0 + lrow, g.M - 1);
-    aoff[p] = r * (int)g.lda + (((lane & 7) ^ swz_key(lrow)) << 3);
-  }
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const int nb = min(n0 + (NW * p + wave) * 8, g.N - 8);
-    const bf16 *base;
-    int first;
-    if (nb < g.n1) { base = (const bf16 *)g.W0; first = 0; }
-    else if (nb < g.n2) { base = (const bf16 *)g.W1; first = g.n1; }
-    else { base = (const bf16 *)g.W2; first = g.n2; }
-    bbase[p] = base;
-    const int lrow = (NW * p + wave) * 8 + lr;
-    boff[p] = (nb - first + lr) * (int)g.ldw + (((lane & 7) ^ swz_key(lrow)) << 3);
-  }
-  const bf16 *abase = (const bf16 *)g.A;
-  auto dma = [&](int kt, bf16 *As, bf16 *Bs) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p)
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(abase + aoff[p] + kt * BK),
-                                       LDS_PTR(&As[(NW * p + wave) * 8 * BK]), 16, 0, 0);
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(bbase[p] + boff[p] + kt * BK),
-                                       LDS_PTR(&Bs[(NW * p + wave) * 8 * BK]), 16, 0, 0);
-  };
-
   f32x16 acc[TN][TM];
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -466,21 +456,36 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   const int KT = g.K / BK;
   const int c32 = lane & 31, hi = lane >> 5;
   bf16x8 fa[2][TM], fb[2][TN];
-  auto lfrag = [&](int f, const bf16 *As, const bf16 *Bs, int s) {
+  // Fragments of the two 16-deep substeps of a k half.
+  auto lfrag = [&](const bf16 *H) {
 #pragma unroll
-    for (int j = 0; j < TM; ++j) fa[f][j] = *(const bf16x8 *)&As[swz(wm * WM + 32 * j + c32, 2 * s + hi)];
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i) fb[f][i] = *(const bf16x8 *)&Bs[swz(wn * WN + 32 * i + c32, 2 * s + hi)];
+      for (int j = 0; j < TM; ++j) fa[s][j] = *(const bf16x8 *)&H[hswz(wm * WM + 32 * j + c32, 2 * s + hi)];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) fb[s][i] = *(const bf16x8 *)&H[hswz(BM + wn * WN + 32 * i + c32, 2 * s + hi)];
+    }
   };
-  auto compute = [&]() {
+  // A compute phase: 2 TN TM MFMAs (16, or 12 for 64x96 wave tiles), with
+  // load(q), q = 0..3, issued after every fourth (third), while the other
+  // group reads fragments and issues none.
+  auto compute = [&](auto load) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
+        for (int j = 0; j < TM; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][i], fa[f][j], acc[i][j], 0, 0, 0);
+          constexpr int per = 2 * TN * TM / (BM / 64);
+          const int idx = (f * TN + i) * TM + j;
+          if (idx % per == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(idx / per);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -489,62 +494,128 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     __asm__ volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Waits the compiler sees (a vmcnt(0) in inline asm would leave its own
-  // tracking of the DMA in flight): vmcnt(0), and lgkmcnt(0).
-  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  // lgkmcnt(0): a load phase's fragment reads have landed
   auto wait_lds = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); };
-  // Where the compiler cannot tell which group runs, it adds a vmcnt(0)
-  // before a load phase; both groups have waited for their DMA by then.
-  auto ktile = [&](int kt, const bf16 *As, const bf16 *Bs, bf16 *nAs, bf16 *nBs) {
-    lfrag(0, As, Bs, 0);
-    lfrag(1, As, Bs, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < KT) dma(kt + 1, nAs, nBs);
-    wait_lds();
-    bar();
-    compute();
-    bar();
-    lfrag(0, As, Bs, 2);
-    lfrag(1, As, Bs, 3);
-    wait_lds();
-    if (grp == 1) wait_dma();
-    bar();
-    compute();
-    if (grp == 0) wait_dma();
-    // group 1's last compute phase ends the kernel's barriers
-    if (!(grp == 1 && kt == KT - 1)) bar();
+
+  // Group 0 streams the A rows of every k half into LDS, group 1 the B rows,
+  // by direct global->LDS loads (global_load_lds_dwordx4): one instruction
+  // of a wave fills 1 KB = 16 rows of a half, lane i landing at row i/4,
+  // 16-byte slot i%4, which holds logical chunk (i%4) ^ (i/16): the lane
+  // loads that chunk, so the swizzle costs nothing.  Instruction p of wave
+  // w (0..3 in its group) fills rows 16 (w + 4 p) .. +16 of its operand;
+  // with 192-row B tiles the last instruction of each wave repeats the last
+  // 16 rows (same bytes to the same place), so that every wave issues the
+  // same number.  16-row groups never straddle a weight segment (boundaries are
+  // multiples of 128; N is a multiple of 128, so a clamped group is wholly
+  // past N).
+  //
+  // Schedule.  Phases p0..p3 of k-tile t: group 0 loads fragments of half 0
+  // (p0), computes (p1), loads half 1 (p2), computes (p3); group 1 runs one
+  // phase behind.  Half 0 of buffer t%2 is free once both groups have read
+  // it (end of p1), half 1 at the end of p3.  A load instruction blocks the
+  // wave that issues it until the CU accepts it (about 64 bytes a clock), so
+  // the loads go into the compute phases, between MFMAs, where the other
+  // group issues none: each group fills half 1 of k-tile t+1 in its first
+  // compute phase of k-tile t and half 0 of k-tile t+2 in its second (a
+  // quarter of a k-tile, 16 KB, per phase).  Each wave waits for its own
+  // loads in its load phases, before the barrier that ends them: for half 1
+  // of k-tile t in its first of k-tile t, for half 0 of k-tile t+1 in its
+  // second, three phases after issuing them, with the loads of the phase in
+  // between still in flight.
+  constexpr int NI = BM / 64;  // 1 KB loads per wave per half
+  static_assert(BN / 64 <= NI && BN % 16 == 0, "B rows per wave");
+  static_assert((2 * TN * TM) % NI == 0, "loads spread evenly over a compute phase's MFMAs");
+  const int w4 = wave & 3, lrow = lane >> 2;
+  const int lc8 = ((lane & 3) ^ (lane >> 4)) << 3;
+  int off[NI], drow[NI];
+  const bf16 *base[NI];
+#pragma unroll
+  for (int p = 0; p < NI; ++p) {
+    if (grp == 0) {
+      const int row = 16 * (w4 + 4 * p);
+      drow[p] = row;
+      base[p] = (const bf16 *)g.A;
+      off[p] = min(m0 + row + lrow, g.M - 1) * (int)g.lda + lc8;
+    } else {
+      const int row = min(16 * (w4 + 4 * p), BN - 16);
+      drow[p] = BM + row;
+      const int nb = min(n0 + row, g.N - 16);
+      int first;
+      if (nb < g.n1) { base[p] = (const bf16 *)g.W0; first = 0; }
+      else if (nb < g.n2) { base[p] = (const bf16 *)g.W1; first = g.n1; }
+      else { base[p] = (const bf16 *)g.W2; first = g.n2; }
+      off[p] = (nb - first + lrow) * (int)g.ldw + lc8;
+    }
+  }
+  auto dma1 = [&](int p, int kt, int half, bf16 *H) {
+    dma16(base[p] + off[p] + kt * BK + half * HK, &H[drow[p] * HK]);
   };
-  dma(0, sa0, sb0);
-  wait_dma();
+  auto dma = [&](int kt, int half, bf16 *H) {
+#pragma unroll
+    for (int p = 0; p < NI; ++p) dma1(p, kt, half, H);
+  };
+  // One k-tile: c0, c1 its halves; n1 the half 1 of the other buffer.
+  // D1: k-tile t+1 exists; D0: k-tile t+2 exists.  STEADY: both, known at
+  // compile time; otherwise tested (the last two or three k-tiles).
+  auto ktile = [&](auto steady, int kt, bf16 *c0, bf16 *c1, bf16 *n1) {
+    constexpr bool STEADY = decltype(steady)::value;
+    const bool D1 = STEADY || kt + 1 < KT, D0 = STEADY || kt + 2 < KT;
+    lfrag(c0);
+    wait_lds();
+    if (D1) wait_vm<NI>();  // half 1 of k-tile t (half 0 of t+1 may be in flight)
+    else wait_vm<0>();
+    bar();
+    compute([&](int q) {
+      if (D1) dma1(q, kt + 1, 1, n1);
+    });
+    bar();
+    lfrag(c1);
+    wait_lds();
+    if (D1) wait_vm<NI>();  // half 0 of k-tile t+1 (half 1 of t+1 may be in flight)
+    bar();
+    compute([&](int q) {
+      if (D0) dma1(q, kt + 2, 0, c0);
+    });
+    // group 1's last compute phase ends the kernel's barriers
+    if (D1 || grp == 0) bar();
+  };
+  // Prologue: half 0 and half 1 of k-tile 0, half 0 of k-tile 1; wait for
+  // the first.  Group 1 then starts one phase behind.
+  dma(0, 0, h00);
+  dma(0, 1, h01);
+  if (KT > 1) {
+    dma(1, 0, h10);
+    wait_vm<2 * NI>();
+  } else {
+    wait_vm<NI>();
+  }
   bar();
   if (grp == 1) bar();
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    ktile(kt, sa0, sb0, sa1, sb1);
-    ktile(kt + 1, sa1, sb1, sa0, sb0);
+  for (; kt + 3 < KT; kt += 2) {
+    ktile(std::true_type{}, kt, h00, h01, h11);
+    ktile(std::true_type{}, kt + 1, h10, h11, h01);
   }
-  if (kt < KT) ktile(kt, sa0, sb0, sa1, sb1);
-  // Staging areas: 32 x 68 floats per wave, two waves per 32 KB buffer.  A
+  for (; kt + 1 < KT; kt += 2) {
+    ktile(std::false_type{}, kt, h00, h01, h11);
+    ktile(std::false_type{}, kt + 1, h10, h11, h01);
+  }
+  if (kt < KT) ktile(std::false_type{}, kt, h00, h01, h11);
+  // Staging areas: 32 x 68 floats per wave, two waves per half object.  A
   // group reaches its epilogue only after both groups' last LDS reads
   // (group 0 after the barrier that ends group 1's last load phase), and no
   // DMA is in flight by then.
-  static_assert(2 * 32 * kStagePitch * 4 <= BM * BK * 2 && 2 * 32 * kStagePitch * 4 <= BN * BK * 2,
-                "staging area");
+  static_assert(2 * 32 * kStagePitch * 4 <= HR * HK * 2, "staging area");
   if constexpr (EPI == EPI_QKV) {
     tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
   } else {
-    bf16 *const sbuf = wave < 2 ? sa0 : wave < 4 ? sa1 : wave < 6 ? sb0 : sb1;
+    bf16 *const sbuf = wave < 2 ? h00 : wave < 4 ? h01 : wave < 6 ? h10 : h11;
     float *stg = (float *)sbuf + (wave & 1) * 32 * kStagePitch;
     tile_epilogue_staged<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, stg);
   }
 }
 
 // ------------------------------------------------------------------ decode rows
-
-template <int N>
-DEV void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Wait until at most min(ahead, MAXA) chunks of NI loads each are in flight.
 template <int NI, int MAXA>
