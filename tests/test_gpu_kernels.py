@@ -19,6 +19,13 @@ GEMM_SHAPES = [
     (513, 1920, 1664),
     # residual add on 192-column tiles (N = 768, 1152, 384), ragged M
     (700, 768, 3072),
+    # 1, 2, 4 and 5 k-tiles of 64: every way the k loop can end (its
+    # two-k-tile steady state, the tested tail pair, the last single
+    # k-tile); N = 768 and 384 also take 192-column tiles for epilogues 2, 3
+    (300, 256, 64),
+    (520, 512, 128),
+    (600, 768, 256),
+    (260, 384, 320),
     # decode-row kernel (M <= 64): 1, 2, 3 and 4 row blocks, ragged M; 32-column
     # tiles where 64-column ones would number fewer than 128
     (1, 128, 64),
