@@ -73,13 +73,28 @@ DEV void epi_store4(const GemmArgs &g, int m, int n, float v0, float v1, float v
 // angle of their position, then divided by their RMS over the head (the
 // partner lane l ^ 32 holds the other 64 columns), and stored as bf16; v is
 // stored transposed for the attention kernels.
+//
+// q and k go through the wave's 16 KB of LDS (stg), 32 rows at a time, so
+// that every global access covers whole rows: the block's cos and sin table
+// rows are loaded 4 rows (1 KB) per instruction and each lane reads its own
+// values from LDS; the rotated, normalised rows are written to LDS and read
+// back so that 16 lanes store a row's 128 values (256 bytes) together.  Read
+// per lane instead, each instruction touched 32 rows.  LDS rows are 16
+// chunks of 16 bytes, chunk x of row r stored at x ^ (r % 16), so the 16
+// lanes of one ds_read_b128 phase (16 rows, one chunk) hit 16 bank groups.
+// A wave's LDS operations run in order, so each reuse of the area needs no
+// wait.  Row data of another lane (its position, sequence, cache row) comes
+// by shuffle from the lane that holds that row.
 template <int TM>
-DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int c32, int hi) {
+DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int c32, int hi, int lane,
+                 float *stg) {
   const QkvEpi &e = g.qkv;
   const int head = nw0 / 128;
   const bool is_q = head < e.H, is_k = !is_q && head < e.H + e.Hkv;
   const int kvh = is_q ? 0 : (is_k ? head - e.H : head - e.H - e.Hkv);
   const int kvd = e.Hkv * 128;
+  const int srow = lane >> 4, sch = lane & 15;  // staged access: row 4 k + srow, chunk sch
+  auto sidx = [](int r, int x) { return 64 * r + 4 * (x ^ (r & 15)); };  // float index of chunk x
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     __builtin_amdgcn_sched_barrier(0);  // one row block at a time (register pressure)
@@ -112,13 +127,26 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
       continue;
     }
     if (e.cos) {
+      // this block's table rows: row r = 4 k + srow, float4 chunk sch
+      float4 tc[8], ts[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pr = __shfl(p, 4 * k + srow, 64);
+        tc[k] = *(const float4 *)(e.cos + (long long)pr * 64 + 4 * sch);
+        ts[k] = *(const float4 *)(e.sin + (long long)pr * 64 + 4 * sch);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        *(float4 *)&stg[sidx(4 * k + srow, sch)] = tc[k];
+        *(float4 *)&stg[2048 + sidx(4 * k + srow, sch)] = ts[k];
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int pi = 32 * i + 8 * c + 4 * hi;
-          const float4 cs = *(const float4 *)(e.cos + (long long)p * 64 + pi);
-          const float4 sn = *(const float4 *)(e.sin + (long long)p * 64 + pi);
+          const int x = 8 * i + 2 * c + hi;  // chunk of angles 32 i + 8 c + 4 hi .. +4
+          const float4 cs = *(const float4 *)&stg[sidx(c32, x)];
+          const float4 sn = *(const float4 *)&stg[2048 + sidx(c32, x)];
           const float cc[4] = {cs.x, cs.y, cs.z, cs.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -138,26 +166,42 @@ DEV void epi_qkv(const GemmArgs &g, f32x16 (&acc)[4][TM], int mw0, int nw0, int 
       ssum += __shfl_xor(ssum, 32, 64);
       rs = 1.0f / sqrtf(ssum * (1.0f / 128.0f) + e.eps);
     }
-    if (m >= g.M) continue;
-    bf16 *dst = is_q ? e.q_out + (long long)m * e.H * 128 + head * 128
-                     : (e.k_out ? e.k_out + (long long)m * kvd + kvh * 128 : nullptr);
+    // The row's K cache row (its page and slot), from the lane that holds the row.
     bf16 *ck = nullptr;
-    if (is_k && e.use_cache) {
+    if (is_k && e.use_cache && m < g.M) {
       const int b = e.seq ? e.seq[m] : m;
       const int page = e.kv.table[b * e.kv.pages_per_seq + p / e.kv.page_size];
       ck = (bf16 *)(e.kv.base + (long long)e.layer * e.kv.layer_stride + (long long)page * e.kv.page_stride) +
            (long long)(p % e.kv.page_size) * kvd + kvh * 128;
     }
+    // Stage the row block as bf16: row c32, columns 32 i + 8 c + 4 hi .. +4,
+    // in chunk 4 i + c, half hi.
+    bf16 *sb = (bf16 *)stg;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int col = 32 * i + 8 * c + 4 * hi;
         bf16x4 o = {f2bf(acc[i][j][4 * c] * rs), f2bf(acc[i][j][4 * c + 1] * rs),
                     f2bf(acc[i][j][4 * c + 2] * rs), f2bf(acc[i][j][4 * c + 3] * rs)};
-        if (dst) *(bf16x4 *)(dst + col) = o;
-        if (ck) *(bf16x4 *)(ck + col) = o;
+        *(bf16x4 *)&sb[2 * sidx(c32, 4 * i + c) + 4 * hi] = o;
       }
+    // Store 4 rows per instruction: row r = 4 k + srow, columns 8 sch .. +8.
+    const unsigned long long ckp = (unsigned long long)ck;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + srow;
+      const int mr = mw0 + 32 * j + r;
+      const bf16x8 v = *(const bf16x8 *)&sb[2 * sidx(r, sch)];
+      const unsigned lo = __shfl((unsigned)ckp, r, 64), hi32 = __shfl((unsigned)(ckp >> 32), r, 64);
+      if (mr >= g.M) continue;
+      if (is_q) {
+        *(bf16x8 *)(e.q_out + (long long)mr * e.H * 128 + head * 128 + 8 * sch) = v;
+      } else {
+        if (e.k_out) *(bf16x8 *)(e.k_out + (long long)mr * kvd + kvh * 128 + 8 * sch) = v;
+        bf16 *ckr = (bf16 *)(((unsigned long long)hi32 << 32) | lo);
+        if (ckr) *(bf16x8 *)(ckr + 8 * sch) = v;
+      }
+    }
   }
 }
 
@@ -214,14 +258,14 @@ DEV void tile_origin(const GemmArgs &g, int &m0, int &n0) {
 // row is m0 + wm WM and first column n0 + wn WN.
 template <int TM, int TN, int WM, int WN, int EPI>
 DEV void tile_epilogue(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, int n0, int wm, int wn, int c32,
-                       int hi) {
+                       int hi, int lane, float *stg) {
   // A wave whose columns lie beyond N computed on clamped rows; drop it.
   const bool active = (n0 + wn * WN) < g.N;
   if (!active) return;
   const int nw0 = n0 + wn * WN;  // first column of this wave (multiple of WN)
   if constexpr (EPI == EPI_QKV) {
     static_assert(WN == 128, "the QKV epilogue needs one head per wave");
-    epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi);
+    epi_qkv<TM>(g, acc, m0 + wm * WM, nw0, c32, hi, lane, stg);
     return;
   } else {
 #pragma unroll
@@ -606,10 +650,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   // (group 0 after the barrier that ends group 1's last load phase), and no
   // DMA is in flight by then.
   static_assert(2 * 32 * kStagePitch * 4 <= HR * HK * 2, "staging area");
+  bf16 *const sbuf = wave < 2 ? h00 : wave < 4 ? h01 : wave < 6 ? h10 : h11;
   if constexpr (EPI == EPI_QKV) {
-    tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi);
+    // 16 KB per wave: two waves per half object
+    static_assert(2 * 16384 <= HR * HK * 2, "QKV staging area");
+    tile_epilogue<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, (float *)sbuf + (wave & 1) * 4096);
   } else {
-    bf16 *const sbuf = wave < 2 ? h00 : wave < 4 ? h01 : wave < 6 ? h10 : h11;
     float *stg = (float *)sbuf + (wave & 1) * 32 * kStagePitch;
     tile_epilogue_staged<TM, TN, WM, WN, EPI>(g, acc, m0, n0, wm, wn, c32, hi, lane, stg);
   }
