@@ -495,10 +495,37 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
     dma_cols(sqt, qtb, a.ldt, col0 + tt * KT, wave, NWV, lane);
     dma_cols(sdot, otb, a.ldt, col0 + tt * KT, wave, NWV, lane);
   };
+  // The wave's u-th load of tile tt (u < 16): instruction j = wave + 4 (u % 4)
+  // of Q, dO, Q^T, dO^T in turn, as dma() issues them.
+  static_assert(NWV == 4, "four loads of each operand per wave");
+  auto dma1 = [&](int u, int tt, bf16 *sq, bf16 *sdo, bf16 *sqt, bf16 *sdot) {
+    const int j = wave + NWV * (u & 3), op = u >> 2;
+    if (op < 2) {
+      const int row = 4 * j + (lane >> 4), pc = lane & 15;
+      const int src = min(tt * KT + row, len - 1);
+      const bf16 *base = op == 0 ? qbase : obase;
+      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(base + (long long)src * H * DH + ((pc ^ (row & 15)) << 3)),
+                                       LDS_PTR(&(op == 0 ? sq : sdo)[j * 512]), 16, 0, 0);
+    } else {
+      const int dim = 8 * j + (lane >> 3), pc = lane & 7;
+      const bf16 *base = op == 2 ? qtb : otb;
+      __builtin_amdgcn_global_load_lds(
+          GLOBAL_PTR(base + (long long)dim * a.ldt + col0 + tt * KT + ((pc ^ ((dim >> 1) & 7)) << 3)),
+          LDS_PTR(&(op == 2 ? sqt : sdot)[j * 512]), 16, 0, 0);
+    }
+  };
+  // One tile; load(u), u < 16, issues the wave's loads of the next tile.  With
+  // one wave per SIMD, a burst of load instructions at the start of a tile
+  // (each blocks the wave until the CU accepts it) would leave the matrix core
+  // idle, so they go one after each pair of S^T / dP^T MFMAs.
   auto tile = [&](int tt, const bf16 *sq, const bf16 *sdo, const bf16 *sqt, const bf16 *sdot, const float *sl,
-                  const float *sd) {
+                  const float *sd, auto load) {
     // the tile reaches this wave's keys (positions >= key), and the wave has keys
-    if (!(tt * KT + KT - 1 >= kw && kw < len)) return;
+    if (!(tt * KT + KT - 1 >= kw && kw < len)) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) load(u);
+      return;
+    }
     f32x16 sacc[2], dpacc[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
@@ -510,6 +537,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
         const bf16x8 oa = *(const bf16x8 *)&sdo[kidx(32 * pb + c32, 2 * s + g)];
         sacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc[pb], 0, 0, 0);
         dpacc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc[pb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(8 * pb + s);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // lane (key, g): positions 32 pb + 8 (e/4) + 4 g + e%4 of the tile; the
@@ -557,12 +587,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdMfmaArgs a) {
   auto step = [&](int tt, const bf16 *sq, const bf16 *sdo, const bf16 *sqt, const bf16 *sdot, const float *sl,
                   const float *sd, bf16 *nq, bf16 *ndo, bf16 *nqt, bf16 *ndot, float *nsl, float *nsd) {
     const bool more = tt + 1 <= t_end;
-    if (more) {
-      dma(tt + 1, nq, ndo, nqt, ndot);
-      fetch_ld(tt + 1);
-    }
+    if (more) fetch_ld(tt + 1);
     __builtin_amdgcn_sched_barrier(0);
-    tile(tt, sq, sdo, sqt, sdot, sl, sd);
+    tile(tt, sq, sdo, sqt, sdot, sl, sd, [&](int u) {
+      if (more) dma1(u, tt + 1, nq, ndo, nqt, ndot);
+    });
     if (more) put_ld(nsl, nsd);
     land();
   };
