@@ -53,6 +53,36 @@ def prof_read(B, names):
     return out
 
 
+def gemm_by_shape(B, model, M):
+    """Per-shape figures of the prefill GEMMs recorded since the last
+    profile enable: each launch of the block-GEMM and LM-head classes is
+    matched to the named product whose algorithmic flops and bytes it has
+    (W1 and W2 have the same flops and differ in bytes)."""
+    d, H, Hkv, F, V = model.d_model, model.n_head, model.n_kv_head, model.d_ff, model.vocab
+    dims = {"qkv": ((H + 2 * Hkv) * model.head_dim, d, 2), "o": (d, H * model.head_dim, 8),
+            "w1": (F, d, 2), "w2": (d, F, 8), "lm_head": (V, d, 4)}  # N, K, output bytes per element
+    expect = {n: (2.0 * M * N * K, 2.0 * (M * K + N * K) + ob * M * N) for n, (N, K, ob) in dims.items()}
+    out = {}
+    for cls in ("gemm", "lmhead"):
+        c = B.PROF_CLASSES[cls]
+        for i in range(B.gpt_profile_read(c)["launches"]):
+            r = B.gpt_profile_read_launch(c, i)
+            name = min(expect, key=lambda n: abs(expect[n][0] - r["flops"]) / expect[n][0] +
+                       abs(expect[n][1] - r["bytes"]) / expect[n][1])
+            acc = out.setdefault(name, {"M": M, "N": dims[name][0], "K": dims[name][1], "launches": 0,
+                                        "ms": 0.0, "flops": 0.0})
+            acc["launches"] += 1
+            acc["ms"] += r["ms"]
+            acc["flops"] += r["flops"]
+    for acc in out.values():
+        tfs = acc["flops"] / (acc["ms"] * 1e-3) / 1e12
+        acc["us_per_launch"] = round(acc.pop("ms") * 1e3 / acc["launches"], 2)
+        acc.pop("flops")
+        acc["achieved_tflops"] = round(tfs, 1)
+        acc["frac"] = round(tfs / PEAK_BF16_TFLOPS, 4)
+    return out
+
+
 def bench_prefill(B, torch, dm, w, steps, warmup, prof_mask=0):
     """Time `steps` prefills with nothing else in the timed region, then run
     the same `steps` again with the library's HIP-event timing enabled for
@@ -658,7 +688,8 @@ def main():
                 "frac": round(gemm_tfs / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 2),
                 "flops_per_launch": g["flops"] / max(g["launches"], 1),
-                "algorithmic_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1), 0)}
+                "algorithmic_bytes_per_launch": round(g["bytes"] / max(g["launches"], 1), 0),
+                "by_shape": gemm_by_shape(B, w2.model, M)}
     breakdown = {
         "gemm_ms_per_step": round(g["ms"] / args.steps, 3),
         "attention": {"ms_per_step": round(attn["ms"] / args.steps, 3),

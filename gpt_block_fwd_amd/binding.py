@@ -29,7 +29,7 @@ EXPORTS = ("gpt_last_error", "rope_tables", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_lengths", "gpt_workspace_bytes", "gpt_prefill", "gpt_prefill_loss",
            "gpt_decode_step", "gpt_decode_step_noalloc",
            "gpt_select_tokens", "gpt_train_workspace_bytes", "gpt_loss_grads", "gpt_adam_step",
-           "gpt_profile_enable", "gpt_profile_mask", "gpt_profile_read",
+           "gpt_profile_enable", "gpt_profile_mask", "gpt_profile_read", "gpt_profile_read_launch",
            "gpt_debug_gemm", "gpt_debug_attn_prefill")
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.gpt_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double)]
+    L.gpt_profile_read_launch.argtypes = [i32, ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     L.gpt_debug_gemm.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp]
     L.gpt_debug_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
     for name in EXPORTS:
@@ -253,6 +255,12 @@ def gpt_profile_read(cls: int):
     _check(lib().gpt_profile_read(cls, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl),
                                   ctypes.byref(by)))
     return {"ms": ms.value, "launches": n.value, "flops": fl.value, "bytes": by.value}
+
+
+def gpt_profile_read_launch(cls: int, i: int):
+    ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().gpt_profile_read_launch(cls, i, ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)))
+    return {"ms": ms.value, "flops": fl.value, "bytes": by.value}
 
 
 def gpt_debug_gemm(A, W, M: int, N: int, K: int, C, epi: int, ksplit: int = 1, stream=None):

@@ -1616,4 +1616,21 @@ gpt_status gpt_profile_read(int32_t cls, double *ms, int64_t *launches, double *
   return GPT_OK;
 }
 
+gpt_status gpt_profile_read_launch(int32_t cls, int64_t i, double *ms, double *flops, double *bytes) {
+  if (cls < 0 || cls >= GPT_PROF_NCLASSES) return fail(GPT_ERR_ARG, "bad class");
+  if (i < 0) return fail(GPT_ERR_ARG, "negative launch index");
+  int64_t n = 0;
+  for (auto &r : g_prof.recs) {
+    if (r.cls != cls || n++ != i) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return hip_check("profile sync");
+    float t = 0;
+    hipEventElapsedTime(&t, r.a, r.b);
+    if (ms) *ms = t;
+    if (flops) *flops = r.flops;
+    if (bytes) *bytes = r.bytes;
+    return GPT_OK;
+  }
+  return fail(GPT_ERR_ARG, "launch %lld of class %d not recorded (%lld are)", (long long)i, (int)cls, (long long)n);
+}
+
 }  // extern "C"

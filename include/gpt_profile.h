@@ -47,6 +47,13 @@ gpt_status gpt_profile_mask(uint32_t mask);
 gpt_status gpt_profile_read(int32_t cls, double *ms, int64_t *launches, double *flops,
                             double *bytes);
 
+/* The launch with index i (0-based, in launch order) among those of class
+ * cls recorded since the last enable: its kernel time in milliseconds and
+ * its algorithmic flops and bytes, so that launches of different shapes can
+ * be told apart.  NULL outputs are skipped.  GPT_ERR_ARG for a bad class, or
+ * when fewer than i + 1 launches of the class are recorded. */
+gpt_status gpt_profile_read_launch(int32_t cls, int64_t i, double *ms, double *flops, double *bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,3 +84,35 @@ def test_traffic_summary_scales_by_the_known_copies(tmp_path):
     assert t["fetch"]["launches"] == 49 and t["write"]["launches"] == 49
     assert t["bytes_per_launch"] == pytest.approx((1000.0 * 2.0 + 300.0) * 1024.0)
     assert t["gemm_sources_sha256"] == bench.gemm_source_hash()
+
+
+class _FakeProfile:
+    """Stands in for the binding's profile reads with given launch records."""
+    PROF_CLASSES = {"gemm": 0, "lmhead": 1}
+
+    def __init__(self, recs):
+        self.recs = recs
+
+    def gpt_profile_read(self, cls):
+        return {"launches": len(self.recs[cls])}
+
+    def gpt_profile_read_launch(self, cls, i):
+        return self.recs[cls][i]
+
+
+def test_gemm_by_shape_tells_the_prefill_products_apart():
+    """Depth-12 launches in layer order, twice, then the LM head: each is named
+    by its flops and bytes (W1 and W2 differ only in bytes), and a shape's
+    TFLOP/s is its flops over its summed time."""
+    m, M = wl.depth_model(12), 16384
+
+    def rec(N, K, out_b, ms):
+        return {"ms": ms, "flops": 2.0 * M * N * K, "bytes": 2.0 * (M * K + N * K) + out_b * M * N}
+    layer = [rec(1024, 768, 2, 0.040), rec(768, 768, 8, 0.030), rec(3072, 768, 2, 0.080), rec(768, 3072, 8, 0.090)]
+    shapes = bench.gemm_by_shape(_FakeProfile({0: layer * 2, 1: [rec(65536, 768, 4, 2.0)]}), m, M)
+    assert set(shapes) == {"qkv", "o", "w1", "w2", "lm_head"}
+    assert (shapes["w1"]["N"], shapes["w1"]["K"]) == (3072, 768)
+    assert (shapes["w2"]["N"], shapes["w2"]["K"]) == (768, 3072)
+    assert shapes["w2"]["launches"] == 2 and shapes["w2"]["us_per_launch"] == pytest.approx(90.0)
+    assert shapes["lm_head"]["achieved_tflops"] == pytest.approx(2.0 * M * 65536 * 768 / 2e-3 / 1e12, rel=1e-3)
+    assert shapes["o"]["frac"] == pytest.approx(2.0 * M * 768 * 768 / 30e-6 / 1e12 / 2500.0, rel=1e-3)
