@@ -294,12 +294,24 @@ GEMM_SOURCES = ["gpt_block_fwd_amd/csrc/gemm.hip", "gpt_block_fwd_amd/csrc/kerne
 COPY_BYTES = 1 << 30
 
 
+def code_tokens(text):
+    """C++/HIP source without its comments and with whitespace collapsed, so
+    that an edit to comments or layout leaves the code's identity unchanged.
+    (No source hashed here has comment markers inside string literals.)"""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_source_hash():
+    """Identity of the GEMM kernels' code (comments and layout excluded): the
+    traffic figure is reported only for the code it was measured on."""
     import hashlib
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -6,12 +6,11 @@
 // buffer split into its two 32-deep k halves) by direct-to-LDS loads with a
 // 16-byte XOR swizzle, one v_mfma_f32_32x32x16_bf16 per 32x32 block and
 // 16-deep k substep; eight waves in two groups that alternate load and
-// compute phases.  The MFMA
-// A operand is the weight tile and the B operand the activation tile, so a
-// lane's accumulator holds one activation row and runs of 4 consecutive
-// output columns (vector stores in the epilogue).  Workgroup ids are remapped
-// so consecutive tiles share an XCD (8 XCDs, round-robin dispatch) and
-// grouped a few tile-rows at a time for L2 reuse.
+// compute phases.  The MFMA A operand is the weight tile and the B operand
+// the activation tile, so a lane's accumulator holds one activation row and
+// runs of 4 consecutive output columns (vector stores in the epilogue).
+// Workgroup ids are remapped so consecutive tiles share an XCD (8 XCDs,
+// round-robin dispatch) and grouped a few tile-rows at a time for L2 reuse.
 //
 // Decode-row kernel (M <= 64): one workgroup per 64 output columns (and k
 // range, when k is split), weight and activation chunks staged through a
@@ -26,9 +25,10 @@ namespace {
 
 constexpr int BK = 64;
 
-// LDS tile [rows][64 bf16]: 16-byte chunk c of row r is stored in slot
-// c ^ ((r / 2) % 8), so the 16 rows one ds_read_b128 phase touches (lanes
-// 0-15 of a fragment read) land in 16 distinct 16-byte bank groups.
+// LDS tile [rows][64 bf16] (decode-row kernel): 16-byte chunk c of row r is
+// stored in slot c ^ ((r / 2) % 8), so the 16 rows one ds_read_b128 phase
+// touches (lanes 0-15 of a fragment read) land in 16 distinct 16-byte bank
+// groups.
 DEV int swz_key(int row) { return (row >> 1) & 7; }
 DEV int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 3); }
 

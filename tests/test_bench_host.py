@@ -116,3 +116,11 @@ def test_gemm_by_shape_tells_the_prefill_products_apart():
     assert shapes["w2"]["launches"] == 2 and shapes["w2"]["us_per_launch"] == pytest.approx(90.0)
     assert shapes["lm_head"]["achieved_tflops"] == pytest.approx(2.0 * M * 65536 * 768 / 2e-3 / 1e12, rel=1e-3)
     assert shapes["o"]["frac"] == pytest.approx(2.0 * M * 768 * 768 / 30e-6 / 1e12 / 2500.0, rel=1e-3)
+
+
+def test_code_identity_ignores_comments_and_layout_only():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* result */\n}\n"
+    b = "// a new header comment\nint f(int x)\n{\n    return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_tokens(a) == bench.code_tokens(b)
+    assert bench.code_tokens(a) != bench.code_tokens(c)
