@@ -236,10 +236,9 @@ DEV void wait_vm() {
 // of logical tiles, then walk them GROUP_M tile-rows at a time (column by
 // column within a group) for L2 reuse.
 template <int BM, int BN, int GROUP_M>
-DEV void tile_origin(const GemmArgs &g, int &m0, int &n0) {
+DEV void tile_origin(const GemmArgs &g, int pid, int &m0, int &n0) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
   {
     const int xcd = pid & 7, idx = pid >> 3;
     const int per_lo = ntiles >> 3, rem = ntiles & 7;
@@ -442,6 +441,72 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
   }
 }
 
+// LM-head epilogue of the persistent kernel (128x64 wave tiles): the same
+// (max, sum exp) partials and logits stores (EPI_LOGITS) or target logits
+// (EPI_LOSS) as tile_epilogue_staged, but staged 16 rows at a time: the next
+// tile's first loads occupy three of the four operand halves, which leaves
+// each wave 8 KB of LDS, and a 16-row block at the conflict-free pitch of 68
+// floats takes 4.25 KB.  In each half of a 32-row block the lanes that hold
+// its rows write them, and the wave reads the block back 4 rows of 64 columns
+// per instruction (every logits store writes whole 128-byte lines).
+//
+// tcol (EPI_LOSS): row 32 j + c32's target column less nw0.
+template <int TM, int EPI>
+DEV void tile_epilogue_lm16(const GemmArgs &g, f32x16 (&acc)[2][TM], int mw0, int nw0, int c32, int hi, int lane,
+                            float *stg, const int (&tcol)[TM]) {
+  static_assert(EPI == EPI_LOGITS || EPI == EPI_LOSS, "LM-head epilogues");
+  if (nw0 >= g.N) return;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = mw0 + 32 * j + c32;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) se += fast_exp2((acc[i][j][r] - mx) * kLog2e);
+    se += __shfl_xor(se, 32, 64);
+    if (m < g.M && hi == 0) {
+      float *pp = g.part + ((long long)m * (g.N / 64) + nw0 / 64) * 2;
+      *(float2 *)pp = make_float2(mx, se);
+    }
+  }
+  const int rr = lane >> 4, cc = 4 * (lane & 15);  // read-back: row 4 q + rr, columns cc .. cc + 3
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((c32 >> 4) == h) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *(f32x4 *)&stg[(c32 & 15) * kStagePitch + 32 * i + 8 * c + 4 * hi] =
+                (f32x4){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+      }
+      if constexpr (EPI == EPI_LOSS) {
+        const int m = mw0 + 32 * j + c32, col = tcol[j];
+        if ((c32 >> 4) == h && hi == 0 && m < g.M && col >= 0 && col < 64)
+          g.tgt[m] = stg[(c32 & 15) * kStagePitch + col];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * q + rr;
+          const f32x4 v = *(const f32x4 *)&stg[r * kStagePitch + cc];
+          const int m = mw0 + 32 * j + 16 * h + r;
+          // nothing in this pass reads the logits again: non-temporal stores
+          if (m < g.M) __builtin_nontemporal_store(v, (f32x4 *)((float *)g.C + (long long)m * g.ldc + nw0 + cc));
+        }
+      }
+    }
+  }
+}
+
 // Eight waves in two groups of four (one wave per SIMD each); group q owns
 // rows 128 q .. 128 q + 127 of the 256x256 tile, wave w of a group columns
 // 64 w .. 64 w + 63 (for QKV: rows 64 (w / 2) .. and columns 128 (w % 2) ..
@@ -454,7 +519,17 @@ DEV void tile_epilogue_staged(const GemmArgs &g, f32x16 (&acc)[TN][TM], int m0, 
 // k half, so a half can be refilled as soon as both groups have read it; the
 // direct-to-LDS loads that refill them are issued between the MFMAs of the
 // compute phases (the schedule is spelled out in the kernel).
-template <int BM, int BN, int EPI>
+//
+// PERS: a persistent grid (one workgroup per CU) walks the tiles, tile
+// blockIdx.x, then + gridDim.x, ...  Between two tiles, each wave issues the
+// next tile's first loads (both halves of k-tile 0, half 0 of k-tile 1) before
+// the epilogue of the current one, which stages through the operand half that
+// those leave free plus 32 KB more.  Loads and stores retire in issue order on
+// one counter, so the next tile's first two waits allow the SN stores younger
+// than the loads they wait for (SN: a lower bound on the epilogue's stores per
+// wave, exact for full tiles; after a partial tile everything is waited for),
+// and the epilogue's stores drain while k-tile 0 computes.
+template <int BM, int BN, int EPI, bool PERS = false>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   if constexpr (EPI == EPI_F32) {
     if (gridDim.y > 1) {  // k split: this grid row's slice of K and its output slab
@@ -489,13 +564,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   // an XCD runs at once write longer runs of each logits row (measured on
   // the depth-12 LM head: 2.24 ms with 8, 2.18 with 4, 1.98 with 2)
   constexpr bool LOGITS = EPI == EPI_LOGITS || EPI == EPI_LOSS || EPI == EPI_LOGITS_BF16;
-  tile_origin<BM, BN, LOGITS ? 2 : 4>(g, m0, n0);
+  constexpr int GM = LOGITS ? 2 : 4;
+  int tile = blockIdx.x;
+  tile_origin<BM, BN, GM>(g, tile, m0, n0);
 
   f32x16 acc[TN][TM];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = (f32x16){};
+      for (int j = 0; j < TM; ++j) acc[i][j] = (f32x16){};
+  };
+  zero_acc();
 
   const int KT = g.K / BK;
   const int c32 = lane & 31, hi = lane >> 5;
@@ -573,24 +653,27 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   const int lc8 = ((lane & 3) ^ (lane >> 4)) << 3;
   int off[NI], drow[NI];
   const bf16 *base[NI];
+  auto operands = [&](int tm0, int tn0) {  // this wave's load sources for the tile at (tm0, tn0)
 #pragma unroll
-  for (int p = 0; p < NI; ++p) {
-    if (grp == 0) {
-      const int row = 16 * (w4 + 4 * p);
-      drow[p] = row;
-      base[p] = (const bf16 *)g.A;
-      off[p] = min(m0 + row + lrow, g.M - 1) * (int)g.lda + lc8;
-    } else {
-      const int row = min(16 * (w4 + 4 * p), BN - 16);
-      drow[p] = BM + row;
-      const int nb = min(n0 + row, g.N - 16);
-      int first;
-      if (nb < g.n1) { base[p] = (const bf16 *)g.W0; first = 0; }
-      else if (nb < g.n2) { base[p] = (const bf16 *)g.W1; first = g.n1; }
-      else { base[p] = (const bf16 *)g.W2; first = g.n2; }
-      off[p] = (nb - first + lrow) * (int)g.ldw + lc8;
+    for (int p = 0; p < NI; ++p) {
+      if (grp == 0) {
+        const int row = 16 * (w4 + 4 * p);
+        drow[p] = row;
+        base[p] = (const bf16 *)g.A;
+        off[p] = min(tm0 + row + lrow, g.M - 1) * (int)g.lda + lc8;
+      } else {
+        const int row = min(16 * (w4 + 4 * p), BN - 16);
+        drow[p] = BM + row;
+        const int nb = min(tn0 + row, g.N - 16);
+        int first = 0;
+        if (LOGITS || nb < g.n1) base[p] = (const bf16 *)g.W0;  // the LM head is one weight
+        else if (nb < g.n2) { base[p] = (const bf16 *)g.W1; first = g.n1; }
+        else { base[p] = (const bf16 *)g.W2; first = g.n2; }
+        off[p] = (nb - first + lrow) * (int)g.ldw + lc8;
+      }
     }
-  }
+  };
+  operands(m0, n0);
   auto dma1 = [&](int p, int kt, int half, bf16 *H) {
     dma16(base[p] + off[p] + kt * BK + half * HK, &H[drow[p] * HK]);
   };
@@ -598,15 +681,25 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < NI; ++p) dma1(p, kt, half, H);
   };
+  // Stores per wave in the persistent kernel's epilogue (a lower bound): the
+  // (max, sum exp) partials of its TM row blocks, plus the logits themselves.
+  constexpr int SN = EPI == EPI_LOGITS ? TM * (1 + 4 * TN) : TM;
+  static_assert(!PERS || ((EPI == EPI_LOGITS || EPI == EPI_LOSS) && TN == 2 && !WIDE && 2 * NI + SN < 64),
+                "persistent kernel: LM-head epilogues on 64-column wave tiles");
+  // follow: k-tile 0 of a tile whose first loads were issued before the
+  // previous tile's epilogue stores
+  bool follow = false;
   // One k-tile: c0, c1 its halves; n1 the half 1 of the other buffer.
   // D1: k-tile t+1 exists; D0: k-tile t+2 exists.  STEADY: both, known at
   // compile time; otherwise tested (the last two or three k-tiles).
   auto ktile = [&](auto steady, int kt, bf16 *c0, bf16 *c1, bf16 *n1) {
     constexpr bool STEADY = decltype(steady)::value;
     const bool D1 = STEADY || kt + 1 < KT, D0 = STEADY || kt + 2 < KT;
+    const bool fz = PERS && follow && kt == 0;
     lfrag(c0);
     wait_lds();
-    if (D1) wait_vm<NI>();  // half 1 of k-tile t (half 0 of t+1 may be in flight)
+    if (fz) wait_vm<NI + SN>();  // as below, with the previous tile's stores behind
+    else if (D1) wait_vm<NI>();  // half 1 of k-tile t (half 0 of t+1 may be in flight)
     else wait_vm<0>();
     bar();
     compute([&](int q) {
@@ -615,7 +708,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     bar();
     lfrag(c1);
     wait_lds();
-    if (D1) wait_vm<NI>();  // half 0 of k-tile t+1 (half 1 of t+1 may be in flight)
+    if (fz) wait_vm<NI + SN>();
+    else if (D1) wait_vm<NI>();  // half 0 of k-tile t+1 (half 1 of t+1 may be in flight)
     bar();
     compute([&](int q) {
       if (D0) dma1(q, kt + 2, 0, c0);
@@ -635,6 +729,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
   }
   bar();
   if (grp == 1) bar();
+  // EPI_LOSS, persistent: the target columns of the wave's rows (less its
+  // first column), loaded as the tile starts, so that their wait does not
+  // fall after the next tile's first loads (it would cover those too).
+  int tcol[TM];
+  for (;;) {
+  if constexpr (PERS)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      tcol[j] = -1;
+      if constexpr (EPI == EPI_LOSS)
+        tcol[j] = g.targets[min(m0 + wm * WM + 32 * j + c32, g.M - 1)] - (n0 + wn * WN);
+    }
   int kt = 0;
   for (; kt + 3 < KT; kt += 2) {
     ktile(std::true_type{}, kt, h00, h01, h11);
@@ -645,11 +751,52 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g) {
     ktile(std::false_type{}, kt + 1, h10, h11, h01);
   }
   if (kt < KT) ktile(std::false_type{}, kt, h00, h01, h11);
+  if constexpr (PERS) {
+    // Both groups' LDS reads of this tile are done (group 0 past the barrier
+    // that ends group 1's last load phase, group 1 past its own).  The next
+    // tile's k-tile 0 and half 0 of k-tile 1 go into h00, h01, h10; the
+    // epilogue stages through h11 (waves 0-3) and hsp (waves 4-7).  KT >= 2.
+    __shared__ float hsp[4 * 16 * kStagePitch];
+    const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+    if constexpr (EPI == EPI_LOSS)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) asm volatile("" ::"v"(tcol[j]));  // their wait comes before the loads below
+    int next = tile + gridDim.x;
+    const bool more = next < ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    if (more) {
+      int tm0, tn0;
+      tile_origin<BM, BN, GM>(g, next, tm0, tn0);
+      operands(tm0, tn0);
+      dma(0, 0, h00);
+      dma(0, 1, h01);
+      dma(1, 0, h10);
+    }
+    float *stg = (wave < 4 ? (float *)h11 : hsp) + (wave & 3) * 16 * kStagePitch;
+    if constexpr (PERS) tile_epilogue_lm16<TM, EPI>(g, acc, m0 + wm * WM, n0 + wn * WN, c32, hi, lane, stg, tcol);
+    if (!more) return;
+    // The next tile's origin and load sources are computed again rather
+    // than kept through the epilogue (the opaque copy of next stops the
+    // compiler from reusing the first computation).
+    asm volatile("" : "+s"(next));
+    tile_origin<BM, BN, GM>(g, next, m0, n0);
+    operands(m0, n0);
+    zero_acc();
+    if (full) wait_vm<2 * NI + SN>();  // k-tile 0 half 0; the rest and the stores may be in flight
+    else wait_vm<0>();
+    // every wave's staging reads are done before k-tile 0 refills h11
+    bar();
+    if (grp == 1) bar();
+    follow = full;
+    tile = next;
+    continue;
+  }
+  break;
+  }
   // Staging areas: 32 x 68 floats per wave, two waves per half object.  A
   // group reaches its epilogue only after both groups' last LDS reads
   // (group 0 after the barrier that ends group 1's last load phase), and no
   // DMA is in flight by then.
-  static_assert(2 * 32 * kStagePitch * 4 <= HR * HK * 2, "staging area");
+  static_assert(2 * 32 * kStagePitch * 4 <= HR * HK * 2 && (!PERS || 4 * 16 * kStagePitch * 4 <= HR * HK * 2), "staging area");
   bf16 *const sbuf = wave < 2 ? h00 : wave < 4 ? h01 : wave < 6 ? h10 : h11;
   if constexpr (EPI == EPI_QKV) {
     // 16 KB per wave: two waves per half object
@@ -794,6 +941,20 @@ void launch_rows(const GemmArgs &g, int ks, long long slab, hipStream_t s) {
   else launch_rows_d<EPI, 64>(g, ks, slab, s);
 }
 
+// Compute units of the current device, rounded down to a multiple of the 8
+// XCDs (the persistent GEMM's grid).
+int persistent_grid() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess)
+      cus = 256;
+    n = std::max(8, cus / 8 * 8);
+  }
+  return n;
+}
+
 template <int EPI>
 void launch_big(const GemmArgs &g, hipStream_t s) {
   constexpr int BM = 256;
@@ -801,6 +962,15 @@ void launch_big(const GemmArgs &g, hipStream_t s) {
                 "partial width");
   const int tm = (g.M + BM - 1) / BM;
   const int t256 = tm * ((g.N + 255) / 256);
+  if constexpr (EPI == EPI_LOGITS || EPI == EPI_LOSS) {
+    // the LM head: many tiles per CU, so a persistent grid overlaps each
+    // tile's epilogue with the next tile's first loads (needs 2+ k-tiles)
+    const int grid = persistent_grid();
+    if (t256 > grid && g.K >= 2 * BK) {
+      gemm_pp_kernel<BM, 256, EPI, true><<<grid, 512, 0, s>>>(g);
+      return;
+    }
+  }
   if constexpr (EPI == EPI_RESID || EPI == EPI_F32) {
     // 192-column tiles when N splits into them and they take fewer
     // column-rounds over the 256 CUs (d = 768: 256 tiles instead of 192)

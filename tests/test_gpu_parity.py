@@ -194,6 +194,36 @@ def test_small_bf16_loss(n_layer, n_head, lens):
     assert m0 == 0.0
 
 
+def test_lm_head_persistent_ragged_tiles():
+    """The LM head's persistent grid (one workgroup per CU walking the tiles,
+    each tile's first loads issued before the previous tile's epilogue):
+    2229 rows and a 16512-entry vocabulary give 9 x 65 = 585 tiles of
+    256 x 256, with a partial last row of tiles and a half-empty last column
+    of tiles, so workgroups take two or three tiles and some follow a
+    partial one.  Logits, lse and softmax against the oracle; the fused
+    cross-entropy against the same prefill's logits."""
+    cfg = wl.small_model(1, 1, vocab=16512)
+    w = wl.ragged_prefill(cfg, [1500, 700, 29], seed=11)
+    W, dm = device_model(cfg)
+    logits, lse, probs = gpu_prefill(dm, w.tokens, w.seqlens, want_probs=True)
+    ref = np.concatenate(oracle.prefill(cfg, W, w.tokens, w.seqlens)[0])
+    st = logit_stats(logits, ref)
+    print(st)
+    assert st["max_abs"] <= 3e-2
+    assert st["rows_explained"], st
+    lg = logits.astype(np.float64)
+    np.testing.assert_allclose(lse, oracle.logsumexp(lg), atol=2e-5)
+    np.testing.assert_allclose(probs, oracle.softmax(lg), atol=2e-6)
+    tg = w.next_token_targets()
+    tg[7] = cfg.vocab - 1          # the last column, in the half-empty tile
+    tg[2228 - 1] = 16384           # the first column of that tile
+    loss, lse2, _ = gpu_loss(dm, w.tokens, w.seqlens, tg)
+    np.testing.assert_array_equal(lse, lse2)
+    rows = np.nonzero(tg >= 0)[0]
+    own = lse2[rows].astype(np.float64) - logits[rows, tg[rows]]
+    np.testing.assert_allclose(loss[rows], own, rtol=0, atol=2e-6)
+
+
 @pytest.mark.parametrize("temperature", [0.0, 0.7])
 def test_small_bf16_decode_teacher_forced(temperature):
     """Prefill ragged prompts into the paged cache, decode 40 steps crossing
