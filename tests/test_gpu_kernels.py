@@ -37,6 +37,10 @@ GEMM_SHAPES = [
     # 64-column tiles: 160 and 512 of them
     (48, 10240, 768),
     (8, 32768, 256),
+    # more 256x256 tiles than CUs, ragged in M and N: 9 x 33 tiles of 2
+    # k-tiles, 6 x 50 of 5
+    (2100, 8320, 128),
+    (1300, 12800, 320),
 ]
 
 
